@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the quantized-KV hot path on one MI355X.
+
+Workload (default): batch 1, 24 query heads, 4 KV heads, head_dim 256, an int8
+cache with per-row absmax scales holding 65,536 tokens, one query token.  One
+step = kvq_append of the new token's K/V row + split-KV decode + fixed-order
+combine, i.e. the whole hot path.  Steps rotate over 16 layer caches (16 x
+130 MiB) so the 256 MB Infinity Cache cannot serve the KV bytes, and run as
+HIP-graph replays of 16 steps.  Inputs are seeded synthetic tensors already
+resident in HBM when the timed region starts.
+
+Prints ONE JSON line.  `value` is the effective KV-read bandwidth of the whole
+step: algorithmic bytes (K and V codes plus per-row scales of every cached
+token) / wall time per step.  `roofline` rates the dominant kernel (the split
+decode) by its own duration, measured with HIP events on its stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode µs/step + KV-read HBM GB/s, Hq24/Hkv4/D256 int8 at 64K ctx"
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_decode_int8_64k_traffic.json")
+KERNEL_SOURCES = ["quantized_kv_cache_02_amd/csrc/kvq_split.hip",
+                  "quantized_kv_cache_02_amd/csrc/kvq_device.h",
+                  "quantized_kv_cache_02_amd/csrc/kvq_params.h"]
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_per_launch_alg: float):
+    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_digest") != kernel_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(dtype: str, ctx: int, hkv: int, d: int) -> int:
+    row = d if dtype in ("int8", "fp8") else d // 2
+    return 2 * ctx * hkv * (row + 4)
+
+
+def build_layers(kvq, torch, w, layers: int, dev):
+    """`layers` caches of the workload, each quantized by kvq_append from the same rows."""
+    k = w.k.to(dev)
+    v = w.v.to(dev)
+    caches = []
+    for _ in range(layers):
+        c = kvq.KVCache(w.dtype, w.mode, w.Hkv, w.D, w.block_size, w.num_blocks, device=dev)
+        kvq.append(c, k, v, torch.zeros(w.B, dtype=torch.int32, device=dev))
+        caches.append(c)
+    torch.cuda.synchronize()
+    return caches, k[:, -1:].contiguous(), v[:, -1:].contiguous()
+
+
+def time_config(kvq, torch, ki, dtype: str, ctx: int, layers: int, steps: int, warmup: int, dev):
+    w = ki.make_workload(3, ctx=ctx, dtype=dtype)
+    caches, kn, vn = build_layers(kvq, torch, w, layers, dev)
+    q = w.q.to(dev)
+    lens = torch.from_numpy(w.lens).to(dev)
+    pos = (lens - 1).contiguous()
+    B, Tq, Hq, D = q.shape
+    ws = torch.empty(kvq.workspace_bytes(caches[0], B, Hq, Tq, ctx), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    S = kvq.num_splits(caches[0], B, Hq, Tq, ctx)
+
+    def step(c, s):
+        kvq.append(c, kn, vn, pos, stream=s)
+        kvq.split_decode(c, q, lens, ctx, w.sm_scale, ws, stream=s)
+        kvq.combine(c, B, Hq, Tq, ctx, ws, out, stream=s)
+
+    def split_only(c, s):
+        kvq.split_decode(c, q, lens, ctx, w.sm_scale, ws, stream=s)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graphs = {}
+    with torch.cuda.stream(stream):
+        for c in caches:  # warm the kernels once outside capture
+            step(c, stream)
+        for name, fn in (("step", step), ("split", split_only)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for c in caches:
+                    fn(c, stream)
+            graphs[name] = g
+    torch.cuda.synchronize()
+
+    reps = max(1, (steps + layers - 1) // layers)
+    wreps = max(1, (warmup + layers - 1) // layers)
+    with torch.cuda.stream(stream):
+        for _ in range(wreps):
+            graphs["step"].replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(reps):
+            graphs["step"].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        step_ms = e0.elapsed_time(e1) / (reps * layers)
+        # dominant kernel alone: back-to-back split launches, timed on their stream
+        sreps = max(4, reps // 2)
+        graphs["split"].replay()
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(sreps):
+            graphs["split"].replay()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        split_ms = s0.elapsed_time(s1) / (sreps * layers)
+    nbytes = algorithmic_bytes(dtype, ctx, w.Hkv, w.D)
+    return dict(ctx=ctx, dtype=dtype, steps=reps * layers, warmup=wreps * layers, step_ms=step_ms,
+                split_ms=split_ms, wall_s=wall_s, bytes=nbytes, splits=S, workload=w)
+
+
+def cpu_baseline(ki, w, seconds: float):
+    """The oracle as it stands on the same workload: one step = dequantize the
+    layer cache to fp32, then fp64 attention.  Runs whole steps until `seconds`
+    of CPU time have passed (at least one)."""
+    import oracle
+
+    oracle.build(force=False)
+    ocache = oracle.build_cache(w)
+    qb = ki.bf16_bits(w.q)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        K, V = ocache.dequantize(w.lens)
+        oracle.attend(qb, K, V, w.lens, w.sm_scale, None, w.Hkv)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or el / n * (n + 1) > 2.5 * seconds:
+            break
+    return n, el / n, oracle.num_threads()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=640)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--ctx", type=int, default=65536)
+    ap.add_argument("--dtype", default="int8", choices=["int8", "int4"])
+    ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", default="", help="also time the context sweep for int8 and int4 "
+                                                "and write the lines to this JSON-lines file")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 20 times "
+                         "(reference dispatch for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the decode path is not run across "
+              "GPUs (see DESIGN.md for how it would shard). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kvq_inputs as ki
+    import quantized_kv_cache_02_amd as kvq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    kvq.lib()
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "dispatches": 20}))
+        return
+
+    r = time_config(kvq, torch, ki, args.dtype, args.ctx, args.layers, args.steps, args.warmup, dev)
+    w = r.pop("workload")
+    achieved = r["bytes"] / (r["split_ms"] * 1e-3) / 1e9
+    value = r["bytes"] / (r["step_ms"] * 1e-3) / 1e9
+    traffic = measured_traffic(r["bytes"])
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": r["steps"],
+        "warmup": r["warmup"],
+        "ms_per_step": round(r["step_ms"], 5),
+        "us_per_step": round(r["step_ms"] * 1e3, 2),
+        "split_kernel_us": round(r["split_ms"] * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA, f32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": f"decode B1 Hq24 Hkv4 D256, {args.dtype} per-row absmax cache, "
+                        f"{args.ctx}-token context, 1 query token, {args.layers} layer caches rotated",
+            "cache_dtype": args.dtype,
+            "context": args.ctx,
+            "splits": r["splits"],
+            "algorithmic_bytes_per_step": r["bytes"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        n, sec, threads = cpu_baseline(ki, w, args.cpu_seconds)
+        line["cpu_baseline"] = {
+            "value": round(r["bytes"] / sec / 1e9, 4),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} oracle steps (dequantize the {args.ctx}-token layer cache to fp32, "
+                      f"then fp64 attention) on the same workload, {sec * 1e3:.0f} ms/step",
+        }
+    print(json.dumps(line), flush=True)
+
+    if args.sweep:
+        with open(args.sweep, "w") as f:
+            for dt in ("int8", "int4"):
+                for ctx in ki.SWEEP_CTX:
+                    layers = args.layers if ctx <= 65536 else 8
+                    s = time_config(kvq, torch, ki, dt, ctx, layers, max(64, args.steps // 4),
+                                    args.warmup, dev)
+                    s.pop("workload")
+                    s["step_GBps"] = s["bytes"] / (s["step_ms"] * 1e-3) / 1e9
+                    s["split_GBps"] = s["bytes"] / (s["split_ms"] * 1e-3) / 1e9
+                    s["split_frac_of_peak"] = s["split_GBps"] / PEAK_HBM_GBPS
+                    f.write(json.dumps(s) + "\n")
+                    f.flush()
+                    print(f"[sweep] {dt} ctx={ctx} step {s['step_ms'] * 1e3:.2f} us "
+                          f"split {s['split_ms'] * 1e3:.2f} us {s['split_GBps']:.0f} GB/s",
+                          file=sys.stderr, flush=True)
+                    torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

@@ -203,7 +203,7 @@ def make_workload(cfg: int, ctx: Optional[int] = None, dtype: Optional[str] = No
         table = _paged_table(b, max_blocks, s0 + 4)
         num_blocks = b * max_blocks
     else:
-        block_size = lmax
+        block_size = max(16, (lmax + 15) // 16 * 16)  # contiguous capacity
         table = None
         num_blocks = b
 
@@ -247,7 +247,7 @@ def random_workload(seed: int, B: int, Hkv: int, G: int, D: int, Tq: int, lens,
     v = randn_bf16((B, max(lmax, 1), Hkv, D), seed + 2)
     if block_size is None:
         table = None
-        bs = max(lmax, 16)
+        bs = max(16, (lmax + 15) // 16 * 16)  # contiguous capacity, a multiple of 16
         nb = B
     else:
         bs = block_size

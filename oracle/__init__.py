@@ -64,6 +64,8 @@ def lib():
         L.kvo_attend.restype = None
         L.kvo_cache_bytes_per_token.argtypes = [I, I, I, I, I]
         L.kvo_cache_bytes_per_token.restype = D
+        L.kvo_num_threads.argtypes = []
+        L.kvo_num_threads.restype = I
         _lib = L
     return _lib
 
@@ -189,6 +191,10 @@ def attend(q_bits: np.ndarray, K: np.ndarray, V: np.ndarray, lens, scale: float,
     lib().kvo_attend(_p(q_bits), _p(K), _p(V), B, Tq, Hq, hkv, D, K.shape[2], _p(lens),
                      float(scale), _p(sk), _p(out), _p(lse))
     return out, lse
+
+
+def num_threads() -> int:
+    return lib().kvo_num_threads()
 
 
 def cache_bytes_per_token(bits: int, per_row_scales: bool, layers: int, Hkv: int, D: int) -> float:

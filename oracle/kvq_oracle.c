@@ -316,3 +316,15 @@ double kvo_cache_bytes_per_token(int bits, int per_row_scales, int layers, int H
   double row = (double)D * bits / 8.0 + (per_row_scales ? 4.0 : 0.0);
   return 2.0 * layers * Hkv * row;
 }
+
+/* Threads the OpenMP loops above use (for reporting the CPU baseline). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int kvo_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,112 @@
+// kvq_device.h -- gfx950 device helpers: bf16 handling, wave reductions,
+// MFMA wrappers and the in-register code -> fp16 unpackers used by the decode
+// kernel.  GPU code only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_params.h"
+
+namespace kvq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 for finite inputs.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Byte permute of the 8 bytes {hi:lo}: selector byte k picks output byte k
+// (0..3 = bytes of lo, 4..7 = bytes of hi).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Packed fp16 add (v_pk_add_f16).  16-bit packed math only; no packed fp32.
+__device__ __forceinline__ uint32_t pk_add_h(uint32_t a, half2_t b) {
+  return as_u32(as_h2(a) + b);
+}
+
+// ---------------------------------------------------------------------------
+// Code -> fp16 unpacking.  The integer grids use one identity: the fp16 with
+// bit pattern 0x64XY equals 1024 + 0xXY exactly (fp16 spacing at 1024 is 1).
+//   int8: XY = c ^ 0x80 = c + 128, so 0x64XY - 1152 = c.
+//   int4: XY = (n ^ 8) << 4 = 16 (n + 8), so 0x64XY - 1152 = 16 n; the factor 16
+//         is folded into the scales by the caller.
+// fp8 E4M3FN uses the hardware converter, exact for every finite code.
+// ---------------------------------------------------------------------------
+
+constexpr uint32_t kMagic = 0x64646464u;
+
+// int8: one dword of 4 codes (c0..c3, low byte first) -> two packed fp16
+// dwords (c0, c1), (c2, c3).
+__device__ __forceinline__ void int8x4_to_h(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  uint32_t x = w ^ 0x80808080u;
+  lo = pk_add_h(perm(kMagic, x, 0x04010400u), bias);
+  hi = pk_add_h(perm(kMagic, x, 0x04030402u), bias);
+}
+
+// int4: one dword of 8 nibbles n0..n7 (n0 = low nibble of byte 0) -> four
+// packed fp16 dwords holding 16*n in the order (n0,n2) (n4,n6) (n1,n3) (n5,n7).
+__device__ __forceinline__ void int4x8_to_h(uint32_t w, uint32_t out[4]) {
+  const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  uint32_t x = w ^ 0x88888888u;
+  uint32_t ev = (x << 4) & 0xF0F0F0F0u;  // 16*(n_even+8) in each byte
+  uint32_t od = x & 0xF0F0F0F0u;         // 16*(n_odd+8)
+  out[0] = pk_add_h(perm(kMagic, ev, 0x04010400u), bias);
+  out[1] = pk_add_h(perm(kMagic, ev, 0x04030402u), bias);
+  out[2] = pk_add_h(perm(kMagic, od, 0x04010400u), bias);
+  out[3] = pk_add_h(perm(kMagic, od, 0x04030402u), bias);
+}
+
+// fp8: one dword of 4 codes -> (c0, c1), (c2, c3) as packed fp16.
+__device__ __forceinline__ void fp8x4_to_h(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  hi = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (lane layouts checked on gfx950):
+//   16x16x16 f16: A lane l = row l%16, k 4(l/16)+e;  B lane l = col l%16,
+//                 k 4(l/16)+e;  C lane l = rows 4(l/16)+e, col l%16.
+//   16x16x32 f16: as above with k 8(l/16)+e for A and B.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float4_t mfma16(half4_t a, half4_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma32(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half4_t u2_to_h4(uint32_t a, uint32_t b) {
+  u32x2_t v = {a, b};
+  return __builtin_bit_cast(half4_t, v);
+}
+__device__ __forceinline__ half8_t u4_to_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4_t v = {a, b, c, d};
+  return __builtin_bit_cast(half8_t, v);
+}
+
+}  // namespace kvq

@@ -1,0 +1,306 @@
+// kvq_host.cpp -- the C ABI of libkvq (include/kvq.h): host-side validation,
+// static grid / workspace sizing, kernel launches.  Never synchronizes, never
+// allocates, never reads device memory, so every entry point can be captured
+// into a HIP graph.
+
+#include "kvq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kvq_params.h"
+
+namespace {
+
+using kvq::CacheArgs;
+
+constexpr int kMaxGroup = 8;     // query heads per KV head
+constexpr int kMaxQTokens = 8;   // query tokens per sequence (1 + 7 drafts)
+constexpr int kTargetWorkgroups = 512;
+constexpr int kMinTilesPerSplit = 8;
+constexpr int kMaxSplits = 4096;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_cache(const kvq_cache* c) {
+  if (c == nullptr) return KVQ_EINVAL;
+  if (c->dtype != KVQ_INT8 && c->dtype != KVQ_INT4 && c->dtype != KVQ_FP8_E4M3FN)
+    return KVQ_EUNSUPPORTED;
+  if (c->scale_mode != KVQ_PER_ROW && c->scale_mode != KVQ_PER_TENSOR &&
+      c->scale_mode != KVQ_PER_CHANNEL)
+    return KVQ_EUNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return KVQ_EUNSUPPORTED;
+  if (c->num_kv_heads < 1 || c->block_size < 16 || c->block_size % 16 != 0 || c->num_blocks < 1)
+    return KVQ_EINVAL;
+  if (c->k_codes == nullptr || c->v_codes == nullptr || c->k_scales == nullptr ||
+      c->v_scales == nullptr)
+    return KVQ_EINVAL;
+  if (!aligned16(c->k_codes) || !aligned16(c->v_codes) || !aligned16(c->k_scales) ||
+      !aligned16(c->v_scales))
+    return KVQ_EINVAL;
+  return KVQ_OK;
+}
+
+CacheArgs cache_args(const kvq_cache* c, const int32_t* table, int32_t max_blocks) {
+  CacheArgs a;
+  a.k_codes = static_cast<uint8_t*>(c->k_codes);
+  a.v_codes = static_cast<uint8_t*>(c->v_codes);
+  a.k_scales = c->k_scales;
+  a.v_scales = c->v_scales;
+  a.Hkv = c->num_kv_heads;
+  a.block_size = c->block_size;
+  a.num_blocks = c->num_blocks;
+  a.block_table = table;
+  a.max_blocks = table ? max_blocks : 0;
+  return a;
+}
+
+struct DecodeShape {
+  int G, R, RB, S;
+};
+
+// Static decode shape: grouping, query rows, row blocks and the split count S,
+// a pure function of (batch, Hkv, max_seq_len) so that graphs and workspaces
+// sized once stay valid.  Independent of the cache layout.
+int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int32_t max_seq_len,
+                 DecodeShape* sh) {
+  int st = check_cache(c);
+  if (st != KVQ_OK) return st;
+  if (batch < 1 || hq < 1 || tq < 1 || max_seq_len < 1) return KVQ_EINVAL;
+  if (hq % c->num_kv_heads != 0) return KVQ_EINVAL;
+  const int G = hq / c->num_kv_heads;
+  if (G > kMaxGroup || tq > kMaxQTokens) return KVQ_EUNSUPPORTED;
+  if (batch > 65535 || c->num_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+  const int64_t ntiles = ((int64_t)max_seq_len + 15) / 16;
+  const int64_t pairs = (int64_t)batch * c->num_kv_heads;
+  int64_t S = (kTargetWorkgroups + pairs - 1) / pairs;
+  int64_t cap = ntiles / kMinTilesPerSplit;
+  if (cap < 1) cap = 1;
+  if (S > cap) S = cap;
+  if (S > kMaxSplits) S = kMaxSplits;
+  sh->G = G;
+  sh->R = G * tq;
+  sh->RB = (sh->R + 15) / 16;
+  sh->S = (int)S;
+  return KVQ_OK;
+}
+
+// Layout of the sequences in the cache: contiguous (no table) or paged.
+int check_layout(const kvq_cache* c, int32_t batch, int32_t max_seq_len, const int32_t* table,
+                 int32_t max_blocks) {
+  if (table == nullptr) {
+    if (c->num_blocks < batch || max_seq_len > c->block_size) return KVQ_EINVAL;
+  } else {
+    if (max_blocks < 1) return KVQ_EINVAL;
+    if ((int64_t)max_seq_len > (int64_t)max_blocks * c->block_size) return KVQ_EINVAL;
+  }
+  return KVQ_OK;
+}
+
+size_t workspace_size(const kvq_cache* c, int32_t batch, const DecodeShape& sh) {
+  const size_t rows = (size_t)batch * c->num_kv_heads * sh.R * sh.S;
+  // o [rows, D] then m [rows] then l [rows], each region 256-byte aligned
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return up(rows * c->head_dim * 4) + 2 * up(rows * 4);
+}
+
+void workspace_ptrs(void* ws, const kvq_cache* c, int32_t batch, const DecodeShape& sh, float** o,
+                    float** m, float** l) {
+  const size_t rows = (size_t)batch * c->num_kv_heads * sh.R * sh.S;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* base = static_cast<char*>(ws);
+  *o = reinterpret_cast<float*>(base);
+  *m = reinterpret_cast<float*>(base + up(rows * c->head_dim * 4));
+  *l = reinterpret_cast<float*>(base + up(rows * c->head_dim * 4) + up(rows * 4));
+}
+
+hipError_t dispatch_split(int dt, int md, int D, int RB, const kvq::SplitArgs& a, int B,
+                          hipStream_t st) {
+#define KVQ_CASE(DT, MD) \
+  if (dt == DT && md == MD) return kvq::launch_split_##DT##_##MD(D, RB, a, B, st);
+  KVQ_CASE(1, 1)
+  KVQ_CASE(1, 2)
+  KVQ_CASE(1, 3)
+  KVQ_CASE(2, 1)
+  KVQ_CASE(2, 2)
+  KVQ_CASE(2, 3)
+  KVQ_CASE(3, 1)
+  KVQ_CASE(3, 2)
+  KVQ_CASE(3, 3)
+#undef KVQ_CASE
+  return hipErrorInvalidValue;
+}
+
+int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int32_t tq,
+               const int32_t* seq_lens, int32_t max_seq_len, float scale, const int32_t* table,
+               int32_t max_blocks, void* ws, size_t ws_bytes, void* stream) {
+  DecodeShape sh;
+  int st = decode_shape(c, batch, hq, tq, max_seq_len, &sh);
+  if (st != KVQ_OK) return st;
+  st = check_layout(c, batch, max_seq_len, table, max_blocks);
+  if (st != KVQ_OK) return st;
+  if (q == nullptr || seq_lens == nullptr || ws == nullptr || !aligned16(q) || !aligned16(ws))
+    return KVQ_EINVAL;
+  if (ws_bytes < workspace_size(c, batch, sh)) return KVQ_EINVAL;
+  kvq::SplitArgs a;
+  a.c = cache_args(c, table, max_blocks);
+  a.q = static_cast<const uint16_t*>(q);
+  a.seq_lens = seq_lens;
+  a.Hq = hq;
+  a.Tq = tq;
+  a.G = sh.G;
+  a.R = sh.R;
+  a.max_seq_len = max_seq_len;
+  a.S = sh.S;
+  a.sm_scale = scale;
+  workspace_ptrs(ws, c, batch, sh, &a.ws_o, &a.ws_m, &a.ws_l);
+  hipError_t e = dispatch_split(c->dtype, c->scale_mode, c->head_dim, sh.RB, a, batch,
+                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
+
+int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int32_t max_seq_len,
+                 const float* sink, void* out, const void* ws, size_t ws_bytes, void* stream) {
+  DecodeShape sh;
+  int st = decode_shape(c, batch, hq, tq, max_seq_len, &sh);
+  if (st != KVQ_OK) return st;
+  if (out == nullptr || ws == nullptr || !aligned16(out) || !aligned16(ws)) return KVQ_EINVAL;
+  if (ws_bytes < workspace_size(c, batch, sh)) return KVQ_EINVAL;
+  kvq::CombineArgs a;
+  float *o, *m, *l;
+  workspace_ptrs(const_cast<void*>(ws), c, batch, sh, &o, &m, &l);
+  a.ws_o = o;
+  a.ws_m = m;
+  a.ws_l = l;
+  a.v_static = c->scale_mode == KVQ_PER_ROW ? nullptr : c->v_scales;
+  a.sink = sink;
+  a.out = static_cast<uint16_t*>(out);
+  a.Hkv = c->num_kv_heads;
+  a.Hq = hq;
+  a.Tq = tq;
+  a.G = sh.G;
+  a.R = sh.R;
+  a.S = sh.S;
+  hipError_t e = kvq::launch_combine(c->scale_mode, c->head_dim, a, batch,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t batch, int32_t tokens,
+               const int32_t* positions, const int32_t* block_table, int32_t max_blocks,
+               void* stream) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (k == nullptr || v == nullptr || positions == nullptr || batch < 1 || tokens < 1)
+    return KVQ_EINVAL;
+  if (!aligned16(k) || !aligned16(v)) return KVQ_EINVAL;
+  int64_t capacity;
+  if (block_table == nullptr) {
+    if (cache->num_blocks < batch) return KVQ_EINVAL;
+    capacity = cache->block_size;
+  } else {
+    if (max_blocks < 1) return KVQ_EINVAL;
+    capacity = (int64_t)max_blocks * cache->block_size;
+  }
+  if (capacity > INT32_MAX) return KVQ_EUNSUPPORTED;
+  kvq::AppendArgs a;
+  a.c = cache_args(cache, block_table, max_blocks);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.positions = positions;
+  a.B = batch;
+  a.Tn = tokens;
+  a.capacity = (int32_t)capacity;
+  hipError_t e = kvq::launch_append(cache->dtype, cache->scale_mode, cache->head_dim, a,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
+
+int32_t kvq_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                       int32_t q_tokens, int32_t max_seq_len) {
+  DecodeShape sh;
+  int st = decode_shape(cache, batch, num_q_heads, q_tokens, max_seq_len, &sh);
+  return st == KVQ_OK ? sh.S : st;
+}
+
+size_t kvq_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                           int32_t q_tokens, int32_t max_seq_len) {
+  DecodeShape sh;
+  if (decode_shape(cache, batch, num_q_heads, q_tokens, max_seq_len, &sh) != KVQ_OK) return 0;
+  return workspace_size(cache, batch, sh);
+}
+
+int kvq_split_decode(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                     int32_t q_tokens, const int32_t* seq_lens, int32_t max_seq_len,
+                     float softmax_scale, const int32_t* block_table, int32_t max_blocks,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return split_impl(cache, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, softmax_scale,
+                    block_table, max_blocks, workspace, workspace_bytes, stream);
+}
+
+int kvq_combine(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int32_t q_tokens,
+                int32_t max_seq_len, const float* head_sink, void* out, const void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return combine_impl(cache, batch, num_q_heads, q_tokens, max_seq_len, head_sink, out, workspace,
+                      workspace_bytes, stream);
+}
+
+int kvq_decode_attend(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                      int32_t q_tokens, const int32_t* seq_lens, int32_t max_seq_len,
+                      float softmax_scale, const float* head_sink, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (out == nullptr || !aligned16(out)) return KVQ_EINVAL;
+  int st = split_impl(cache, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, softmax_scale,
+                      nullptr, 0, workspace, workspace_bytes, stream);
+  if (st != KVQ_OK) return st;
+  return kvq_combine(cache, batch, num_q_heads, q_tokens, max_seq_len, head_sink, out, workspace,
+                     workspace_bytes, stream);
+}
+
+int kvq_paged_decode_attend(const kvq_cache* cache, const void* q, int32_t batch,
+                            int32_t num_q_heads, int32_t q_tokens, const int32_t* seq_lens,
+                            int32_t max_seq_len, float softmax_scale, const float* head_sink,
+                            const int32_t* block_table, int32_t max_blocks, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (block_table == nullptr) return KVQ_EINVAL;
+  if (out == nullptr || !aligned16(out)) return KVQ_EINVAL;
+  int st = split_impl(cache, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, softmax_scale,
+                      block_table, max_blocks, workspace, workspace_bytes, stream);
+  if (st != KVQ_OK) return st;
+  return kvq_combine(cache, batch, num_q_heads, q_tokens, max_seq_len, head_sink, out, workspace,
+                     workspace_bytes, stream);
+}
+
+size_t kvq_cache_bytes(int32_t dtype, int32_t scale_mode, int32_t num_kv_heads, int32_t head_dim,
+                       int64_t tokens) {
+  if (num_kv_heads < 1 || head_dim < 1 || tokens < 0) return 0;
+  size_t row;
+  switch (dtype) {
+    case KVQ_INT8:
+    case KVQ_FP8_E4M3FN: row = (size_t)head_dim; break;
+    case KVQ_INT4: row = (size_t)(head_dim + 1) / 2; break;
+    default: return 0;
+  }
+  if (scale_mode == KVQ_PER_ROW)
+    row += 4;
+  else if (scale_mode != KVQ_PER_TENSOR && scale_mode != KVQ_PER_CHANNEL)
+    return 0;
+  return 2 * (size_t)num_kv_heads * row * (size_t)tokens;
+}
+
+const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_EINVAL: return "KVQ_EINVAL: invalid argument";
+    case KVQ_EUNSUPPORTED: return "KVQ_EUNSUPPORTED: unsupported shape or type";
+    case KVQ_EHIP: return "KVQ_EHIP: HIP runtime error";
+    default: return "unknown kvq status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// kvq_params.h -- parameter blocks passed by value from the host launcher to
+// the HIP kernels, and the launcher entry points of each kernel family.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+enum : int { kInt8 = 1, kInt4 = 2, kFp8 = 3 };
+enum : int { kPerRow = 1, kPerTensor = 2, kPerChannel = 3 };
+
+// Tokens per decode tile: one MFMA M dimension (16 rows of K) per wavefront step.
+constexpr int kTile = 16;
+// Wavefronts per decode workgroup; each owns a private online-softmax state.
+constexpr int kWaves = 4;
+
+struct CacheArgs {
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float* k_scales;  // per-row array, or static table
+  float* v_scales;
+  int32_t Hkv;
+  int32_t block_size;
+  int32_t num_blocks;
+  const int32_t* block_table;  // nullptr: contiguous, sequence b owns block b
+  int32_t max_blocks;
+};
+
+struct AppendArgs {
+  CacheArgs c;
+  const uint16_t* k;  // bf16 [B, Tn, Hkv, D]
+  const uint16_t* v;
+  const int32_t* positions;  // [B]
+  int32_t B;
+  int32_t Tn;
+  int32_t capacity;  // tokens addressable per sequence
+};
+
+struct SplitArgs {
+  CacheArgs c;
+  const uint16_t* q;  // bf16 [B, Tq, Hq, D]
+  const int32_t* seq_lens;
+  int32_t Hq, Tq, G, R;  // R = G * Tq query rows per (sequence, KV head)
+  int32_t max_seq_len;
+  int32_t S;  // splits per (sequence, KV head)
+  float sm_scale;
+  float* ws_o;  // [B, Hkv, R, S, D]  normalized split outputs
+  float* ws_m;  // [B, Hkv, R, S]     split max logit (log2 units)
+  float* ws_l;  // [B, Hkv, R, S]     split normalizer
+};
+
+struct CombineArgs {
+  const float* ws_o;
+  const float* ws_m;
+  const float* ws_l;
+  const float* v_static;  // per-tensor [1] / per-channel [Hkv, D] / nullptr (per-row)
+  const float* sink;      // [Hq] or nullptr
+  uint16_t* out;          // bf16 [B, Tq, Hq, D]
+  int32_t Hkv, Hq, Tq, G, R, S;
+};
+
+hipError_t launch_append(int dtype, int mode, int D, const AppendArgs& a, hipStream_t st);
+hipError_t launch_split(int dtype, int mode, int D, int RB, const SplitArgs& a, int B,
+                        hipStream_t st);
+hipError_t launch_combine(int mode, int D, const CombineArgs& a, int B, hipStream_t st);
+
+// per-(dtype, mode) translation units of the split kernel
+#define KVQ_DECLARE_SPLIT(DT, MD) \
+  hipError_t launch_split_##DT##_##MD(int D, int RB, const SplitArgs& a, int B, hipStream_t st);
+KVQ_DECLARE_SPLIT(1, 1)
+KVQ_DECLARE_SPLIT(1, 2)
+KVQ_DECLARE_SPLIT(1, 3)
+KVQ_DECLARE_SPLIT(2, 1)
+KVQ_DECLARE_SPLIT(2, 2)
+KVQ_DECLARE_SPLIT(2, 3)
+KVQ_DECLARE_SPLIT(3, 1)
+KVQ_DECLARE_SPLIT(3, 2)
+KVQ_DECLARE_SPLIT(3, 3)
+#undef KVQ_DECLARE_SPLIT
+
+}  // namespace kvq

@@ -1,0 +1,533 @@
+// kvq_split.hip -- split-KV decode attention over a quantized (int8 / packed
+// int4 / fp8 E4M3FN) cache for gfx950.  Compiled once per (KVQ_DTYPE,
+// KVQ_MODE) pair; each translation unit instantiates head_dim x row-block
+// variants.
+//
+// Method (kernel page "kv-quant-attn", "Method"; ORT PR "[CUDA] PagedAttention:
+// quantized KV cache ...", "CUDA kernels": split-KV, block-table-aware decode
+// with on-the-fly dequantization):
+//   * one workgroup owns (sequence b, KV head, split s) and serves every query
+//     row of that KV head -- the G grouped query heads times the Tq query
+//     tokens -- from a single pass over the split's cached rows;
+//   * its 4 wavefronts take interleaved 16-token tiles and keep private
+//     online-softmax state (max, sum, accumulator) with no barrier or atomic in
+//     the loop; the wavefronts merge once at the end in a fixed order and the
+//     split's normalized partial goes to the workspace;
+//   * scales: a per-channel K scale is folded into q and the per-channel /
+//     per-tensor V scale is applied to the output by the combine ("[CUDA] Add
+//     INT4 paged KV cache with per-channel scales": exact because
+//     dequantization is linear, the channel index being contracted for K and
+//     free for V).  Per-row scales multiply the logit (K) or the softmax weight
+//     (V) of their token.
+//
+// gfx950 mapping:
+//   S^T = K . Q^T  on v_mfma_f32_16x16x32_f16: A = 16 tokens x 32 channels of
+//                 K codes unpacked to fp16 (integers are exact in fp16), B = q
+//                 rows in fp16 after a power-of-two row normalization.
+//   O  += P . V    on v_mfma_f32_16x16x16_f16: A = the softmax weights, which
+//                 sit in exactly the lanes the S^T result left them in; B = V
+//                 codes, transposed token-major -> channel-major in registers
+//                 with byte permutes and unpacked to fp16.
+//   The softmax weights are fp16 in [0, 1] (relative rounding 2^-11); the
+//   accumulators are fp32.
+
+#include "kvq_device.h"
+
+#ifndef KVQ_DTYPE
+#error "KVQ_DTYPE must be defined"
+#endif
+#ifndef KVQ_MODE
+#error "KVQ_MODE must be defined"
+#endif
+
+namespace kvq {
+namespace {
+
+template <int DT, int D>
+struct Geo {
+  static constexpr int ROWB = (DT == kInt4) ? D / 2 : D;  // bytes per cached row
+  // K tile, lane (token i = l%16, group g = l/16): the lane's quarter of the row
+  // is read as chunks of KCH bytes at row offsets KCH*(4c+g), so the 4 lanes of
+  // a row read one contiguous 4*KCH-byte span per load instruction.
+  static constexpr int KLB = ROWB / 4;
+  static constexpr int KCH = KLB < 16 ? KLB : 16;
+  static constexpr int KNCH = KLB / KCH;
+  static constexpr int KDW = KLB / 4;      // dwords of K codes per lane
+  static constexpr int KSTEPS = D / 32;    // 16x16x32 MFMAs per row block
+  // V tile, lane (column j = l%16, group g = l/16): rows 4g..4g+3, bytes
+  // [VLB*j, VLB*(j+1)) of each row; a load instruction covers 4 whole rows.
+  static constexpr int VLB = ROWB / 16;
+  static constexpr int VDW = VLB >= 4 ? VLB / 4 : 1;
+  static constexpr int NCOL = D / 16;      // 16x16x16 MFMAs per row block
+};
+
+// Channel d that element e (0..7) of k-step `ks` holds in lane group g, for both
+// MFMA operands of S^T (the K codes and the q rows use the same map).
+template <int DT, int D>
+__device__ __forceinline__ int k_channel(int ks, int g, int e) {
+  using G_ = Geo<DT, D>;
+  constexpr int DPC = G_::KCH / 4;  // dwords per chunk
+  if constexpr (DT == kInt4) {
+    const int w = ks;
+    const int byteoff = G_::KCH * (4 * (w / DPC) + g) + 4 * (w % DPC);
+    const int nib = e < 4 ? 2 * e : 2 * (e - 4) + 1;
+    return 2 * byteoff + nib;
+  } else {
+    const int w = 2 * ks + (e >> 2);
+    return G_::KCH * (4 * (w / DPC) + g) + 4 * (w % DPC) + (e & 3);
+  }
+}
+
+// Channel d of column c (0..NCOL-1) of the P.V MFMA in lane column j.
+template <int DT, int D>
+__device__ __forceinline__ int v_channel(int c, int j) {
+  using G_ = Geo<DT, D>;
+  if constexpr (DT == kInt4) {
+    constexpr int nb = G_::VLB >= 4 ? 4 : G_::VLB;  // valid bytes per dword
+    const int w = c / (2 * nb), r = c % (2 * nb);
+    const int k = r % nb, odd = r / nb;
+    return 2 * G_::VLB * j + 2 * (4 * w + k) + odd;
+  } else {
+    return G_::VLB * j + c;
+  }
+}
+
+template <int N>
+struct Bytes {
+  uint32_t w[N >= 4 ? N / 4 : 1];
+};
+
+template <int N>
+__device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* out) {
+  if constexpr (N == 16) {
+    u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  } else if constexpr (N == 8) {
+    u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+    out[0] = v[0]; out[1] = v[1];
+  } else if constexpr (N == 4) {
+    out[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else {
+    static_assert(N == 2, "unsupported chunk");
+    out[0] = *reinterpret_cast<const uint16_t*>(p);
+  }
+}
+
+// Unpack the lane's K codes of k-step ks into the A operand (8 halves).
+template <int DT, int D>
+__device__ __forceinline__ half8_t k_operand(const uint32_t* kw, int ks) {
+  uint32_t h[4];
+  if constexpr (DT == kInt4) {
+    int4x8_to_h(kw[ks], h);
+  } else if constexpr (DT == kInt8) {
+    int8x4_to_h(kw[2 * ks], h[0], h[1]);
+    int8x4_to_h(kw[2 * ks + 1], h[2], h[3]);
+  } else {
+    fp8x4_to_h(kw[2 * ks], h[0], h[1]);
+    fp8x4_to_h(kw[2 * ks + 1], h[2], h[3]);
+  }
+  return u4_to_h8(h[0], h[1], h[2], h[3]);
+}
+
+// Transpose the 4 token rows x 4 bytes of V dword-column w into MFMA B operands:
+// out[q] = (token0, token1, token2, token3) of byte q, q = 0..3, as fp16.
+// `bias_xor` selects the int8 sign flip; int4 inputs are already biased bytes.
+template <int KIND>  // 0: biased magic bytes (int8 after xor, int4 nibbles), 1: fp8
+__device__ __forceinline__ void v_transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                             half4_t out[4]) {
+  const uint32_t s01lo = perm(r1, r0, 0x05010400u);  // (r0.b0, r1.b0, r0.b1, r1.b1)
+  const uint32_t s01hi = perm(r1, r0, 0x07030602u);  // (r0.b2, r1.b2, r0.b3, r1.b3)
+  const uint32_t s23lo = perm(r3, r2, 0x05010400u);
+  const uint32_t s23hi = perm(r3, r2, 0x07030602u);
+  if constexpr (KIND == 1) {
+    out[0] = u2_to_h4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s01lo, 1.0f, false)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s23lo, 1.0f, false)));
+    out[1] = u2_to_h4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s01lo, 1.0f, true)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s23lo, 1.0f, true)));
+    out[2] = u2_to_h4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s01hi, 1.0f, false)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s23hi, 1.0f, false)));
+    out[3] = u2_to_h4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s01hi, 1.0f, true)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s23hi, 1.0f, true)));
+  } else {
+    const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    out[0] = u2_to_h4(pk_add_h(perm(kMagic, s01lo, 0x04010400u), bias),
+                      pk_add_h(perm(kMagic, s23lo, 0x04010400u), bias));
+    out[1] = u2_to_h4(pk_add_h(perm(kMagic, s01lo, 0x04030402u), bias),
+                      pk_add_h(perm(kMagic, s23lo, 0x04030402u), bias));
+    out[2] = u2_to_h4(pk_add_h(perm(kMagic, s01hi, 0x04010400u), bias),
+                      pk_add_h(perm(kMagic, s23hi, 0x04010400u), bias));
+    out[3] = u2_to_h4(pk_add_h(perm(kMagic, s01hi, 0x04030402u), bias),
+                      pk_add_h(perm(kMagic, s23hi, 0x04030402u), bias));
+  }
+}
+
+template <int DT, int MODE, int D, int RB>
+__global__ __launch_bounds__(256) void split_decode_kernel(SplitArgs a) {
+  using G_ = Geo<DT, D>;
+  constexpr int RP = 16 * RB;  // padded query rows
+  constexpr int ROWB = G_::ROWB;
+
+  __shared__ float smem[RP * D];         // q staging (as bf16), then the merge buffer
+  __shared__ float s_m[kWaves][RP];
+  __shared__ float s_l[kWaves][RP];
+  __shared__ int s_e[kWaves];
+
+  const int s = blockIdx.x;
+  const int hkv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 15;  // S^T column / P row / V column index
+  const int g = lane >> 4;  // lane group
+
+  const int Hkv = a.c.Hkv;
+  const int bs = a.c.block_size;
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  const int ntiles = (L + kTile - 1) / kTile;
+  const int tps = (ntiles + a.S - 1) / a.S;
+  const int tb = s * tps;
+  const int te = min(tb + tps, ntiles);
+
+  // ---- stage the R query rows of this KV head into LDS (bf16), zero padding rows
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem);
+  {
+    constexpr int U = D / 8;  // 16-byte units per row
+    for (int u = tid; u < RP * U; u += 256) {
+      const int r = u / U, cu = u % U;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (r < a.R) {
+        const int jq = r / a.G, gh = r % a.G;
+        const uint16_t* src = a.q + ((((size_t)b * a.Tq + jq) * a.Hq) + (size_t)hkv * a.G + gh) * D;
+        v = *reinterpret_cast<const u32x4_t*>(src + cu * 8);
+      }
+      *reinterpret_cast<u32x4_t*>(qs + r * D + cu * 8) = v;
+    }
+  }
+  __syncthreads();
+
+  // ---- B operands of S^T: q rows in this lane's channel order, normalized by a
+  // power of two so every element lies in (-1, 1); row multiplier restores it.
+  half8_t qb[RB][G_::KSTEPS];
+  float rowmul[RB];  // logit (log2 units) = dot * rowmul * per-row K scale
+  int lim[RB];       // tokens visible to this lane's row n: t < lim
+  {
+    const float* kst = a.c.k_scales;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = rb * 16 + n;
+      float qv[G_::KSTEPS][8];
+      float amax = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < G_::KSTEPS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = k_channel<DT, D>(ks, g, e);
+          float x = bf16_to_f32(qs[r * D + d]);
+          if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + d];
+          qv[ks][e] = x;
+          amax = fmaxf(amax, fabsf(x));
+        }
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      int ex = 0;
+      if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
+#pragma unroll
+      for (int ks = 0; ks < G_::KSTEPS; ++ks) {
+        half8_t h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)ldexpf(qv[ks][e], -ex);
+        qb[rb][ks] = h;
+      }
+      float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
+      if constexpr (MODE == kPerTensor) mul *= kst[0];
+      if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
+      rowmul[rb] = ldexpf(mul, ex);
+      lim[rb] = (r < a.R) ? (L - a.Tq + r / a.G + 1) : 0;
+      if (lim[rb] > L) lim[rb] = L;
+    }
+  }
+
+  // ---- per-wavefront online-softmax state
+  float m_run[RB], l_run[RB];
+  float4_t acc[RB][G_::NCOL];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < G_::NCOL; ++c) acc[rb][c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  int ev = -126;  // per-row V: weights are scaled by 2^-ev, 2^ev >= every V scale seen
+
+  const int32_t* table = a.c.block_table;
+  const size_t hk_rows = (size_t)bs;  // rows per (block, head)
+
+  for (int t = tb + wave; t < te; t += kWaves) {
+    const int tok0 = t * kTile;
+    int blk = b;
+    bool blk_ok = true;
+    if (table != nullptr) {
+      blk = table[(size_t)b * a.c.max_blocks + tok0 / bs];
+      blk_ok = (unsigned)blk < (unsigned)a.c.num_blocks;
+      blk = blk_ok ? blk : 0;
+    }
+    blk = __builtin_amdgcn_readfirstlane(blk);
+    const size_t row0 = ((size_t)blk * Hkv + hkv) * hk_rows + (size_t)(tok0 % bs);
+
+    // K codes: token n, this lane's quarter of the row
+    uint32_t kw[G_::KDW];
+    {
+      const uint8_t* kp = a.c.k_codes + (row0 + n) * ROWB + G_::KCH * g;
+#pragma unroll
+      for (int c = 0; c < G_::KNCH; ++c)
+        load_bytes<G_::KCH>(kp + c * 4 * G_::KCH, kw + c * (G_::KCH / 4));
+    }
+    // V codes: rows 4g..4g+3, bytes of column j = n
+    uint32_t vw[4][G_::VDW];
+    {
+      const uint8_t* vp = a.c.v_codes + (row0 + 4 * g) * ROWB + G_::VLB * n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) load_bytes<G_::VLB>(vp + e * ROWB, vw[e]);
+    }
+    float4_t ks4 = {1.f, 1.f, 1.f, 1.f}, vs4 = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (MODE == kPerRow) {
+      ks4 = *reinterpret_cast<const float4_t*>(a.c.k_scales + row0 + 4 * g);
+      vs4 = *reinterpret_cast<const float4_t*>(a.c.v_scales + row0 + 4 * g);
+    }
+
+    // tokens of this lane's P / V rows: tok0 + 4g + e
+    const int tbase = tok0 + 4 * g;
+    const bool tail = !blk_ok || (tok0 + kTile > L);
+    if (tail) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!(blk_ok && tbase + e < L))
+#pragma unroll
+          for (int w = 0; w < G_::VDW; ++w) vw[e][w] = 0u;
+    }
+
+    // per-row V scale: keep the weights' reference exponent >= every scale seen
+    float vsn[4] = {1.f, 1.f, 1.f, 1.f};
+    bool rescale_v = false;
+    float vfac = 1.0f;
+    if constexpr (MODE == kPerRow) {
+      float vmax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (blk_ok && tbase + e < L) vmax = fmaxf(vmax, vs4[e]);
+      vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+      vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+      if (vmax > ldexpf(1.0f, ev)) {
+        int en;
+        (void)frexpf(vmax, &en);
+        vfac = ldexpf(1.0f, ev - en);
+        ev = en;
+        rescale_v = true;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vsn[e] = ldexpf(vs4[e], -ev);
+    }
+
+    half8_t ka[G_::KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < G_::KSTEPS; ++ks) ka[ks] = k_operand<DT, D>(kw, ks);
+
+    half4_t pa[RB];
+    float alpha_acc[RB][4];
+    bool any_grow = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < G_::KSTEPS; ++ks) st = mfma32(ka[ks], qb[rb][ks], st);
+      float z[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float zz = st[e] * rowmul[rb];
+        if constexpr (MODE == kPerRow) zz *= ks4[e];
+        z[e] = (blk_ok && tbase + e < lim[rb]) ? zz : -INFINITY;
+      }
+      float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mnew = fmaxf(m_run[rb], tmax);
+      const bool grow = mnew > m_run[rb];
+      const float alpha = grow ? exp2f(m_run[rb] - mnew) : 1.0f;
+      const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
+      float p[4], psum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = exp2f(z[e] - msafe);
+        psum += p[e];
+      }
+      l_run[rb] = l_run[rb] * alpha + psum;
+      m_run[rb] = mnew;
+      any_grow |= grow;
+      half4_t ph;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pv = p[e];
+        if constexpr (MODE == kPerRow) pv = (blk_ok && tbase + e < L) ? pv * vsn[e] : 0.0f;
+        ph[e] = (_Float16)pv;
+      }
+      pa[rb] = ph;
+      // accumulator rows 4g+e belong to P rows held by lanes 4g+e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) alpha_acc[rb][e] = __shfl(alpha, 4 * g + e);
+    }
+    if (__builtin_amdgcn_ballot_w64(any_grow) != 0 || rescale_v) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int c = 0; c < G_::NCOL; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rb][c][e] *= alpha_acc[rb][e] * vfac;
+    }
+
+    // V: unpack column blocks and accumulate O += P . V
+#pragma unroll
+    for (int w = 0; w < G_::VDW; ++w) {
+      half4_t vb[8];
+      if constexpr (DT == kInt4) {
+        uint32_t ev4[4], od4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = vw[e][w] ^ 0x88888888u;
+          ev4[e] = (x << 4) & 0xF0F0F0F0u;
+          od4[e] = x & 0xF0F0F0F0u;
+        }
+        v_transpose4<0>(ev4[0], ev4[1], ev4[2], ev4[3], vb);
+        v_transpose4<0>(od4[0], od4[1], od4[2], od4[3], vb + 4);
+        constexpr int nb = G_::VLB >= 4 ? 4 : G_::VLB;
+#pragma unroll
+        for (int k = 0; k < nb; ++k) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            acc[rb][2 * nb * w + k] = mfma16(pa[rb], vb[k], acc[rb][2 * nb * w + k]);
+            acc[rb][2 * nb * w + nb + k] = mfma16(pa[rb], vb[4 + k], acc[rb][2 * nb * w + nb + k]);
+          }
+        }
+      } else if constexpr (DT == kInt8) {
+        v_transpose4<0>(vw[0][w] ^ 0x80808080u, vw[1][w] ^ 0x80808080u, vw[2][w] ^ 0x80808080u,
+                        vw[3][w] ^ 0x80808080u, vb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc[rb][4 * w + q] = mfma16(pa[rb], vb[q], acc[rb][4 * w + q]);
+      } else {
+        v_transpose4<1>(vw[0][w], vw[1][w], vw[2][w], vw[3][w], vb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc[rb][4 * w + q] = mfma16(pa[rb], vb[q], acc[rb][4 * w + q]);
+      }
+    }
+  }
+
+  // ---- merge the 4 wavefronts in fixed order, write the split partial
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float lsum = l_run[rb] + __shfl_xor(l_run[rb], 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (g == 0) {
+      s_m[wave][rb * 16 + n] = m_run[rb];
+      s_l[wave][rb * 16 + n] = lsum;
+    }
+  }
+  if (lane == 0) s_e[wave] = ev;
+  __syncthreads();
+
+  float fac[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = rb * 16 + 4 * g + e;
+      float M = s_m[0][r];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+      float f = 0.0f;
+      if (M != -INFINITY) {
+        float Lt = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) Lt += s_l[w][r] * exp2f(s_m[w][r] - M);
+        f = exp2f(s_m[wave][r] - M) / Lt;
+        if constexpr (MODE == kPerRow) f = ldexpf(f, ev);
+        if constexpr (DT == kInt4) f *= 0.0625f;  // V operand holds 16 * code
+      }
+      fac[rb][e] = f;
+    }
+  float* ob = smem;
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int c = 0; c < G_::NCOL; ++c) {
+          const int d = v_channel<DT, D>(c, n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = rb * 16 + 4 * g + e;
+            const float v = acc[rb][c][e] * fac[rb][e];
+            if (w == 0)
+              ob[r * D + d] = v;
+            else
+              ob[r * D + d] += v;
+          }
+        }
+    }
+    __syncthreads();
+  }
+
+  const size_t head = (size_t)b * Hkv + hkv;
+  for (int idx = tid; idx < a.R * D; idx += 256) {
+    const int r = idx / D, d = idx % D;
+    a.ws_o[((head * a.R + r) * a.S + s) * D + d] = ob[r * D + d];
+  }
+  if (tid < a.R) {
+    const int r = tid;
+    float M = s_m[0][r];
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+    float Lt = 0.0f;
+    if (M != -INFINITY)
+      for (int w = 0; w < kWaves; ++w) Lt += s_l[w][r] * exp2f(s_m[w][r] - M);
+    a.ws_m[(head * a.R + r) * a.S + s] = M;
+    a.ws_l[(head * a.R + r) * a.S + s] = Lt;
+  }
+}
+
+template <int DT, int MODE, int D, int RB>
+hipError_t launch_one(const SplitArgs& a, int B, hipStream_t st) {
+  dim3 grid(a.S, a.c.Hkv, B);
+  hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DT, int MODE, int D>
+hipError_t launch_d(int RB, const SplitArgs& a, int B, hipStream_t st) {
+  switch (RB) {
+    case 1: return launch_one<DT, MODE, D, 1>(a, B, st);
+    case 2: return launch_one<DT, MODE, D, 2>(a, B, st);
+    case 3: return launch_one<DT, MODE, D, 3>(a, B, st);
+    case 4: return launch_one<DT, MODE, D, 4>(a, B, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+#define KVQ_CAT2(a, b, c) a##b##_##c
+#define KVQ_CAT(a, b, c) KVQ_CAT2(a, b, c)
+
+hipError_t KVQ_CAT(launch_split_, KVQ_DTYPE, KVQ_MODE)(int D, int RB, const SplitArgs& a, int B,
+                                                        hipStream_t st) {
+  switch (D) {
+    case 64: return launch_d<KVQ_DTYPE, KVQ_MODE, 64>(RB, a, B, st);
+    case 128: return launch_d<KVQ_DTYPE, KVQ_MODE, 128>(RB, a, B, st);
+    case 256: return launch_d<KVQ_DTYPE, KVQ_MODE, 256>(RB, a, B, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq
