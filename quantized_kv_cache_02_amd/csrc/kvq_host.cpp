@@ -17,7 +17,7 @@ using kvq::CacheArgs;
 
 constexpr int kMaxGroup = 8;     // query heads per KV head
 constexpr int kMaxQTokens = 8;   // query tokens per sequence (1 + 7 drafts)
-constexpr int kTargetWorkgroups = 512;
+constexpr int kNumCUs = 256;  // MI355X
 constexpr int kMinTilesPerSplit = 8;
 constexpr int kMaxSplits = 4096;
 
@@ -74,7 +74,10 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   if (batch > 65535 || c->num_kv_heads > 65535) return KVQ_EUNSUPPORTED;
   const int64_t ntiles = ((int64_t)max_seq_len + 15) / 16;
   const int64_t pairs = (int64_t)batch * c->num_kv_heads;
-  int64_t S = (kTargetWorkgroups + pairs - 1) / pairs;
+  const int RB = (G * tq + 15) / 16;
+  // one resident wave of workgroups: CUs x workgroups per CU
+  const int64_t target = (int64_t)kNumCUs * kvq::split_waves_per_simd(c->head_dim, RB);
+  int64_t S = (target + pairs - 1) / pairs;
   int64_t cap = ntiles / kMinTilesPerSplit;
   if (cap < 1) cap = 1;
   if (S > cap) S = cap;

@@ -15,6 +15,15 @@ constexpr int kTile = 16;
 // Wavefronts per decode workgroup; each owns a private online-softmax state.
 constexpr int kWaves = 4;
 
+// Decode-kernel register budget per variant: two waves per SIMD (<= 256
+// registers per lane) while the accumulators of the query row blocks fit,
+// otherwise one wave per SIMD (<= 512).  `RB` is the number of 16-row blocks
+// of query rows (G * Tq rows per KV head).  The host sizes the split count
+// from the same figure: workgroups resident per CU = waves per SIMD.
+constexpr int split_waves_per_simd(int D, int RB) { return RB * D <= 256 ? 2 : 1; }
+// Tiles of codes held in registers per wavefront (one in use, the rest loading).
+constexpr int split_tiles_in_flight(int D, int RB) { return RB * D <= 256 ? 2 : 3; }
+
 struct CacheArgs {
   uint8_t* k_codes;
   uint8_t* v_codes;

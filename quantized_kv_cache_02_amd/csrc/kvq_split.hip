@@ -92,24 +92,22 @@ __device__ __forceinline__ int v_channel(int c, int j) {
   }
 }
 
-template <int N>
-struct Bytes {
-  uint32_t w[N >= 4 ? N / 4 : 1];
-};
-
+// Streaming loads of cache codes: each byte is read once per decode, so they
+// are issued non-temporal (measured on MI355X: the same read pattern goes from
+// 5.7 to 6.2 TB/s).
 template <int N>
 __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* out) {
   if constexpr (N == 16) {
-    u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
     out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
   } else if constexpr (N == 8) {
-    u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+    u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
     out[0] = v[0]; out[1] = v[1];
   } else if constexpr (N == 4) {
-    out[0] = *reinterpret_cast<const uint32_t*>(p);
+    out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
   } else {
     static_assert(N == 2, "unsupported chunk");
-    out[0] = *reinterpret_cast<const uint16_t*>(p);
+    out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
   }
 }
 
@@ -131,7 +129,6 @@ __device__ __forceinline__ half8_t k_operand(const uint32_t* kw, int ks) {
 
 // Transpose the 4 token rows x 4 bytes of V dword-column w into MFMA B operands:
 // out[q] = (token0, token1, token2, token3) of byte q, q = 0..3, as fp16.
-// `bias_xor` selects the int8 sign flip; int4 inputs are already biased bytes.
 template <int KIND>  // 0: biased magic bytes (int8 after xor, int4 nibbles), 1: fp8
 __device__ __forceinline__ void v_transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
                                              half4_t out[4]) {
@@ -161,16 +158,232 @@ __device__ __forceinline__ void v_transpose4(uint32_t r0, uint32_t r1, uint32_t 
   }
 }
 
-template <int DT, int MODE, int D, int RB>
-__global__ __launch_bounds__(256) void split_decode_kernel(SplitArgs a) {
-  using G_ = Geo<DT, D>;
-  constexpr int RP = 16 * RB;  // padded query rows
-  constexpr int ROWB = G_::ROWB;
+// Codes and scales of one 16-token tile as this lane holds them.
+template <int DT, int D>
+struct Tile {
+  uint32_t kw[Geo<DT, D>::KDW];     // K: token n, the lane's quarter of the row
+  uint32_t vw[4][Geo<DT, D>::VDW];  // V: tokens 4g..4g+3, the lane's column bytes
+  float4_t ks4, vs4;                // per-row scales of tokens 4g..4g+3
+  int ok;                           // block-table entry inside the pool
+};
 
-  __shared__ float smem[RP * D];         // q staging (as bf16), then the merge buffer
+template <int DT, int MODE, int D>
+__device__ __forceinline__ void load_tile(const SplitArgs& a, int b, int hkv, int t, int n, int g,
+                                          Tile<DT, D>& T) {
+  using G_ = Geo<DT, D>;
+  constexpr int ROWB = G_::ROWB;
+  const int bs = a.c.block_size;
+  const int tok0 = t * kTile;
+  int blk = b;
+  int ok = 1;
+  if (a.c.block_table != nullptr) {
+    blk = a.c.block_table[(size_t)b * a.c.max_blocks + tok0 / bs];
+    ok = (unsigned)blk < (unsigned)a.c.num_blocks;
+    blk = ok ? blk : 0;
+  }
+  blk = __builtin_amdgcn_readfirstlane(blk);
+  T.ok = __builtin_amdgcn_readfirstlane(ok);
+  const size_t row0 = ((size_t)blk * a.c.Hkv + hkv) * (size_t)bs + (size_t)(tok0 % bs);
+  const uint8_t* kp = a.c.k_codes + (row0 + n) * ROWB + G_::KCH * g;
+#pragma unroll
+  for (int c = 0; c < G_::KNCH; ++c) load_bytes<G_::KCH>(kp + c * 4 * G_::KCH, T.kw + c * (G_::KCH / 4));
+  const uint8_t* vp = a.c.v_codes + (row0 + 4 * g) * ROWB + G_::VLB * n;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) load_bytes<G_::VLB>(vp + e * ROWB, T.vw[e]);
+  if constexpr (MODE == kPerRow) {
+    T.ks4 = *reinterpret_cast<const float4_t*>(a.c.k_scales + row0 + 4 * g);
+    T.vs4 = *reinterpret_cast<const float4_t*>(a.c.v_scales + row0 + 4 * g);
+  }
+}
+
+// Per-wavefront online-softmax state over its tiles.
+template <int DT, int D, int RB>
+struct WaveState {
+  float m[RB];                         // running max logit of row rb*16+n (log2 units)
+  float l[RB];                         // this lane's share of the running sum
+  float4_t acc[RB][Geo<DT, D>::NCOL];  // O rows rb*16+4g+e, column c of lane n
+  float vref;                          // per-row V: weights carry 1/vref, a power of two
+};
+
+template <int DT, int MODE, int D, int RB>
+__device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L, int n, int g,
+                                             const half8_t (&qb)[RB][Geo<DT, D>::KSTEPS],
+                                             const float (&rowmul)[RB], const int (&lim)[RB],
+                                             WaveState<DT, D, RB>& W) {
+  using G_ = Geo<DT, D>;
+  const int tok0 = t * kTile;
+  const int tbase = tok0 + 4 * g;
+  const bool ok = T.ok != 0;
+  bool valid[4];  // token tbase+e exists (row-independent)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) valid[e] = ok && tbase + e < L;
+
+  uint32_t vw[4][G_::VDW];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int w = 0; w < G_::VDW; ++w) vw[e][w] = T.vw[e][w];
+  if (!ok || tok0 + kTile > L) {  // rows past the sequence may hold anything, fp8 NaN included
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (!valid[e])
+#pragma unroll
+        for (int w = 0; w < G_::VDW; ++w) vw[e][w] = 0u;
+  }
+
+  // Per-row V scales: keep vref a power of two >= every scale seen, so the
+  // weights p * s / vref stay in [0, 1].  The reduction runs only on the rare
+  // tiles where some scale exceeds the current reference.
+  float vfac = 1.0f;
+  bool rescale = false;
+  float vsn[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (MODE == kPerRow) {
+    bool vup = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vup |= valid[e] && T.vs4[e] > W.vref;
+    if (__builtin_amdgcn_ballot_w64(vup) != 0) {
+      float vmax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid[e]) vmax = fmaxf(vmax, T.vs4[e]);
+      vmax = group_max4(vmax);
+      int en;
+      (void)frexpf(vmax, &en);  // vmax < 2^en
+      const float nref = ldexpf(1.0f, en);
+      vfac = W.vref / nref;
+      W.vref = nref;
+      rescale = true;
+    }
+    const float inv = 1.0f / W.vref;  // exact: a power of two
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vsn[e] = T.vs4[e] * inv;
+  }
+
+  half4_t pa[RB];
+  float alpha[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    // S^T: two independent accumulation chains over the k-steps
+    float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < G_::KSTEPS; ks += 2) {
+      s0 = mfma32(k_operand<DT, D>(T.kw, ks), qb[rb][ks], s0);
+      if (ks + 1 < G_::KSTEPS) s1 = mfma32(k_operand<DT, D>(T.kw, ks + 1), qb[rb][ks + 1], s1);
+    }
+    float z[4];
+    bool up = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float zz = (s0[e] + s1[e]) * rowmul[rb];
+      if constexpr (MODE == kPerRow) zz *= T.ks4[e];
+      z[e] = (ok && tbase + e < lim[rb]) ? zz : -INFINITY;
+      up |= z[e] > W.m[rb];
+    }
+    // The running max changes only if some logit exceeds it; the cross-lane
+    // reduction runs only then (exactly the same result as reducing always).
+    alpha[rb] = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      const float tmax = group_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+      const float mnew = fmaxf(W.m[rb], tmax);
+      if (mnew > W.m[rb]) {
+        alpha[rb] = exp2f(W.m[rb] - mnew);  // 0 when the old max was -inf
+        W.l[rb] *= alpha[rb];
+        W.m[rb] = mnew;
+        rescale = true;
+      }
+    }
+    const float msafe = (W.m[rb] == -INFINITY) ? 0.0f : W.m[rb];
+    half4_t ph;
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = exp2f(z[e] - msafe);
+      psum += p;
+      float pv = p;
+      if constexpr (MODE == kPerRow) pv = valid[e] ? p * vsn[e] : 0.0f;
+      ph[e] = (_Float16)pv;
+    }
+    W.l[rb] += psum;
+    pa[rb] = ph;
+  }
+  // Rescale the accumulators when some row's max grew or the V reference moved
+  // (rare after the first tiles).  Accumulator rows 4g+e belong to the P rows
+  // held by lanes 4g+e.
+  if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = __shfl(alpha[rb], 4 * g + e) * vfac;
+#pragma unroll
+      for (int c = 0; c < G_::NCOL; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) W.acc[rb][c][e] *= f[e];
+    }
+  }
+
+  // V: unpack column blocks and accumulate O += P . V
+#pragma unroll
+  for (int w = 0; w < G_::VDW; ++w) {
+    half4_t vb[8];
+    if constexpr (DT == kInt4) {
+      uint32_t ev4[4], od4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = vw[e][w] ^ 0x88888888u;
+        ev4[e] = (x << 4) & 0xF0F0F0F0u;
+        od4[e] = x & 0xF0F0F0F0u;
+      }
+      v_transpose4<0>(ev4[0], ev4[1], ev4[2], ev4[3], vb);
+      v_transpose4<0>(od4[0], od4[1], od4[2], od4[3], vb + 4);
+      constexpr int nb = G_::VLB >= 4 ? 4 : G_::VLB;
+#pragma unroll
+      for (int k = 0; k < nb; ++k)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          W.acc[rb][2 * nb * w + k] = mfma16(pa[rb], vb[k], W.acc[rb][2 * nb * w + k]);
+          W.acc[rb][2 * nb * w + nb + k] = mfma16(pa[rb], vb[4 + k], W.acc[rb][2 * nb * w + nb + k]);
+        }
+    } else if constexpr (DT == kInt8) {
+      v_transpose4<0>(vw[0][w] ^ 0x80808080u, vw[1][w] ^ 0x80808080u, vw[2][w] ^ 0x80808080u,
+                      vw[3][w] ^ 0x80808080u, vb);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) W.acc[rb][4 * w + q] = mfma16(pa[rb], vb[q], W.acc[rb][4 * w + q]);
+    } else {
+      v_transpose4<1>(vw[0][w], vw[1][w], vw[2][w], vw[3][w], vb);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) W.acc[rb][4 * w + q] = mfma16(pa[rb], vb[q], W.acc[rb][4 * w + q]);
+    }
+  }
+}
+
+// NB tiles of codes are held per wavefront: while one is processed, the loads
+// of the next NB-1 are in flight.
+template <int DT, int MODE, int D, int RB>
+struct Knobs {
+  static constexpr int NB = split_tiles_in_flight(D, RB);
+  static constexpr int WAVES_PER_EU = split_waves_per_simd(D, RB);
+  // merge buffers: one per wavefront when they fit in 64 KiB of LDS, else one
+  // shared buffer the wavefronts add into in turn
+  static constexpr int MERGE_BUFS = (kWaves * 16 * RB * D * 4 <= 65536) ? kWaves : 1;
+};
+
+template <int DT, int MODE, int D, int RB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    Knobs<DT, MODE, D, RB>::WAVES_PER_EU, Knobs<DT, MODE, D, RB>::WAVES_PER_EU))) void
+split_decode_kernel(SplitArgs a) {
+  using G_ = Geo<DT, D>;
+  using K_ = Knobs<DT, MODE, D, RB>;
+  constexpr int RP = 16 * RB;  // padded query rows
+  constexpr int NB = K_::NB;
+
+  __shared__ float smem[K_::MERGE_BUFS * RP * D];  // q staging (as bf16), then merge buffers
   __shared__ float s_m[kWaves][RP];
   __shared__ float s_l[kWaves][RP];
-  __shared__ int s_e[kWaves];
 
   const int s = blockIdx.x;
   const int hkv = blockIdx.y;
@@ -181,8 +394,24 @@ __global__ __launch_bounds__(256) void split_decode_kernel(SplitArgs a) {
   const int n = lane & 15;  // S^T column / P row / V column index
   const int g = lane >> 4;  // lane group
 
-  const int Hkv = a.c.Hkv;
-  const int bs = a.c.block_size;
+  // ---- issue the loads of the query rows first: they do not depend on the
+  // sequence length, and loads retire in order, so staging them later waits
+  // only for them and not for the tiles issued after them.
+  constexpr int QU = D / 8;                           // 16-byte units per q row
+  constexpr int QPT = (RP * QU + 255) / 256;          // units per thread
+  // (unconditional loads, clamped to row 0, so no branch joins on their data;
+  // padding rows are zeroed when staged)
+  u32x4_t qreg[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int u = (tid + 256 * i) % (RP * QU);
+    const int r = u / QU, cu = u % QU;
+    const int rr = r < a.R ? r : 0;
+    const int jq = rr / a.G, gh = rr % a.G;
+    const uint16_t* src = a.q + ((((size_t)b * a.Tq + jq) * a.Hq) + (size_t)hkv * a.G + gh) * D;
+    qreg[i] = *reinterpret_cast<const u32x4_t*>(src + cu * 8);
+  }
+
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   const int ntiles = (L + kTile - 1) / kTile;
@@ -190,46 +419,64 @@ __global__ __launch_bounds__(256) void split_decode_kernel(SplitArgs a) {
   const int tb = s * tps;
   const int te = min(tb + tps, ntiles);
 
-  // ---- stage the R query rows of this KV head into LDS (bf16), zero padding rows
+  // ---- the wavefront's tiles are tb + wave, tb + wave + 4, ...; start the
+  // loads of the first NB now so their latency overlaps the query prologue.
+  // Loads past the last tile re-read the last tile (already in L2), so every
+  // buffer is always filled by the same instruction sequence.
+  // Every load is issued unconditionally (index clamped into [0, te-1], tile 0
+  // when the wavefront has none: tile 0 is addressable for any length) so no
+  // branch joins on in-flight loads and the waits stay exact.
+  const int t0 = tb + wave;
+  const int tlast = max(te - 1, 0);
+  Tile<DT, D> buf[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) load_tile<DT, MODE, D>(a, b, hkv, min(t0 + i * kWaves, tlast), n, g, buf[i]);
+
+  // ---- stage the query rows in LDS (bf16), zero padding rows
   uint16_t* qs = reinterpret_cast<uint16_t*>(smem);
-  {
-    constexpr int U = D / 8;  // 16-byte units per row
-    for (int u = tid; u < RP * U; u += 256) {
-      const int r = u / U, cu = u % U;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (r < a.R) {
-        const int jq = r / a.G, gh = r % a.G;
-        const uint16_t* src = a.q + ((((size_t)b * a.Tq + jq) * a.Hq) + (size_t)hkv * a.G + gh) * D;
-        v = *reinterpret_cast<const u32x4_t*>(src + cu * 8);
-      }
-      *reinterpret_cast<u32x4_t*>(qs + r * D + cu * 8) = v;
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int u = tid + 256 * i;
+    if (u < RP * QU) {
+      const u32x4_t v = (u / QU < a.R) ? qreg[i] : u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(qs + (u / QU) * D + (u % QU) * 8) = v;
     }
   }
   __syncthreads();
 
   // ---- B operands of S^T: q rows in this lane's channel order, normalized by a
-  // power of two so every element lies in (-1, 1); row multiplier restores it.
+  // power of two so every element lies in (-1, 1); the row multiplier restores it.
   half8_t qb[RB][G_::KSTEPS];
   float rowmul[RB];  // logit (log2 units) = dot * rowmul * per-row K scale
   int lim[RB];       // tokens visible to this lane's row n: t < lim
   {
     const float* kst = a.c.k_scales;
+#pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int r = rb * 16 + n;
       float qv[G_::KSTEPS][8];
       float amax = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < G_::KSTEPS; ++ks)
+      for (int ks = 0; ks < G_::KSTEPS; ++ks) {
+        // the 8 channels of a k-step are 8 consecutive channels (permuted for int4)
+        const int base = k_channel<DT, D>(ks, g, 0);
+        u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qs + r * D + base);
+        float x8[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x8[2 * i] = __uint_as_float(raw[i] << 16);
+          x8[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int d = k_channel<DT, D>(ks, g, e);
-          float x = bf16_to_f32(qs[r * D + d]);
-          if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + d];
+          const int off = k_channel<DT, D>(ks, g, e) - base;  // 0..7
+          float x = x8[off];
+          if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
           qv[ks][e] = x;
           amax = fmaxf(amax, fabsf(x));
         }
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      }
+      amax = group_max4(amax);
       int ex = 0;
       if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
 #pragma unroll
@@ -248,194 +495,34 @@ __global__ __launch_bounds__(256) void split_decode_kernel(SplitArgs a) {
     }
   }
 
-  // ---- per-wavefront online-softmax state
-  float m_run[RB], l_run[RB];
-  float4_t acc[RB][G_::NCOL];
+  WaveState<DT, D, RB> W;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
-    l_run[rb] = 0.0f;
+    W.m[rb] = -INFINITY;
+    W.l[rb] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < G_::NCOL; ++c) acc[rb][c] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < G_::NCOL; ++c) W.acc[rb][c] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
-  int ev = -126;  // per-row V: weights are scaled by 2^-ev, 2^ev >= every V scale seen
+  W.vref = 0x1p-126f;  // smallest normal: any nonzero scale above it raises the reference
 
-  const int32_t* table = a.c.block_table;
-  const size_t hk_rows = (size_t)bs;  // rows per (block, head)
-
-  for (int t = tb + wave; t < te; t += kWaves) {
-    const int tok0 = t * kTile;
-    int blk = b;
-    bool blk_ok = true;
-    if (table != nullptr) {
-      blk = table[(size_t)b * a.c.max_blocks + tok0 / bs];
-      blk_ok = (unsigned)blk < (unsigned)a.c.num_blocks;
-      blk = blk_ok ? blk : 0;
-    }
-    blk = __builtin_amdgcn_readfirstlane(blk);
-    const size_t row0 = ((size_t)blk * Hkv + hkv) * hk_rows + (size_t)(tok0 % bs);
-
-    // K codes: token n, this lane's quarter of the row
-    uint32_t kw[G_::KDW];
-    {
-      const uint8_t* kp = a.c.k_codes + (row0 + n) * ROWB + G_::KCH * g;
+  for (int t = t0; t < te;) {
 #pragma unroll
-      for (int c = 0; c < G_::KNCH; ++c)
-        load_bytes<G_::KCH>(kp + c * 4 * G_::KCH, kw + c * (G_::KCH / 4));
-    }
-    // V codes: rows 4g..4g+3, bytes of column j = n
-    uint32_t vw[4][G_::VDW];
-    {
-      const uint8_t* vp = a.c.v_codes + (row0 + 4 * g) * ROWB + G_::VLB * n;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) load_bytes<G_::VLB>(vp + e * ROWB, vw[e]);
-    }
-    float4_t ks4 = {1.f, 1.f, 1.f, 1.f}, vs4 = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (MODE == kPerRow) {
-      ks4 = *reinterpret_cast<const float4_t*>(a.c.k_scales + row0 + 4 * g);
-      vs4 = *reinterpret_cast<const float4_t*>(a.c.v_scales + row0 + 4 * g);
-    }
-
-    // tokens of this lane's P / V rows: tok0 + 4g + e
-    const int tbase = tok0 + 4 * g;
-    const bool tail = !blk_ok || (tok0 + kTile > L);
-    if (tail) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (!(blk_ok && tbase + e < L))
-#pragma unroll
-          for (int w = 0; w < G_::VDW; ++w) vw[e][w] = 0u;
-    }
-
-    // per-row V scale: keep the weights' reference exponent >= every scale seen
-    float vsn[4] = {1.f, 1.f, 1.f, 1.f};
-    bool rescale_v = false;
-    float vfac = 1.0f;
-    if constexpr (MODE == kPerRow) {
-      float vmax = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (blk_ok && tbase + e < L) vmax = fmaxf(vmax, vs4[e]);
-      vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-      vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
-      if (vmax > ldexpf(1.0f, ev)) {
-        int en;
-        (void)frexpf(vmax, &en);
-        vfac = ldexpf(1.0f, ev - en);
-        ev = en;
-        rescale_v = true;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vsn[e] = ldexpf(vs4[e], -ev);
-    }
-
-    half8_t ka[G_::KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < G_::KSTEPS; ++ks) ka[ks] = k_operand<DT, D>(kw, ks);
-
-    half4_t pa[RB];
-    float alpha_acc[RB][4];
-    bool any_grow = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float4_t st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < G_::KSTEPS; ++ks) st = mfma32(ka[ks], qb[rb][ks], st);
-      float z[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float zz = st[e] * rowmul[rb];
-        if constexpr (MODE == kPerRow) zz *= ks4[e];
-        z[e] = (blk_ok && tbase + e < lim[rb]) ? zz : -INFINITY;
-      }
-      float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m_run[rb], tmax);
-      const bool grow = mnew > m_run[rb];
-      const float alpha = grow ? exp2f(m_run[rb] - mnew) : 1.0f;
-      const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
-      float p[4], psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = exp2f(z[e] - msafe);
-        psum += p[e];
-      }
-      l_run[rb] = l_run[rb] * alpha + psum;
-      m_run[rb] = mnew;
-      any_grow |= grow;
-      half4_t ph;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float pv = p[e];
-        if constexpr (MODE == kPerRow) pv = (blk_ok && tbase + e < L) ? pv * vsn[e] : 0.0f;
-        ph[e] = (_Float16)pv;
-      }
-      pa[rb] = ph;
-      // accumulator rows 4g+e belong to P rows held by lanes 4g+e
-#pragma unroll
-      for (int e = 0; e < 4; ++e) alpha_acc[rb][e] = __shfl(alpha, 4 * g + e);
-    }
-    if (__builtin_amdgcn_ballot_w64(any_grow) != 0 || rescale_v) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int c = 0; c < G_::NCOL; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[rb][c][e] *= alpha_acc[rb][e] * vfac;
-    }
-
-    // V: unpack column blocks and accumulate O += P . V
-#pragma unroll
-    for (int w = 0; w < G_::VDW; ++w) {
-      half4_t vb[8];
-      if constexpr (DT == kInt4) {
-        uint32_t ev4[4], od4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t x = vw[e][w] ^ 0x88888888u;
-          ev4[e] = (x << 4) & 0xF0F0F0F0u;
-          od4[e] = x & 0xF0F0F0F0u;
-        }
-        v_transpose4<0>(ev4[0], ev4[1], ev4[2], ev4[3], vb);
-        v_transpose4<0>(od4[0], od4[1], od4[2], od4[3], vb + 4);
-        constexpr int nb = G_::VLB >= 4 ? 4 : G_::VLB;
-#pragma unroll
-        for (int k = 0; k < nb; ++k) {
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            acc[rb][2 * nb * w + k] = mfma16(pa[rb], vb[k], acc[rb][2 * nb * w + k]);
-            acc[rb][2 * nb * w + nb + k] = mfma16(pa[rb], vb[4 + k], acc[rb][2 * nb * w + nb + k]);
-          }
-        }
-      } else if constexpr (DT == kInt8) {
-        v_transpose4<0>(vw[0][w] ^ 0x80808080u, vw[1][w] ^ 0x80808080u, vw[2][w] ^ 0x80808080u,
-                        vw[3][w] ^ 0x80808080u, vb);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc[rb][4 * w + q] = mfma16(pa[rb], vb[q], acc[rb][4 * w + q]);
-      } else {
-        v_transpose4<1>(vw[0][w], vw[1][w], vw[2][w], vw[3][w], vb);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc[rb][4 * w + q] = mfma16(pa[rb], vb[q], acc[rb][4 * w + q]);
-      }
+    for (int i = 0; i < NB; ++i) {
+      if (t < te) process_tile<DT, MODE, D, RB>(buf[i], t, L, n, g, qb, rowmul, lim, W);
+      load_tile<DT, MODE, D>(a, b, hkv, min(t + NB * kWaves, tlast), n, g, buf[i]);
+      t += kWaves;
     }
   }
 
   // ---- merge the 4 wavefronts in fixed order, write the split partial
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    float lsum = l_run[rb] + __shfl_xor(l_run[rb], 16);
-    lsum += __shfl_xor(lsum, 32);
+    const float lsum = group_sum4(W.l[rb]);
     if (g == 0) {
-      s_m[wave][rb * 16 + n] = m_run[rb];
+      s_m[wave][rb * 16 + n] = W.m[rb];
       s_l[wave][rb * 16 + n] = lsum;
     }
   }
-  if (lane == 0) s_e[wave] = ev;
   __syncthreads();
 
   float fac[RB][4];
@@ -453,14 +540,18 @@ __global__ __launch_bounds__(256) void split_decode_kernel(SplitArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) Lt += s_l[w][r] * exp2f(s_m[w][r] - M);
         f = exp2f(s_m[wave][r] - M) / Lt;
-        if constexpr (MODE == kPerRow) f = ldexpf(f, ev);
+        if constexpr (MODE == kPerRow) f *= W.vref;
         if constexpr (DT == kInt4) f *= 0.0625f;  // V operand holds 16 * code
       }
       fac[rb][e] = f;
     }
-  float* ob = smem;
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+
+  // each wavefront writes its weighted rows; the sum runs in wave order
+  const int nbuf = K_::MERGE_BUFS;
+  for (int round = 0; round < kWaves / nbuf; ++round) {
+    const int w_act = round * nbuf;  // first wave writing this round
+    if (wave >= w_act && wave < w_act + nbuf) {
+      float* ob = smem + (size_t)(wave - w_act) * RP * D;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -469,21 +560,26 @@ __global__ __launch_bounds__(256) void split_decode_kernel(SplitArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = rb * 16 + 4 * g + e;
-            const float v = acc[rb][c][e] * fac[rb][e];
-            if (w == 0)
-              ob[r * D + d] = v;
-            else
-              ob[r * D + d] += v;
+            if (r < a.R) {
+              const float v = W.acc[rb][c][e] * fac[rb][e];
+              if (round == 0)
+                ob[r * D + d] = v;
+              else
+                ob[r * D + d] += v;
+            }
           }
         }
     }
     __syncthreads();
   }
 
-  const size_t head = (size_t)b * Hkv + hkv;
-  for (int idx = tid; idx < a.R * D; idx += 256) {
+  const size_t head = (size_t)b * a.c.Hkv + hkv;
+  for (int idx = tid * 4; idx < a.R * D; idx += 256 * 4) {
     const int r = idx / D, d = idx % D;
-    a.ws_o[((head * a.R + r) * a.S + s) * D + d] = ob[r * D + d];
+    float4_t v = *reinterpret_cast<const float4_t*>(smem + r * D + d);
+#pragma unroll
+    for (int w = 1; w < nbuf; ++w) v += *reinterpret_cast<const float4_t*>(smem + (size_t)w * RP * D + r * D + d);
+    *reinterpret_cast<float4_t*>(a.ws_o + ((head * a.R + r) * a.S + s) * D + d) = v;
   }
   if (tid < a.R) {
     const int r = tid;
