@@ -7,11 +7,15 @@
 // ...", "CUDA kernels" (ApplyHeadSink): the output of head h is rescaled by
 // 1 / (1 + exp(s_h - lse)) after the quantized branch.
 //
-// One wavefront per (sequence, KV head, query row, 64 channels).  With split s
-// holding (m_s in log2 units, l_s, o_s normalized):
+// With split s holding (m_s in log2 units, l_s, o_s normalized):
 //   M = max_s m_s,  w_s = l_s 2^(m_s - M),  L = sum_s w_s,  o = sum_s w_s o_s / L,
 //   lse = ln 2 (M + log2 L).
-// Every sum runs in the same order on every call.
+//
+// One workgroup per (sequence, KV head, query row, 64 channels).  Its 256
+// threads are 16 channel quads x 16 split groups; a thread issues the loads of
+// all its splits before using any (the partials were just written, so one
+// round trip to the cache hierarchy), then the 16 groups are summed in group
+// order through LDS.  Every sum runs in the same order on every call.
 
 #include "kvq_device.h"
 
@@ -19,49 +23,88 @@ namespace kvq {
 namespace {
 
 constexpr int kMaxSplits = 4096;
+constexpr int kGroups = 16;   // split groups per workgroup
+constexpr int kQuads = 16;    // 4-channel columns per workgroup (64 channels)
+constexpr int kBatch = 8;     // loads issued back to back per thread
 
 template <int MODE>
-__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a, int D) {
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int D) {
   __shared__ float w_s[kMaxSplits];
-  const int lane = threadIdx.x;
-  const int d = blockIdx.x * 64 + lane;
+  __shared__ float red[4];
+  __shared__ float4_t part[kGroups][kQuads];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int quad = tid % kQuads, grp = tid / kQuads;
+  const int d = blockIdx.x * 64 + quad * 4;
   const int r = blockIdx.y;
   const int head = blockIdx.z;  // b * Hkv + hkv
   const int b = head / a.Hkv, hkv = head % a.Hkv;
   const int S = a.S;
-  const float* ms = a.ws_m + ((size_t)head * a.R + r) * S;
-  const float* ls = a.ws_l + ((size_t)head * a.R + r) * S;
+  const size_t rowbase = ((size_t)head * a.R + r) * S;
+  const float* ms = a.ws_m + rowbase;
+  const float* ls = a.ws_l + rowbase;
 
-  // M: each lane scans splits lane, lane+64, ...; then a fixed butterfly
+  // M: per-thread max over s = tid, tid+256, ..., then waves, then in wave order
   float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, ms[s]);
+  for (int s = tid; s < S; s += 256) M = fmaxf(M, ms[s]);
   M = wave_max(M);
-  float part = 0.0f;
-  for (int s = lane; s < S; s += 64) {
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float part_l = 0.0f;
+  for (int s = tid; s < S; s += 256) {
     const float w = (M == -INFINITY || ls[s] == 0.0f) ? 0.0f : ls[s] * exp2f(ms[s] - M);
     w_s[s] = w;
-    part += w;
+    part_l += w;
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-  const float Lsum = part;
+  for (int o = 32; o >= 1; o >>= 1) part_l += __shfl_xor(part_l, o);
+  if (lane == 0) red[wave] = part_l;
   __syncthreads();
+  const float Lsum = ((red[0] + red[1]) + red[2]) + red[3];
 
-  float o = 0.0f;
-  if (Lsum > 0.0f) {
-    const float* os = a.ws_o + (((size_t)head * a.R + r) * S) * D + d;
-    for (int s = 0; s < S; ++s) o += w_s[s] * os[(size_t)s * D];
-    o /= Lsum;
+  // weighted sum of this thread's splits s = grp, grp + 16, ...
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const float* os = a.ws_o + rowbase * D + d;
+  for (int s0 = grp; s0 < S; s0 += kGroups * kBatch) {
+    float4_t v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int s = s0 + i * kGroups;
+      v[i] = (s < S) ? *reinterpret_cast<const float4_t*>(os + (size_t)s * D)
+                     : float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int s = s0 + i * kGroups;
+      if (s < S) acc += w_s[s] * v[i];
+    }
   }
-  if constexpr (MODE == kPerTensor) o *= a.v_static[0];
-  if constexpr (MODE == kPerChannel) o *= a.v_static[(size_t)hkv * D + d];
+  part[grp][quad] = acc;
+  __syncthreads();
+  if (grp != 0) return;
+
+  float4_t o = part[0][quad];
+#pragma unroll
+  for (int g2 = 1; g2 < kGroups; ++g2) o += part[g2][quad];
+  float f = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
   const int jq = r / a.G, gh = r % a.G;
   const int h = hkv * a.G + gh;
   if (a.sink != nullptr && Lsum > 0.0f) {
     const float lse = 0.6931471805599453f * (M + log2f(Lsum));
-    o *= 1.0f / (1.0f + expf(a.sink[h] - lse));
+    f *= 1.0f / (1.0f + expf(a.sink[h] - lse));
   }
-  a.out[(((size_t)b * a.Tq + jq) * a.Hq + h) * D + d] = f32_to_bf16(o);
+  uint16_t ob[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float x = o[e] * f;
+    if constexpr (MODE == kPerTensor) x *= a.v_static[0];
+    if constexpr (MODE == kPerChannel) x *= a.v_static[(size_t)hkv * D + d + e];
+    ob[e] = f32_to_bf16(x);
+  }
+  u32x2_t packed = {(uint32_t)ob[0] | ((uint32_t)ob[1] << 16), (uint32_t)ob[2] | ((uint32_t)ob[3] << 16)};
+  *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.Tq + jq) * a.Hq + h) * D + d) = packed;
 }
 
 }  // namespace
@@ -70,9 +113,9 @@ hipError_t launch_combine(int mode, int D, const CombineArgs& a, int B, hipStrea
   if (a.S > kMaxSplits || D % 64 != 0) return hipErrorInvalidValue;
   dim3 grid(D / 64, a.R, B * a.Hkv);
   switch (mode) {
-    case kPerRow: hipLaunchKernelGGL(combine_kernel<kPerRow>, grid, dim3(64), 0, st, a, D); break;
-    case kPerTensor: hipLaunchKernelGGL(combine_kernel<kPerTensor>, grid, dim3(64), 0, st, a, D); break;
-    case kPerChannel: hipLaunchKernelGGL(combine_kernel<kPerChannel>, grid, dim3(64), 0, st, a, D); break;
+    case kPerRow: hipLaunchKernelGGL(combine_kernel<kPerRow>, grid, dim3(256), 0, st, a, D); break;
+    case kPerTensor: hipLaunchKernelGGL(combine_kernel<kPerTensor>, grid, dim3(256), 0, st, a, D); break;
+    case kPerChannel: hipLaunchKernelGGL(combine_kernel<kPerChannel>, grid, dim3(256), 0, st, a, D); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -92,22 +92,35 @@ __device__ __forceinline__ int v_channel(int c, int j) {
   }
 }
 
-// Streaming loads of cache codes: each byte is read once per decode, so they
-// are issued non-temporal (measured on MI355X: the same read pattern goes from
-// 5.7 to 6.2 TB/s).
+// Cache codes and row scales are read with buffer loads through a descriptor
+// that covers exactly the valid rows of the tile: rows past the sequence end,
+// tiles past the split's last one and blocks outside the pool read as zero
+// without a memory access (the descriptor's record count is 0 or the valid
+// bytes).  So every wavefront runs one unconditional load sequence -- the
+// compiler's waits stay exact -- and ragged tails never see stale bytes.  All
+// offsets go in the per-lane offset, which is the part the range check covers.
+// The loads are non-temporal: each byte is read once per decode (measured on
+// MI355X: the same read pattern goes from 5.7 to 6.2 TB/s).
+constexpr int kBufWord3 = 0x00020000;  // gfx9 raw-buffer descriptor format word
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufWord3);
+}
+
 template <int N>
-__device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* out) {
+__device__ __forceinline__ void load_bytes(__amdgpu_buffer_rsrc_t r, int off, uint32_t* out) {
   if constexpr (N == 16) {
-    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
     out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
   } else if constexpr (N == 8) {
-    u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal);
     out[0] = v[0]; out[1] = v[1];
   } else if constexpr (N == 4) {
-    out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
   } else {
     static_assert(N == 2, "unsupported chunk");
-    out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNonTemporal);
   }
 }
 
@@ -167,9 +180,11 @@ struct Tile {
   int ok;                           // block-table entry inside the pool
 };
 
+// Issue the loads of tile t (tokens 16t..16t+15).  `live` is false for the
+// tiles a wavefront loads past the end of its split; those read nothing.
 template <int DT, int MODE, int D>
-__device__ __forceinline__ void load_tile(const SplitArgs& a, int b, int hkv, int t, int n, int g,
-                                          Tile<DT, D>& T) {
+__device__ __forceinline__ void load_tile(const SplitArgs& a, int b, int hkv, int t, bool live,
+                                          int L, int n, int g, Tile<DT, D>& T) {
   using G_ = Geo<DT, D>;
   constexpr int ROWB = G_::ROWB;
   const int bs = a.c.block_size;
@@ -177,22 +192,33 @@ __device__ __forceinline__ void load_tile(const SplitArgs& a, int b, int hkv, in
   int blk = b;
   int ok = 1;
   if (a.c.block_table != nullptr) {
-    blk = a.c.block_table[(size_t)b * a.c.max_blocks + tok0 / bs];
+    const int idx = min(tok0 / bs, a.c.max_blocks - 1);  // in range even for dead tiles
+    blk = a.c.block_table[(size_t)b * a.c.max_blocks + idx];
     ok = (unsigned)blk < (unsigned)a.c.num_blocks;
     blk = ok ? blk : 0;
   }
   blk = __builtin_amdgcn_readfirstlane(blk);
   T.ok = __builtin_amdgcn_readfirstlane(ok);
+  int rows = (live && ok) ? min(kTile, L - tok0) : 0;
+  rows = __builtin_amdgcn_readfirstlane(rows);
   const size_t row0 = ((size_t)blk * a.c.Hkv + hkv) * (size_t)bs + (size_t)(tok0 % bs);
-  const uint8_t* kp = a.c.k_codes + (row0 + n) * ROWB + G_::KCH * g;
+  const auto kr = make_rsrc(a.c.k_codes + row0 * ROWB, rows * ROWB);
+  const auto vr = make_rsrc(a.c.v_codes + row0 * ROWB, rows * ROWB);
+  const int koff = n * ROWB + G_::KCH * g;
 #pragma unroll
-  for (int c = 0; c < G_::KNCH; ++c) load_bytes<G_::KCH>(kp + c * 4 * G_::KCH, T.kw + c * (G_::KCH / 4));
-  const uint8_t* vp = a.c.v_codes + (row0 + 4 * g) * ROWB + G_::VLB * n;
+  for (int c = 0; c < G_::KNCH; ++c)
+    load_bytes<G_::KCH>(kr, koff + c * 4 * G_::KCH, T.kw + c * (G_::KCH / 4));
+  const int voff = 4 * g * ROWB + G_::VLB * n;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) load_bytes<G_::VLB>(vp + e * ROWB, T.vw[e]);
+  for (int e = 0; e < 4; ++e) load_bytes<G_::VLB>(vr, voff + e * ROWB, T.vw[e]);
   if constexpr (MODE == kPerRow) {
-    T.ks4 = *reinterpret_cast<const float4_t*>(a.c.k_scales + row0 + 4 * g);
-    T.vs4 = *reinterpret_cast<const float4_t*>(a.c.v_scales + row0 + 4 * g);
+    uint32_t w[4];
+    load_bytes<16>(make_rsrc(a.c.k_scales + row0, rows * 4), 16 * g, w);
+    T.ks4 = float4_t{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                     __uint_as_float(w[3])};
+    load_bytes<16>(make_rsrc(a.c.v_scales + row0, rows * 4), 16 * g, w);
+    T.vs4 = float4_t{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                     __uint_as_float(w[3])};
   }
 }
 
@@ -218,18 +244,8 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
 #pragma unroll
   for (int e = 0; e < 4; ++e) valid[e] = ok && tbase + e < L;
 
-  uint32_t vw[4][G_::VDW];
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-#pragma unroll
-    for (int w = 0; w < G_::VDW; ++w) vw[e][w] = T.vw[e][w];
-  if (!ok || tok0 + kTile > L) {  // rows past the sequence may hold anything, fp8 NaN included
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (!valid[e])
-#pragma unroll
-        for (int w = 0; w < G_::VDW; ++w) vw[e][w] = 0u;
-  }
+  // (rows past the sequence were read as zero by the bounded loads)
+  const auto& vw = T.vw;
 
   // Per-row V scales: keep vref a power of two >= every scale seen, so the
   // weights p * s / vref stay in [0, 1].  The reduction runs only on the rare
@@ -421,16 +437,13 @@ split_decode_kernel(SplitArgs a) {
 
   // ---- the wavefront's tiles are tb + wave, tb + wave + 4, ...; start the
   // loads of the first NB now so their latency overlaps the query prologue.
-  // Loads past the last tile re-read the last tile (already in L2), so every
-  // buffer is always filled by the same instruction sequence.
-  // Every load is issued unconditionally (index clamped into [0, te-1], tile 0
-  // when the wavefront has none: tile 0 is addressable for any length) so no
-  // branch joins on in-flight loads and the waits stay exact.
+  // Every load is issued unconditionally (tiles past the split read nothing),
+  // so no branch joins on in-flight loads and the waits stay exact.
   const int t0 = tb + wave;
-  const int tlast = max(te - 1, 0);
   Tile<DT, D> buf[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) load_tile<DT, MODE, D>(a, b, hkv, min(t0 + i * kWaves, tlast), n, g, buf[i]);
+  for (int i = 0; i < NB; ++i)
+    load_tile<DT, MODE, D>(a, b, hkv, t0 + i * kWaves, t0 + i * kWaves < te, L, n, g, buf[i]);
 
   // ---- stage the query rows in LDS (bf16), zero padding rows
   uint16_t* qs = reinterpret_cast<uint16_t*>(smem);
@@ -509,7 +522,7 @@ split_decode_kernel(SplitArgs a) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (t < te) process_tile<DT, MODE, D, RB>(buf[i], t, L, n, g, qb, rowmul, lim, W);
-      load_tile<DT, MODE, D>(a, b, hkv, min(t + NB * kWaves, tlast), n, g, buf[i]);
+      load_tile<DT, MODE, D>(a, b, hkv, t + NB * kWaves, t + NB * kWaves < te, L, n, g, buf[i]);
       t += kWaves;
     }
   }
