@@ -92,6 +92,21 @@ __device__ __forceinline__ int v_channel(int c, int j) {
   }
 }
 
+// Inverse of v_channel within a lane: the column c holding channel
+// NCOL * j + o (every lane covers NCOL consecutive channels).
+template <int DT, int D>
+__device__ __forceinline__ constexpr int col_of(int o) {
+  using G_ = Geo<DT, D>;
+  if constexpr (DT == kInt4) {
+    constexpr int nb = G_::VLB >= 4 ? 4 : G_::VLB;
+    const int w = o / 8, within = o % 8;  // 8 channels per dword of nibbles
+    const int k = within / 2, odd = within % 2;
+    return 2 * nb * w + odd * nb + k;
+  } else {
+    return o;
+  }
+}
+
 // Cache codes and row scales are read with buffer loads through a descriptor
 // that covers exactly the valid rows of the tile: rows past the sequence end,
 // tiles past the split's last one and blocks outside the pool read as zero
@@ -397,7 +412,7 @@ split_decode_kernel(SplitArgs a) {
   constexpr int RP = 16 * RB;  // padded query rows
   constexpr int NB = K_::NB;
 
-  __shared__ float smem[K_::MERGE_BUFS * RP * D];  // q staging (as bf16), then merge buffers
+  __shared__ __attribute__((aligned(16))) float smem[K_::MERGE_BUFS * RP * D];  // q staging (as bf16), then merge buffers
   __shared__ float s_m[kWaves][RP];
   __shared__ float s_l[kWaves][RP];
 
@@ -559,7 +574,12 @@ split_decode_kernel(SplitArgs a) {
       fac[rb][e] = f;
     }
 
-  // each wavefront writes its weighted rows; the sum runs in wave order
+  // each wavefront writes its weighted rows; the sum runs in wave order.
+  // Lane column n owns the NCOL consecutive channels [NCOL*n, NCOL*(n+1)); they
+  // go to LDS as 16-byte chunks whose order is rotated by n / (64 / NCOL) so the
+  // 16 lanes of a pass hit distinct banks.
+  constexpr int NCH = G_::NCOL / 4;                 // 16-byte chunks per lane and row
+  constexpr int ROT = G_::NCOL >= 16 ? 4 : (G_::NCOL == 8 ? 8 : 16);
   const int nbuf = K_::MERGE_BUFS;
   for (int round = 0; round < kWaves / nbuf; ++round) {
     const int w_act = round * nbuf;  // first wave writing this round
@@ -568,17 +588,20 @@ split_decode_kernel(SplitArgs a) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int c = 0; c < G_::NCOL; ++c) {
-          const int d = v_channel<DT, D>(c, n);
+        for (int e = 0; e < 4; ++e) {
+          const int r = rb * 16 + 4 * g + e;
+          if (r < a.R) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = rb * 16 + 4 * g + e;
-            if (r < a.R) {
-              const float v = W.acc[rb][c][e] * fac[rb][e];
+            for (int k = 0; k < NCH; ++k) {
+              float4_t v;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = W.acc[rb][col_of<DT, D>(4 * k + i)][e] * fac[rb][e];
+              const int slot = (k + n / ROT) % NCH;
+              float4_t* dst = reinterpret_cast<float4_t*>(ob + r * D + G_::NCOL * n + 4 * slot);
               if (round == 0)
-                ob[r * D + d] = v;
+                *dst = v;
               else
-                ob[r * D + d] += v;
+                *dst += v;
             }
           }
         }
@@ -589,9 +612,11 @@ split_decode_kernel(SplitArgs a) {
   const size_t head = (size_t)b * a.c.Hkv + hkv;
   for (int idx = tid * 4; idx < a.R * D; idx += 256 * 4) {
     const int r = idx / D, d = idx % D;
-    float4_t v = *reinterpret_cast<const float4_t*>(smem + r * D + d);
+    const int jn = d / G_::NCOL, k = (d % G_::NCOL) / 4;
+    const int off = r * D + G_::NCOL * jn + 4 * ((k + jn / ROT) % NCH);
+    float4_t v = *reinterpret_cast<const float4_t*>(smem + off);
 #pragma unroll
-    for (int w = 1; w < nbuf; ++w) v += *reinterpret_cast<const float4_t*>(smem + (size_t)w * RP * D + r * D + d);
+    for (int w = 1; w < nbuf; ++w) v += *reinterpret_cast<const float4_t*>(smem + (size_t)w * RP * D + off);
     *reinterpret_cast<float4_t*>(a.ws_o + ((head * a.R + r) * a.S + s) * D + d) = v;
   }
   if (tid < a.R) {
