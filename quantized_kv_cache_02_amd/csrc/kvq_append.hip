@@ -66,6 +66,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int j = (int)(rest % a.Tn);
   const int b = (int)(rest / a.Tn);
 
+  // the row load does not depend on the position: issue it first so the two
+  // memory round trips overlap (unconditional, clamped for idle lanes)
+  const uint16_t* x = (side ? a.v : a.k) + (((size_t)b * a.Tn + j) * Hkv + h) * D;
+  const bool active = lane < ACTIVE;
+  uint16_t raw[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) raw[e] = x[active ? lane * EPL + e : 0];
+
   const int pos = a.positions[b] + j;
   if (pos < 0 || pos >= a.capacity) return;
   const int bs = a.c.block_size;
@@ -75,14 +83,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     if (blk < 0 || blk >= a.c.num_blocks) return;
   }
   const size_t ri = ((size_t)blk * Hkv + h) * bs + (size_t)(pos % bs);
-  const uint16_t* x = (side ? a.v : a.k) + (((size_t)b * a.Tn + j) * Hkv + h) * D;
   uint8_t* codes = (side ? a.c.v_codes : a.c.k_codes) + ri * ROWB;
   float* scales = side ? a.c.v_scales : a.c.k_scales;
 
   float xv[EPL];
-  const bool active = lane < ACTIVE;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) xv[e] = active ? bf16_to_f32(x[lane * EPL + e]) : 0.0f;
+  for (int e = 0; e < EPL; ++e) xv[e] = active ? bf16_to_f32(raw[e]) : 0.0f;
 
   float s_row = 0.0f;
   if constexpr (MODE == kPerRow) {

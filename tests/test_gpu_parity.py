@@ -223,14 +223,14 @@ def test_query_tokens_beyond_length():
 def test_split_count_does_not_change_results_beyond_rounding():
     """Raising the host bound changes the number of splits; results stay within tolerance
     of the oracle and of each other."""
-    w = ki.make_workload(3, ctx=8192, dtype="int8")
+    ctx = 2048
+    w = ki.make_workload(3, ctx=ctx, dtype="int8")
     cache = gu.gpu_cache(w)
     gu.gpu_build(w, cache)
     cap = cache.block_size
-    a = gu.gpu_decode(w, cache, None, max_seq_len=8192)
-    s_a = kvq.num_splits(cache, 1, 24, 1, 8192)
-    w2 = ki.make_workload(3, ctx=8192, dtype="int8")
-    big = kvq.KVCache(w2.dtype, w2.mode, w2.Hkv, w2.D, 65536, 1)
+    a = gu.gpu_decode(w, cache, None, max_seq_len=ctx)
+    s_a = kvq.num_splits(cache, 1, 24, 1, ctx)
+    big = kvq.KVCache(w.dtype, w.mode, w.Hkv, w.D, 65536, 1)
     big.k_codes[:, :, :cap] = cache.k_codes
     big.v_codes[:, :, :cap] = cache.v_codes
     big.k_scales[:, :, :cap] = cache.k_scales
