@@ -44,6 +44,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int D) {
   const float* ms = a.ws_m + rowbase;
   const float* ls = a.ws_l + rowbase;
 
+  // The first batch of partial outputs does not depend on the split maxima:
+  // issue those loads first so they share one round trip with m and l.
+  const float* os = a.ws_o + rowbase * D + d;
+  float4_t v0[kBatch];
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    const int s = grp + i * kGroups;
+    v0[i] = *reinterpret_cast<const float4_t*>(os + (size_t)(s < S ? s : 0) * D);
+  }
+
   // M: per-thread max over s = tid, tid+256, ..., then waves, then in wave order
   float M = -INFINITY;
   for (int s = tid; s < S; s += 256) M = fmaxf(M, ms[s]);
@@ -64,16 +74,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int D) {
   __syncthreads();
   const float Lsum = ((red[0] + red[1]) + red[2]) + red[3];
 
-  // weighted sum of this thread's splits s = grp, grp + 16, ...
+  // weighted sum of this thread's splits s = grp, grp + 16, ... in order
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const float* os = a.ws_o + rowbase * D + d;
-  for (int s0 = grp; s0 < S; s0 += kGroups * kBatch) {
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    const int s = grp + i * kGroups;
+    if (s < S) acc += w_s[s] * v0[i];
+  }
+  for (int s0 = grp + kGroups * kBatch; s0 < S; s0 += kGroups * kBatch) {
     float4_t v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int s = s0 + i * kGroups;
-      v[i] = (s < S) ? *reinterpret_cast<const float4_t*>(os + (size_t)s * D)
-                     : float4_t{0.f, 0.f, 0.f, 0.f};
+      v[i] = *reinterpret_cast<const float4_t*>(os + (size_t)(s < S ? s : 0) * D);
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
