@@ -177,6 +177,30 @@ int kvq_paged_decode_attend(const kvq_cache* cache, const void* q, int32_t batch
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvq_append_decode_attend -- one decode step in one call: quantize the query
+ * tokens' new K and V rows into the cache, then attend ([P] "CUDA kernels":
+ * the operator quantizes the new rows on write with ReshapeAndCache and then
+ * runs the paged decode; [K] "Usage": append(k, v) followed by attend(q)).
+ *
+ *   k_new, v_new  bf16 [batch, q_tokens, num_kv_heads, head_dim]: row j of
+ *                 sequence b is written at position seq_lens[b] - q_tokens + j
+ *                 (the query tokens are the last tokens of the sequence).
+ *   block_table   int32 [batch, max_blocks], or NULL for the contiguous cache.
+ *   Everything else as kvq_decode_attend / kvq_paged_decode_attend.
+ *
+ * The cache afterwards holds exactly what kvq_append(k_new, v_new,
+ * positions = seq_lens - q_tokens) would have written, and `out` equals that
+ * append followed by the decode.  The new rows are quantized inside the decode
+ * kernel by the wavefront that reads them, which saves a launch per step.
+ */
+int kvq_append_decode_attend(const kvq_cache* cache, const void* k_new, const void* v_new,
+                             const void* q, int32_t batch, int32_t num_q_heads, int32_t q_tokens,
+                             const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                             const float* head_sink, const int32_t* block_table,
+                             int32_t max_blocks, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * The two phases the decode entry points are made of, for callers that
  * schedule them separately ([K] "Method": the sequence is split across
  * workgroups and the partials are merged in a fixed order).

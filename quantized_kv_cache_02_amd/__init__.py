@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "INT8", "INT4", "FP8_E4M3FN", "PER_ROW", "PER_TENSOR", "PER_CHANNEL",
     "KVCache", "KvqError", "append", "num_splits", "workspace_bytes", "decode_attend",
-    "paged_decode_attend", "split_decode", "combine", "cache_bytes", "lib", "LIB_PATH",
+    "paged_decode_attend", "append_decode_attend", "split_decode", "combine", "cache_bytes",
+    "lib", "LIB_PATH",
 ]
 
 INT8, INT4, FP8_E4M3FN = 1, 2, 3
@@ -27,7 +28,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 EXPORTS = (
     "kvq_append", "kvq_num_splits", "kvq_workspace_bytes", "kvq_decode_attend",
-    "kvq_paged_decode_attend", "kvq_split_decode", "kvq_combine", "kvq_cache_bytes",
+    "kvq_paged_decode_attend", "kvq_append_decode_attend", "kvq_split_decode", "kvq_combine",
+    "kvq_cache_bytes",
     "kvq_status_string",
 )
 
@@ -69,6 +71,9 @@ def lib():
         L.kvq_paged_decode_attend.argtypes = [CP, P, I32, I32, I32, P, I32, F, P, P, I32, P, P,
                                               SZ, P]
         L.kvq_paged_decode_attend.restype = ctypes.c_int
+        L.kvq_append_decode_attend.argtypes = [CP, P, P, P, I32, I32, I32, P, I32, F, P, P, I32,
+                                               P, P, SZ, P]
+        L.kvq_append_decode_attend.restype = ctypes.c_int
         L.kvq_split_decode.argtypes = [CP, P, I32, I32, I32, P, I32, F, P, I32, P, SZ, P]
         L.kvq_split_decode.restype = ctypes.c_int
         L.kvq_combine.argtypes = [CP, I32, I32, I32, I32, P, P, P, SZ, P]
@@ -215,6 +220,32 @@ def paged_decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor,
                                          _ptr(block_table), block_table.shape[1], _ptr(out),
                                          _ptr(ws), nbytes, _stream(stream)),
            "kvq_paged_decode_attend")
+    return out
+
+
+def append_decode_attend(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                         q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                         softmax_scale: float, block_table: Optional[torch.Tensor] = None,
+                         head_sink: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step: write the query tokens' K/V rows (bf16 [B, Tq, Hkv, D]) at
+    positions seq_lens - Tq + j, then attend.  block_table None = contiguous cache."""
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (q, "q")):
+        _want(t, torch.bfloat16, nm)
+    _want(seq_lens, torch.int32, "seq_lens")
+    B, Tq, Hq, _ = q.shape
+    mb = 0
+    if block_table is not None:
+        _want(block_table, torch.int32, "block_table")
+        mb = block_table.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    ws, nbytes = _workspace(cache, B, Hq, Tq, max_seq_len, workspace, q.device)
+    _check(lib().kvq_append_decode_attend(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq,
+                                          Tq, _ptr(seq_lens), max_seq_len, float(softmax_scale),
+                                          _ptr(head_sink), _ptr(block_table), mb, _ptr(out),
+                                          _ptr(ws), nbytes, _stream(stream)),
+           "kvq_append_decode_attend")
     return out
 
 

@@ -140,7 +140,8 @@ hipError_t dispatch_split(int dt, int md, int D, int RB, const kvq::SplitArgs& a
 
 int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int32_t tq,
                const int32_t* seq_lens, int32_t max_seq_len, float scale, const int32_t* table,
-               int32_t max_blocks, void* ws, size_t ws_bytes, void* stream) {
+               int32_t max_blocks, void* ws, size_t ws_bytes, void* stream,
+               const void* k_new = nullptr, const void* v_new = nullptr) {
   DecodeShape sh;
   int st = decode_shape(c, batch, hq, tq, max_seq_len, &sh);
   if (st != KVQ_OK) return st;
@@ -160,6 +161,8 @@ int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int
   a.max_seq_len = max_seq_len;
   a.S = sh.S;
   a.sm_scale = scale;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
   workspace_ptrs(ws, c, batch, sh, &a.ws_o, &a.ws_m, &a.ws_l);
   hipError_t e = dispatch_split(c->dtype, c->scale_mode, c->head_dim, sh.RB, a, batch,
                                 static_cast<hipStream_t>(stream));
@@ -277,6 +280,22 @@ int kvq_paged_decode_attend(const kvq_cache* cache, const void* q, int32_t batch
   if (out == nullptr || !aligned16(out)) return KVQ_EINVAL;
   int st = split_impl(cache, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, softmax_scale,
                       block_table, max_blocks, workspace, workspace_bytes, stream);
+  if (st != KVQ_OK) return st;
+  return kvq_combine(cache, batch, num_q_heads, q_tokens, max_seq_len, head_sink, out, workspace,
+                     workspace_bytes, stream);
+}
+
+int kvq_append_decode_attend(const kvq_cache* cache, const void* k_new, const void* v_new,
+                             const void* q, int32_t batch, int32_t num_q_heads, int32_t q_tokens,
+                             const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                             const float* head_sink, const int32_t* block_table,
+                             int32_t max_blocks, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (k_new == nullptr || v_new == nullptr || !aligned16(k_new) || !aligned16(v_new))
+    return KVQ_EINVAL;
+  if (out == nullptr || !aligned16(out)) return KVQ_EINVAL;
+  int st = split_impl(cache, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, softmax_scale,
+                      block_table, max_blocks, workspace, workspace_bytes, stream, k_new, v_new);
   if (st != KVQ_OK) return st;
   return kvq_combine(cache, batch, num_q_heads, q_tokens, max_seq_len, head_sink, out, workspace,
                      workspace_bytes, stream);

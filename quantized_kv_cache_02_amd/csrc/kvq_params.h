@@ -54,6 +54,10 @@ struct SplitArgs {
   int32_t max_seq_len;
   int32_t S;  // splits per (sequence, KV head)
   float sm_scale;
+  // fused append (both null when not fused): bf16 [B, Tq, Hkv, D] rows of the
+  // query tokens, written at positions seq_len - Tq + j before they are read
+  const uint16_t* k_new;
+  const uint16_t* v_new;
   float* ws_o;  // [B, Hkv, R, S, D]  normalized split outputs
   float* ws_m;  // [B, Hkv, R, S]     split max logit (log2 units)
   float* ws_l;  // [B, Hkv, R, S]     split normalizer

@@ -31,7 +31,7 @@
 //   The softmax weights are fp16 in [0, 1] (relative rounding 2^-11); the
 //   accumulators are fp32.
 
-#include "kvq_device.h"
+#include "kvq_quant.h"
 
 #ifndef KVQ_DTYPE
 #error "KVQ_DTYPE must be defined"
@@ -449,6 +449,36 @@ split_decode_kernel(SplitArgs a) {
   const int tps = (ntiles + a.S - 1) / a.S;
   const int tb = s * tps;
   const int te = min(tb + tps, ntiles);
+
+  // ---- fused append: the wavefront that will read the tile holding a new
+  // position quantizes and stores that row first (the same arithmetic as
+  // kvq_append), then waits for its stores before it issues any tile load.
+  // No other wavefront reads those rows in this launch.
+  if (a.k_new != nullptr) {
+    const int first = max(L - a.Tq, 0);
+    bool wrote = false;
+    for (int p = first; p < L; ++p) {
+      const int t = p / kTile;
+      if (t < tb || t >= te || (t - tb) % kWaves != wave) continue;  // wave-uniform
+      int blk = b;
+      if (a.c.block_table != nullptr) {
+        blk = a.c.block_table[(size_t)b * a.c.max_blocks + p / a.c.block_size];
+        if ((unsigned)blk >= (unsigned)a.c.num_blocks) continue;
+      }
+      const size_t ri = ((size_t)blk * a.c.Hkv + hkv) * a.c.block_size + (size_t)(p % a.c.block_size);
+      const size_t xi = (((size_t)b * a.Tq + (p - (L - a.Tq))) * a.c.Hkv + hkv) * D;
+      using RG = RowGeo<DT, D>;
+      uint16_t rk[RG::EPL], rv[RG::EPL];
+      load_row<DT, D>(a.k_new + xi, lane, rk);
+      load_row<DT, D>(a.v_new + xi, lane, rv);
+      quantize_store_row<DT, MODE, D>(rk, lane, a.c.k_codes + ri * RG::ROWB, a.c.k_scales + ri,
+                                      MODE == kPerChannel ? a.c.k_scales + (size_t)hkv * D : a.c.k_scales);
+      quantize_store_row<DT, MODE, D>(rv, lane, a.c.v_codes + ri * RG::ROWB, a.c.v_scales + ri,
+                                      MODE == kPerChannel ? a.c.v_scales + (size_t)hkv * D : a.c.v_scales);
+      wrote = true;
+    }
+    if (wrote) __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before any load of those rows
+  }
 
   // ---- the wavefront's tiles are tb + wave, tb + wave + 4, ...; start the
   // loads of the first NB now so their latency overlaps the query prologue.

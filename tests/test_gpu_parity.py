@@ -290,3 +290,87 @@ def test_graph_capture_replays_equal_eager():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
         _ = (q.float() * 2).sum().item()  # unrelated eager work between replays
+
+
+# ------------------------------------------------- fused append + decode
+
+def _fused_vs_separate(w, what):
+    """Cache built from all but the last Tq rows, then one kvq_append_decode_attend;
+    against kvq_append of every row + decode: identical cache bytes, identical output."""
+    dev = "cuda"
+    gu.log(what)
+    table = None if w.block_table is None else torch.from_numpy(w.block_table).to(dev)
+    fused, sep = gu.gpu_cache(w), gu.gpu_cache(w)
+    Tq = w.Tq
+    for b in range(w.B):
+        L = int(w.lens[b])
+        # a contiguous cache holds sequence b in block b: a one-entry table
+        # sends this one-sequence append there
+        bt = (torch.tensor([[b]], dtype=torch.int32, device=dev) if table is None
+              else table[b:b + 1].contiguous())
+        head = max(L - Tq, 0)
+        k = w.k[b:b + 1].to(dev)
+        v = w.v[b:b + 1].to(dev)
+        z = torch.zeros(1, dtype=torch.int32, device=dev)
+        if head > 0:
+            kvq.append(fused, k[:, :head].contiguous(), v[:, :head].contiguous(), z, bt)
+        if L > 0:
+            kvq.append(sep, k[:, :L].contiguous(), v[:, :L].contiguous(), z, bt)
+    # the new rows: the last Tq positions of every sequence (rows before 0 unused)
+    kn = torch.zeros(w.B, Tq, w.Hkv, w.D, dtype=torch.bfloat16)
+    vn = torch.zeros_like(kn)
+    for b in range(w.B):
+        L = int(w.lens[b])
+        for j in range(Tq):
+            p = L - Tq + j
+            if p >= 0:
+                kn[b, j] = w.k[b, p]
+                vn[b, j] = w.v[b, p]
+    q = w.q.to(dev)
+    lens = torch.from_numpy(w.lens).to(dev)
+    sink = None if w.sink is None else torch.from_numpy(w.sink).to(dev)
+    msl = max(int(w.lens.max()), 1)
+    got = kvq.append_decode_attend(fused, kn.to(dev), vn.to(dev), q, lens, msl, w.sm_scale,
+                                   block_table=table, head_sink=sink)
+    if table is None:
+        want = kvq.decode_attend(sep, q, lens, msl, w.sm_scale, head_sink=sink)
+    else:
+        want = kvq.paged_decode_attend(sep, q, lens, msl, w.sm_scale, table, head_sink=sink)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.k_codes, sep.k_codes) and torch.equal(fused.v_codes, sep.v_codes), what
+    if w.mode == PER_ROW:
+        assert torch.equal(fused.k_scales, sep.k_scales) and torch.equal(fused.v_scales, sep.v_scales)
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16)), what
+    ref, _, _ = oracle.reference(w)
+    gu.check_output(got, ref, what)
+
+
+def test_fused_append_decode_64k_int8():
+    _fused_vs_separate(ki.make_workload(3, ctx=65536, dtype="int8"), "fused 64K int8")
+
+
+def test_fused_append_decode_paged_fp8_sink():
+    _fused_vs_separate(ki.make_workload(4, max_len=3000), "fused paged fp8 sink")
+
+
+def test_fused_append_decode_spec_int4_per_channel():
+    _fused_vs_separate(ki.make_workload(5, ctx=1000), "fused paged int4 spec")
+
+
+def test_fused_append_decode_drafts_across_splits():
+    # 2884 tokens = 181 tiles; the drafts 2876..2883 fall on both sides of a
+    # split boundary, so two workgroups each append part of them
+    w = ki.random_workload(5900, B=1, Hkv=2, G=4, D=128, Tq=8, lens=[2884], dtype=INT8,
+                           mode=PER_ROW, block_size=None)
+    S = kvq.num_splits(gu.gpu_cache(w), 1, w.Hq, w.Tq, 2884)
+    tps = (181 + S - 1) // S
+    assert (2876 // 16) // tps != (2883 // 16) // tps, f"S={S} puts the drafts in one split"
+    _fused_vs_separate(w, "fused drafts across splits")
+
+
+@pytest.mark.parametrize("lens", [[8], [3, 0, 9], [9, 17, 24], [15, 16, 31], [130, 1000, 4100]])
+def test_fused_append_decode_drafts_across_tiles(lens):
+    for dt, md, paged in ((INT8, PER_ROW, False), (INT4, PER_ROW, True), (FP8, PER_TENSOR, True)):
+        w = ki.random_workload(5000 + sum(lens) + dt, B=len(lens), Hkv=2, G=3, D=128, Tq=8,
+                               lens=lens, dtype=dt, mode=md, block_size=16 if paged else None)
+        _fused_vs_separate(w, f"fused dt={dt} lens={lens}")
