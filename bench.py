@@ -3,8 +3,9 @@
 
 Workload (default): batch 1, 24 query heads, 4 KV heads, head_dim 256, an int8
 cache with per-row absmax scales holding 65,536 tokens, one query token.  One
-step = kvq_append of the new token's K/V row + split-KV decode + fixed-order
-combine, i.e. the whole hot path.  Steps rotate over 16 layer caches (16 x
+step = quantize-on-append of the new token's K/V row + split-KV decode +
+fixed-order combine, i.e. the whole hot path, issued as kvq_append_decode_attend
+(the append runs inside the split kernel) unless --separate-append is given.  Steps rotate over 16 layer caches (16 x
 130 MiB) so the 256 MB Infinity Cache cannot serve the KV bytes, and run as
 HIP-graph replays of 16 steps.  Inputs are seeded synthetic tensors already
 resident in HBM when the timed region starts.
@@ -73,7 +74,8 @@ def build_layers(kvq, torch, w, layers: int, dev):
     return caches, k[:, -1:].contiguous(), v[:, -1:].contiguous()
 
 
-def time_config(kvq, torch, ki, dtype: str, ctx: int, layers: int, steps: int, warmup: int, dev):
+def time_config(kvq, torch, ki, dtype: str, ctx: int, layers: int, steps: int, warmup: int, dev,
+                fused: bool = True):
     w = ki.make_workload(3, ctx=ctx, dtype=dtype)
     caches, kn, vn = build_layers(kvq, torch, w, layers, dev)
     q = w.q.to(dev)
@@ -85,9 +87,13 @@ def time_config(kvq, torch, ki, dtype: str, ctx: int, layers: int, steps: int, w
     S = kvq.num_splits(caches[0], B, Hq, Tq, ctx)
 
     def step(c, s):
-        kvq.append(c, kn, vn, pos, stream=s)
-        kvq.split_decode(c, q, lens, ctx, w.sm_scale, ws, stream=s)
-        kvq.combine(c, B, Hq, Tq, ctx, ws, out, stream=s)
+        if fused:
+            kvq.append_decode_attend(c, kn, vn, q, lens, ctx, w.sm_scale, out=out, workspace=ws,
+                                     stream=s)
+        else:
+            kvq.append(c, kn, vn, pos, stream=s)
+            kvq.split_decode(c, q, lens, ctx, w.sm_scale, ws, stream=s)
+            kvq.combine(c, B, Hq, Tq, ctx, ws, out, stream=s)
 
     def split_only(c, s):
         kvq.split_decode(c, q, lens, ctx, w.sm_scale, ws, stream=s)
@@ -168,6 +174,9 @@ def main():
     ap.add_argument("--dtype", default="int8", choices=["int8", "int4"])
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--separate-append", action="store_true",
+                    help="run the step as three launches (kvq_append, split, combine) instead of "
+                         "kvq_append_decode_attend (append fused into the split kernel, then combine)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default="", help="also time the context sweep for int8 and int4 "
                                                 "and write the lines to this JSON-lines file")
@@ -202,7 +211,9 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "dispatches": 20}))
         return
 
-    r = time_config(kvq, torch, ki, args.dtype, args.ctx, args.layers, args.steps, args.warmup, dev)
+    fused = not args.separate_append
+    r = time_config(kvq, torch, ki, args.dtype, args.ctx, args.layers, args.steps, args.warmup, dev,
+                    fused)
     w = r.pop("workload")
     achieved = r["bytes"] / (r["split_ms"] * 1e-3) / 1e9
     value = r["bytes"] / (r["step_ms"] * 1e-3) / 1e9
@@ -225,6 +236,8 @@ def main():
         "config": {
             "workload": f"decode B1 Hq24 Hkv4 D256, {args.dtype} per-row absmax cache, "
                         f"{args.ctx}-token context, 1 query token, {args.layers} layer caches rotated",
+            "step": ("kvq_append_decode_attend (append fused into the split kernel) + combine"
+                     if fused else "kvq_append + split decode + combine"),
             "cache_dtype": args.dtype,
             "context": args.ctx,
             "splits": r["splits"],
@@ -257,7 +270,7 @@ def main():
                 for ctx in ki.SWEEP_CTX:
                     layers = args.layers if ctx <= 65536 else 8
                     s = time_config(kvq, torch, ki, dt, ctx, layers, max(64, args.steps // 4),
-                                    args.warmup, dev)
+                                    args.warmup, dev, fused)
                     s.pop("workload")
                     s["step_GBps"] = s["bytes"] / (s["step_ms"] * 1e-3) / 1e9
                     s["split_GBps"] = s["bytes"] / (s["split_ms"] * 1e-3) / 1e9
