@@ -56,47 +56,70 @@ def measured_traffic(bytes_per_launch_alg: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def algorithmic_bytes(dtype: str, ctx: int, hkv: int, d: int) -> int:
-    row = d if dtype in ("int8", "fp8") else d // 2
-    return 2 * ctx * hkv * (row + 4)
+def algorithmic_bytes(w) -> int:
+    """K and V codes plus per-row scales of every cached token the step reads."""
+    row = w.D // 2 if w.dtype == 2 else w.D
+    per_row_scale = 4 if w.mode == 1 else 0
+    return int(2 * int(w.lens.sum()) * w.Hkv * (row + per_row_scale))
 
 
 def build_layers(kvq, torch, w, layers: int, dev):
-    """`layers` caches of the workload, each quantized by kvq_append from the same rows."""
+    """`layers` caches of the workload, each quantized by kvq_append from the same
+    rows, and the step's new rows (the last Tq of each sequence), [B, Tq, Hkv, D]."""
     k = w.k.to(dev)
     v = w.v.to(dev)
+    table = None if w.block_table is None else torch.from_numpy(w.block_table).to(dev)
     caches = []
     for _ in range(layers):
-        c = kvq.KVCache(w.dtype, w.mode, w.Hkv, w.D, w.block_size, w.num_blocks, device=dev)
-        kvq.append(c, k, v, torch.zeros(w.B, dtype=torch.int32, device=dev))
+        c = kvq.KVCache(w.dtype, w.mode, w.Hkv, w.D, w.block_size, w.num_blocks, w.k_static,
+                        w.v_static, device=dev)
+        if table is None:
+            kvq.append(c, k, v, torch.zeros(w.B, dtype=torch.int32, device=dev))
+        else:
+            for b in range(w.B):
+                L = int(w.lens[b])
+                if L > 0:
+                    kvq.append(c, k[b:b + 1, :L].contiguous(), v[b:b + 1, :L].contiguous(),
+                               torch.zeros(1, dtype=torch.int32, device=dev), table[b:b + 1].contiguous())
         caches.append(c)
+    kn = torch.zeros(w.B, w.Tq, w.Hkv, w.D, dtype=torch.bfloat16, device=dev)
+    vn = torch.zeros_like(kn)
+    for b in range(w.B):
+        L = int(w.lens[b])
+        for j in range(w.Tq):
+            p = L - w.Tq + j
+            if p >= 0:
+                kn[b, j] = k[b, p]
+                vn[b, j] = v[b, p]
     torch.cuda.synchronize()
-    return caches, k[:, -1:].contiguous(), v[:, -1:].contiguous()
+    return caches, table, kn, vn
 
 
-def time_config(kvq, torch, ki, dtype: str, ctx: int, layers: int, steps: int, warmup: int, dev,
-                fused: bool = True):
-    w = ki.make_workload(3, ctx=ctx, dtype=dtype)
-    caches, kn, vn = build_layers(kvq, torch, w, layers, dev)
+def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fused: bool = True):
+    """Time `steps` decode steps of workload `w` rotated over `layers` caches, as
+    HIP-graph replays of one step per layer, and the split kernel alone."""
+    caches, table, kn, vn = build_layers(kvq, torch, w, layers, dev)
     q = w.q.to(dev)
     lens = torch.from_numpy(w.lens).to(dev)
-    pos = (lens - 1).contiguous()
+    pos = (lens - w.Tq).clamp(min=0).contiguous()
+    sink = None if w.sink is None else torch.from_numpy(w.sink).to(dev)
     B, Tq, Hq, D = q.shape
-    ws = torch.empty(kvq.workspace_bytes(caches[0], B, Hq, Tq, ctx), dtype=torch.uint8, device=dev)
+    msl = max(int(w.lens.max()), 1)
+    ws = torch.empty(kvq.workspace_bytes(caches[0], B, Hq, Tq, msl), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
-    S = kvq.num_splits(caches[0], B, Hq, Tq, ctx)
+    S = kvq.num_splits(caches[0], B, Hq, Tq, msl)
 
     def step(c, s):
         if fused:
-            kvq.append_decode_attend(c, kn, vn, q, lens, ctx, w.sm_scale, out=out, workspace=ws,
-                                     stream=s)
+            kvq.append_decode_attend(c, kn, vn, q, lens, msl, w.sm_scale, block_table=table,
+                                     head_sink=sink, out=out, workspace=ws, stream=s)
         else:
-            kvq.append(c, kn, vn, pos, stream=s)
-            kvq.split_decode(c, q, lens, ctx, w.sm_scale, ws, stream=s)
-            kvq.combine(c, B, Hq, Tq, ctx, ws, out, stream=s)
+            kvq.append(c, kn, vn, pos, block_table=table, stream=s)
+            kvq.split_decode(c, q, lens, msl, w.sm_scale, ws, block_table=table, stream=s)
+            kvq.combine(c, B, Hq, Tq, msl, ws, out, head_sink=sink, stream=s)
 
     def split_only(c, s):
-        kvq.split_decode(c, q, lens, ctx, w.sm_scale, ws, stream=s)
+        kvq.split_decode(c, q, lens, msl, w.sm_scale, ws, block_table=table, stream=s)
 
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
@@ -139,9 +162,17 @@ def time_config(kvq, torch, ki, dtype: str, ctx: int, layers: int, steps: int, w
         s1.record(stream)
         torch.cuda.synchronize()
         split_ms = s0.elapsed_time(s1) / (sreps * layers)
-    nbytes = algorithmic_bytes(dtype, ctx, w.Hkv, w.D)
-    return dict(ctx=ctx, dtype=dtype, steps=reps * layers, warmup=wreps * layers, step_ms=step_ms,
-                split_ms=split_ms, wall_s=wall_s, bytes=nbytes, splits=S, workload=w)
+    del graphs, caches
+    return dict(workload=w.name, steps=reps * layers, warmup=wreps * layers, step_ms=step_ms,
+                split_ms=split_ms, wall_s=wall_s, bytes=algorithmic_bytes(w), splits=S)
+
+
+def time_config(kvq, torch, ki, dtype: str, ctx: int, layers: int, steps: int, warmup: int, dev,
+                fused: bool = True):
+    w = ki.make_workload(3, ctx=ctx, dtype=dtype)
+    r = time_workload(kvq, torch, w, layers, steps, warmup, dev, fused)
+    r.update(ctx=ctx, dtype=dtype, workload=w)
+    return r
 
 
 def cpu_baseline(ki, w, seconds: float):
@@ -281,6 +312,20 @@ def main():
                           f"split {s['split_ms'] * 1e3:.2f} us {s['split_GBps']:.0f} GB/s",
                           file=sys.stderr, flush=True)
                     torch.cuda.empty_cache()
+            for cfg in (2, 4, 5):
+                w = ki.make_workload(cfg)
+                s = time_workload(kvq, torch, w, args.layers, max(64, args.steps // 4), args.warmup,
+                                  dev, fused)
+                s["cfg"] = cfg
+                s["step_GBps"] = s["bytes"] / (s["step_ms"] * 1e-3) / 1e9
+                s["split_GBps"] = s["bytes"] / (s["split_ms"] * 1e-3) / 1e9
+                s["split_frac_of_peak"] = s["split_GBps"] / PEAK_HBM_GBPS
+                f.write(json.dumps(s) + "\n")
+                f.flush()
+                print(f"[sweep] cfg{cfg} {w.name} step {s['step_ms'] * 1e3:.2f} us "
+                      f"split {s['split_ms'] * 1e3:.2f} us {s['split_GBps']:.0f} GB/s",
+                      file=sys.stderr, flush=True)
+                torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

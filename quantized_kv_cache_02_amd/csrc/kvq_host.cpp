@@ -84,7 +84,10 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   int64_t cap = ntiles / kMinTilesPerSplit;
   if (cap < 1) cap = 1;
   if (S > cap) S = cap;
-  if (S > kMaxSplits) S = kMaxSplits;
+  // every split within the block-table entries a workgroup holds
+  const int64_t need = (ntiles + kvq::kMaxTilesPerSplit - 1) / kvq::kMaxTilesPerSplit;
+  if (S < need) S = need;
+  if (S > kMaxSplits) return KVQ_EUNSUPPORTED;
   sh->G = G;
   sh->R = G * tq;
   sh->RB = (sh->R + 15) / 16;

@@ -15,6 +15,13 @@ constexpr int kTile = 16;
 // Wavefronts per decode workgroup; each owns a private online-softmax state.
 constexpr int kWaves = 4;
 
+// Block-table entries of a paged cache are read once per decode workgroup, in
+// its prologue, and held in registers: a wavefront keeps the entries of up to
+// kTableRegs * 64 of its tiles, so a split spans at most kMaxTilesPerSplit
+// tiles (the host sizes the split count accordingly).
+constexpr int kTableRegs = 4;
+constexpr int kMaxTilesPerSplit = kWaves * 64 * kTableRegs;
+
 // Decode-kernel register budget per variant: two waves per SIMD (<= 256
 // registers per lane) while the accumulators of the query row blocks fit,
 // otherwise one wave per SIMD (<= 512).  `RB` is the number of 16-row blocks

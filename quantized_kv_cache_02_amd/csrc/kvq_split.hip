@@ -195,24 +195,49 @@ struct Tile {
   int ok;                           // block-table entry inside the pool
 };
 
-// Issue the loads of tile t (tokens 16t..16t+15).  `live` is false for the
-// tiles a wavefront loads past the end of its split; those read nothing.
+// Block-table entries of a wavefront's tiles.  The wavefront's k-th tile is
+// t0 + kWaves * k; its entry sits in lane k % 64 of register k / 64.  Loaded
+// once before the first tile, so the tile loop never waits on a table read.
+struct TableRegs {
+  int e0, e1, e2, e3;  // kTableRegs == 4 (named, not an array: stays in registers)
+};
+static_assert(kTableRegs == 4, "TableRegs holds four registers");
+
+__device__ __forceinline__ int table_load_one(const int32_t* row, const SplitArgs& a, int t0,
+                                              int waves, int j, int lane) {
+  const int64_t t = (int64_t)t0 + (int64_t)waves * (64 * j + lane);
+  const int64_t idx = t * kTile / a.c.block_size;  // clamped: dead tiles stay in range
+  return row[idx < a.c.max_blocks ? idx : a.c.max_blocks - 1];
+}
+
+__device__ __forceinline__ TableRegs load_table(const SplitArgs& a, int b, int t0, int waves,
+                                                int lane) {
+  const int32_t* row = a.c.block_table + (size_t)b * a.c.max_blocks;
+  return TableRegs{table_load_one(row, a, t0, waves, 0, lane), table_load_one(row, a, t0, waves, 1, lane),
+                   table_load_one(row, a, t0, waves, 2, lane), table_load_one(row, a, t0, waves, 3, lane)};
+}
+
+// Entry of the wavefront's k-th tile (k wave-uniform, k < kTableRegs * 64 for
+// every live tile; larger k only occurs for dead tiles, which read nothing).
+__device__ __forceinline__ int table_entry(const TableRegs& r, int k) {
+  const int j = k >> 6;
+  const int v = j == 0 ? r.e0 : j == 1 ? r.e1 : j == 2 ? r.e2 : r.e3;
+  return __builtin_amdgcn_readlane(v, k & 63);
+}
+
+// Issue the loads of tile t (tokens 16t..16t+15) of block `blk` (the table
+// entry of a paged cache, the sequence index of a contiguous one).  `live` is
+// false for the tiles a wavefront loads past the end of its split; those read
+// nothing.
 template <int DT, int MODE, int D>
-__device__ __forceinline__ void load_tile(const SplitArgs& a, int b, int hkv, int t, bool live,
+__device__ __forceinline__ void load_tile(const SplitArgs& a, int hkv, int t, bool live, int blk,
                                           int L, int n, int g, Tile<DT, D>& T) {
   using G_ = Geo<DT, D>;
   constexpr int ROWB = G_::ROWB;
   const int bs = a.c.block_size;
   const int tok0 = t * kTile;
-  int blk = b;
-  int ok = 1;
-  if (a.c.block_table != nullptr) {
-    const int idx = min(tok0 / bs, a.c.max_blocks - 1);  // in range even for dead tiles
-    blk = a.c.block_table[(size_t)b * a.c.max_blocks + idx];
-    ok = (unsigned)blk < (unsigned)a.c.num_blocks;
-    blk = ok ? blk : 0;
-  }
-  blk = __builtin_amdgcn_readfirstlane(blk);
+  const int ok = (unsigned)blk < (unsigned)a.c.num_blocks;
+  blk = __builtin_amdgcn_readfirstlane(ok ? blk : 0);
   T.ok = __builtin_amdgcn_readfirstlane(ok);
   int rows = (live && ok) ? min(kTile, L - tok0) : 0;
   rows = __builtin_amdgcn_readfirstlane(rows);
@@ -485,10 +510,14 @@ split_decode_kernel(SplitArgs a) {
   // Every load is issued unconditionally (tiles past the split read nothing),
   // so no branch joins on in-flight loads and the waits stay exact.
   const int t0 = tb + wave;
+  const bool paged = a.c.block_table != nullptr;
+  TableRegs tbl;
+  if (paged) tbl = load_table(a, b, t0, kWaves, lane);
   Tile<DT, D> buf[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    load_tile<DT, MODE, D>(a, b, hkv, t0 + i * kWaves, t0 + i * kWaves < te, L, n, g, buf[i]);
+    load_tile<DT, MODE, D>(a, hkv, t0 + i * kWaves, t0 + i * kWaves < te, paged ? table_entry(tbl, i) : b,
+                           L, n, g, buf[i]);
 
   // ---- stage the query rows in LDS (bf16), zero padding rows
   uint16_t* qs = reinterpret_cast<uint16_t*>(smem);
@@ -563,12 +592,14 @@ split_decode_kernel(SplitArgs a) {
   }
   W.vref = 0x1p-126f;  // smallest normal: any nonzero scale above it raises the reference
 
-  for (int t = t0; t < te;) {
+  for (int t = t0, k = 0; t < te;) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (t < te) process_tile<DT, MODE, D, RB>(buf[i], t, L, n, g, qb, rowmul, lim, W);
-      load_tile<DT, MODE, D>(a, b, hkv, t + NB * kWaves, t + NB * kWaves < te, L, n, g, buf[i]);
+      load_tile<DT, MODE, D>(a, hkv, t + NB * kWaves, t + NB * kWaves < te,
+                             paged ? table_entry(tbl, k + NB) : b, L, n, g, buf[i]);
       t += kWaves;
+      ++k;
     }
   }
 
