@@ -116,7 +116,7 @@ def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fuse
         else:
             kvq.append(c, kn, vn, pos, block_table=table, stream=s)
             kvq.split_decode(c, q, lens, msl, w.sm_scale, ws, block_table=table, stream=s)
-            kvq.combine(c, B, Hq, Tq, msl, ws, out, head_sink=sink, stream=s)
+            kvq.combine(c, B, Hq, Tq, lens, msl, ws, out, head_sink=sink, stream=s)
 
     def split_only(c, s):
         kvq.split_decode(c, q, lens, msl, w.sm_scale, ws, block_table=table, stream=s)

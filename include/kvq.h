@@ -117,9 +117,12 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t bat
                int32_t max_blocks, void* stream);
 
 /*
- * kvq_num_splits -- number S of sequence splits the decode uses for a shape.
- * A pure function of its (host) arguments, so a captured graph and the
- * workspace size stay valid for every step that keeps the same bound.
+ * kvq_num_splits -- the decode's split divisor W for a shape: the tiles of
+ * all sequences are cut into chunks of C = max(ceil(T / W), 8) tiles (T = the
+ * 16-token tiles of the batch), so a single sequence of max_seq_len tokens is
+ * read by W workgroups per KV head.  A pure function of its (host) arguments,
+ * so a captured graph and the workspace size stay valid for every step that
+ * keeps the same bound.
  */
 int32_t kvq_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
                        int32_t q_tokens, int32_t max_seq_len);
@@ -205,9 +208,13 @@ int kvq_append_decode_attend(const kvq_cache* cache, const void* k_new, const vo
  * schedule them separately ([K] "Method": the sequence is split across
  * workgroups and the partials are merged in a fixed order).
  *
- * kvq_split_decode writes, for every (sequence, KV head, query row, split),
- * the split's max logit m, normalizer l and normalized partial output into the
- * workspace.  block_table may be NULL (contiguous cache; max_blocks ignored).
+ * kvq_split_decode writes, for every chunk of every sequence, KV head and
+ * query row, the chunk's max logit m, normalizer l and normalized partial
+ * output into the workspace.  Chunks are cut over the whole batch: the T
+ * 16-token tiles of all sequences are divided into chunks of
+ * C = max(ceil(T / W), 8) tiles that never straddle two sequences
+ * (W = kvq_num_splits), so ragged batches keep every workgroup equally busy.
+ * block_table may be NULL (contiguous cache; max_blocks ignored).
  */
 int kvq_split_decode(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
                      int32_t q_tokens, const int32_t* seq_lens, int32_t max_seq_len,
@@ -215,13 +222,14 @@ int kvq_split_decode(const kvq_cache* cache, const void* q, int32_t batch, int32
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * kvq_combine merges the splits of a preceding kvq_split_decode (same cache,
- * shape and max_seq_len) in split order, applies the static V scale
+ * kvq_combine merges the chunks of a preceding kvq_split_decode (same cache,
+ * shape, seq_lens and max_seq_len) in chunk order, applies the static V scale
  * (per-tensor / per-channel), then the head sink, and writes bf16 `out`.
+ * seq_lens (device) locates each sequence's chunks exactly as the split did.
  */
 int kvq_combine(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int32_t q_tokens,
-                int32_t max_seq_len, const float* head_sink, void* out, const void* workspace,
-                size_t workspace_bytes, void* stream);
+                const int32_t* seq_lens, int32_t max_seq_len, const float* head_sink, void* out,
+                const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kvq_cache_bytes -- host-only footprint of one layer's cache: codes of K and

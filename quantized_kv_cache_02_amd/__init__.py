@@ -76,7 +76,7 @@ def lib():
         L.kvq_append_decode_attend.restype = ctypes.c_int
         L.kvq_split_decode.argtypes = [CP, P, I32, I32, I32, P, I32, F, P, I32, P, SZ, P]
         L.kvq_split_decode.restype = ctypes.c_int
-        L.kvq_combine.argtypes = [CP, I32, I32, I32, I32, P, P, P, SZ, P]
+        L.kvq_combine.argtypes = [CP, I32, I32, I32, P, I32, P, P, P, SZ, P]
         L.kvq_combine.restype = ctypes.c_int
         L.kvq_cache_bytes.argtypes = [I32, I32, I32, I32, ctypes.c_int64]
         L.kvq_cache_bytes.restype = SZ
@@ -261,12 +261,13 @@ def split_decode(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_se
            "kvq_split_decode")
 
 
-def combine(cache: KVCache, batch: int, num_q_heads: int, q_tokens: int, max_seq_len: int,
-            workspace: torch.Tensor, out: torch.Tensor,
+def combine(cache: KVCache, batch: int, num_q_heads: int, q_tokens: int, seq_lens: torch.Tensor,
+            max_seq_len: int, workspace: torch.Tensor, out: torch.Tensor,
             head_sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Phase 2 of decode: fixed-order merge of the splits into bf16 `out`."""
-    _check(lib().kvq_combine(cache.struct, batch, num_q_heads, q_tokens, max_seq_len,
-                             _ptr(head_sink), _ptr(out), _ptr(workspace),
+    """Phase 2 of decode: fixed-order merge of the chunks into bf16 `out`."""
+    _want(seq_lens, torch.int32, "seq_lens")
+    _check(lib().kvq_combine(cache.struct, batch, num_q_heads, q_tokens, _ptr(seq_lens),
+                             max_seq_len, _ptr(head_sink), _ptr(out), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream)),
            "kvq_combine")
     return out

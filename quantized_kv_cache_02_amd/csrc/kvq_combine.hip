@@ -11,13 +11,15 @@
 //   M = max_s m_s,  w_s = l_s 2^(m_s - M),  L = sum_s w_s,  o = sum_s w_s o_s / L,
 //   lse = ln 2 (M + log2 L).
 //
-// One workgroup per (sequence, KV head, query row, 64 channels).  Its 256
-// threads are 16 channel quads x 16 split groups; a thread issues the loads of
-// all its splits before using any (the partials were just written, so one
-// round trip to the cache hierarchy), then the 16 groups are summed in group
-// order through LDS.  Every sum runs in the same order on every call.
+// One workgroup per (sequence, KV head, query row, 64 channels).  It first
+// locates the sequence's chunk slots with the decode kernel's schedule, then
+// its 256 threads -- 16 channel quads x 16 split groups -- issue the loads of
+// their splits before using any (the partials were just written, so one round
+// trip to the cache hierarchy), and the 16 groups are summed in group order
+// through LDS.  Every sum runs in the same order on every call.
 
 #include "kvq_device.h"
+#include "kvq_sched.h"
 
 namespace kvq {
 namespace {
@@ -27,8 +29,8 @@ constexpr int kGroups = 16;   // split groups per workgroup
 constexpr int kQuads = 16;    // 4-channel columns per workgroup (64 channels)
 constexpr int kBatch = 8;     // loads issued back to back per thread
 
-template <int MODE>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int D) {
+template <int MODE, int D>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   __shared__ float w_s[kMaxSplits];
   __shared__ float red[4];
   __shared__ float4_t part[kGroups][kQuads];
@@ -39,8 +41,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int D) {
   const int r = blockIdx.y;
   const int head = blockIdx.z;  // b * Hkv + hkv
   const int b = head / a.Hkv, hkv = head % a.Hkv;
-  const int S = a.S;
-  const size_t rowbase = ((size_t)head * a.R + r) * S;
+  // The chunk slots [P, P + S) that hold sequence b's partials.  With one
+  // sequence P = 0, and every slot that may hold one (Sld) is loaded at once,
+  // beside the length that says how many do (S, computed once the loads are
+  // out); the others are never used.
+  const int L0 = a.seq_lens[0];
+  int P, Sld;
+  if (a.B == 1) {
+    P = 0;
+    Sld = min(a.S, kMaxSplits);
+  } else {
+    const Chunk ch = find_chunk(a.seq_lens, a.B, a.max_seq_len, a.NW, -1, b, lane);
+    Sld = min(ch.S, kMaxSplits);  // the host bounds S by kMaxSplits
+    // an empty sequence owns no slot; its (unused) loads read slot 0
+    P = Sld > 0 ? ch.P : 0;
+  }
+  const size_t rowbase = ((size_t)hkv * a.R + r) * a.S + P;
   const float* ms = a.ws_m + rowbase;
   const float* ls = a.ws_l + rowbase;
 
@@ -51,12 +67,21 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int D) {
 #pragma unroll
   for (int i = 0; i < kBatch; ++i) {
     const int s = grp + i * kGroups;
-    v0[i] = *reinterpret_cast<const float4_t*>(os + (size_t)(s < S ? s : 0) * D);
+    v0[i] = *reinterpret_cast<const float4_t*>(os + (size_t)(s < Sld ? s : 0) * D);
+  }
+  int S = Sld;
+  if (a.B == 1) {
+    const int nt = (clamp_len(L0, a.max_seq_len) + kTile - 1) / kTile;
+    const int C = max((nt + a.NW - 1) / a.NW, kMinTilesPerSplit);
+    S = min((nt + C - 1) / C, Sld);
   }
 
   // M: per-thread max over s = tid, tid+256, ..., then waves, then in wave order
   float M = -INFINITY;
-  for (int s = tid; s < S; s += 256) M = fmaxf(M, ms[s]);
+  for (int s = tid; s < Sld; s += 256) {
+    const float m = ms[s];
+    if (s < S) M = fmaxf(M, m);
+  }
   M = wave_max(M);
   if (lane == 0) red[wave] = M;
   __syncthreads();
@@ -120,18 +145,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int D) {
   *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.Tq + jq) * a.Hq + h) * D + d) = packed;
 }
 
-}  // namespace
-
-hipError_t launch_combine(int mode, int D, const CombineArgs& a, int B, hipStream_t st) {
-  if (a.S > kMaxSplits || D % 64 != 0) return hipErrorInvalidValue;
-  dim3 grid(D / 64, a.R, B * a.Hkv);
-  switch (mode) {
-    case kPerRow: hipLaunchKernelGGL(combine_kernel<kPerRow>, grid, dim3(256), 0, st, a, D); break;
-    case kPerTensor: hipLaunchKernelGGL(combine_kernel<kPerTensor>, grid, dim3(256), 0, st, a, D); break;
-    case kPerChannel: hipLaunchKernelGGL(combine_kernel<kPerChannel>, grid, dim3(256), 0, st, a, D); break;
+template <int MODE>
+hipError_t launch_mode(int D, const CombineArgs& a, dim3 grid, hipStream_t st) {
+  switch (D) {
+    case 64: hipLaunchKernelGGL((combine_kernel<MODE, 64>), grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<MODE, 128>), grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<MODE, 256>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(int mode, int D, const CombineArgs& a, int B, hipStream_t st) {
+  dim3 grid(D / 64, a.R, B * a.Hkv);
+  switch (mode) {
+    case kPerRow: return launch_mode<kPerRow>(D, a, grid, st);
+    case kPerTensor: return launch_mode<kPerTensor>(D, a, grid, st);
+    case kPerChannel: return launch_mode<kPerChannel>(D, a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace kvq

@@ -3,6 +3,8 @@
 // allocates, never reads device memory, so every entry point can be captured
 // into a HIP graph.
 
+#include <algorithm>
+
 #include "kvq.h"
 
 #include <hip/hip_runtime.h>
@@ -18,7 +20,6 @@ using kvq::CacheArgs;
 constexpr int kMaxGroup = 8;     // query heads per KV head
 constexpr int kMaxQTokens = 8;   // query tokens per sequence (1 + 7 drafts)
 constexpr int kNumCUs = 256;  // MI355X
-constexpr int kMinTilesPerSplit = 8;
 constexpr int kMaxSplits = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -57,7 +58,9 @@ CacheArgs cache_args(const kvq_cache* c, const int32_t* table, int32_t max_block
 }
 
 struct DecodeShape {
-  int G, R, RB, S;
+  int G, R, RB, S;  // S: reported by kvq_num_splits (= NW)
+  int NW;           // nominal workgroups per KV head, batch * S
+  int NSLOT;        // chunk slots per KV head, NW + batch - 1
 };
 
 // Static decode shape: grouping, query rows, row blocks and the split count S,
@@ -73,25 +76,31 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   if (G > kMaxGroup || tq > kMaxQTokens) return KVQ_EUNSUPPORTED;
   if (batch > 65535 || c->num_kv_heads > 65535) return KVQ_EUNSUPPORTED;
   const int64_t ntiles = ((int64_t)max_seq_len + 15) / 16;
-  const int64_t pairs = (int64_t)batch * c->num_kv_heads;
-  const int RB = (G * tq + 15) / 16;
-  // one workgroup per CU: measured on MI355X at 64K tokens, B1 Hkv4 D256 int8,
-  // 256 workgroups (16 tiles per wavefront) beat 512 (8 per wavefront), 28.1
-  // vs 29.4 us -- fewer concurrent streams, half the partials to merge
-  (void)RB;
-  const int64_t target = kNumCUs;
-  int64_t S = (target + pairs - 1) / pairs;
-  int64_t cap = ntiles / kMinTilesPerSplit;
-  if (cap < 1) cap = 1;
-  if (S > cap) S = cap;
-  // every split within the block-table entries a workgroup holds
-  const int64_t need = (ntiles + kvq::kMaxTilesPerSplit - 1) / kvq::kMaxTilesPerSplit;
-  if (S < need) S = need;
-  if (S > kMaxSplits) return KVQ_EUNSUPPORTED;
+  const int64_t Hkv = c->num_kv_heads;
+  // Balanced schedule: the tiles of all sequences of a KV head are cut into
+  // chunks of C = max(ceil(T / NW), kMinTilesPerSplit) tiles, sequence by
+  // sequence, so at most NW + batch - 1 chunk workgroups per KV head.  NW is
+  // sized so that the whole grid fits one workgroup per CU (measured on
+  // MI355X at 64K tokens, B1 Hkv4 D256 int8: 256 workgroups, 16 tiles per
+  // wavefront, beat 512, 28.1 vs 29.4 us), with at least kMinTilesPerSplit
+  // tiles per chunk for a full-length sequence, and few enough tiles per chunk
+  // for the block-table registers.
+  int64_t NW = std::max<int64_t>(kNumCUs / Hkv, 1) - (batch - 1);
+  NW = std::min<int64_t>(NW, (int64_t)batch * ntiles / kvq::kMinTilesPerSplit);
+  NW = std::max<int64_t>(NW, 1);
+  const int64_t need = ((int64_t)batch * ntiles + kvq::kMaxTilesPerSplit - 1) / kvq::kMaxTilesPerSplit;
+  NW = std::max(NW, need);
+  // chunks of one sequence: at most NW + 1, and at most one per
+  // kMinTilesPerSplit tiles; the combine merges up to kMaxSplits
+  const int64_t most = std::min<int64_t>(NW + 1, (ntiles + kvq::kMinTilesPerSplit - 1) /
+                                                     kvq::kMinTilesPerSplit);
+  if (most > kMaxSplits || NW + batch - 1 > INT32_MAX / 2) return KVQ_EUNSUPPORTED;
   sh->G = G;
   sh->R = G * tq;
   sh->RB = (sh->R + 15) / 16;
-  sh->S = (int)S;
+  sh->S = (int)NW;
+  sh->NW = (int)NW;
+  sh->NSLOT = (int)(NW + batch - 1);
   return KVQ_OK;
 }
 
@@ -108,7 +117,8 @@ int check_layout(const kvq_cache* c, int32_t batch, int32_t max_seq_len, const i
 }
 
 size_t workspace_size(const kvq_cache* c, int32_t batch, const DecodeShape& sh) {
-  const size_t rows = (size_t)batch * c->num_kv_heads * sh.R * sh.S;
+  (void)batch;
+  const size_t rows = (size_t)c->num_kv_heads * sh.R * sh.NSLOT;
   // o [rows, D] then m [rows] then l [rows], each region 256-byte aligned
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return up(rows * c->head_dim * 4) + 2 * up(rows * 4);
@@ -116,7 +126,8 @@ size_t workspace_size(const kvq_cache* c, int32_t batch, const DecodeShape& sh) 
 
 void workspace_ptrs(void* ws, const kvq_cache* c, int32_t batch, const DecodeShape& sh, float** o,
                     float** m, float** l) {
-  const size_t rows = (size_t)batch * c->num_kv_heads * sh.R * sh.S;
+  (void)batch;
+  const size_t rows = (size_t)c->num_kv_heads * sh.R * sh.NSLOT;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char* base = static_cast<char*>(ws);
   *o = reinterpret_cast<float*>(base);
@@ -162,7 +173,9 @@ int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int
   a.G = sh.G;
   a.R = sh.R;
   a.max_seq_len = max_seq_len;
-  a.S = sh.S;
+  a.B = batch;
+  a.NW = sh.NW;
+  a.S = sh.NSLOT;
   a.sm_scale = scale;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
@@ -172,12 +185,14 @@ int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int
   return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
 
-int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int32_t max_seq_len,
-                 const float* sink, void* out, const void* ws, size_t ws_bytes, void* stream) {
+int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, const int32_t* seq_lens,
+                 int32_t max_seq_len, const float* sink, void* out, const void* ws, size_t ws_bytes,
+                 void* stream) {
   DecodeShape sh;
   int st = decode_shape(c, batch, hq, tq, max_seq_len, &sh);
   if (st != KVQ_OK) return st;
-  if (out == nullptr || ws == nullptr || !aligned16(out) || !aligned16(ws)) return KVQ_EINVAL;
+  if (seq_lens == nullptr || out == nullptr || ws == nullptr || !aligned16(out) || !aligned16(ws))
+    return KVQ_EINVAL;
   if (ws_bytes < workspace_size(c, batch, sh)) return KVQ_EINVAL;
   kvq::CombineArgs a;
   float *o, *m, *l;
@@ -188,12 +203,16 @@ int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   a.v_static = c->scale_mode == KVQ_PER_ROW ? nullptr : c->v_scales;
   a.sink = sink;
   a.out = static_cast<uint16_t*>(out);
+  a.seq_lens = seq_lens;
+  a.max_seq_len = max_seq_len;
+  a.B = batch;
+  a.NW = sh.NW;
   a.Hkv = c->num_kv_heads;
   a.Hq = hq;
   a.Tq = tq;
   a.G = sh.G;
   a.R = sh.R;
-  a.S = sh.S;
+  a.S = sh.NSLOT;
   hipError_t e = kvq::launch_combine(c->scale_mode, c->head_dim, a, batch,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
@@ -256,10 +275,10 @@ int kvq_split_decode(const kvq_cache* cache, const void* q, int32_t batch, int32
 }
 
 int kvq_combine(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int32_t q_tokens,
-                int32_t max_seq_len, const float* head_sink, void* out, const void* workspace,
-                size_t workspace_bytes, void* stream) {
-  return combine_impl(cache, batch, num_q_heads, q_tokens, max_seq_len, head_sink, out, workspace,
-                      workspace_bytes, stream);
+                const int32_t* seq_lens, int32_t max_seq_len, const float* head_sink, void* out,
+                const void* workspace, size_t workspace_bytes, void* stream) {
+  return combine_impl(cache, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, head_sink, out,
+                      workspace, workspace_bytes, stream);
 }
 
 int kvq_decode_attend(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
@@ -270,8 +289,8 @@ int kvq_decode_attend(const kvq_cache* cache, const void* q, int32_t batch, int3
   int st = split_impl(cache, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, softmax_scale,
                       nullptr, 0, workspace, workspace_bytes, stream);
   if (st != KVQ_OK) return st;
-  return kvq_combine(cache, batch, num_q_heads, q_tokens, max_seq_len, head_sink, out, workspace,
-                     workspace_bytes, stream);
+  return kvq_combine(cache, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, head_sink, out,
+                     workspace, workspace_bytes, stream);
 }
 
 int kvq_paged_decode_attend(const kvq_cache* cache, const void* q, int32_t batch,
@@ -284,8 +303,8 @@ int kvq_paged_decode_attend(const kvq_cache* cache, const void* q, int32_t batch
   int st = split_impl(cache, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, softmax_scale,
                       block_table, max_blocks, workspace, workspace_bytes, stream);
   if (st != KVQ_OK) return st;
-  return kvq_combine(cache, batch, num_q_heads, q_tokens, max_seq_len, head_sink, out, workspace,
-                     workspace_bytes, stream);
+  return kvq_combine(cache, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, head_sink, out,
+                     workspace, workspace_bytes, stream);
 }
 
 int kvq_append_decode_attend(const kvq_cache* cache, const void* k_new, const void* v_new,
@@ -300,8 +319,8 @@ int kvq_append_decode_attend(const kvq_cache* cache, const void* k_new, const vo
   int st = split_impl(cache, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, softmax_scale,
                       block_table, max_blocks, workspace, workspace_bytes, stream, k_new, v_new);
   if (st != KVQ_OK) return st;
-  return kvq_combine(cache, batch, num_q_heads, q_tokens, max_seq_len, head_sink, out, workspace,
-                     workspace_bytes, stream);
+  return kvq_combine(cache, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, head_sink, out,
+                     workspace, workspace_bytes, stream);
 }
 
 size_t kvq_cache_bytes(int32_t dtype, int32_t scale_mode, int32_t num_kv_heads, int32_t head_dim,

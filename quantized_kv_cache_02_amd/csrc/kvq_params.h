@@ -21,6 +21,8 @@ constexpr int kWaves = 4;
 // tiles (the host sizes the split count accordingly).
 constexpr int kTableRegs = 4;
 constexpr int kMaxTilesPerSplit = kWaves * 64 * kTableRegs;
+// Smallest chunk of the balanced split schedule, in tiles.
+constexpr int kMinTilesPerSplit = 8;
 
 // Decode-kernel register budget per variant: two waves per SIMD (<= 256
 // registers per lane) while the accumulators of the query row blocks fit,
@@ -59,15 +61,17 @@ struct SplitArgs {
   const int32_t* seq_lens;
   int32_t Hq, Tq, G, R;  // R = G * Tq query rows per (sequence, KV head)
   int32_t max_seq_len;
-  int32_t S;  // splits per (sequence, KV head)
+  int32_t B;   // sequences
+  int32_t NW;  // nominal workgroups per KV head (the schedule's divisor)
+  int32_t S;   // chunk slots per KV head: NW + B - 1 (the grid's x extent)
   float sm_scale;
   // fused append (both null when not fused): bf16 [B, Tq, Hkv, D] rows of the
   // query tokens, written at positions seq_len - Tq + j before they are read
   const uint16_t* k_new;
   const uint16_t* v_new;
-  float* ws_o;  // [B, Hkv, R, S, D]  normalized split outputs
-  float* ws_m;  // [B, Hkv, R, S]     split max logit (log2 units)
-  float* ws_l;  // [B, Hkv, R, S]     split normalizer
+  float* ws_o;  // [Hkv, R, S, D]  normalized chunk outputs, slot-major per row
+  float* ws_m;  // [Hkv, R, S]     chunk max logit (log2 units)
+  float* ws_l;  // [Hkv, R, S]     chunk normalizer
 };
 
 struct CombineArgs {
@@ -77,6 +81,8 @@ struct CombineArgs {
   const float* v_static;  // per-tensor [1] / per-channel [Hkv, D] / nullptr (per-row)
   const float* sink;      // [Hq] or nullptr
   uint16_t* out;          // bf16 [B, Tq, Hq, D]
+  const int32_t* seq_lens;
+  int32_t max_seq_len, B, NW;
   int32_t Hkv, Hq, Tq, G, R, S;
 };
 

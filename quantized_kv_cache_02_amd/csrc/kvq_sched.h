@@ -1,0 +1,109 @@
+// kvq_sched.h -- the balanced split schedule shared by the decode and combine
+// kernels.  GPU code only.
+//
+// Kernel page "kv-quant-attn", "Method": the cached sequence is cut into
+// splits that separate workgroups reduce, and the partials are merged in a
+// fixed order.  With a batch of ragged lengths, a fixed number of splits per
+// sequence leaves the workgroups of the longest sequence on the critical path
+// while the others idle, so the cut is made over the whole batch instead:
+//
+//   n_b = ceil(L_b / 16)                 16-token tiles of sequence b
+//   T   = sum_b n_b                      tiles of one KV head
+//   C   = max(ceil(T / NW), kMinTilesPerSplit)   tiles per chunk
+//   S_b = ceil(n_b / C)                  chunks of sequence b (never straddling two)
+//   P_b = sum_{b' < b} S_b'              first chunk slot of sequence b
+//
+// NW is the host's nominal workgroup count per KV head.  Since
+// sum_b S_b < T / C + B <= NW + B, the NW + B - 1 slots per KV head cover every
+// chunk; slots past the last chunk are idle.  Every workgroup derives the same
+// integers from the same seq_lens with wave-level sums, so the decode kernel
+// and the combine agree on where each partial lives.  The schedule depends on
+// the lengths only, so repeated calls cut identically and stay bitwise equal.
+#pragma once
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+__device__ __forceinline__ int clamp_len(int L, int max_seq_len) {
+  return L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_scan_i(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+struct Chunk {
+  int b;       // sequence (-1: idle slot)
+  int first;   // first tile of the chunk
+  int end;     // one past its last tile
+  int L;       // the sequence's length (clamped)
+  int P;       // first slot of the sequence
+  int S;       // chunks of the sequence
+};
+
+// Tiles per chunk over the whole batch (every lane gets the same value).
+__device__ __forceinline__ int chunk_tiles(const int32_t* seq_lens, int B, int max_seq_len, int NW,
+                                           int lane) {
+  int T = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int i = base + lane;
+    const int L = i < B ? clamp_len(seq_lens[i], max_seq_len) : 0;
+    T += wave_sum_i((L + kTile - 1) / kTile);
+  }
+  const int C = (T + NW - 1) / NW;
+  return C > kMinTilesPerSplit ? C : kMinTilesPerSplit;
+}
+
+// The chunk of workgroup `slot`, or, with slot < 0, just P_b and S_b of
+// sequence `want_b`.  Wave-uniform results.
+__device__ __forceinline__ Chunk find_chunk(const int32_t* seq_lens, int B, int max_seq_len, int NW,
+                                            int slot, int want_b, int lane) {
+  const int C = chunk_tiles(seq_lens, B, max_seq_len, NW, lane);
+  Chunk ch{-1, 0, 0, 0, 0, 0};
+  int P = 0;  // chunks of the sequences before this pass
+  for (int base = 0; base < B; base += 64) {
+    const int i = base + lane;
+    const int L = i < B ? clamp_len(seq_lens[i], max_seq_len) : 0;
+    const int n = (L + kTile - 1) / kTile;
+    const int Sb = (n + C - 1) / C;
+    const int incl = wave_scan_i(Sb, lane);
+    const int Pb = P + incl - Sb;
+    const bool hit = (i < B) && (slot >= 0 ? (Sb > 0 && Pb <= slot && slot < Pb + Sb) : i == want_b);
+    const uint64_t m = __ballot(hit);
+    if (m != 0) {
+      const int l = __builtin_ctzll(m);
+      ch.b = base + l;
+      ch.L = __shfl(L, l);
+      ch.P = __shfl(Pb, l);
+      ch.S = __shfl(Sb, l);
+      const int c = slot >= 0 ? slot - ch.P : 0;
+      const int nb = __shfl(n, l);
+      ch.first = c * C;
+      ch.end = min(ch.first + C, nb);
+      break;
+    }
+    P += __shfl(incl, 63);
+  }
+  ch.b = __builtin_amdgcn_readfirstlane(ch.b);
+  ch.first = __builtin_amdgcn_readfirstlane(ch.first);
+  ch.end = __builtin_amdgcn_readfirstlane(ch.end);
+  ch.L = __builtin_amdgcn_readfirstlane(ch.L);
+  ch.P = __builtin_amdgcn_readfirstlane(ch.P);
+  ch.S = __builtin_amdgcn_readfirstlane(ch.S);
+  return ch;
+}
+
+}  // namespace kvq

@@ -32,6 +32,7 @@
 //   accumulators are fp32.
 
 #include "kvq_quant.h"
+#include "kvq_sched.h"
 
 #ifndef KVQ_DTYPE
 #error "KVQ_DTYPE must be defined"
@@ -441,39 +442,56 @@ split_decode_kernel(SplitArgs a) {
   __shared__ float s_m[kWaves][RP];
   __shared__ float s_l[kWaves][RP];
 
-  const int s = blockIdx.x;
+  const int slot = blockIdx.x;
   const int hkv = blockIdx.y;
-  const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 15;  // S^T column / P row / V column index
   const int g = lane >> 4;  // lane group
 
-  // ---- issue the loads of the query rows first: they do not depend on the
-  // sequence length, and loads retire in order, so staging them later waits
-  // only for them and not for the tiles issued after them.
   constexpr int QU = D / 8;                           // 16-byte units per q row
   constexpr int QPT = (RP * QU + 255) / 256;          // units per thread
-  // (unconditional loads, clamped to row 0, so no branch joins on their data;
-  // padding rows are zeroed when staged)
+  // Query rows of sequence bq: unconditional loads, clamped to row 0, so no
+  // branch joins on their data (padding rows are zeroed when staged).  Issued
+  // before the tiles: loads retire in order, so staging them later waits only
+  // for them.
   u32x4_t qreg[QPT];
+  auto load_q = [&](int bq) {
 #pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int u = (tid + 256 * i) % (RP * QU);
-    const int r = u / QU, cu = u % QU;
-    const int rr = r < a.R ? r : 0;
-    const int jq = rr / a.G, gh = rr % a.G;
-    const uint16_t* src = a.q + ((((size_t)b * a.Tq + jq) * a.Hq) + (size_t)hkv * a.G + gh) * D;
-    qreg[i] = *reinterpret_cast<const u32x4_t*>(src + cu * 8);
-  }
+    for (int i = 0; i < QPT; ++i) {
+      const int u = (tid + 256 * i) % (RP * QU);
+      const int r = u / QU, cu = u % QU;
+      const int rr = r < a.R ? r : 0;
+      const int jq = rr / a.G, gh = rr % a.G;
+      const uint16_t* src = a.q + ((((size_t)bq * a.Tq + jq) * a.Hq) + (size_t)hkv * a.G + gh) * D;
+      qreg[i] = *reinterpret_cast<const u32x4_t*>(src + cu * 8);
+    }
+  };
 
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
-  const int ntiles = (L + kTile - 1) / kTile;
-  const int tps = (ntiles + a.S - 1) / a.S;
-  const int tb = s * tps;
-  const int te = min(tb + tps, ntiles);
+  // ---- this workgroup's chunk under the balanced schedule (every wavefront
+  // derives the same one; an idle slot leaves as a whole before any barrier).
+  // One sequence: chunk = slot, and the query loads go out before the length
+  // arrives.
+  int b, L, tb, te;
+  if (a.B == 1) {
+    b = 0;
+    load_q(0);
+    L = clamp_len(a.seq_lens[0], a.max_seq_len);
+    const int nt = (L + kTile - 1) / kTile;
+    const int C = max((nt + a.NW - 1) / a.NW, kMinTilesPerSplit);
+    tb = slot * C;
+    te = min(tb + C, nt);
+    if (tb >= nt) return;
+  } else {
+    const Chunk ch = find_chunk(a.seq_lens, a.B, a.max_seq_len, a.NW, slot, -1, lane);
+    if (ch.b < 0) return;
+    b = ch.b;
+    L = ch.L;
+    tb = ch.first;
+    te = ch.end;
+    load_q(b);
+  }
 
   // ---- fused append: the wavefront that will read the tile holding a new
   // position quantizes and stores that row first (the same arithmetic as
@@ -670,7 +688,6 @@ split_decode_kernel(SplitArgs a) {
     __syncthreads();
   }
 
-  const size_t head = (size_t)b * a.c.Hkv + hkv;
   for (int idx = tid * 4; idx < a.R * D; idx += 256 * 4) {
     const int r = idx / D, d = idx % D;
     const int jn = d / G_::NCOL, k = (d % G_::NCOL) / 4;
@@ -678,7 +695,7 @@ split_decode_kernel(SplitArgs a) {
     float4_t v = *reinterpret_cast<const float4_t*>(smem + off);
 #pragma unroll
     for (int w = 1; w < nbuf; ++w) v += *reinterpret_cast<const float4_t*>(smem + (size_t)w * RP * D + off);
-    *reinterpret_cast<float4_t*>(a.ws_o + ((head * a.R + r) * a.S + s) * D + d) = v;
+    *reinterpret_cast<float4_t*>(a.ws_o + (((size_t)hkv * a.R + r) * a.S + slot) * D + d) = v;
   }
   if (tid < a.R) {
     const int r = tid;
@@ -687,14 +704,15 @@ split_decode_kernel(SplitArgs a) {
     float Lt = 0.0f;
     if (M != -INFINITY)
       for (int w = 0; w < kWaves; ++w) Lt += s_l[w][r] * exp2f(s_m[w][r] - M);
-    a.ws_m[(head * a.R + r) * a.S + s] = M;
-    a.ws_l[(head * a.R + r) * a.S + s] = Lt;
+    a.ws_m[((size_t)hkv * a.R + r) * a.S + slot] = M;
+    a.ws_l[((size_t)hkv * a.R + r) * a.S + slot] = Lt;
   }
 }
 
 template <int DT, int MODE, int D, int RB>
 hipError_t launch_one(const SplitArgs& a, int B, hipStream_t st) {
-  dim3 grid(a.S, a.c.Hkv, B);
+  (void)B;
+  dim3 grid(a.S, a.c.Hkv, 1);
   hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -213,6 +213,26 @@ def test_ragged_lengths(lens):
     gu.run_and_check(w, f"lens={lens}")
 
 
+@pytest.mark.parametrize("lens", [[1, 0, 7000, 33, 2500], [20000, 1, 1, 1], [0, 0, 0, 65], [0, 0]])
+def test_balanced_schedule_ragged(lens):
+    """Chunks are cut over the whole batch: one long sequence takes most of the
+    workgroups, empty ones take none, and the combine finds each sequence's
+    chunks from seq_lens."""
+    w = ki.random_workload(4500 + sum(lens), B=len(lens), Hkv=2, G=4, D=128, Tq=1, lens=lens,
+                           dtype=INT8, mode=PER_ROW, block_size=16)
+    gu.run_and_check(w, f"balanced lens={lens}")
+
+
+def test_balanced_schedule_many_sequences():
+    """More sequences than lanes: the schedule's sums run over several passes."""
+    rng = np.random.default_rng(4600)
+    lens = [int(x) for x in rng.integers(0, 400, size=150)]
+    lens[77] = 3000
+    w = ki.random_workload(4601, B=len(lens), Hkv=1, G=2, D=64, Tq=1, lens=lens, dtype=INT4,
+                           mode=PER_ROW, block_size=None)
+    gu.run_and_check(w, "balanced 150 sequences")
+
+
 def test_query_tokens_beyond_length():
     """Tq larger than the cached length: early drafts see nothing and output zeros."""
     w = ki.random_workload(77, B=1, Hkv=1, G=2, D=64, Tq=6, lens=[3], dtype=INT8, mode=PER_ROW,
