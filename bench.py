@@ -32,7 +32,9 @@ PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_decode_int8_64k_traffic.json")
 KERNEL_SOURCES = ["quantized_kv_cache_02_amd/csrc/kvq_split.hip",
                   "quantized_kv_cache_02_amd/csrc/kvq_device.h",
-                  "quantized_kv_cache_02_amd/csrc/kvq_params.h"]
+                  "quantized_kv_cache_02_amd/csrc/kvq_params.h",
+                  "quantized_kv_cache_02_amd/csrc/kvq_quant.h",
+                  "quantized_kv_cache_02_amd/csrc/kvq_sched.h"]
 
 
 def kernel_digest() -> str:
