@@ -213,6 +213,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default="", help="also time the context sweep for int8 and int4 "
                                                 "and write the lines to this JSON-lines file")
+    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5],
+                    help="time another of the seeded workloads instead (2, 4, 5: their own "
+                         "shapes; the JSON line then reports that workload)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 20 times "
                          "(reference dispatch for HBM byte counters)")
@@ -245,6 +248,16 @@ def main():
         return
 
     fused = not args.separate_append
+    if args.workload != 3:
+        w = ki.make_workload(args.workload)
+        r = time_workload(kvq, torch, w, args.layers, args.steps, args.warmup, dev, fused)
+        r.pop("workload")
+        print(json.dumps({"workload": w.name, "us_per_step": round(r["step_ms"] * 1e3, 2),
+                          "split_kernel_us": round(r["split_ms"] * 1e3, 2),
+                          "split_GBps": round(r["bytes"] / (r["split_ms"] * 1e-3) / 1e9, 1),
+                          "algorithmic_bytes_per_step": r["bytes"], "splits": r["splits"]}),
+              flush=True)
+        return
     r = time_config(kvq, torch, ki, args.dtype, args.ctx, args.layers, args.steps, args.warmup, dev,
                     fused)
     w = r.pop("workload")

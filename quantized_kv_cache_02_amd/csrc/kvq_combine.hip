@@ -12,14 +12,14 @@
 //   lse = ln 2 (M + log2 L).
 //
 // One workgroup per (sequence, KV head, query row, 64 channels).  It first
-// locates the sequence's chunk slots with the decode kernel's schedule, then
+// locates the sequence's chunk slots (recorded by the decode kernel), then
 // its 256 threads -- 16 channel quads x 16 split groups -- issue the loads of
 // their splits before using any (the partials were just written, so one round
 // trip to the cache hierarchy), and the 16 groups are summed in group order
 // through LDS.  Every sum runs in the same order on every call.
 
 #include "kvq_device.h"
-#include "kvq_sched.h"
+#include "kvq_sched.h"  // clamp_len
 
 namespace kvq {
 namespace {
@@ -31,7 +31,7 @@ constexpr int kBatch = 8;     // loads issued back to back per thread
 
 template <int MODE, int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  __shared__ float w_s[kMaxSplits];
+  extern __shared__ float w_s[];  // [SMAX] chunk weights
   __shared__ float red[4];
   __shared__ float4_t part[kGroups][kQuads];
   const int tid = threadIdx.x;
@@ -49,12 +49,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   int P, Sld;
   if (a.B == 1) {
     P = 0;
-    Sld = min(a.S, kMaxSplits);
+    Sld = min(a.S, a.SMAX);
   } else {
-    const Chunk ch = find_chunk(a.seq_lens, a.B, a.max_seq_len, a.NW, -1, b, lane);
-    Sld = min(ch.S, kMaxSplits);  // the host bounds S by kMaxSplits
+    // the split kernel recorded the sequence's chunk slots in the workspace
+    const int Sb = a.chunks[2 * b + 1];
+    Sld = min(Sb, a.SMAX);  // the host bounds every S_b by SMAX
     // an empty sequence owns no slot; its (unused) loads read slot 0
-    P = Sld > 0 ? ch.P : 0;
+    P = Sld > 0 ? a.chunks[2 * b] : 0;
   }
   const size_t rowbase = ((size_t)hkv * a.R + r) * a.S + P;
   const float* ms = a.ws_m + rowbase;
@@ -147,10 +148,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 template <int MODE>
 hipError_t launch_mode(int D, const CombineArgs& a, dim3 grid, hipStream_t st) {
+  if (a.SMAX < 1 || a.SMAX > kMaxSplits) return hipErrorInvalidValue;
+  const size_t lds = (size_t)a.SMAX * sizeof(float);
   switch (D) {
-    case 64: hipLaunchKernelGGL((combine_kernel<MODE, 64>), grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<MODE, 128>), grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((combine_kernel<MODE, 256>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((combine_kernel<MODE, 64>), grid, dim3(256), lds, st, a); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<MODE, 128>), grid, dim3(256), lds, st, a); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<MODE, 256>), grid, dim3(256), lds, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -18,7 +18,6 @@ namespace {
 using kvq::CacheArgs;
 
 constexpr int kMaxGroup = 8;     // query heads per KV head
-constexpr int kMaxQTokens = 8;   // query tokens per sequence (1 + 7 drafts)
 constexpr int kNumCUs = 256;  // MI355X
 constexpr int kMaxSplits = 4096;
 
@@ -60,6 +59,9 @@ CacheArgs cache_args(const kvq_cache* c, const int32_t* table, int32_t max_block
 struct DecodeShape {
   int G, R, RB, S;  // S: reported by kvq_num_splits (= NW)
   int NW;           // nominal workgroups per KV head, batch * S
+  int RBN;          // workgroups per chunk (row-split launches), 1 otherwise
+  int RBK;          // row blocks per workgroup (the kernel variant)
+  int SMAX;         // most chunks one sequence can get
   int NSLOT;        // chunk slots per KV head, NW + batch - 1
 };
 
@@ -73,7 +75,7 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   if (batch < 1 || hq < 1 || tq < 1 || max_seq_len < 1) return KVQ_EINVAL;
   if (hq % c->num_kv_heads != 0) return KVQ_EINVAL;
   const int G = hq / c->num_kv_heads;
-  if (G > kMaxGroup || tq > kMaxQTokens) return KVQ_EUNSUPPORTED;
+  if (G > kMaxGroup || tq > kvq::kMaxQTokens) return KVQ_EUNSUPPORTED;
   if (batch > 65535 || c->num_kv_heads > 65535) return KVQ_EUNSUPPORTED;
   const int64_t ntiles = ((int64_t)max_seq_len + 15) / 16;
   const int64_t Hkv = c->num_kv_heads;
@@ -85,8 +87,23 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   // wavefront, beat 512, 28.1 vs 29.4 us), with at least kMinTilesPerSplit
   // tiles per chunk for a full-length sequence, and few enough tiles per chunk
   // for the block-table registers.
-  int64_t NW = std::max<int64_t>(kNumCUs / Hkv, 1) - (batch - 1);
-  NW = std::min<int64_t>(NW, (int64_t)batch * ntiles / kvq::kMinTilesPerSplit);
+  // More than 256 accumulator columns per lane (row blocks x head_dim) do not
+  // fit a wavefront's registers with the q operand and the tiles in flight:
+  // then every 16-row block gets its own workgroup and the chunk's workgroups
+  // share its bytes through L2.
+  const int RB = (G * tq + 15) / 16;
+  const int RBN = (RB > 1 && RB * c->head_dim > kvq::kSplitMaxAccColumns) ? RB : 1;
+  // Compute-bound variants (packed int4, whose tiles carry half the bytes, and
+  // row-split launches) run two workgroups per CU -- two wavefronts per SIMD
+  // hide each other's dependency stalls (measured on MI355X: int4 at 256K
+  // tokens 78.1 -> 68.6 us, workload 5 173.6 -> 90.7 us) -- as long as a chunk
+  // keeps at least 2 * kMinTilesPerSplit tiles.
+  const int64_t per_head = std::max<int64_t>(kNumCUs / (Hkv * RBN), 1);
+  const int64_t all_tiles = (int64_t)batch * ntiles;
+  int64_t NW = per_head - (batch - 1);
+  if ((RBN > 1 || c->dtype == KVQ_INT4) && 2 * per_head - (batch - 1) <= all_tiles / (2 * kvq::kMinTilesPerSplit))
+    NW = 2 * per_head - (batch - 1);
+  NW = std::min<int64_t>(NW, all_tiles / kvq::kMinTilesPerSplit);
   NW = std::max<int64_t>(NW, 1);
   const int64_t need = ((int64_t)batch * ntiles + kvq::kMaxTilesPerSplit - 1) / kvq::kMaxTilesPerSplit;
   NW = std::max(NW, need);
@@ -100,6 +117,9 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   sh->RB = (sh->R + 15) / 16;
   sh->S = (int)NW;
   sh->NW = (int)NW;
+  sh->RBN = RBN;
+  sh->SMAX = (int)std::min<int64_t>(most, NW + batch - 1);
+  sh->RBK = RBN > 1 ? 1 : RB;
   sh->NSLOT = (int)(NW + batch - 1);
   return KVQ_OK;
 }
@@ -117,15 +137,15 @@ int check_layout(const kvq_cache* c, int32_t batch, int32_t max_seq_len, const i
 }
 
 size_t workspace_size(const kvq_cache* c, int32_t batch, const DecodeShape& sh) {
-  (void)batch;
   const size_t rows = (size_t)c->num_kv_heads * sh.R * sh.NSLOT;
-  // o [rows, D] then m [rows] then l [rows], each region 256-byte aligned
+  // o [rows, D], m [rows], l [rows], then the chunk table [batch] (first slot,
+  // chunk count), each region 256-byte aligned
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return up(rows * c->head_dim * 4) + 2 * up(rows * 4);
+  return up(rows * c->head_dim * 4) + 2 * up(rows * 4) + up((size_t)batch * 8);
 }
 
 void workspace_ptrs(void* ws, const kvq_cache* c, int32_t batch, const DecodeShape& sh, float** o,
-                    float** m, float** l) {
+                    float** m, float** l, int32_t** chunks) {
   (void)batch;
   const size_t rows = (size_t)c->num_kv_heads * sh.R * sh.NSLOT;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -133,6 +153,7 @@ void workspace_ptrs(void* ws, const kvq_cache* c, int32_t batch, const DecodeSha
   *o = reinterpret_cast<float*>(base);
   *m = reinterpret_cast<float*>(base + up(rows * c->head_dim * 4));
   *l = reinterpret_cast<float*>(base + up(rows * c->head_dim * 4) + up(rows * 4));
+  *chunks = reinterpret_cast<int32_t*>(base + up(rows * c->head_dim * 4) + 2 * up(rows * 4));
 }
 
 hipError_t dispatch_split(int dt, int md, int D, int RB, const kvq::SplitArgs& a, int B,
@@ -176,11 +197,12 @@ int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int
   a.B = batch;
   a.NW = sh.NW;
   a.S = sh.NSLOT;
+  a.RBN = sh.RBN;
   a.sm_scale = scale;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
-  workspace_ptrs(ws, c, batch, sh, &a.ws_o, &a.ws_m, &a.ws_l);
-  hipError_t e = dispatch_split(c->dtype, c->scale_mode, c->head_dim, sh.RB, a, batch,
+  workspace_ptrs(ws, c, batch, sh, &a.ws_o, &a.ws_m, &a.ws_l, &a.ws_chunks);
+  hipError_t e = dispatch_split(c->dtype, c->scale_mode, c->head_dim, sh.RBK, a, batch,
                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
@@ -196,7 +218,10 @@ int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, cons
   if (ws_bytes < workspace_size(c, batch, sh)) return KVQ_EINVAL;
   kvq::CombineArgs a;
   float *o, *m, *l;
-  workspace_ptrs(const_cast<void*>(ws), c, batch, sh, &o, &m, &l);
+  int32_t* chunks;
+  workspace_ptrs(const_cast<void*>(ws), c, batch, sh, &o, &m, &l, &chunks);
+  a.chunks = chunks;
+  a.SMAX = sh.SMAX;
   a.ws_o = o;
   a.ws_m = m;
   a.ws_l = l;

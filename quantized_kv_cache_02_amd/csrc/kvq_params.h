@@ -21,17 +21,19 @@ constexpr int kWaves = 4;
 // tiles (the host sizes the split count accordingly).
 constexpr int kTableRegs = 4;
 constexpr int kMaxTilesPerSplit = kWaves * 64 * kTableRegs;
+// Query tokens per sequence and step (1 + up to 7 speculative drafts).
+constexpr int kMaxQTokens = 8;
 // Smallest chunk of the balanced split schedule, in tiles.
 constexpr int kMinTilesPerSplit = 8;
 
-// Decode-kernel register budget per variant: two waves per SIMD (<= 256
-// registers per lane) while the accumulators of the query row blocks fit,
-// otherwise one wave per SIMD (<= 512).  `RB` is the number of 16-row blocks
-// of query rows (G * Tq rows per KV head).  The host sizes the split count
-// from the same figure: workgroups resident per CU = waves per SIMD.
-constexpr int split_waves_per_simd(int D, int RB) { return RB * D <= 256 ? 2 : 1; }
-// Tiles of codes held in registers per wavefront (one in use, the rest loading).
-constexpr int split_tiles_in_flight(int D, int RB) { return RB * D <= 256 ? 2 : 3; }
+// Decode-kernel register budget: two wavefronts per SIMD (<= 256 registers
+// per lane).  The kernel is built for row-block counts RB (16 query rows each)
+// with RB * D <= 256, whose accumulators fit that budget beside the q operand
+// and the tiles in flight; wider row sets get one workgroup per row block.
+constexpr int kSplitWavesPerSimd = 2;
+constexpr int kSplitMaxAccColumns = 256;  // RB * D
+// Tiles of codes held in registers per wavefront (one in use, one loading).
+constexpr int kSplitTilesInFlight = 2;
 
 struct CacheArgs {
   uint8_t* k_codes;
@@ -63,7 +65,9 @@ struct SplitArgs {
   int32_t max_seq_len;
   int32_t B;   // sequences
   int32_t NW;  // nominal workgroups per KV head (the schedule's divisor)
-  int32_t S;   // chunk slots per KV head: NW + B - 1 (the grid's x extent)
+  int32_t S;   // chunk slots per KV head: NW + B - 1
+  int32_t RBN; // workgroups per chunk, one per 16-row block of query rows (1: one
+               // workgroup serves every row)
   float sm_scale;
   // fused append (both null when not fused): bf16 [B, Tq, Hkv, D] rows of the
   // query tokens, written at positions seq_len - Tq + j before they are read
@@ -72,6 +76,8 @@ struct SplitArgs {
   float* ws_o;  // [Hkv, R, S, D]  normalized chunk outputs, slot-major per row
   float* ws_m;  // [Hkv, R, S]     chunk max logit (log2 units)
   float* ws_l;  // [Hkv, R, S]     chunk normalizer
+  int32_t* ws_chunks;  // [B][2] first chunk slot and chunk count of each sequence
+                       // (written when B > 1 by the workgroup of slot 0, KV head 0)
 };
 
 struct CombineArgs {
@@ -82,7 +88,9 @@ struct CombineArgs {
   const float* sink;      // [Hq] or nullptr
   uint16_t* out;          // bf16 [B, Tq, Hq, D]
   const int32_t* seq_lens;
+  const int32_t* chunks;  // [B][2] as written by the split kernel (used when B > 1)
   int32_t max_seq_len, B, NW;
+  int32_t SMAX;           // most chunks one sequence can have
   int32_t Hkv, Hq, Tq, G, R, S;
 };
 

@@ -69,8 +69,10 @@ __device__ __forceinline__ int chunk_tiles(const int32_t* seq_lens, int B, int m
 
 // The chunk of workgroup `slot`, or, with slot < 0, just P_b and S_b of
 // sequence `want_b`.  Wave-uniform results.
+// With `table` non-null, also writes every sequence's (P_b, S_b) there.
 __device__ __forceinline__ Chunk find_chunk(const int32_t* seq_lens, int B, int max_seq_len, int NW,
-                                            int slot, int want_b, int lane) {
+                                            int slot, int want_b, int lane,
+                                            int32_t* table = nullptr) {
   const int C = chunk_tiles(seq_lens, B, max_seq_len, NW, lane);
   Chunk ch{-1, 0, 0, 0, 0, 0};
   int P = 0;  // chunks of the sequences before this pass
@@ -81,9 +83,13 @@ __device__ __forceinline__ Chunk find_chunk(const int32_t* seq_lens, int B, int 
     const int Sb = (n + C - 1) / C;
     const int incl = wave_scan_i(Sb, lane);
     const int Pb = P + incl - Sb;
+    if (table != nullptr && i < B) {
+      table[2 * i] = Pb;
+      table[2 * i + 1] = Sb;
+    }
     const bool hit = (i < B) && (slot >= 0 ? (Sb > 0 && Pb <= slot && slot < Pb + Sb) : i == want_b);
     const uint64_t m = __ballot(hit);
-    if (m != 0) {
+    if (m != 0 && ch.b < 0) {
       const int l = __builtin_ctzll(m);
       ch.b = base + l;
       ch.L = __shfl(L, l);
@@ -93,7 +99,7 @@ __device__ __forceinline__ Chunk find_chunk(const int32_t* seq_lens, int B, int 
       const int nb = __shfl(n, l);
       ch.first = c * C;
       ch.end = min(ch.first + C, nb);
-      break;
+      if (table == nullptr) break;  // the table needs every pass
     }
     P += __shfl(incl, 63);
   }

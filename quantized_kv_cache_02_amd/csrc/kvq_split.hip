@@ -422,8 +422,8 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
 // of the next NB-1 are in flight.
 template <int DT, int MODE, int D, int RB>
 struct Knobs {
-  static constexpr int NB = split_tiles_in_flight(D, RB);
-  static constexpr int WAVES_PER_EU = split_waves_per_simd(D, RB);
+  static constexpr int NB = kSplitTilesInFlight;
+  static constexpr int WAVES_PER_EU = kSplitWavesPerSimd;
   // merge buffers: one per wavefront when they fit in 64 KiB of LDS, else one
   // shared buffer the wavefronts add into in turn
   static constexpr int MERGE_BUFS = (kWaves * 16 * RB * D * 4 <= 65536) ? kWaves : 1;
@@ -442,8 +442,21 @@ split_decode_kernel(SplitArgs a) {
   __shared__ float s_m[kWaves][RP];
   __shared__ float s_l[kWaves][RP];
 
-  const int slot = blockIdx.x;
   const int hkv = blockIdx.y;
+  // Row-split launches (RBN > 1) give each of a chunk's RBN row blocks its own
+  // workgroup.  The x index packs (chunk slot, row block) so that the RBN
+  // workgroups of one chunk are 8 dispatch positions apart: the dispatcher
+  // deals workgroups to the 8 XCDs in turn, so they share one L2 and read the
+  // chunk's bytes from HBM once.
+  int slot = blockIdx.x, rbi = 0;
+  if (a.RBN > 1) {
+    const int grp = slot / (8 * a.RBN), rem = slot % (8 * a.RBN);
+    rbi = rem / 8;
+    slot = grp * 8 + rem % 8;
+    if (slot >= a.S) return;
+  }
+  const int row0 = rbi * RP;               // first query row of this workgroup
+  const int Rw = min(RP, a.R - row0);      // its query rows
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -462,7 +475,7 @@ split_decode_kernel(SplitArgs a) {
     for (int i = 0; i < QPT; ++i) {
       const int u = (tid + 256 * i) % (RP * QU);
       const int r = u / QU, cu = u % QU;
-      const int rr = r < a.R ? r : 0;
+      const int rr = row0 + (r < Rw ? r : 0);
       const int jq = rr / a.G, gh = rr % a.G;
       const uint16_t* src = a.q + ((((size_t)bq * a.Tq + jq) * a.Hq) + (size_t)hkv * a.G + gh) * D;
       qreg[i] = *reinterpret_cast<const u32x4_t*>(src + cu * 8);
@@ -484,7 +497,10 @@ split_decode_kernel(SplitArgs a) {
     te = min(tb + C, nt);
     if (tb >= nt) return;
   } else {
-    const Chunk ch = find_chunk(a.seq_lens, a.B, a.max_seq_len, a.NW, slot, -1, lane);
+    // the first wavefront of slot 0, KV head 0, row block 0 also records every
+    // sequence's chunk slots for the combine
+    int32_t* table = (slot == 0 && hkv == 0 && rbi == 0 && wave == 0) ? a.ws_chunks : nullptr;
+    const Chunk ch = find_chunk(a.seq_lens, a.B, a.max_seq_len, a.NW, slot, -1, lane, table);
     if (ch.b < 0) return;
     b = ch.b;
     L = ch.L;
@@ -498,25 +514,38 @@ split_decode_kernel(SplitArgs a) {
   // kvq_append), then waits for its stores before it issues any tile load.
   // No other wavefront reads those rows in this launch.
   if (a.k_new != nullptr) {
-    const int first = max(L - a.Tq, 0);
-    bool wrote = false;
-    for (int p = first; p < L; ++p) {
+    // Position L - Tq + j of query token j.  All of the wavefront's rows are
+    // loaded first (unconditional loads from clamped addresses), so their
+    // latencies overlap; then the owned ones are quantized and stored.
+    using RG = RowGeo<DT, D>;
+    uint16_t rk[kMaxQTokens][RG::EPL], rv[kMaxQTokens][RG::EPL];
+    int rblk[kMaxQTokens];
+    bool mine[kMaxQTokens];
+#pragma unroll
+    for (int j = 0; j < kMaxQTokens; ++j) {
+      const int p = L - a.Tq + j;
       const int t = p / kTile;
-      if (t < tb || t >= te || (t - tb) % kWaves != wave) continue;  // wave-uniform
-      int blk = b;
+      mine[j] = j < a.Tq && p >= 0 && t >= tb && t < te && (t - tb) % kWaves == wave;  // wave-uniform
+      const int jj = j < a.Tq ? j : 0;
+      const size_t xi = (((size_t)b * a.Tq + jj) * a.c.Hkv + hkv) * D;
+      load_row<DT, D>(a.k_new + xi, lane, rk[j]);
+      load_row<DT, D>(a.v_new + xi, lane, rv[j]);
+      rblk[j] = b;
       if (a.c.block_table != nullptr) {
-        blk = a.c.block_table[(size_t)b * a.c.max_blocks + p / a.c.block_size];
-        if ((unsigned)blk >= (unsigned)a.c.num_blocks) continue;
+        const int pc = p < 0 ? 0 : p;
+        rblk[j] = a.c.block_table[(size_t)b * a.c.max_blocks + pc / a.c.block_size];
       }
-      const size_t ri = ((size_t)blk * a.c.Hkv + hkv) * a.c.block_size + (size_t)(p % a.c.block_size);
-      const size_t xi = (((size_t)b * a.Tq + (p - (L - a.Tq))) * a.c.Hkv + hkv) * D;
-      using RG = RowGeo<DT, D>;
-      uint16_t rk[RG::EPL], rv[RG::EPL];
-      load_row<DT, D>(a.k_new + xi, lane, rk);
-      load_row<DT, D>(a.v_new + xi, lane, rv);
-      quantize_store_row<DT, MODE, D>(rk, lane, a.c.k_codes + ri * RG::ROWB, a.c.k_scales + ri,
+    }
+    bool wrote = false;
+#pragma unroll
+    for (int j = 0; j < kMaxQTokens; ++j) {
+      if (!mine[j] || (unsigned)rblk[j] >= (unsigned)a.c.num_blocks) continue;
+      const int p = L - a.Tq + j;
+      const size_t ri =
+          ((size_t)rblk[j] * a.c.Hkv + hkv) * a.c.block_size + (size_t)(p % a.c.block_size);
+      quantize_store_row<DT, MODE, D>(rk[j], lane, a.c.k_codes + ri * RG::ROWB, a.c.k_scales + ri,
                                       MODE == kPerChannel ? a.c.k_scales + (size_t)hkv * D : a.c.k_scales);
-      quantize_store_row<DT, MODE, D>(rv, lane, a.c.v_codes + ri * RG::ROWB, a.c.v_scales + ri,
+      quantize_store_row<DT, MODE, D>(rv[j], lane, a.c.v_codes + ri * RG::ROWB, a.c.v_scales + ri,
                                       MODE == kPerChannel ? a.c.v_scales + (size_t)hkv * D : a.c.v_scales);
       wrote = true;
     }
@@ -543,7 +572,7 @@ split_decode_kernel(SplitArgs a) {
   for (int i = 0; i < QPT; ++i) {
     const int u = tid + 256 * i;
     if (u < RP * QU) {
-      const u32x4_t v = (u / QU < a.R) ? qreg[i] : u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t v = (u / QU < Rw) ? qreg[i] : u32x4_t{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4_t*>(qs + (u / QU) * D + (u % QU) * 8) = v;
     }
   }
@@ -595,7 +624,7 @@ split_decode_kernel(SplitArgs a) {
       if constexpr (MODE == kPerTensor) mul *= kst[0];
       if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
       rowmul[rb] = ldexpf(mul, ex);
-      lim[rb] = (r < a.R) ? (L - a.Tq + r / a.G + 1) : 0;
+      lim[rb] = (r < Rw) ? (L - a.Tq + (row0 + r) / a.G + 1) : 0;
       if (lim[rb] > L) lim[rb] = L;
     }
   }
@@ -669,7 +698,7 @@ split_decode_kernel(SplitArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rb * 16 + 4 * g + e;
-          if (r < a.R) {
+          if (r < Rw) {
 #pragma unroll
             for (int k = 0; k < NCH; ++k) {
               float4_t v;
@@ -688,33 +717,42 @@ split_decode_kernel(SplitArgs a) {
     __syncthreads();
   }
 
-  for (int idx = tid * 4; idx < a.R * D; idx += 256 * 4) {
+  for (int idx = tid * 4; idx < Rw * D; idx += 256 * 4) {
     const int r = idx / D, d = idx % D;
     const int jn = d / G_::NCOL, k = (d % G_::NCOL) / 4;
     const int off = r * D + G_::NCOL * jn + 4 * ((k + jn / ROT) % NCH);
     float4_t v = *reinterpret_cast<const float4_t*>(smem + off);
 #pragma unroll
     for (int w = 1; w < nbuf; ++w) v += *reinterpret_cast<const float4_t*>(smem + (size_t)w * RP * D + off);
-    *reinterpret_cast<float4_t*>(a.ws_o + (((size_t)hkv * a.R + r) * a.S + slot) * D + d) = v;
+    *reinterpret_cast<float4_t*>(a.ws_o + (((size_t)hkv * a.R + row0 + r) * a.S + slot) * D + d) = v;
   }
-  if (tid < a.R) {
+  if (tid < Rw) {
     const int r = tid;
     float M = s_m[0][r];
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
     float Lt = 0.0f;
     if (M != -INFINITY)
       for (int w = 0; w < kWaves; ++w) Lt += s_l[w][r] * exp2f(s_m[w][r] - M);
-    a.ws_m[((size_t)hkv * a.R + r) * a.S + slot] = M;
-    a.ws_l[((size_t)hkv * a.R + r) * a.S + slot] = Lt;
+    a.ws_m[((size_t)hkv * a.R + row0 + r) * a.S + slot] = M;
+    a.ws_l[((size_t)hkv * a.R + row0 + r) * a.S + slot] = Lt;
   }
 }
 
 template <int DT, int MODE, int D, int RB>
 hipError_t launch_one(const SplitArgs& a, int B, hipStream_t st) {
+  // Only variants whose accumulators fit a wavefront's registers are built: the
+  // host gives wider row sets one workgroup per 16-row block instead.
   (void)B;
-  dim3 grid(a.S, a.c.Hkv, 1);
-  hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB>), grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+  if constexpr (RB * D > kSplitMaxAccColumns) {
+    (void)a;
+    (void)st;
+    return hipErrorInvalidValue;
+  } else {
+    const int gx = a.RBN > 1 ? (a.S + 7) / 8 * 8 * a.RBN : a.S;
+    dim3 grid(gx, a.c.Hkv, 1);
+    hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
 }
 
 template <int DT, int MODE, int D>
