@@ -65,6 +65,8 @@ class Workload:
     k_static: Optional[np.ndarray] = None  # fp32 [1] or [Hkv, D]
     v_static: Optional[np.ndarray] = None
     sink: Optional[np.ndarray] = None  # fp32 [Hq]
+    softcap: float = 0.0  # > 0: logits capped as softcap * tanh(z / softcap)
+    window: int = 0       # > 0: a query at position p sees tokens p - window + 1 .. p
     sm_scale: float = 0.0
     meta: dict = field(default_factory=dict)
 
@@ -237,7 +239,7 @@ def make_workload(cfg: int, ctx: Optional[int] = None, dtype: Optional[str] = No
 
 def random_workload(seed: int, B: int, Hkv: int, G: int, D: int, Tq: int, lens,
                     dtype: int, mode: int, block_size: Optional[int] = None,
-                    sink: bool = False) -> Workload:
+                    sink: bool = False, softcap: float = 0.0, window: int = 0) -> Workload:
     """Small seeded workload of any geometry for property tests."""
     lens = np.asarray(lens, np.int32)
     lmax = int(lens.max()) if lens.size else 0
@@ -267,4 +269,4 @@ def random_workload(seed: int, B: int, Hkv: int, G: int, D: int, Tq: int, lens,
     return Workload(name=f"random-{seed}", cfg=0, B=B, Hq=hq, Hkv=Hkv, D=D, Tq=Tq, dtype=dtype,
                     mode=mode, q=q, k=k, v=v, lens=lens, block_size=bs, num_blocks=nb,
                     block_table=table, k_static=k_static, v_static=v_static, sink=sk,
-                    sm_scale=sm)
+                    sm_scale=sm, softcap=float(np.float32(softcap)), window=int(window))

@@ -62,6 +62,8 @@ def lib():
         L.kvo_dequantize.restype = None
         L.kvo_attend.argtypes = [P, P, P, I, I, I, I, I, I, P, F, P, P, P]
         L.kvo_attend.restype = None
+        L.kvo_attend_ex.argtypes = [P, P, P, I, I, I, I, I, I, P, F, P, F, I, P, P]
+        L.kvo_attend_ex.restype = None
         L.kvo_cache_bytes_per_token.argtypes = [I, I, I, I, I]
         L.kvo_cache_bytes_per_token.restype = D
         L.kvo_num_threads.argtypes = []
@@ -176,9 +178,12 @@ class Cache:
 
 
 def attend(q_bits: np.ndarray, K: np.ndarray, V: np.ndarray, lens, scale: float,
-           sink: Optional[np.ndarray] = None, Hkv: Optional[int] = None):
+           sink: Optional[np.ndarray] = None, Hkv: Optional[int] = None, softcap: float = 0.0,
+           window: int = 0):
     """fp64 softmax attention.  q_bits bf16 bits [B, Tq, Hq, D]; K, V fp32
-    [B, Hkv, Lmax, D].  Returns (out fp64 [B, Tq, Hq, D], lse fp64 [B, Tq, Hq])."""
+    [B, Hkv, Lmax, D].  softcap > 0 caps every scaled logit as c tanh(z / c);
+    window > 0 lets a query at position p see tokens p - window + 1 .. p only.
+    Returns (out fp64 [B, Tq, Hq, D], lse fp64 [B, Tq, Hq])."""
     q_bits = np.ascontiguousarray(q_bits, np.uint16)
     K = np.ascontiguousarray(K, np.float32)
     V = np.ascontiguousarray(V, np.float32)
@@ -188,8 +193,8 @@ def attend(q_bits: np.ndarray, K: np.ndarray, V: np.ndarray, lens, scale: float,
     out = np.empty((B, Tq, Hq, D), np.float64)
     lse = np.empty((B, Tq, Hq), np.float64)
     sk = _c(sink, np.float32)
-    lib().kvo_attend(_p(q_bits), _p(K), _p(V), B, Tq, Hq, hkv, D, K.shape[2], _p(lens),
-                     float(scale), _p(sk), _p(out), _p(lse))
+    lib().kvo_attend_ex(_p(q_bits), _p(K), _p(V), B, Tq, Hq, hkv, D, K.shape[2], _p(lens),
+                        float(scale), _p(sk), float(softcap), int(window), _p(out), _p(lse))
     return out, lse
 
 
@@ -230,5 +235,5 @@ def reference(w, cache: Optional[Cache] = None):
         cache = build_cache(w)
     K, V = cache.dequantize(w.lens, w.block_table)
     qb = w.q.contiguous().view(torch.int16).numpy().view(np.uint16)
-    out, lse = attend(qb, K, V, w.lens, w.sm_scale, w.sink, w.Hkv)
+    out, lse = attend(qb, K, V, w.lens, w.sm_scale, w.sink, w.Hkv, w.softcap, w.window)
     return out, lse, cache

@@ -258,9 +258,27 @@ void kvo_dequantize(int dtype, int mode, int Hkv, int D, int block_size, const u
  *   no visible token: o = 0 and lse = -inf
  * out fp64 [B, Tq, Hq, D]; lse_out fp64 [B, Tq, Hq] (may be NULL).
  */
-void kvo_attend(const uint16_t* q, const float* K, const float* V, int B, int Tq, int Hq, int Hkv,
-                int D, int Lmax, const int32_t* lens, float scale, const float* sink, double* out,
-                double* lse_out) {
+/* Logit of query row qd against key row k: z = scale * q . k, then, with a
+ * soft cap c > 0, z -> c * tanh(z / c) ([P] "CUDA kernels": the paged decode
+ * kernel takes a softcap; the cap applies to the scaled attention logits). */
+static double kvo_logit(const double* qd, const float* k, int D, float scale, float softcap) {
+  double z = 0.0;
+  for (int d = 0; d < D; ++d) z += qd[d] * (double)k[d];
+  z *= (double)scale;
+  if (softcap > 0.0f) z = (double)softcap * tanh(z / (double)softcap);
+  return z;
+}
+
+/* fp64 softmax attention over the dequantized cache, with GQA (query head h
+ * reads KV head h / (Hq / Hkv)), causal speculative drafts (query j of
+ * sequence b sits at position lens[b] - Tq + j and sees tokens at or before it),
+ * an optional sliding window (window > 0: only tokens pos - window + 1 .. pos;
+ * [P] "CUDA kernels": sliding-window decode), an optional logit soft cap and an
+ * optional per-head sink (o *= 1 / (1 + exp(sink[h] - lse)), [P] ApplyHeadSink).
+ * A query with no visible token outputs zeros. */
+void kvo_attend_ex(const uint16_t* q, const float* K, const float* V, int B, int Tq, int Hq, int Hkv,
+                   int D, int Lmax, const int32_t* lens, float scale, const float* sink,
+                   float softcap, int window, double* out, double* lse_out) {
   int G = Hq / Hkv;
 #pragma omp parallel for collapse(3) schedule(dynamic)
   for (int b = 0; b < B; ++b)
@@ -271,8 +289,10 @@ void kvo_attend(const uint16_t* q, const float* K, const float* V, int B, int Tq
         double* o = out + qi;
         for (int d = 0; d < D; ++d) o[d] = 0.0;
         int pos = lens[b] - Tq + j;
-        int nvis = pos + 1 < lens[b] ? pos + 1 : lens[b];
-        if (nvis <= 0) {
+        int hi = pos + 1 < lens[b] ? pos + 1 : lens[b]; /* tokens [lo, hi) are visible */
+        int lo = window > 0 ? pos - window + 1 : 0;
+        if (lo < 0) lo = 0;
+        if (hi <= lo) {
           if (lse_out) lse_out[((size_t)b * Tq + j) * Hq + h] = -INFINITY;
           continue;
         }
@@ -282,19 +302,14 @@ void kvo_attend(const uint16_t* q, const float* K, const float* V, int B, int Tq
         for (int d = 0; d < D; ++d) qd[d] = (double)kvo_bf16_to_float(q[qi + d]);
         double m = -INFINITY;
         /* pass 1: max logit */
-        for (int t = 0; t < nvis; ++t) {
-          double z = 0.0;
-          for (int d = 0; d < D; ++d) z += qd[d] * (double)Kb[(size_t)t * D + d];
-          z *= (double)scale;
+        for (int t = lo; t < hi; ++t) {
+          double z = kvo_logit(qd, Kb + (size_t)t * D, D, scale, softcap);
           if (z > m) m = z;
         }
         /* pass 2: normalizer and weighted sum of V */
         double l = 0.0;
-        for (int t = 0; t < nvis; ++t) {
-          double z = 0.0;
-          for (int d = 0; d < D; ++d) z += qd[d] * (double)Kb[(size_t)t * D + d];
-          z *= (double)scale;
-          double p = exp(z - m);
+        for (int t = lo; t < hi; ++t) {
+          double p = exp(kvo_logit(qd, Kb + (size_t)t * D, D, scale, softcap) - m);
           l += p;
           for (int d = 0; d < D; ++d) o[d] += p * (double)Vb[(size_t)t * D + d];
         }
@@ -306,6 +321,13 @@ void kvo_attend(const uint16_t* q, const float* K, const float* V, int B, int Tq
         }
         if (lse_out) lse_out[((size_t)b * Tq + j) * Hq + h] = lse;
       }
+}
+
+/* The same without soft cap or window. */
+void kvo_attend(const uint16_t* q, const float* K, const float* V, int B, int Tq, int Hq, int Hkv,
+                int D, int Lmax, const int32_t* lens, float scale, const float* sink, double* out,
+                double* lse_out) {
+  kvo_attend_ex(q, K, V, B, Tq, Hq, Hkv, D, Lmax, lens, scale, sink, 0.0f, 0, out, lse_out);
 }
 
 /* Bytes of cache one token occupies across `layers` layers: K and V rows of

@@ -68,8 +68,10 @@ def fp8_codes_argmin(y: np.ndarray) -> np.ndarray:
     return code | (sign << 7)
 
 
-def attention_loops(q, K, V, lens, scale, sink=None):
-    """Pure-Python softmax attention.  q [B, Tq, Hq, D] floats, K, V [B, Hkv, L, D]."""
+def attention_loops(q, K, V, lens, scale, sink=None, softcap=0.0, window=0):
+    """Pure-Python softmax attention.  q [B, Tq, Hq, D] floats, K, V [B, Hkv, L, D].
+    softcap > 0: each scaled logit z becomes softcap * tanh(z / softcap).
+    window > 0: the query at position pos attends tokens pos - window + 1 .. pos."""
     B, Tq, Hq, D = q.shape
     Hkv = K.shape[1]
     G = Hq // Hkv
@@ -79,22 +81,26 @@ def attention_loops(q, K, V, lens, scale, sink=None):
             for h in range(Hq):
                 hk = h // G
                 pos = int(lens[b]) - Tq + j
-                n = min(pos + 1, int(lens[b]))
-                if n <= 0:
+                seen = [t for t in range(int(lens[b]))
+                        if t <= pos and (window == 0 or t > pos - window)]
+                if not seen:
                     continue
                 zs = []
-                for t in range(n):
+                for t in seen:
                     z = 0.0
                     for d in range(D):
                         z += float(q[b, j, h, d]) * float(K[b, hk, t, d])
-                    zs.append(z * scale)
+                    z *= scale
+                    if softcap > 0:
+                        z = softcap * math.tanh(z / softcap)
+                    zs.append(z)
                 m = max(zs)
                 ws = [math.exp(z - m) for z in zs]
                 l = sum(ws)
                 for d in range(D):
                     acc = 0.0
-                    for t in range(n):
-                        acc += ws[t] * float(V[b, hk, t, d])
+                    for i, t in enumerate(seen):
+                        acc += ws[i] * float(V[b, hk, t, d])
                     out[b, j, h, d] = acc / l
                 if sink is not None:
                     lse = m + math.log(l)

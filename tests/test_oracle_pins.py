@@ -279,6 +279,81 @@ def test_attend_matches_python_loops_tiny(oracle_lib):
         assert np.max(np.abs(out - ref)) <= 1e-12
 
 
+# ---------------------------------------------- soft cap and sliding window
+# ORT PR "[CUDA] PagedAttention: quantized KV cache ...", "CUDA kernels": the
+# paged decode kernel takes a softcap and a sliding window.
+
+def test_softcap_window_match_python_loops_tiny(oracle_lib):
+    cases = [(1, 1, 2, 32, 1, [9], 1.5, 0), (2, 2, 3, 32, 2, [1, 17], 0.0, 4),
+             (1, 2, 4, 64, 3, [40], 2.0, 7), (2, 1, 1, 32, 4, [3, 9], 0.7, 2)]
+    for seed, (B, Hkv, G, D, Tq, lens, cap, win) in enumerate(cases):
+        w = ki.random_workload(700 + seed, B=B, Hkv=Hkv, G=G, D=D, Tq=Tq, lens=lens, dtype=INT8,
+                               mode=PER_ROW, sink=(seed % 2 == 1), softcap=cap, window=win)
+        out, _, cache = oracle_lib.reference(w)
+        K, V = cache.dequantize(w.lens)
+        # the cap is an fp32 argument, like the softmax scale
+        ref = bf.attention_loops(w.q.double().numpy(), K, V, w.lens, w.sm_scale, w.sink,
+                                 softcap=float(np.float32(cap)), window=win)
+        assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("window,Tq", [(1, 1), (5, 1), (16, 3), (33, 8)])
+def test_window_matches_torch_sdpa_mask(oracle_lib, window, Tq):
+    """The window as a boolean mask handed to torch SDPA in float64."""
+    rng = np.random.default_rng(window * 10 + Tq)
+    B, Hkv, G, D = 2, 2, 3, 64
+    lens = np.array([37, 90], np.int32)
+    K = rng.standard_normal((B, Hkv, 90, D)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, 90, D)).astype(np.float32)
+    q = ki.randn_bf16((B, Tq, G * Hkv, D), 51 + window)
+    scale = 1 / 8
+    out, _ = oracle_lib.attend(_bits(q), K, V, lens, scale, window=window)
+    for b in range(B):
+        L = int(lens[b])
+        qt = q[b].double().transpose(0, 1)
+        kt = torch.from_numpy(K[b, :, :L].astype(np.float64)).repeat_interleave(G, 0)
+        vt = torch.from_numpy(V[b, :, :L].astype(np.float64)).repeat_interleave(G, 0)
+        pos = L - Tq + torch.arange(Tq)[:, None]
+        t = torch.arange(L)[None, :]
+        mask = (t <= pos) & (t > pos - window)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+        assert np.max(np.abs(out[b] - ref.transpose(0, 1).numpy())) <= 1e-12
+
+
+def test_window_and_softcap_limits(oracle_lib):
+    rng = np.random.default_rng(77)
+    B, Hkv, G, D, Tq, L = 1, 2, 2, 32, 3, 50
+    K = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    q = ki.randn_bf16((B, Tq, G * Hkv, D), 78)
+    lens = np.array([L], np.int32)
+    base, _ = oracle_lib.attend(_bits(q), K, V, lens, 0.3)
+    # a window covering the whole sequence changes nothing
+    wide, _ = oracle_lib.attend(_bits(q), K, V, lens, 0.3, window=L)
+    np.testing.assert_array_equal(wide, base)
+    # window 1: each query sees only its own token, whose value row it returns
+    one, _ = oracle_lib.attend(_bits(q), K, V, lens, 0.3, window=1)
+    for j in range(Tq):
+        for h in range(G * Hkv):
+            np.testing.assert_array_equal(one[0, j, h], V[0, h // G, L - Tq + j].astype(np.float64))
+    # an enormous cap is the identity on logits of size O(1)
+    loose, _ = oracle_lib.attend(_bits(q), K, V, lens, 0.3, softcap=1e9)
+    assert np.max(np.abs(loose - base)) <= 1e-12
+    # a tiny cap flattens every logit to ~0: the mean of the visible value rows
+    flat, _ = oracle_lib.attend(_bits(q), K, V, lens, 0.3, softcap=1e-9)
+    for j in range(Tq):
+        n = L - Tq + j + 1
+        for h in range(G * Hkv):
+            mean = V[0, h // G, :n].astype(np.float64).mean(axis=0)
+            assert np.max(np.abs(flat[0, j, h] - mean)) <= 1e-7
+    # the cap bounds the logit spread: weights stay within exp(2 c) of each other,
+    # so a cap of 0.5 pulls the output towards the mean compared to no cap
+    capped, _ = oracle_lib.attend(_bits(q), K, V, lens, 0.3, softcap=0.5)
+    n = L - Tq + 1
+    mean = V[0, 0, :n].astype(np.float64).mean(axis=0)
+    assert np.linalg.norm(capped[0, 0, 0] - mean) < np.linalg.norm(base[0, 0, 0] - mean)
+
+
 def test_gqa_matches_replicated_heads(oracle_lib):
     """kv-quant-attn page, Correctness: GQA ratios 1:1 .. 8:1 match a replicated-head reference."""
     rng = np.random.default_rng(8)
