@@ -59,10 +59,16 @@ def measured_traffic(bytes_per_launch_alg: float):
 
 
 def algorithmic_bytes(w) -> int:
-    """K and V codes plus per-row scales of every cached token the step reads."""
+    """K and V codes plus per-row scales of every cached token the step's queries
+    can see (all of them, or those inside a sliding window)."""
     row = w.D // 2 if w.dtype == 2 else w.D
     per_row_scale = 4 if w.mode == 1 else 0
-    return int(2 * int(w.lens.sum()) * w.Hkv * (row + per_row_scale))
+    tokens = 0
+    for L in w.lens:
+        L = int(L)
+        lo = max(0, L - w.Tq - w.window + 1) if w.window > 0 else 0
+        tokens += L - lo
+    return int(2 * tokens * w.Hkv * (row + per_row_scale))
 
 
 def build_layers(kvq, torch, w, layers: int, dev):
@@ -111,8 +117,14 @@ def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fuse
     out = torch.empty_like(q)
     S = kvq.num_splits(caches[0], B, Hq, Tq, msl)
 
+    options = w.softcap > 0 or w.window > 0
+
     def step(c, s):
-        if fused:
+        if options:
+            kvq.attend_ex(c, q, lens, msl, w.sm_scale, block_table=table, head_sink=sink,
+                          k_new=kn if fused else None, v_new=vn if fused else None,
+                          softcap=w.softcap, window=w.window, out=out, workspace=ws, stream=s)
+        elif fused:
             kvq.append_decode_attend(c, kn, vn, q, lens, msl, w.sm_scale, block_table=table,
                                      head_sink=sink, out=out, workspace=ws, stream=s)
         else:
@@ -121,7 +133,10 @@ def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fuse
             kvq.combine(c, B, Hq, Tq, lens, msl, ws, out, head_sink=sink, stream=s)
 
     def split_only(c, s):
-        kvq.split_decode(c, q, lens, msl, w.sm_scale, ws, block_table=table, stream=s)
+        if options:  # the options entry point has no split-only form: time the step
+            step(c, s)
+        else:
+            kvq.split_decode(c, q, lens, msl, w.sm_scale, ws, block_table=table, stream=s)
 
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
@@ -327,11 +342,18 @@ def main():
                           f"split {s['split_ms'] * 1e3:.2f} us {s['split_GBps']:.0f} GB/s",
                           file=sys.stderr, flush=True)
                     torch.cuda.empty_cache()
-            for cfg in (2, 4, 5):
-                w = ki.make_workload(cfg)
+            extra = [ki.make_workload(cfg) for cfg in (2, 4, 5)]
+            for win, cap in ((4096, 0.0), (0, 30.0)):
+                w = ki.make_workload(3, ctx=65536, dtype="int8")
+                w.window, w.softcap = win, cap
+                w.name = f"{w.name}-window{win}-softcap{int(cap)}"
+                extra.append(w)
+            for w in extra:
+                cfg = w.cfg
                 s = time_workload(kvq, torch, w, args.layers, max(64, args.steps // 4), args.warmup,
                                   dev, fused)
                 s["cfg"] = cfg
+                s["window"], s["softcap"] = w.window, w.softcap
                 s["step_GBps"] = s["bytes"] / (s["step_ms"] * 1e-3) / 1e9
                 s["split_GBps"] = s["bytes"] / (s["split_ms"] * 1e-3) / 1e9
                 s["split_frac_of_peak"] = s["split_GBps"] / PEAK_HBM_GBPS

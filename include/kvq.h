@@ -94,6 +94,22 @@ typedef struct kvq_cache {
 } kvq_cache;
 
 /*
+ * Options of kvq_attend_ex ([P] "CUDA kernels": the paged decode kernel takes a
+ * logit soft cap and a sliding window).
+ *   softcap  > 0: every scaled logit z = softmax_scale * q . k becomes
+ *            softcap * tanh(z / softcap) before the softmax (the head-sink logit is
+ *            not capped); 0: off.  Finite, >= 0.
+ *   window   > 0: the query at position p attends only the tokens
+ *            p - window + 1 .. p (with the causal bound of speculative drafts);
+ *            whole 16-token tiles before the first query's window are not read.
+ *            0: every cached token.
+ */
+typedef struct kvq_attn_options {
+  float softcap;
+  int32_t window;
+} kvq_attn_options;
+
+/*
  * kvq_append -- quantize `tokens` new K and V rows per sequence on write and
  * store them at positions positions[b] + j (j < tokens).
  *
@@ -202,6 +218,21 @@ int kvq_append_decode_attend(const kvq_cache* cache, const void* k_new, const vo
                              const float* head_sink, const int32_t* block_table,
                              int32_t max_blocks, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_attend_ex -- the decode step with every option: an optional fused append
+ * (k_new and v_new both non-NULL: as kvq_append_decode_attend; both NULL: the
+ * cache already holds the rows), contiguous (block_table NULL) or paged cache,
+ * optional head sink, and the attention options above (options NULL: none).
+ * Arguments otherwise as kvq_append_decode_attend.  KVQ_EINVAL also for a
+ * negative or non-finite soft cap, a negative window, or only one of k_new /
+ * v_new.
+ */
+int kvq_attend_ex(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                  int32_t batch, int32_t num_q_heads, int32_t q_tokens, const int32_t* seq_lens,
+                  int32_t max_seq_len, float softmax_scale, const float* head_sink,
+                  const int32_t* block_table, int32_t max_blocks, const kvq_attn_options* options,
+                  void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The two phases the decode entry points are made of, for callers that

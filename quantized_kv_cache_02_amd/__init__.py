@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "INT8", "INT4", "FP8_E4M3FN", "PER_ROW", "PER_TENSOR", "PER_CHANNEL",
     "KVCache", "KvqError", "append", "num_splits", "workspace_bytes", "decode_attend",
-    "paged_decode_attend", "append_decode_attend", "split_decode", "combine", "cache_bytes",
+    "paged_decode_attend", "append_decode_attend", "attend_ex", "split_decode", "combine",
+    "cache_bytes",
     "lib", "LIB_PATH",
 ]
 
@@ -28,8 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 EXPORTS = (
     "kvq_append", "kvq_num_splits", "kvq_workspace_bytes", "kvq_decode_attend",
-    "kvq_paged_decode_attend", "kvq_append_decode_attend", "kvq_split_decode", "kvq_combine",
-    "kvq_cache_bytes",
+    "kvq_paged_decode_attend", "kvq_append_decode_attend", "kvq_attend_ex", "kvq_split_decode",
+    "kvq_combine", "kvq_cache_bytes",
     "kvq_status_string",
 )
 
@@ -46,6 +47,10 @@ class _Cache(ctypes.Structure):
         ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
         ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
     ]
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("softcap", ctypes.c_float), ("window", ctypes.c_int32)]
 
 
 _lib = None
@@ -74,6 +79,9 @@ def lib():
         L.kvq_append_decode_attend.argtypes = [CP, P, P, P, I32, I32, I32, P, I32, F, P, P, I32,
                                                P, P, SZ, P]
         L.kvq_append_decode_attend.restype = ctypes.c_int
+        L.kvq_attend_ex.argtypes = [CP, P, P, P, I32, I32, I32, P, I32, F, P, P, I32,
+                                    ctypes.POINTER(_Options), P, P, SZ, P]
+        L.kvq_attend_ex.restype = ctypes.c_int
         L.kvq_split_decode.argtypes = [CP, P, I32, I32, I32, P, I32, F, P, I32, P, SZ, P]
         L.kvq_split_decode.restype = ctypes.c_int
         L.kvq_combine.argtypes = [CP, I32, I32, I32, P, I32, P, P, P, SZ, P]
@@ -246,6 +254,36 @@ def append_decode_attend(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tenso
                                           _ptr(head_sink), _ptr(block_table), mb, _ptr(out),
                                           _ptr(ws), nbytes, _stream(stream)),
            "kvq_append_decode_attend")
+    return out
+
+
+def attend_ex(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+              softmax_scale: float, block_table: Optional[torch.Tensor] = None,
+              head_sink: Optional[torch.Tensor] = None, k_new: Optional[torch.Tensor] = None,
+              v_new: Optional[torch.Tensor] = None, softcap: float = 0.0, window: int = 0,
+              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """The decode step with every option: optional fused append (k_new, v_new bf16
+    [B, Tq, Hkv, D]), contiguous or paged cache, optional sink, logit soft cap and
+    sliding window (0 = off)."""
+    _want(q, torch.bfloat16, "q")
+    _want(seq_lens, torch.int32, "seq_lens")
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        if t is not None:
+            _want(t, torch.bfloat16, nm)
+    B, Tq, Hq, _ = q.shape
+    mb = 0
+    if block_table is not None:
+        _want(block_table, torch.int32, "block_table")
+        mb = block_table.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    ws, nbytes = _workspace(cache, B, Hq, Tq, max_seq_len, workspace, q.device)
+    opts = _Options(float(softcap), int(window))
+    _check(lib().kvq_attend_ex(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, Tq,
+                               _ptr(seq_lens), max_seq_len, float(softmax_scale), _ptr(head_sink),
+                               _ptr(block_table), mb, ctypes.byref(opts), _ptr(out), _ptr(ws),
+                               nbytes, _stream(stream)),
+           "kvq_attend_ex")
     return out
 
 

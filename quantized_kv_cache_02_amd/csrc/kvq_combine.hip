@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
   int S = Sld;
   if (a.B == 1) {
-    const int nt = (clamp_len(L0, a.max_seq_len) + kTile - 1) / kTile;
+    const Span sp = visible_tiles(clamp_len(L0, a.max_seq_len), a.Tq, a.window);
+    const int nt = sp.end - sp.first;
     const int C = max((nt + a.NW - 1) / a.NW, kMinTilesPerSplit);
     S = min((nt + C - 1) / C, Sld);
   }

@@ -176,7 +176,8 @@ hipError_t dispatch_split(int dt, int md, int D, int RB, const kvq::SplitArgs& a
 int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int32_t tq,
                const int32_t* seq_lens, int32_t max_seq_len, float scale, const int32_t* table,
                int32_t max_blocks, void* ws, size_t ws_bytes, void* stream,
-               const void* k_new = nullptr, const void* v_new = nullptr) {
+               const void* k_new = nullptr, const void* v_new = nullptr,
+               const kvq_attn_options* opts = nullptr) {
   DecodeShape sh;
   int st = decode_shape(c, batch, hq, tq, max_seq_len, &sh);
   if (st != KVQ_OK) return st;
@@ -199,6 +200,8 @@ int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int
   a.S = sh.NSLOT;
   a.RBN = sh.RBN;
   a.sm_scale = scale;
+  a.softcap = opts ? opts->softcap : 0.0f;
+  a.window = opts ? opts->window : 0;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   workspace_ptrs(ws, c, batch, sh, &a.ws_o, &a.ws_m, &a.ws_l, &a.ws_chunks);
@@ -209,7 +212,7 @@ int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int
 
 int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, const int32_t* seq_lens,
                  int32_t max_seq_len, const float* sink, void* out, const void* ws, size_t ws_bytes,
-                 void* stream) {
+                 void* stream, int32_t window = 0) {
   DecodeShape sh;
   int st = decode_shape(c, batch, hq, tq, max_seq_len, &sh);
   if (st != KVQ_OK) return st;
@@ -222,6 +225,7 @@ int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, cons
   workspace_ptrs(const_cast<void*>(ws), c, batch, sh, &o, &m, &l, &chunks);
   a.chunks = chunks;
   a.SMAX = sh.SMAX;
+  a.window = window;
   a.ws_o = o;
   a.ws_m = m;
   a.ws_l = l;
@@ -346,6 +350,26 @@ int kvq_append_decode_attend(const kvq_cache* cache, const void* k_new, const vo
   if (st != KVQ_OK) return st;
   return kvq_combine(cache, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, head_sink, out,
                      workspace, workspace_bytes, stream);
+}
+
+int kvq_attend_ex(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                  int32_t batch, int32_t num_q_heads, int32_t q_tokens, const int32_t* seq_lens,
+                  int32_t max_seq_len, float softmax_scale, const float* head_sink,
+                  const int32_t* block_table, int32_t max_blocks, const kvq_attn_options* options,
+                  void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return KVQ_EINVAL;
+  if (k_new != nullptr && (!aligned16(k_new) || !aligned16(v_new))) return KVQ_EINVAL;
+  if (out == nullptr || !aligned16(out)) return KVQ_EINVAL;
+  if (options != nullptr) {
+    const float cap = options->softcap;
+    if (!(cap >= 0.0f) || cap > 3.0e38f || options->window < 0) return KVQ_EINVAL;
+  }
+  int st = split_impl(cache, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, softmax_scale,
+                      block_table, max_blocks, workspace, workspace_bytes, stream, k_new, v_new,
+                      options);
+  if (st != KVQ_OK) return st;
+  return combine_impl(cache, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, head_sink, out,
+                      workspace, workspace_bytes, stream, options ? options->window : 0);
 }
 
 size_t kvq_cache_bytes(int32_t dtype, int32_t scale_mode, int32_t num_kv_heads, int32_t head_dim,

@@ -69,6 +69,8 @@ struct SplitArgs {
   int32_t RBN; // workgroups per chunk, one per 16-row block of query rows (1: one
                // workgroup serves every row)
   float sm_scale;
+  float softcap;   // > 0: logits z -> softcap * tanh(z / softcap)
+  int32_t window;  // > 0: a query at position p sees tokens p - window + 1 .. p
   // fused append (both null when not fused): bf16 [B, Tq, Hkv, D] rows of the
   // query tokens, written at positions seq_len - Tq + j before they are read
   const uint16_t* k_new;
@@ -91,6 +93,7 @@ struct CombineArgs {
   const int32_t* chunks;  // [B][2] as written by the split kernel (used when B > 1)
   int32_t max_seq_len, B, NW;
   int32_t SMAX;           // most chunks one sequence can have
+  int32_t window;         // the split's sliding window (it shapes the chunks)
   int32_t Hkv, Hq, Tq, G, R, S;
 };
 

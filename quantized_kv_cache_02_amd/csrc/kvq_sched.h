@@ -7,7 +7,9 @@
 // sequence leaves the workgroups of the longest sequence on the critical path
 // while the others idle, so the cut is made over the whole batch instead:
 //
-//   n_b = ceil(L_b / 16)                 16-token tiles of sequence b
+//   n_b = ceil(L_b / 16) - f_b          16-token tiles sequence b's queries see
+//                                        (f_b: the first tile inside a sliding
+//                                        window, 0 without one)
 //   T   = sum_b n_b                      tiles of one KV head
 //   C   = max(ceil(T / NW), kMinTilesPerSplit)   tiles per chunk
 //   S_b = ceil(n_b / C)                  chunks of sequence b (never straddling two)
@@ -45,6 +47,20 @@ __device__ __forceinline__ int wave_scan_i(int v, int lane) {
   return v;
 }
 
+// Tiles [first, end) of a sequence of length L that its Tq queries can see: a
+// sliding window hides every token before L - Tq - window + 1 (the first
+// query's window) ([P] "CUDA kernels": sliding-window decode).
+struct Span {
+  int first, end;
+};
+__device__ __forceinline__ Span visible_tiles(int L, int Tq, int window) {
+  const int end = (L + kTile - 1) / kTile;
+  int lo = window > 0 ? L - Tq - window + 1 : 0;
+  lo = lo < 0 ? 0 : lo;
+  const int first = lo / kTile;
+  return Span{first < end ? first : end, end};
+}
+
 struct Chunk {
   int b;       // sequence (-1: idle slot)
   int first;   // first tile of the chunk
@@ -56,12 +72,13 @@ struct Chunk {
 
 // Tiles per chunk over the whole batch (every lane gets the same value).
 __device__ __forceinline__ int chunk_tiles(const int32_t* seq_lens, int B, int max_seq_len, int NW,
-                                           int lane) {
+                                           int Tq, int window, int lane) {
   int T = 0;
   for (int base = 0; base < B; base += 64) {
     const int i = base + lane;
     const int L = i < B ? clamp_len(seq_lens[i], max_seq_len) : 0;
-    T += wave_sum_i((L + kTile - 1) / kTile);
+    const Span sp = visible_tiles(L, Tq, window);
+    T += wave_sum_i(sp.end - sp.first);
   }
   const int C = (T + NW - 1) / NW;
   return C > kMinTilesPerSplit ? C : kMinTilesPerSplit;
@@ -71,15 +88,16 @@ __device__ __forceinline__ int chunk_tiles(const int32_t* seq_lens, int B, int m
 // sequence `want_b`.  Wave-uniform results.
 // With `table` non-null, also writes every sequence's (P_b, S_b) there.
 __device__ __forceinline__ Chunk find_chunk(const int32_t* seq_lens, int B, int max_seq_len, int NW,
-                                            int slot, int want_b, int lane,
+                                            int Tq, int window, int slot, int want_b, int lane,
                                             int32_t* table = nullptr) {
-  const int C = chunk_tiles(seq_lens, B, max_seq_len, NW, lane);
+  const int C = chunk_tiles(seq_lens, B, max_seq_len, NW, Tq, window, lane);
   Chunk ch{-1, 0, 0, 0, 0, 0};
   int P = 0;  // chunks of the sequences before this pass
   for (int base = 0; base < B; base += 64) {
     const int i = base + lane;
     const int L = i < B ? clamp_len(seq_lens[i], max_seq_len) : 0;
-    const int n = (L + kTile - 1) / kTile;
+    const Span sp = visible_tiles(L, Tq, window);
+    const int n = sp.end - sp.first;
     const int Sb = (n + C - 1) / C;
     const int incl = wave_scan_i(Sb, lane);
     const int Pb = P + incl - Sb;
@@ -96,8 +114,9 @@ __device__ __forceinline__ Chunk find_chunk(const int32_t* seq_lens, int B, int 
       ch.P = __shfl(Pb, l);
       ch.S = __shfl(Sb, l);
       const int c = slot >= 0 ? slot - ch.P : 0;
-      const int nb = __shfl(n, l);
-      ch.first = c * C;
+      const int f0 = __shfl(sp.first, l);
+      const int nb = __shfl(sp.end, l);
+      ch.first = f0 + c * C;
       ch.end = min(ch.first + C, nb);
       if (table == nullptr) break;  // the table needs every pass
     }

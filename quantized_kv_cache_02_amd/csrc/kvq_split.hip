@@ -272,10 +272,11 @@ struct WaveState {
   float vref;                          // per-row V: weights carry 1/vref, a power of two
 };
 
-template <int DT, int MODE, int D, int RB>
+template <int DT, int MODE, int D, int RB, bool CAP>
 __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L, int n, int g,
                                              const half8_t (&qb)[RB][Geo<DT, D>::KSTEPS],
                                              const float (&rowmul)[RB], const int (&lim)[RB],
+                                             const int (&lo)[RB], float cap2, float icap2,
                                              WaveState<DT, D, RB>& W) {
   using G_ = Geo<DT, D>;
   const int tok0 = t * kTile;
@@ -333,7 +334,9 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
     for (int e = 0; e < 4; ++e) {
       float zz = (s0[e] + s1[e]) * rowmul[rb];
       if constexpr (MODE == kPerRow) zz *= T.ks4[e];
-      z[e] = (ok && tbase + e < lim[rb]) ? zz : -INFINITY;
+      // soft cap in log2 units: cap2 = softcap * log2(e)
+      if constexpr (CAP) zz = cap2 * tanhf(zz * icap2);
+      z[e] = (ok && tbase + e < lim[rb] && tbase + e >= lo[rb]) ? zz : -INFINITY;
       up |= z[e] > W.m[rb];
     }
     // The running max changes only if some logit exceeds it; the cross-lane
@@ -429,7 +432,7 @@ struct Knobs {
   static constexpr int MERGE_BUFS = (kWaves * 16 * RB * D * 4 <= 65536) ? kWaves : 1;
 };
 
-template <int DT, int MODE, int D, int RB>
+template <int DT, int MODE, int D, int RB, bool CAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     Knobs<DT, MODE, D, RB>::WAVES_PER_EU, Knobs<DT, MODE, D, RB>::WAVES_PER_EU))) void
 split_decode_kernel(SplitArgs a) {
@@ -491,16 +494,17 @@ split_decode_kernel(SplitArgs a) {
     b = 0;
     load_q(0);
     L = clamp_len(a.seq_lens[0], a.max_seq_len);
-    const int nt = (L + kTile - 1) / kTile;
-    const int C = max((nt + a.NW - 1) / a.NW, kMinTilesPerSplit);
-    tb = slot * C;
-    te = min(tb + C, nt);
-    if (tb >= nt) return;
+    const Span sp = visible_tiles(L, a.Tq, a.window);
+    const int C = max((sp.end - sp.first + a.NW - 1) / a.NW, kMinTilesPerSplit);
+    tb = sp.first + slot * C;
+    te = min(tb + C, sp.end);
+    if (tb >= sp.end) return;
   } else {
     // the first wavefront of slot 0, KV head 0, row block 0 also records every
     // sequence's chunk slots for the combine
     int32_t* table = (slot == 0 && hkv == 0 && rbi == 0 && wave == 0) ? a.ws_chunks : nullptr;
-    const Chunk ch = find_chunk(a.seq_lens, a.B, a.max_seq_len, a.NW, slot, -1, lane, table);
+    const Chunk ch = find_chunk(a.seq_lens, a.B, a.max_seq_len, a.NW, a.Tq, a.window, slot, -1, lane,
+                                table);
     if (ch.b < 0) return;
     b = ch.b;
     L = ch.L;
@@ -582,7 +586,8 @@ split_decode_kernel(SplitArgs a) {
   // power of two so every element lies in (-1, 1); the row multiplier restores it.
   half8_t qb[RB][G_::KSTEPS];
   float rowmul[RB];  // logit (log2 units) = dot * rowmul * per-row K scale
-  int lim[RB];       // tokens visible to this lane's row n: t < lim
+  int lim[RB];       // tokens visible to this lane's row n: lo <= t < lim
+  int lo[RB];
   {
     const float* kst = a.c.k_scales;
 #pragma unroll
@@ -626,9 +631,13 @@ split_decode_kernel(SplitArgs a) {
       rowmul[rb] = ldexpf(mul, ex);
       lim[rb] = (r < Rw) ? (L - a.Tq + (row0 + r) / a.G + 1) : 0;
       if (lim[rb] > L) lim[rb] = L;
+      lo[rb] = a.window > 0 ? lim[rb] - a.window : 0;
     }
   }
 
+  // soft cap in log2 units (the CAP variant is launched when softcap > 0)
+  const float cap2 = CAP ? a.softcap * 1.4426950408889634f : 0.0f;
+  const float icap2 = CAP ? 1.0f / cap2 : 0.0f;
   WaveState<DT, D, RB> W;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -642,7 +651,8 @@ split_decode_kernel(SplitArgs a) {
   for (int t = t0, k = 0; t < te;) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      if (t < te) process_tile<DT, MODE, D, RB>(buf[i], t, L, n, g, qb, rowmul, lim, W);
+      if (t < te)
+        process_tile<DT, MODE, D, RB, CAP>(buf[i], t, L, n, g, qb, rowmul, lim, lo, cap2, icap2, W);
       load_tile<DT, MODE, D>(a, hkv, t + NB * kWaves, t + NB * kWaves < te,
                              paged ? table_entry(tbl, k + NB) : b, L, n, g, buf[i]);
       t += kWaves;
@@ -750,7 +760,10 @@ hipError_t launch_one(const SplitArgs& a, int B, hipStream_t st) {
   } else {
     const int gx = a.RBN > 1 ? (a.S + 7) / 8 * 8 * a.RBN : a.S;
     dim3 grid(gx, a.c.Hkv, 1);
-    hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB>), grid, dim3(256), 0, st, a);
+    if (a.softcap > 0.0f)
+      hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, false>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
 }

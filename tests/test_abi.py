@@ -96,6 +96,26 @@ def test_invalid_paged_and_append_rejected():
     assert L.kvq_append(None, FAKE, FAKE, 1, 1, FAKE, None, 0, None) == -1
 
 
+def test_invalid_attend_options_rejected():
+    L = kvq.lib()
+    c = _cache()
+
+    def call(opts, k_new=FAKE, v_new=FAKE):
+        o = None if opts is None else ctypes.byref(kvq._Options(*opts))
+        return L.kvq_attend_ex(ctypes.byref(c), k_new, v_new, FAKE, 1, 24, 1, FAKE, 4096, 0.1,
+                               None, None, 0, o, FAKE, FAKE, 1 << 30, None)
+
+    assert call((-1.0, 0)) == -1               # negative soft cap
+    assert call((float("nan"), 0)) == -1       # non-finite soft cap
+    assert call((float("inf"), 0)) == -1
+    assert call((0.0, -5)) == -1               # negative window
+    assert call((30.0, 0), v_new=None) == -1   # one of the new rows only
+    # valid options still meet the shape checks of the decode
+    o = ctypes.byref(kvq._Options(30.0, 128))
+    assert L.kvq_attend_ex(ctypes.byref(c), None, None, FAKE, 1, 25, 1, FAKE, 4096, 0.1, None,
+                           None, 0, o, FAKE, FAKE, 1 << 30, None) == -1
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, 5):
         assert kvq.lib().kvq_status_string(s)

@@ -394,3 +394,91 @@ def test_fused_append_decode_drafts_across_tiles(lens):
         w = ki.random_workload(5000 + sum(lens) + dt, B=len(lens), Hkv=2, G=3, D=128, Tq=8,
                                lens=lens, dtype=dt, mode=md, block_size=16 if paged else None)
         _fused_vs_separate(w, f"fused dt={dt} lens={lens}")
+
+
+# ------------------------------------------- soft cap and sliding window
+# ORT PR "[CUDA] PagedAttention: quantized KV cache ...", "CUDA kernels": the
+# paged decode kernel takes a softcap and a sliding window (kvq_attend_ex).
+
+def _attend_ex_and_check(w, what, cache=None, table=None):
+    gu.log(what)
+    if cache is None:
+        cache = gu.gpu_cache(w)
+        table = gu.gpu_build(w, cache)
+    q = w.q.cuda()
+    lens = torch.from_numpy(w.lens).cuda()
+    sink = None if w.sink is None else torch.from_numpy(w.sink).cuda()
+    msl = max(int(w.lens.max()), 1)
+    out = kvq.attend_ex(cache, q, lens, msl, w.sm_scale, block_table=table, head_sink=sink,
+                        softcap=w.softcap, window=w.window)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.reference(w)
+    gu.check_output(out, ref, what)
+    return out
+
+
+OPTION_CASES = [
+    # dtype, mode, paged, B lens, Tq, G, D, softcap, window, sink
+    (INT8, PER_ROW, False, [300, 5000], 1, 4, 128, 1.5, 0, False),
+    (FP8, PER_TENSOR, True, [50, 1000, 7000], 2, 4, 128, 0.0, 100, True),
+    (INT4, PER_CHANNEL, True, [3000, 64], 8, 3, 256, 2.0, 700, False),
+    (INT8, PER_ROW, True, [33, 2000], 4, 2, 64, 0.0, 1, True),
+    (INT8, PER_ROW, False, [4100], 3, 6, 256, 30.0, 17, False),
+    (INT4, PER_ROW, False, [900, 1], 1, 8, 128, 0.8, 5000, False),
+    (FP8, PER_CHANNEL, True, [12000], 1, 6, 256, 5.0, 4096, True),
+]
+
+
+@pytest.mark.parametrize("case", OPTION_CASES, ids=[f"case{i}" for i in range(len(OPTION_CASES))])
+def test_softcap_and_window(case):
+    dt, md, paged, lens, Tq, G, D, cap, win, sink = case
+    w = ki.random_workload(6000 + sum(lens) + Tq, B=len(lens), Hkv=2, G=G, D=D, Tq=Tq, lens=lens,
+                           dtype=dt, mode=md, block_size=16 if paged else None, sink=sink,
+                           softcap=cap, window=win)
+    _attend_ex_and_check(w, f"options {case}")
+
+
+def test_window_64k_int8_reads_only_the_window():
+    w = ki.make_workload(3, ctx=65536, dtype="int8")
+    w.window = 4096
+    w.softcap = float(np.float32(30.0))
+    _attend_ex_and_check(w, "64K int8, window 4096, softcap 30")
+
+
+def test_window_wider_than_sequence_equals_plain_decode():
+    w = ki.random_workload(6100, B=2, Hkv=2, G=4, D=128, Tq=2, lens=[700, 70], dtype=INT8,
+                           mode=PER_ROW, block_size=16)
+    cache = gu.gpu_cache(w)
+    table = gu.gpu_build(w, cache)
+    plain = gu.gpu_decode(w, cache, table)
+    w.window = 100000
+    wide = _attend_ex_and_check(w, "window wider than the sequence", cache, table)
+    assert torch.equal(plain.view(torch.int16), wide.view(torch.int16))
+
+
+def test_attend_ex_fused_append_with_window():
+    """The fused append under a window: the new rows land (bit-exact codes) and
+    the output matches the oracle."""
+    w = ki.random_workload(6200, B=2, Hkv=2, G=3, D=128, Tq=4, lens=[1000, 37], dtype=INT8,
+                           mode=PER_ROW, block_size=16, window=50, softcap=3.0)
+    dev = "cuda"
+    table = torch.from_numpy(w.block_table).to(dev)
+    cache = gu.gpu_cache(w)
+    kn = torch.zeros(w.B, w.Tq, w.Hkv, w.D, dtype=torch.bfloat16)
+    vn = torch.zeros_like(kn)
+    for b in range(w.B):
+        L = int(w.lens[b])
+        head = L - w.Tq
+        z = torch.zeros(1, dtype=torch.int32, device=dev)
+        kvq.append(cache, w.k[b:b + 1, :head].contiguous().to(dev),
+                   w.v[b:b + 1, :head].contiguous().to(dev), z, table[b:b + 1].contiguous())
+        kn[b] = w.k[b, head:L]
+        vn[b] = w.v[b, head:L]
+    q = w.q.to(dev)
+    lens = torch.from_numpy(w.lens).to(dev)
+    out = kvq.attend_ex(cache, q, lens, int(w.lens.max()), w.sm_scale, block_table=table,
+                        k_new=kn.to(dev), v_new=vn.to(dev), softcap=w.softcap, window=w.window)
+    torch.cuda.synchronize()
+    ref, _, ocache = oracle.reference(w)
+    gu.compare_codes(w, cache, ocache)
+    gu.check_output(out, ref, "fused append, window 50, softcap 3")
