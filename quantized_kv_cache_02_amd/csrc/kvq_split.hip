@@ -334,8 +334,13 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
     for (int e = 0; e < 4; ++e) {
       float zz = (s0[e] + s1[e]) * rowmul[rb];
       if constexpr (MODE == kPerRow) zz *= T.ks4[e];
-      // soft cap in log2 units: cap2 = softcap * log2(e)
-      if constexpr (CAP) zz = cap2 * tanhf(zz * icap2);
+      // soft cap in log2 units: with x = z / softcap, z2 = z log2(e), cap2 =
+      // softcap log2(e): cap2 tanh(x) = cap2 (1 - 2 / (1 + 2^(2 z2 / softcap)))
+      // (icap2 = 2 / softcap); the hardware exp2 and reciprocal, 1 ulp each
+      if constexpr (CAP) {
+        const float ex = __builtin_amdgcn_exp2f(zz * icap2);
+        zz = cap2 - 2.0f * cap2 * __builtin_amdgcn_rcpf(ex + 1.0f);
+      }
       z[e] = (ok && tbase + e < lim[rb] && tbase + e >= lo[rb]) ? zz : -INFINITY;
       up |= z[e] > W.m[rb];
     }
@@ -637,7 +642,7 @@ split_decode_kernel(SplitArgs a) {
 
   // soft cap in log2 units (the CAP variant is launched when softcap > 0)
   const float cap2 = CAP ? a.softcap * 1.4426950408889634f : 0.0f;
-  const float icap2 = CAP ? 1.0f / cap2 : 0.0f;
+  const float icap2 = CAP ? 2.0f / a.softcap : 0.0f;
   WaveState<DT, D, RB> W;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
