@@ -65,6 +65,7 @@ class Workload:
     k_static: Optional[np.ndarray] = None  # fp32 [1] or [Hkv, D]
     v_static: Optional[np.ndarray] = None
     sink: Optional[np.ndarray] = None  # fp32 [Hq]
+    v_mode: int = 0       # the V scale mode when it differs from the K one (0: same)
     softcap: float = 0.0  # > 0: logits capped as softcap * tanh(z / softcap)
     window: int = 0       # > 0: a query at position p sees tokens p - window + 1 .. p
     sm_scale: float = 0.0
@@ -239,7 +240,8 @@ def make_workload(cfg: int, ctx: Optional[int] = None, dtype: Optional[str] = No
 
 def random_workload(seed: int, B: int, Hkv: int, G: int, D: int, Tq: int, lens,
                     dtype: int, mode: int, block_size: Optional[int] = None,
-                    sink: bool = False, softcap: float = 0.0, window: int = 0) -> Workload:
+                    sink: bool = False, softcap: float = 0.0, window: int = 0,
+                    v_mode: Optional[int] = None) -> Workload:
     """Small seeded workload of any geometry for property tests."""
     lens = np.asarray(lens, np.int32)
     lmax = int(lens.max()) if lens.size else 0
@@ -257,16 +259,20 @@ def random_workload(seed: int, B: int, Hkv: int, G: int, D: int, Tq: int, lens,
         table = _paged_table(B, mb, seed + 4)
         nb = B * mb
     qmax = {INT8: 127.0, INT4: 7.0, FP8: 448.0}[dtype]
+    vm = mode if v_mode is None else v_mode
     k_static = v_static = None
     if mode == PER_TENSOR:
         k_static = _static_per_tensor(k, qmax)
-        v_static = _static_per_tensor(v, qmax)
     elif mode == PER_CHANNEL:
         k_static = _static_per_channel(randn_bf16((256, Hkv, D), seed + 6), qmax)
+    if vm == PER_TENSOR:
+        v_static = _static_per_tensor(v, qmax)
+    elif vm == PER_CHANNEL:
         v_static = _static_per_channel(randn_bf16((256, Hkv, D), seed + 16), qmax)
     sk = torch.randn(hq, generator=gen(seed + 5)).numpy().astype(np.float32) if sink else None
     sm = float(np.float32(1.0) / np.float32(math.sqrt(D)))
     return Workload(name=f"random-{seed}", cfg=0, B=B, Hq=hq, Hkv=Hkv, D=D, Tq=Tq, dtype=dtype,
                     mode=mode, q=q, k=k, v=v, lens=lens, block_size=bs, num_blocks=nb,
                     block_table=table, k_static=k_static, v_static=v_static, sink=sk,
-                    sm_scale=sm, softcap=float(np.float32(softcap)), window=int(window))
+                    sm_scale=sm, softcap=float(np.float32(softcap)), window=int(window),
+                    v_mode=0 if vm == mode else vm)

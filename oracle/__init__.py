@@ -56,9 +56,9 @@ def lib():
         L.kvo_quantize_row.restype = None
         L.kvo_dequantize_row.argtypes = [P, I, I, I, F, P, P]
         L.kvo_dequantize_row.restype = None
-        L.kvo_append.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I, I, P, P, I]
+        L.kvo_append.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, I, I, P, P, I]
         L.kvo_append.restype = None
-        L.kvo_dequantize.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I, P, P, I, I, P, P]
+        L.kvo_dequantize.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, I, P, P, I, I, P, P]
         L.kvo_dequantize.restype = None
         L.kvo_attend.argtypes = [P, P, P, I, I, I, I, I, I, P, F, P, P, P]
         L.kvo_attend.restype = None
@@ -136,8 +136,10 @@ class Cache:
     for per-row scales, scales [num_blocks, Hkv, bs] fp32."""
 
     def __init__(self, dtype, mode, Hkv, D, block_size, num_blocks, k_static=None,
-                 v_static=None):
+                 v_static=None, v_mode=None):
+        """mode: the K scale mode; v_mode: the V scale mode (default: the same)."""
         self.dtype, self.mode, self.Hkv, self.D = dtype, mode, Hkv, D
+        self.v_mode = mode if not v_mode else v_mode
         self.block_size, self.num_blocks = block_size, num_blocks
         rb = row_bytes(dtype, D)
         self.k_codes = np.zeros((num_blocks, Hkv, block_size, rb), np.uint8)
@@ -155,7 +157,7 @@ class Cache:
         pos = np.ascontiguousarray(positions, np.int32)
         bt = _c(block_table, np.int32)
         mb = 0 if bt is None else bt.shape[1]
-        lib().kvo_append(self.dtype, self.mode, self.Hkv, self.D, self.block_size,
+        lib().kvo_append(self.dtype, self.mode, self.v_mode, self.Hkv, self.D, self.block_size,
                          _p(self.k_codes), _p(self.v_codes), _p(self.k_scales),
                          _p(self.v_scales), _p(self.k_static), _p(self.v_static),
                          _p(k_bits), _p(v_bits), B, Tn, _p(pos), _p(bt), mb)
@@ -170,7 +172,7 @@ class Cache:
         mb = 0 if bt is None else bt.shape[1]
         K = np.empty((B, self.Hkv, lmax, self.D), np.float32)
         V = np.empty_like(K)
-        lib().kvo_dequantize(self.dtype, self.mode, self.Hkv, self.D, self.block_size,
+        lib().kvo_dequantize(self.dtype, self.mode, self.v_mode, self.Hkv, self.D, self.block_size,
                              _p(self.k_codes), _p(self.v_codes), _p(self.k_scales),
                              _p(self.v_scales), _p(self.k_static), _p(self.v_static), B,
                              _p(lens), _p(bt), mb, lmax, _p(K), _p(V))
@@ -211,7 +213,8 @@ def build_cache(w, lens=None):
     fresh oracle cache by one bulk append per sequence."""
     import torch  # only for the bf16 bit view of the workload tensors
 
-    c = Cache(w.dtype, w.mode, w.Hkv, w.D, w.block_size, w.num_blocks, w.k_static, w.v_static)
+    c = Cache(w.dtype, w.mode, w.Hkv, w.D, w.block_size, w.num_blocks, w.k_static, w.v_static,
+              v_mode=w.v_mode)
     lens = w.lens if lens is None else lens
     kb = w.k.contiguous().view(torch.int16).numpy().view(np.uint16)
     vb = w.v.contiguous().view(torch.int16).numpy().view(np.uint16)

@@ -198,9 +198,10 @@ static size_t row_index(int b, int p, int h, int Hkv, int block_size, const int3
 /*
  * Append Tn new tokens per sequence: k, v are bf16 [B, Tn, Hkv, D]; token j of
  * sequence b is written at position positions[b] + j.  Only those rows (and
- * their scales) are written.
+ * their scales) are written.  K rows use k_mode, V rows v_mode ([P]: separate
+ * k_scale and v_scale inputs, each per-tensor or per-channel).
  */
-void kvo_append(int dtype, int mode, int Hkv, int D, int block_size, uint8_t* k_codes,
+void kvo_append(int dtype, int k_mode, int v_mode, int Hkv, int D, int block_size, uint8_t* k_codes,
                 uint8_t* v_codes, float* k_scales, float* v_scales, const float* k_static,
                 const float* v_static, const uint16_t* k, const uint16_t* v, int B, int Tn,
                 const int32_t* positions, const int32_t* block_table, int max_blocks) {
@@ -211,12 +212,12 @@ void kvo_append(int dtype, int mode, int Hkv, int D, int block_size, uint8_t* k_
         int p = positions[b] + j;
         size_t ri = row_index(b, p, h, Hkv, block_size, block_table, max_blocks);
         size_t xi = (((size_t)b * Tn + j) * Hkv + h) * (size_t)D;
-        const float* ks = mode == KVO_PER_CHANNEL ? k_static + (size_t)h * D : k_static;
-        const float* vs = mode == KVO_PER_CHANNEL ? v_static + (size_t)h * D : v_static;
-        kvo_quantize_row(k + xi, D, dtype, mode, ks, k_codes + ri * rb,
-                         mode == KVO_PER_ROW ? k_scales + ri : NULL);
-        kvo_quantize_row(v + xi, D, dtype, mode, vs, v_codes + ri * rb,
-                         mode == KVO_PER_ROW ? v_scales + ri : NULL);
+        const float* ks = k_mode == KVO_PER_CHANNEL ? k_static + (size_t)h * D : k_static;
+        const float* vs = v_mode == KVO_PER_CHANNEL ? v_static + (size_t)h * D : v_static;
+        kvo_quantize_row(k + xi, D, dtype, k_mode, ks, k_codes + ri * rb,
+                         k_mode == KVO_PER_ROW ? k_scales + ri : NULL);
+        kvo_quantize_row(v + xi, D, dtype, v_mode, vs, v_codes + ri * rb,
+                         v_mode == KVO_PER_ROW ? v_scales + ri : NULL);
       }
 }
 
@@ -224,7 +225,8 @@ void kvo_append(int dtype, int mode, int Hkv, int D, int block_size, uint8_t* k_
  * Materialize the dequantized cache of every sequence as dense fp32
  * [B, Hkv, Lmax, D] (positions >= lens[b] are left as zero).
  */
-void kvo_dequantize(int dtype, int mode, int Hkv, int D, int block_size, const uint8_t* k_codes,
+void kvo_dequantize(int dtype, int k_mode, int v_mode, int Hkv, int D, int block_size,
+                    const uint8_t* k_codes,
                     const uint8_t* v_codes, const float* k_scales, const float* v_scales,
                     const float* k_static, const float* v_static, int B, const int32_t* lens,
                     const int32_t* block_table, int max_blocks, int Lmax, float* k_out,
@@ -238,12 +240,12 @@ void kvo_dequantize(int dtype, int mode, int Hkv, int D, int block_size, const u
       for (int p = 0; p < lens[b]; ++p) {
         size_t ri = row_index(b, p, h, Hkv, block_size, block_table, max_blocks);
         size_t oi = (((size_t)b * Hkv + h) * Lmax + p) * (size_t)D;
-        const float* ks = mode == KVO_PER_CHANNEL ? k_static + (size_t)h * D : k_static;
-        const float* vs = mode == KVO_PER_CHANNEL ? v_static + (size_t)h * D : v_static;
-        kvo_dequantize_row(k_codes + ri * rb, D, dtype, mode, mode == KVO_PER_ROW ? k_scales[ri] : 0.0f,
-                           ks, k_out + oi);
-        kvo_dequantize_row(v_codes + ri * rb, D, dtype, mode, mode == KVO_PER_ROW ? v_scales[ri] : 0.0f,
-                           vs, v_out + oi);
+        const float* ks = k_mode == KVO_PER_CHANNEL ? k_static + (size_t)h * D : k_static;
+        const float* vs = v_mode == KVO_PER_CHANNEL ? v_static + (size_t)h * D : v_static;
+        kvo_dequantize_row(k_codes + ri * rb, D, dtype, k_mode,
+                           k_mode == KVO_PER_ROW ? k_scales[ri] : 0.0f, ks, k_out + oi);
+        kvo_dequantize_row(v_codes + ri * rb, D, dtype, v_mode,
+                           v_mode == KVO_PER_ROW ? v_scales[ri] : 0.0f, vs, v_out + oi);
       }
 }
 

@@ -279,6 +279,41 @@ def test_attend_matches_python_loops_tiny(oracle_lib):
         assert np.max(np.abs(out - ref)) <= 1e-12
 
 
+# ------------------------------------------------- separate K and V scale modes
+# ORT PR "[CUDA] PagedAttention: quantized KV cache ...": k_scale and v_scale are
+# separate inputs; each side may use its own granularity.
+
+@pytest.mark.parametrize("dtype", [INT8, INT4, FP8])
+def test_mixed_modes_compose_the_pure_caches(oracle_lib, dtype):
+    """A cache with K in mode A and V in mode B holds, byte for byte, the K side
+    of an all-A cache and the V side of an all-B cache."""
+    modes = (PER_ROW, PER_TENSOR, PER_CHANNEL)
+    for km in modes:
+        for vm in modes:
+            if km == vm:
+                continue
+            w = ki.random_workload(800 + 10 * km + vm + dtype, B=2, Hkv=2, G=2, D=64, Tq=1,
+                                   lens=[40, 19], dtype=dtype, mode=km, v_mode=vm, block_size=16)
+            mixed = oracle_lib.build_cache(w)
+            wk = ki.random_workload(800 + 10 * km + vm + dtype, B=2, Hkv=2, G=2, D=64, Tq=1,
+                                    lens=[40, 19], dtype=dtype, mode=km, v_mode=km, block_size=16)
+            wv = ki.random_workload(800 + 10 * km + vm + dtype, B=2, Hkv=2, G=2, D=64, Tq=1,
+                                    lens=[40, 19], dtype=dtype, mode=vm, v_mode=vm, block_size=16)
+            ck = oracle_lib.build_cache(wk)
+            cv = oracle_lib.build_cache(wv)
+            np.testing.assert_array_equal(mixed.k_codes, ck.k_codes)
+            np.testing.assert_array_equal(mixed.v_codes, cv.v_codes)
+            if km == PER_ROW:
+                np.testing.assert_array_equal(mixed.k_scales, ck.k_scales)
+            if vm == PER_ROW:
+                np.testing.assert_array_equal(mixed.v_scales, cv.v_scales)
+            K, V = mixed.dequantize(w.lens, w.block_table)
+            K1, _ = ck.dequantize(w.lens, w.block_table)
+            _, V1 = cv.dequantize(w.lens, w.block_table)
+            np.testing.assert_array_equal(K, K1)
+            np.testing.assert_array_equal(V, V1)
+
+
 # ---------------------------------------------- soft cap and sliding window
 # ORT PR "[CUDA] PagedAttention: quantized KV cache ...", "CUDA kernels": the
 # paged decode kernel takes a softcap and a sliding window.
