@@ -75,11 +75,12 @@ typedef enum kvq_status {
   KVQ_EHIP = -3          /* the HIP runtime reported a launch error */
 } kvq_status;
 
-/* One layer's quantized cache.  K and V share dtype and scale mode.
- * k_scales / v_scales point at the per-row arrays (KVQ_PER_ROW, written by
- * kvq_append) or at the static tables (KVQ_PER_TENSOR [1], KVQ_PER_CHANNEL
- * [num_kv_heads, head_dim]), which must be finite and >= 0; a zero static
- * scale stores code 0. */
+/* One layer's quantized cache.  K and V share the dtype; scale_mode is the K
+ * side's scale mode and v_scale_mode the V side's (0: the same as scale_mode;
+ * [P]: k_scale and v_scale are separate inputs).  k_scales / v_scales point at
+ * the per-row arrays (KVQ_PER_ROW, written by kvq_append) or at the static
+ * tables (KVQ_PER_TENSOR [1], KVQ_PER_CHANNEL [num_kv_heads, head_dim]), which
+ * must be finite and >= 0; a zero static scale stores code 0. */
 typedef struct kvq_cache {
   int32_t dtype;        /* kvq_dtype */
   int32_t scale_mode;   /* kvq_scale_mode */
@@ -91,6 +92,7 @@ typedef struct kvq_cache {
   void* v_codes;
   float* k_scales;
   float* v_scales;
+  int32_t v_scale_mode; /* kvq_scale_mode of V, or 0: as scale_mode */
 } kvq_cache;
 
 /*

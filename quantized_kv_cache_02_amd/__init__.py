@@ -46,6 +46,7 @@ class _Cache(ctypes.Structure):
         ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
         ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
         ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("v_scale_mode", ctypes.c_int32),
     ]
 
 
@@ -128,30 +129,34 @@ class KVCache:
            (row_bytes = D, or D/2 for packed int4);
     scales fp32 [num_blocks, Hkv, block_size] per-row, or the static
            per-tensor [1] / per-channel [Hkv, D] tables given at construction.
+    scale_mode is the K side's mode and v_scale_mode the V side's (0: the same).
     A contiguous [B, Hkv, T, D] cache is num_blocks = B, block_size = T.
     """
 
     def __init__(self, dtype: int, scale_mode: int, num_kv_heads: int, head_dim: int,
                  block_size: int, num_blocks: int, k_static=None, v_static=None,
-                 device="cuda"):
+                 device="cuda", v_scale_mode: int = 0):
         self.dtype, self.scale_mode = dtype, scale_mode
+        self.v_scale_mode = v_scale_mode
+        vmode = v_scale_mode or scale_mode
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.block_size, self.num_blocks = block_size, num_blocks
         rb = head_dim // 2 if dtype == INT4 else head_dim
         shape = (num_blocks, num_kv_heads, block_size, rb)
         self.k_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
         self.v_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
-        if scale_mode == PER_ROW:
-            self.k_scales = torch.zeros(shape[:3], dtype=torch.float32, device=device)
-            self.v_scales = torch.zeros(shape[:3], dtype=torch.float32, device=device)
-        else:
-            if k_static is None or v_static is None:
-                raise KvqError("static scale modes need k_static and v_static")
-            self.k_scales = torch.as_tensor(k_static, dtype=torch.float32).reshape(-1).to(device)
-            self.v_scales = torch.as_tensor(v_static, dtype=torch.float32).reshape(-1).to(device)
+        def scales(mode, static, side):
+            if mode == PER_ROW:
+                return torch.zeros(shape[:3], dtype=torch.float32, device=device)
+            if static is None:
+                raise KvqError(f"a static {side} scale mode needs {side}_static")
+            return torch.as_tensor(static, dtype=torch.float32).reshape(-1).to(device)
+
+        self.k_scales = scales(scale_mode, k_static, "k")
+        self.v_scales = scales(vmode, v_static, "v")
         self._struct = _Cache(dtype, scale_mode, num_kv_heads, head_dim, block_size, num_blocks,
                               self.k_codes.data_ptr(), self.v_codes.data_ptr(),
-                              self.k_scales.data_ptr(), self.v_scales.data_ptr())
+                              self.k_scales.data_ptr(), self.v_scales.data_ptr(), v_scale_mode)
 
     @property
     def struct(self):

@@ -37,10 +37,12 @@ def _units():
         ("kvq_append.o", os.path.join(CSRC, "kvq_append.hip"), []),
         ("kvq_combine.o", os.path.join(CSRC, "kvq_combine.hip"), []),
     ]
+    # one unit per (dtype, K scale mode, V scales per row or static)
     for dt in (1, 2, 3):
         for md in (1, 2, 3):
-            units.append((f"kvq_split_{dt}_{md}.o", os.path.join(CSRC, "kvq_split.hip"),
-                          [f"-DKVQ_DTYPE={dt}", f"-DKVQ_MODE={md}"]))
+            for vr in (0, 1):
+                units.append((f"kvq_split_{dt}_{md}_{vr}.o", os.path.join(CSRC, "kvq_split.hip"),
+                              [f"-DKVQ_DTYPE={dt}", f"-DKVQ_MODE={md}", f"-DKVQ_VROW={vr}"]))
     return units
 
 

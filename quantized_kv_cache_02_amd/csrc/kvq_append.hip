@@ -7,7 +7,7 @@
 namespace kvq {
 namespace {
 
-template <int DT, int MODE, int D>
+template <int DT, int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   using R = RowGeo<DT, D>;
   const int lane = threadIdx.x & 63;
@@ -37,43 +37,36 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
   const size_t ri = ((size_t)blk * Hkv + h) * bs + (size_t)(pos % bs);
   float* scales = side ? a.c.v_scales : a.c.k_scales;
-  quantize_store_row<DT, MODE, D>(raw, lane, (side ? a.c.v_codes : a.c.k_codes) + ri * R::ROWB,
-                                  scales + ri,
-                                  MODE == kPerChannel ? scales + (size_t)h * D : scales);
+  const int mode = side ? a.vmode : a.kmode;
+  quantize_store_row_mode<DT, D>(mode, raw, lane, (side ? a.c.v_codes : a.c.k_codes) + ri * R::ROWB,
+                                 scales + ri, mode == kPerChannel ? scales + (size_t)h * D : scales);
 }
 
-template <int DT, int MODE>
-hipError_t launch_dm(int D, const AppendArgs& a, hipStream_t st) {
+template <int DT>
+hipError_t launch_dt(int D, const AppendArgs& a, hipStream_t st) {
   const long nrows = (long)a.B * a.Tn * a.c.Hkv * 2;
   const long nblk = (nrows + 3) / 4;
   if (nblk > 0x7FFFFFFFL) return hipErrorInvalidValue;
   dim3 grid((unsigned)nblk);
   switch (D) {
-    case 64: hipLaunchKernelGGL((append_kernel<DT, MODE, 64>), grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((append_kernel<DT, MODE, 128>), grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL((append_kernel<DT, MODE, 256>), grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((append_kernel<DT, 64>), grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((append_kernel<DT, 128>), grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((append_kernel<DT, 256>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int DT>
-hipError_t launch_dt(int mode, int D, const AppendArgs& a, hipStream_t st) {
-  switch (mode) {
-    case kPerRow: return launch_dm<DT, kPerRow>(D, a, st);
-    case kPerTensor: return launch_dm<DT, kPerTensor>(D, a, st);
-    case kPerChannel: return launch_dm<DT, kPerChannel>(D, a, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 }  // namespace
 
-hipError_t launch_append(int dtype, int mode, int D, const AppendArgs& a, hipStream_t st) {
+hipError_t launch_append(int dtype, int kmode, int vmode, int D, const AppendArgs& a,
+                         hipStream_t st) {
+  auto ok = [](int m) { return m == kPerRow || m == kPerTensor || m == kPerChannel; };
+  if (!ok(kmode) || !ok(vmode) || a.kmode != kmode || a.vmode != vmode) return hipErrorInvalidValue;
   switch (dtype) {
-    case kInt8: return launch_dt<kInt8>(mode, D, a, st);
-    case kInt4: return launch_dt<kInt4>(mode, D, a, st);
-    case kFp8: return launch_dt<kFp8>(mode, D, a, st);
+    case kInt8: return launch_dt<kInt8>(D, a, st);
+    case kInt4: return launch_dt<kInt4>(D, a, st);
+    case kFp8: return launch_dt<kFp8>(D, a, st);
     default: return hipErrorInvalidValue;
   }
 }

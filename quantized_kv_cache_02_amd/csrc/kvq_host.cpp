@@ -30,6 +30,9 @@ int check_cache(const kvq_cache* c) {
   if (c->scale_mode != KVQ_PER_ROW && c->scale_mode != KVQ_PER_TENSOR &&
       c->scale_mode != KVQ_PER_CHANNEL)
     return KVQ_EUNSUPPORTED;
+  if (c->v_scale_mode != 0 && c->v_scale_mode != KVQ_PER_ROW && c->v_scale_mode != KVQ_PER_TENSOR &&
+      c->v_scale_mode != KVQ_PER_CHANNEL)
+    return KVQ_EUNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return KVQ_EUNSUPPORTED;
   if (c->num_kv_heads < 1 || c->block_size < 16 || c->block_size % 16 != 0 || c->num_blocks < 1)
     return KVQ_EINVAL;
@@ -41,6 +44,8 @@ int check_cache(const kvq_cache* c) {
     return KVQ_EINVAL;
   return KVQ_OK;
 }
+
+int v_mode_of(const kvq_cache* c) { return c->v_scale_mode != 0 ? c->v_scale_mode : c->scale_mode; }
 
 CacheArgs cache_args(const kvq_cache* c, const int32_t* table, int32_t max_blocks) {
   CacheArgs a;
@@ -156,10 +161,12 @@ void workspace_ptrs(void* ws, const kvq_cache* c, int32_t batch, const DecodeSha
   *chunks = reinterpret_cast<int32_t*>(base + up(rows * c->head_dim * 4) + 2 * up(rows * 4));
 }
 
-hipError_t dispatch_split(int dt, int md, int D, int RB, const kvq::SplitArgs& a, int B,
+hipError_t dispatch_split(int dt, int md, bool vrow, int D, int RB, const kvq::SplitArgs& a, int B,
                           hipStream_t st) {
-#define KVQ_CASE(DT, MD) \
-  if (dt == DT && md == MD) return kvq::launch_split_##DT##_##MD(D, RB, a, B, st);
+#define KVQ_CASE(DT, MD)                                                                        \
+  if (dt == DT && md == MD)                                                                     \
+    return vrow ? kvq::launch_split_##DT##_##MD##_1(D, RB, a, B, st)                            \
+                : kvq::launch_split_##DT##_##MD##_0(D, RB, a, B, st);
   KVQ_CASE(1, 1)
   KVQ_CASE(1, 2)
   KVQ_CASE(1, 3)
@@ -205,7 +212,9 @@ int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   workspace_ptrs(ws, c, batch, sh, &a.ws_o, &a.ws_m, &a.ws_l, &a.ws_chunks);
-  hipError_t e = dispatch_split(c->dtype, c->scale_mode, c->head_dim, sh.RBK, a, batch,
+  a.vmode = v_mode_of(c);
+  hipError_t e = dispatch_split(c->dtype, c->scale_mode, a.vmode == KVQ_PER_ROW, c->head_dim, sh.RBK, a,
+                                batch,
                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
@@ -229,7 +238,7 @@ int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, cons
   a.ws_o = o;
   a.ws_m = m;
   a.ws_l = l;
-  a.v_static = c->scale_mode == KVQ_PER_ROW ? nullptr : c->v_scales;
+  a.v_static = v_mode_of(c) == KVQ_PER_ROW ? nullptr : c->v_scales;
   a.sink = sink;
   a.out = static_cast<uint16_t*>(out);
   a.seq_lens = seq_lens;
@@ -242,7 +251,7 @@ int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, cons
   a.G = sh.G;
   a.R = sh.R;
   a.S = sh.NSLOT;
-  hipError_t e = kvq::launch_combine(c->scale_mode, c->head_dim, a, batch,
+  hipError_t e = kvq::launch_combine(v_mode_of(c), c->head_dim, a, batch,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
@@ -276,7 +285,9 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t bat
   a.B = batch;
   a.Tn = tokens;
   a.capacity = (int32_t)capacity;
-  hipError_t e = kvq::launch_append(cache->dtype, cache->scale_mode, cache->head_dim, a,
+  a.kmode = cache->scale_mode;
+  a.vmode = v_mode_of(cache);
+  hipError_t e = kvq::launch_append(cache->dtype, cache->scale_mode, v_mode_of(cache), cache->head_dim, a,
                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }

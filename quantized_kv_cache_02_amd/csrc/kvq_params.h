@@ -55,6 +55,7 @@ struct AppendArgs {
   int32_t B;
   int32_t Tn;
   int32_t capacity;  // tokens addressable per sequence
+  int32_t kmode, vmode;  // scale modes of the K and V rows
 };
 
 struct SplitArgs {
@@ -69,6 +70,7 @@ struct SplitArgs {
   int32_t RBN; // workgroups per chunk, one per 16-row block of query rows (1: one
                // workgroup serves every row)
   float sm_scale;
+  int32_t vmode;   // V scale mode (the K mode is the kernel's template mode)
   float softcap;   // > 0: logits z -> softcap * tanh(z / softcap)
   int32_t window;  // > 0: a query at position p sees tokens p - window + 1 .. p
   // fused append (both null when not fused): bf16 [B, Tq, Hkv, D] rows of the
@@ -97,14 +99,17 @@ struct CombineArgs {
   int32_t Hkv, Hq, Tq, G, R, S;
 };
 
-hipError_t launch_append(int dtype, int mode, int D, const AppendArgs& a, hipStream_t st);
+hipError_t launch_append(int dtype, int kmode, int vmode, int D, const AppendArgs& a,
+                         hipStream_t st);
 hipError_t launch_split(int dtype, int mode, int D, int RB, const SplitArgs& a, int B,
                         hipStream_t st);
 hipError_t launch_combine(int mode, int D, const CombineArgs& a, int B, hipStream_t st);
 
-// per-(dtype, mode) translation units of the split kernel
-#define KVQ_DECLARE_SPLIT(DT, MD) \
-  hipError_t launch_split_##DT##_##MD(int D, int RB, const SplitArgs& a, int B, hipStream_t st);
+// translation units of the split kernel per (dtype, K scale mode, V scale per
+// row or static): launch_split_<dtype>_<K mode>_<V per row>
+#define KVQ_DECLARE_SPLIT(DT, MD)                                                                  \
+  hipError_t launch_split_##DT##_##MD##_0(int D, int RB, const SplitArgs& a, int B, hipStream_t st); \
+  hipError_t launch_split_##DT##_##MD##_1(int D, int RB, const SplitArgs& a, int B, hipStream_t st);
 KVQ_DECLARE_SPLIT(1, 1)
 KVQ_DECLARE_SPLIT(1, 2)
 KVQ_DECLARE_SPLIT(1, 3)

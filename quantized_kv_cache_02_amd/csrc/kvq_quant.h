@@ -125,4 +125,18 @@ __device__ __forceinline__ void quantize_store_row(const uint16_t (&raw)[RowGeo<
   }
 }
 
+// The same with the scale mode chosen at run time (uniform over the wavefront).
+template <int DT, int D>
+__device__ __forceinline__ void quantize_store_row_mode(int mode,
+                                                        const uint16_t (&raw)[RowGeo<DT, D>::EPL],
+                                                        int lane, uint8_t* codes, float* scale_out,
+                                                        const float* static_s) {
+  if (mode == kPerRow)
+    quantize_store_row<DT, kPerRow, D>(raw, lane, codes, scale_out, static_s);
+  else if (mode == kPerTensor)
+    quantize_store_row<DT, kPerTensor, D>(raw, lane, codes, scale_out, static_s);
+  else
+    quantize_store_row<DT, kPerChannel, D>(raw, lane, codes, scale_out, static_s);
+}
+
 }  // namespace kvq

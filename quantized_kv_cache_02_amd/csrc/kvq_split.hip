@@ -37,12 +37,20 @@
 #ifndef KVQ_DTYPE
 #error "KVQ_DTYPE must be defined"
 #endif
+#ifndef KVQ_VROW
+#error "KVQ_VROW must be defined (1: V scales per row, 0: static)"
+#endif
 #ifndef KVQ_MODE
 #error "KVQ_MODE must be defined"
 #endif
 
 namespace kvq {
 namespace {
+
+// The translation unit's V scale kind: per-row scales ride with the tiles; a
+// static V scale (per tensor or per channel) is applied by the combine.  The
+// template MODE is the K side's scale mode.
+constexpr bool kVRow = KVQ_VROW != 0;
 
 template <int DT, int D>
 struct Geo {
@@ -257,6 +265,9 @@ __device__ __forceinline__ void load_tile(const SplitArgs& a, int hkv, int t, bo
     load_bytes<16>(make_rsrc(a.c.k_scales + row0, rows * 4), 16 * g, w);
     T.ks4 = float4_t{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
                      __uint_as_float(w[3])};
+  }
+  if constexpr (kVRow) {
+    uint32_t w[4];
     load_bytes<16>(make_rsrc(a.c.v_scales + row0, rows * 4), 16 * g, w);
     T.vs4 = float4_t{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
                      __uint_as_float(w[3])};
@@ -295,7 +306,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
   float vfac = 1.0f;
   bool rescale = false;
   float vsn[4] = {1.f, 1.f, 1.f, 1.f};
-  if constexpr (MODE == kPerRow) {
+  if constexpr (kVRow) {
     bool vup = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vup |= valid[e] && T.vs4[e] > W.vref;
@@ -365,7 +376,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
       const float p = exp2f(z[e] - msafe);
       psum += p;
       float pv = p;
-      if constexpr (MODE == kPerRow) pv = valid[e] ? p * vsn[e] : 0.0f;
+      if constexpr (kVRow) pv = valid[e] ? p * vsn[e] : 0.0f;
       ph[e] = (_Float16)pv;
     }
     W.l[rb] += psum;
@@ -554,8 +565,9 @@ split_decode_kernel(SplitArgs a) {
           ((size_t)rblk[j] * a.c.Hkv + hkv) * a.c.block_size + (size_t)(p % a.c.block_size);
       quantize_store_row<DT, MODE, D>(rk[j], lane, a.c.k_codes + ri * RG::ROWB, a.c.k_scales + ri,
                                       MODE == kPerChannel ? a.c.k_scales + (size_t)hkv * D : a.c.k_scales);
-      quantize_store_row<DT, MODE, D>(rv[j], lane, a.c.v_codes + ri * RG::ROWB, a.c.v_scales + ri,
-                                      MODE == kPerChannel ? a.c.v_scales + (size_t)hkv * D : a.c.v_scales);
+      quantize_store_row_mode<DT, D>(a.vmode, rv[j], lane, a.c.v_codes + ri * RG::ROWB,
+                                     a.c.v_scales + ri,
+                                     a.vmode == kPerChannel ? a.c.v_scales + (size_t)hkv * D : a.c.v_scales);
       wrote = true;
     }
     if (wrote) __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before any load of those rows
@@ -691,7 +703,7 @@ split_decode_kernel(SplitArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) Lt += s_l[w][r] * exp2f(s_m[w][r] - M);
         f = exp2f(s_m[wave][r] - M) / Lt;
-        if constexpr (MODE == kPerRow) f *= W.vref;
+        if constexpr (kVRow) f *= W.vref;
         if constexpr (DT == kInt4) f *= 0.0625f;  // V operand holds 16 * code
       }
       fac[rb][e] = f;
@@ -786,11 +798,11 @@ hipError_t launch_d(int RB, const SplitArgs& a, int B, hipStream_t st) {
 
 }  // namespace
 
-#define KVQ_CAT2(a, b, c) a##b##_##c
-#define KVQ_CAT(a, b, c) KVQ_CAT2(a, b, c)
+#define KVQ_CAT2(a, b, c, d) a##b##_##c##_##d
+#define KVQ_CAT(a, b, c, d) KVQ_CAT2(a, b, c, d)
 
-hipError_t KVQ_CAT(launch_split_, KVQ_DTYPE, KVQ_MODE)(int D, int RB, const SplitArgs& a, int B,
-                                                        hipStream_t st) {
+hipError_t KVQ_CAT(launch_split_, KVQ_DTYPE, KVQ_MODE, KVQ_VROW)(int D, int RB, const SplitArgs& a,
+                                                                  int B, hipStream_t st) {
   switch (D) {
     case 64: return launch_d<KVQ_DTYPE, KVQ_MODE, 64>(RB, a, B, st);
     case 128: return launch_d<KVQ_DTYPE, KVQ_MODE, 128>(RB, a, B, st);

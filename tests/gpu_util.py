@@ -32,7 +32,7 @@ def log(msg: str):
 
 def gpu_cache(w: ki.Workload, device="cuda") -> kvq.KVCache:
     return kvq.KVCache(w.dtype, w.mode, w.Hkv, w.D, w.block_size, w.num_blocks, w.k_static,
-                       w.v_static, device=device)
+                       w.v_static, device=device, v_scale_mode=w.v_mode)
 
 
 def gpu_build(w: ki.Workload, cache: kvq.KVCache, device="cuda"):
@@ -74,7 +74,7 @@ def compare_codes(w: ki.Workload, cache: kvq.KVCache, ocache: oracle.Cache):
     kc = cache.k_codes.cpu().numpy()
     vc = cache.v_codes.cpu().numpy()
     ks = cache.k_scales.cpu().numpy() if w.mode == ki.PER_ROW else None
-    vs = cache.v_scales.cpu().numpy() if w.mode == ki.PER_ROW else None
+    vs = cache.v_scales.cpu().numpy() if (w.v_mode or w.mode) == ki.PER_ROW else None
     for b in range(w.B):
         L = int(w.lens[b])
         if L == 0:
@@ -94,6 +94,7 @@ def compare_codes(w: ki.Workload, cache: kvq.KVCache, ocache: oracle.Cache):
             assert np.array_equal(vc[sel], ocache.v_codes[sel]), f"V codes differ (b={b}, {sel})"
             if ks is not None:
                 assert ks[sel].tobytes() == ocache.k_scales[sel].tobytes(), f"K scales differ b={b}"
+            if vs is not None:
                 assert vs[sel].tobytes() == ocache.v_scales[sel].tobytes(), f"V scales differ b={b}"
 
 

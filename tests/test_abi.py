@@ -56,7 +56,8 @@ def _decode(c, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), -2), (dict(head_dim=512), -2), (dict(dtype=7), -2),
-    (dict(scale_mode=0), -2), (dict(block_size=8), -1), (dict(block_size=24), -1),
+    (dict(scale_mode=0), -2), (dict(v_scale_mode=4), -2), (dict(v_scale_mode=-1), -2),
+    (dict(block_size=8), -1), (dict(block_size=24), -1),
     (dict(num_kv_heads=0), -1), (dict(k_codes=None), -1), (dict(v_scales=0x40004), -1),
 ])
 def test_invalid_cache_rejected(kw, status):

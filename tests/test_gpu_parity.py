@@ -198,6 +198,47 @@ def test_matrix_contiguous(dtype, mode, D):
     gu.run_and_check(w, f"matrix dt={dtype} md={mode} D={D} contiguous")
 
 
+# K and V in different scale modes (ORT PR "[CUDA] PagedAttention: quantized KV
+# cache ...": k_scale and v_scale are separate inputs)
+MIXED = [(dt, km, vm) for dt in (INT8, INT4, FP8) for km in (PER_ROW, PER_TENSOR, PER_CHANNEL)
+         for vm in (PER_ROW, PER_TENSOR, PER_CHANNEL) if km != vm]
+
+
+@pytest.mark.parametrize("dtype,kmode,vmode", MIXED)
+def test_mixed_scale_modes(dtype, kmode, vmode):
+    D = (64, 128, 256)[(kmode + vmode) % 3]
+    paged = (dtype + kmode) % 2 == 0
+    w = ki.random_workload(2500 + 10 * dtype + 3 * kmode + vmode, B=2, Hkv=2, G=3, D=D, Tq=2,
+                           lens=[45, 700], dtype=dtype, mode=kmode, v_mode=vmode,
+                           block_size=16 if paged else None, sink=True)
+    gu.run_and_check(w, f"mixed dt={dtype} K={kmode} V={vmode} D={D} paged={paged}")
+
+
+def test_mixed_modes_fused_append():
+    """The fused append writes K rows in the K mode and V rows in the V mode."""
+    w = ki.random_workload(2600, B=2, Hkv=2, G=3, D=128, Tq=3, lens=[500, 40], dtype=INT4,
+                           mode=PER_CHANNEL, v_mode=PER_ROW, block_size=16)
+    dev = "cuda"
+    table = torch.from_numpy(w.block_table).to(dev)
+    cache = gu.gpu_cache(w)
+    kn = torch.zeros(w.B, w.Tq, w.Hkv, w.D, dtype=torch.bfloat16)
+    vn = torch.zeros_like(kn)
+    for b in range(w.B):
+        L = int(w.lens[b])
+        head = L - w.Tq
+        z = torch.zeros(1, dtype=torch.int32, device=dev)
+        kvq.append(cache, w.k[b:b + 1, :head].contiguous().to(dev),
+                   w.v[b:b + 1, :head].contiguous().to(dev), z, table[b:b + 1].contiguous())
+        kn[b] = w.k[b, head:L]
+        vn[b] = w.v[b, head:L]
+    out = kvq.attend_ex(cache, w.q.to(dev), torch.from_numpy(w.lens).to(dev), int(w.lens.max()),
+                        w.sm_scale, block_table=table, k_new=kn.to(dev), v_new=vn.to(dev))
+    torch.cuda.synchronize()
+    ref, _, ocache = oracle.reference(w)
+    gu.compare_codes(w, cache, ocache)
+    gu.check_output(out, ref, "fused append, K per-channel, V per-row")
+
+
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("Tq", [1, 3, 8])
 def test_gqa_and_query_tokens(G, Tq):
