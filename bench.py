@@ -192,6 +192,36 @@ def time_config(kvq, torch, ki, dtype: str, ctx: int, layers: int, steps: int, w
     return r
 
 
+def time_sdpa_bf16(torch, ctx: int, layers: int, iters: int, dev, expanded: bool):
+    """torch's bf16 scaled_dot_product_attention on the same decode geometry
+    (B1, 24 query heads over 4 KV heads, D 256, one query token) over `layers`
+    rotated unquantized caches: the comparison the kernel page draws its
+    crossover against.  expanded: K/V already repeated to the 24 query heads
+    (6x the bytes, torch's fused backends); else enable_gqa on the 4 KV heads.
+    Returns ms per call (eager launches, HIP events)."""
+    import torch.nn.functional as F
+
+    g = torch.Generator(device="cpu").manual_seed(900 + ctx % 997)
+    hk = 24 if expanded else 4
+    q = torch.randn(1, 24, 1, 256, generator=g).to(torch.bfloat16).to(dev)
+    ks = [torch.randn(1, hk, ctx, 256, generator=g).to(torch.bfloat16).to(dev) for _ in range(layers)]
+    vs = [torch.randn(1, hk, ctx, 256, generator=g).to(torch.bfloat16).to(dev) for _ in range(layers)]
+    for i in range(layers):
+        F.scaled_dot_product_attention(q, ks[i], vs[i], enable_gqa=not expanded)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for it in range(iters):
+        F.scaled_dot_product_attention(q, ks[it % layers], vs[it % layers], enable_gqa=not expanded)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del ks, vs
+    torch.cuda.empty_cache()
+    return ms
+
+
 def cpu_baseline(ki, w, seconds: float):
     """The oracle as it stands on the same workload: one step = dequantize the
     layer cache to fp32, then fp64 attention.  Runs whole steps until `seconds`
@@ -231,6 +261,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5],
                     help="time another of the seeded workloads instead (2, 4, 5: their own "
                          "shapes; the JSON line then reports that workload)")
+    ap.add_argument("--crossover", default="",
+                    help="time torch bf16 SDPA against the int8 step over the context sweep and "
+                         "write JSON lines to this file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 20 times "
                          "(reference dispatch for HBM byte counters)")
@@ -251,6 +284,26 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     kvq.lib()
+
+    if args.crossover:
+        with open(args.crossover, "w") as f:
+            for ctx in ki.SWEEP_CTX:
+                layers = args.layers if ctx <= 65536 else 8
+                sd = time_sdpa_bf16(torch, ctx, layers, 8 * layers, dev, expanded=False)
+                sde = time_sdpa_bf16(torch, ctx, max(2, layers // 4) if ctx > 65536 else layers,
+                                     8 * layers, dev, expanded=True)
+                r = time_config(kvq, torch, ki, "int8", ctx, layers, max(64, args.steps // 4),
+                                args.warmup, dev, True)
+                r.pop("workload")
+                line = {"ctx": ctx, "sdpa_bf16_gqa_us": round(sd * 1e3, 2),
+                        "sdpa_bf16_expanded_us": round(sde * 1e3, 2),
+                        "int8_step_us": round(r["step_ms"] * 1e3, 2),
+                        "int8_split_us": round(r["split_ms"] * 1e3, 2),
+                        "bf16_bytes": 2 * ctx * 4 * 256 * 2, "int8_bytes": r["bytes"]}
+                f.write(json.dumps(line) + "\n")
+                f.flush()
+                print(f"[crossover] {line}", file=sys.stderr, flush=True)
+        return
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
