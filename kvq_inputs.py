@@ -25,9 +25,9 @@ from typing import Optional
 import numpy as np
 import torch
 
-INT8, INT4, FP8 = 1, 2, 3
+INT8, INT4, FP8, BF16 = 1, 2, 3, 4
 PER_ROW, PER_TENSOR, PER_CHANNEL = 1, 2, 3
-DTYPE_NAMES = {"int8": INT8, "int4": INT4, "fp8": FP8}
+DTYPE_NAMES = {"int8": INT8, "int4": INT4, "fp8": FP8, "bf16": BF16}
 MODE_NAMES = {"per_row": PER_ROW, "per_tensor": PER_TENSOR, "per_channel": PER_CHANNEL}
 
 SWEEP_CTX = (1024, 4096, 16384, 65536, 262144)
@@ -81,7 +81,7 @@ class Workload:
 
     @property
     def row_bytes(self) -> int:
-        return self.D // 2 if self.dtype == INT4 else self.D
+        return self.D // 2 if self.dtype == INT4 else 2 * self.D if self.dtype == BF16 else self.D
 
 
 def gen(seed: int) -> torch.Generator:
@@ -133,6 +133,7 @@ def make_workload(cfg: int, ctx: Optional[int] = None, dtype: Optional[str] = No
     cfg 1  tiny decode: B1 Hq4 Hkv1 D64, 256 cached tokens, int8 per-row.
     cfg 2  B1 Hq24 Hkv4 D256, 4096 tokens, 1 % of (head, channel) pairs x8, int8 per-row.
     cfg 3  same geometry, ``ctx`` in SWEEP_CTX, ``dtype`` int8 or int4, per-row.
+    (``dtype="bf16"`` gives any of them as an unquantized cache, without scales.)
     cfg 4  paged fp8 per-tensor: B4 Hq32 Hkv8 D128, lengths ~ U[1, 32768], block 16,
            random block table over a shared pool, a head-sink logit per query head.
     cfg 5  paged int4 per-channel speculative decode: B4 Hq24 Hkv4 D256, 32768 prompt
@@ -164,6 +165,8 @@ def make_workload(cfg: int, ctx: Optional[int] = None, dtype: Optional[str] = No
         raise ValueError(f"unknown workload {cfg}")
     if dtype is not None:
         dt = DTYPE_NAMES[dtype]
+    if dt == BF16:  # the same workload through an unquantized cache: no scales
+        md = 0
     b = B if B is not None else b
     hkv = Hkv if Hkv is not None else hkv
     g = G if G is not None else g
@@ -258,7 +261,9 @@ def random_workload(seed: int, B: int, Hkv: int, G: int, D: int, Tq: int, lens,
         mb = max(1, (lmax + bs - 1) // bs)
         table = _paged_table(B, mb, seed + 4)
         nb = B * mb
-    qmax = {INT8: 127.0, INT4: 7.0, FP8: 448.0}[dtype]
+    if dtype == BF16:  # unquantized: no scales of either side
+        mode, v_mode = 0, 0
+    qmax = {INT8: 127.0, INT4: 7.0, FP8: 448.0, BF16: 0.0}[dtype]
     vm = mode if v_mode is None else v_mode
     k_static = v_static = None
     if mode == PER_TENSOR:

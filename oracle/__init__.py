@@ -19,6 +19,7 @@ _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libkvq_oracle.so")
 
 INT8, INT4, FP8 = 1, 2, 3
+BF16 = 4  # unquantized cache: the codes are the bf16 values, no scales
 PER_ROW, PER_TENSOR, PER_CHANNEL = 1, 2, 3
 QMAX = {INT8: 127.0, INT4: 7.0, FP8: 448.0}
 
@@ -81,7 +82,7 @@ def _c(a, dtype):
 
 
 def row_bytes(dtype: int, D: int) -> int:
-    return D // 2 if dtype == INT4 else D
+    return D // 2 if dtype == INT4 else 2 * D if dtype == BF16 else D
 
 
 # ------------------------------------------------------------------ codecs
@@ -137,7 +138,10 @@ class Cache:
 
     def __init__(self, dtype, mode, Hkv, D, block_size, num_blocks, k_static=None,
                  v_static=None, v_mode=None):
-        """mode: the K scale mode; v_mode: the V scale mode (default: the same)."""
+        """mode: the K scale mode; v_mode: the V scale mode (default: the same).
+        A bf16 cache has no scales (both modes are 0)."""
+        if dtype == BF16:
+            mode, v_mode = 0, 0
         self.dtype, self.mode, self.Hkv, self.D = dtype, mode, Hkv, D
         self.v_mode = mode if not v_mode else v_mode
         self.block_size, self.num_blocks = block_size, num_blocks

@@ -23,6 +23,9 @@
  *     attention on the dequantized cache).
  *   - head sink: the output is rescaled by 1/(1+exp(s_h - lse)) (PagedAttention
  *     PR, "CUDA kernels", ApplyHeadSink).
+ *   - an unquantized bf16 cache, the baseline the kernel page's crossover is
+ *     measured against (kv-quant-attn page, "Performance"): its "codes" are the
+ *     bf16 values themselves (two bytes, little-endian) and it has no scales.
  *
  * Readings taken where the pages are silent (each is listed in the design doc):
  *   integer codes round half to even and clamp symmetrically to [-Qmax, Qmax]
@@ -44,6 +47,7 @@
 #define KVO_INT8 1
 #define KVO_INT4 2
 #define KVO_FP8 3
+#define KVO_BF16 4
 #define KVO_PER_ROW 1
 #define KVO_PER_TENSOR 2
 #define KVO_PER_CHANNEL 3
@@ -113,7 +117,9 @@ static float qmax_of(int dtype) {
   return dtype == KVO_INT8 ? 127.0f : dtype == KVO_INT4 ? 7.0f : 448.0f;
 }
 
-int kvo_row_bytes(int dtype, int D) { return dtype == KVO_INT4 ? D / 2 : D; }
+int kvo_row_bytes(int dtype, int D) {
+  return dtype == KVO_INT4 ? D / 2 : dtype == KVO_BF16 ? 2 * D : D;
+}
 
 /* Code of one element from y = x / s. */
 static int encode_int(float y, float qmax) {
@@ -130,9 +136,18 @@ static int encode_int(float y, float qmax) {
  *   PER_CHANNEL: s_d = static_scale[d] (this KV head's table row).
  * Codes: int8 -> D bytes; fp8 -> D bytes; int4 -> D/2 bytes, element 2i in the
  * low nibble and 2i+1 in the high nibble, two's complement.
+ * bf16 (unquantized): the 2D bytes of the input itself, element d at bytes
+ * 2d (low) and 2d+1 (high); mode, scales and row_scale are not used.
  */
 void kvo_quantize_row(const uint16_t* x, int D, int dtype, int mode, const float* static_scale,
                       uint8_t* codes, float* row_scale) {
+  if (dtype == KVO_BF16) {
+    for (int d = 0; d < D; ++d) {
+      codes[2 * d] = (uint8_t)(x[d] & 0xFF);
+      codes[2 * d + 1] = (uint8_t)(x[d] >> 8);
+    }
+    return;
+  }
   float qmax = qmax_of(dtype);
   float s_row = 0.0f;
   if (mode == KVO_PER_ROW) {
@@ -171,9 +186,15 @@ static double code_value(const uint8_t* codes, int d, int dtype) {
   return (double)(nib >= 8 ? nib - 16 : nib);
 }
 
-/* Dequantize one row: xhat_d = float(c_d) * s_d, one fp32 multiply. */
+/* Dequantize one row: xhat_d = float(c_d) * s_d, one fp32 multiply.  A bf16
+ * row is read back as its values (no scale). */
 void kvo_dequantize_row(const uint8_t* codes, int D, int dtype, int mode, float row_scale,
                         const float* static_scale, float* out) {
+  if (dtype == KVO_BF16) {
+    for (int d = 0; d < D; ++d)
+      out[d] = kvo_bf16_to_float((uint16_t)(codes[2 * d] | (codes[2 * d + 1] << 8)));
+    return;
+  }
   for (int d = 0; d < D; ++d) {
     float s = mode == KVO_PER_ROW ? row_scale : mode == KVO_PER_TENSOR ? static_scale[0] : static_scale[d];
     float c = (float)code_value(codes, d, dtype);

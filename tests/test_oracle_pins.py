@@ -17,7 +17,7 @@ import kvq_inputs as ki
 from tests import bruteforce as bf
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-INT8, INT4, FP8 = 1, 2, 3
+INT8, INT4, FP8, BF16 = 1, 2, 3, 4
 PER_ROW, PER_TENSOR, PER_CHANNEL = 1, 2, 3
 
 
@@ -219,6 +219,77 @@ def test_bulk_append_equals_sequential_and_touches_nothing_else(oracle_lib, dtyp
         assert np.all(bulk.k_scales[written] >= 0)
     else:
         assert np.all(bulk.k_scales == -7.0)  # static modes write no scale
+
+
+# ------------------------------------------------------ unquantized bf16 cache
+# kv-quant-attn page, "Performance": the int8 decode is compared with a bf16
+# cache.  The same layout holds the bf16 values themselves and no scales.
+
+def test_bf16_cache_stores_every_value_and_reads_it_back(oracle_lib):
+    """Every bf16 bit pattern is stored as its own two bytes (little-endian)
+    and read back as torch's bf16 -> fp32 conversion, bit for bit."""
+    bits = np.arange(65536, dtype=np.uint16).reshape(256, 256)
+    codes, scales = oracle_lib.quantize_rows(bits, BF16, 0)
+    assert codes.shape == (256, 512)
+    assert np.array_equal(codes.view("<u2"), bits)
+    assert np.all(scales == 0)
+    back = oracle_lib.dequantize_rows(codes, 256, BF16, 0)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(back.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_bf16_cache_append_writes_only_its_rows(oracle_lib, paged):
+    w = ki.random_workload(760, B=2, Hkv=2, G=2, D=64, Tq=1, lens=[40, 40], dtype=BF16,
+                           mode=PER_ROW, block_size=16 if paged else None)
+    c = oracle_lib.Cache(w.dtype, w.mode, w.Hkv, w.D, w.block_size, w.num_blocks)
+    assert c.mode == 0 and c.v_mode == 0 and c.k_codes.shape[-1] == 2 * w.D
+    c.k_codes[...] = 0xA5
+    c.v_codes[...] = 0x5A
+    c.k_scales[...] = -7.0
+    kb, vb = _bits(w.k), _bits(w.v)
+    bt = w.block_table
+    c.append(kb[:, 3:40], vb[:, 3:40], np.array([3, 3], np.int32), bt)
+    written = np.zeros(c.k_codes.shape[:3], bool)
+    for b in range(2):
+        for p in range(3, 40):
+            blk = b if bt is None else bt[b, p // w.block_size]
+            written[blk, :, p % w.block_size] = True
+            for h in range(2):
+                row = c.k_codes[blk, h, p % w.block_size].view("<u2")
+                assert np.array_equal(row, kb[b, p, h])
+                assert np.array_equal(c.v_codes[blk, h, p % w.block_size].view("<u2"), vb[b, p, h])
+    assert np.all(c.k_codes[~written] == 0xA5) and np.all(c.v_codes[~written] == 0x5A)
+    assert np.all(c.k_scales == -7.0)  # no scales are written
+
+
+@pytest.mark.parametrize("Tq,paged,sink", [(1, False, False), (3, True, True), (8, True, False)])
+def test_bf16_cache_attention_matches_torch_sdpa(oracle_lib, Tq, paged, sink):
+    """Decode over a bf16 cache is exact attention over the bf16 K and V values,
+    with K and V taken from the workload by torch, not from the oracle cache."""
+    w = ki.random_workload(770 + Tq, B=2, Hkv=2, G=3, D=64, Tq=Tq, lens=[Tq + 20, 75],
+                           dtype=BF16, mode=PER_ROW, block_size=16 if paged else None,
+                           sink=sink)
+    out, lse, _ = oracle_lib.reference(w)
+    K = w.k.float().permute(0, 2, 1, 3).contiguous().numpy()  # [B, Hkv, Lmax, D]
+    V = w.v.float().permute(0, 2, 1, 3).contiguous().numpy()
+    ref = _sdpa_ref(w.q.double().numpy(), K, V, w.lens, w.sm_scale, Tq)
+    if sink:
+        # o *= 1 / (1 + exp(s_h - lse)), with lse of the exact logits computed here
+        G = w.Hq // w.Hkv
+        qd = w.q.double()
+        lse_ref = np.zeros((w.B, Tq, w.Hq))
+        for b in range(w.B):
+            L = int(w.lens[b])
+            for j in range(Tq):
+                for h in range(w.Hq):
+                    z = float(w.sm_scale) * (torch.from_numpy(K[b, h // G, :L - Tq + j + 1]).double()
+                                             @ qd[b, j, h])
+                    lse_ref[b, j, h] = torch.logsumexp(z, 0).item()
+        assert np.max(np.abs(lse - lse_ref)) <= 1e-12
+        f = 1.0 / (1.0 + np.exp(w.sink.astype(np.float64)[None, None, :] - lse_ref))
+        ref = ref * f[..., None]
+    assert np.max(np.abs(out - ref)) <= 1e-12
 
 
 def test_sequential_build_of_tiny_workload(oracle_lib):
