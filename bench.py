@@ -47,7 +47,8 @@ def kernel_digest() -> str:
 
 def measured_traffic(bytes_per_launch_alg: float):
     """HBM bytes per split-kernel launch from the committed rocprofv3 counter
-    summary, or None when it is missing or was taken on other kernel sources."""
+    summary, or None when it is missing, was taken on other kernel sources or
+    on another workload (other algorithmic bytes)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -55,20 +56,24 @@ def measured_traffic(bytes_per_launch_alg: float):
         return None
     if t.get("kernel_digest") != kernel_digest():
         return None
+    if t.get("algorithmic_bytes_per_launch") != int(bytes_per_launch_alg):
+        return None
     return t.get("hbm_bytes_per_launch")
 
 
 def algorithmic_bytes(w) -> int:
     """K and V codes plus per-row scales of every cached token the step's queries
-    can see (all of them, or those inside a sliding window)."""
-    row = w.D // 2 if w.dtype == 2 else w.D
-    per_row_scale = 4 if w.mode == 1 else 0
+    can see (all of them, or those inside a sliding window).  An unquantized
+    bf16 cache reads 2 D bytes per row and no scale."""
+    row = w.D // 2 if w.dtype == 2 else 2 * w.D if w.dtype == 4 else w.D
+    # per-row scales, K side and V side (v_mode 0: the same mode as K)
+    per_row_scale = 4 * (w.mode == 1) + 4 * ((w.v_mode or w.mode) == 1)
     tokens = 0
     for L in w.lens:
         L = int(L)
         lo = max(0, L - w.Tq - w.window + 1) if w.window > 0 else 0
         tokens += L - lo
-    return int(2 * tokens * w.Hkv * (row + per_row_scale))
+    return int(tokens * w.Hkv * (2 * row + per_row_scale))
 
 
 def build_layers(kvq, torch, w, layers: int, dev):
@@ -80,7 +85,7 @@ def build_layers(kvq, torch, w, layers: int, dev):
     caches = []
     for _ in range(layers):
         c = kvq.KVCache(w.dtype, w.mode, w.Hkv, w.D, w.block_size, w.num_blocks, w.k_static,
-                        w.v_static, device=dev)
+                        w.v_static, device=dev, v_scale_mode=w.v_mode)
         if table is None:
             kvq.append(c, k, v, torch.zeros(w.B, dtype=torch.int32, device=dev))
         else:
@@ -249,7 +254,7 @@ def main():
     ap.add_argument("--steps", type=int, default=640)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--ctx", type=int, default=65536)
-    ap.add_argument("--dtype", default="int8", choices=["int8", "int4"])
+    ap.add_argument("--dtype", default="int8", choices=["int8", "int4", "bf16"])
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--separate-append", action="store_true",
@@ -262,8 +267,9 @@ def main():
                     help="time another of the seeded workloads instead (2, 4, 5: their own "
                          "shapes; the JSON line then reports that workload)")
     ap.add_argument("--crossover", default="",
-                    help="time torch bf16 SDPA against the int8 step over the context sweep and "
-                         "write JSON lines to this file")
+                    help="time the int8 step against the same step over an unquantized bf16 "
+                         "cache (this library's kernel) and torch bf16 SDPA, over the context "
+                         "sweep, and write JSON lines to this file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 20 times "
                          "(reference dispatch for HBM byte counters)")
@@ -295,11 +301,16 @@ def main():
                 r = time_config(kvq, torch, ki, "int8", ctx, layers, max(64, args.steps // 4),
                                 args.warmup, dev, True)
                 r.pop("workload")
+                rb = time_config(kvq, torch, ki, "bf16", ctx, layers, max(64, args.steps // 4),
+                                 args.warmup, dev, True)
+                rb.pop("workload")
                 line = {"ctx": ctx, "sdpa_bf16_gqa_us": round(sd * 1e3, 2),
                         "sdpa_bf16_expanded_us": round(sde * 1e3, 2),
+                        "bf16_step_us": round(rb["step_ms"] * 1e3, 2),
+                        "bf16_split_us": round(rb["split_ms"] * 1e3, 2),
                         "int8_step_us": round(r["step_ms"] * 1e3, 2),
                         "int8_split_us": round(r["split_ms"] * 1e3, 2),
-                        "bf16_bytes": 2 * ctx * 4 * 256 * 2, "int8_bytes": r["bytes"]}
+                        "bf16_bytes": rb["bytes"], "int8_bytes": r["bytes"]}
                 f.write(json.dumps(line) + "\n")
                 f.flush()
                 print(f"[crossover] {line}", file=sys.stderr, flush=True)
@@ -345,11 +356,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA, f32 accumulate",
+        "dtype": ("bf16 MFMA, f32 accumulate" if args.dtype == "bf16"
+                  else "f16 MFMA, f32 accumulate"),
         "data": "synthetic",
         "config": {
-            "workload": f"decode B1 Hq24 Hkv4 D256, {args.dtype} per-row absmax cache, "
-                        f"{args.ctx}-token context, 1 query token, {args.layers} layer caches rotated",
+            "workload": f"decode B1 Hq24 Hkv4 D256, "
+                        f"{'unquantized bf16' if args.dtype == 'bf16' else args.dtype + ' per-row absmax'} "
+                        f"cache, {args.ctx}-token context, 1 query token, {args.layers} layer caches "
+                        f"rotated",
             "step": ("kvq_append_decode_attend (append fused into the split kernel) + combine"
                      if fused else "kvq_append + split decode + combine"),
             "cache_dtype": args.dtype,

@@ -31,7 +31,8 @@
  * Data layout of a cache (one layer, one side each for K and V):
  *   codes   [num_blocks, num_kv_heads, block_size, row_bytes] bytes, where
  *           row_bytes = head_dim for int8 / fp8 and head_dim / 2 for int4
- *           (two signed 4-bit values per byte, element 2i in the low nibble)
+ *           (two signed 4-bit values per byte, element 2i in the low nibble);
+ *           2 * head_dim for the unquantized bf16 cache (the values themselves)
  *   scales  KVQ_PER_ROW:     fp32 [num_blocks, num_kv_heads, block_size],
  *                            written by kvq_append next to each row
  *           KVQ_PER_TENSOR:  fp32 [1], static, filled by the caller
@@ -52,17 +53,24 @@
 extern "C" {
 #endif
 
-/* Cache element types: [P] T_CACHE (int8, float8e4m3fn); [F] packed int4. */
+/* Cache element types: [P] T_CACHE (int8, float8e4m3fn); [F] packed int4.
+ * KVQ_BF16 is the unquantized cache the quantized ones are measured against
+ * ([K] "Performance": int8 decode against a bf16 cache): rows hold the bf16
+ * values as appended, there are no scales (scale_mode and v_scale_mode must be
+ * KVQ_NO_SCALE; k_scales / v_scales are never read and may be NULL), and the
+ * decode is exact attention over those values. */
 typedef enum kvq_dtype {
   KVQ_INT8 = 1,       /* signed, symmetric grid [-127, 127] */
   KVQ_INT4 = 2,       /* signed, symmetric grid [-7, 7], two per byte */
-  KVQ_FP8_E4M3FN = 3  /* OCP E4M3, no infinities, saturating at +-448 */
+  KVQ_FP8_E4M3FN = 3, /* OCP E4M3, no infinities, saturating at +-448 */
+  KVQ_BF16 = 4        /* unquantized bf16 rows */
 } kvq_dtype;
 
 /* Scale granularity: per row ([K] "Method": every K and V row carries its own
  * absmax scale, computed when written); per tensor / per channel ([P] the
  * k_scale / v_scale inputs with PER_TENSOR | PER_CHANNEL quant types). */
 typedef enum kvq_scale_mode {
+  KVQ_NO_SCALE = 0, /* KVQ_BF16 only */
   KVQ_PER_ROW = 1,
   KVQ_PER_TENSOR = 2,
   KVQ_PER_CHANNEL = 3
@@ -125,7 +133,8 @@ typedef struct kvq_attn_options {
  * Each code is the nearest grid value to x / s (fp32 division), ties to even,
  * clamped to [-Qmax, Qmax] (fp8 saturates at +-448 and keeps the sign of
  * zero); s == 0 gives code 0.  Only the addressed rows and their scales are
- * written ([P] "CUDA kernels": ReshapeAndCache quantizes on write).
+ * written ([P] "CUDA kernels": ReshapeAndCache quantizes on write).  A
+ * KVQ_BF16 cache stores the rows as given.
  * Device-side preconditions (not checked on the host, which never reads
  * device data): rows whose position falls outside the sequence's capacity or
  * whose block_table entry is outside [0, num_blocks) are skipped.
@@ -268,7 +277,8 @@ int kvq_combine(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int3
  * kvq_cache_bytes -- host-only footprint of one layer's cache: codes of K and
  * V plus, for KVQ_PER_ROW, one fp32 scale per row ([K] opening paragraphs
  * and "Cache footprint"; [F] "Motivation and Context": static per-channel
- * scales add nothing per token).  Static tables are not counted.
+ * scales add nothing per token).  Static tables are not counted.  KVQ_BF16
+ * (with KVQ_NO_SCALE) counts 2 * head_dim bytes per row.
  */
 size_t kvq_cache_bytes(int32_t dtype, int32_t scale_mode, int32_t num_kv_heads, int32_t head_dim,
                        int64_t tokens);

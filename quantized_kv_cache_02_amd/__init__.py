@@ -15,15 +15,15 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "INT8", "INT4", "FP8_E4M3FN", "PER_ROW", "PER_TENSOR", "PER_CHANNEL",
+    "INT8", "INT4", "FP8_E4M3FN", "BF16", "NO_SCALE", "PER_ROW", "PER_TENSOR", "PER_CHANNEL",
     "KVCache", "KvqError", "append", "num_splits", "workspace_bytes", "decode_attend",
     "paged_decode_attend", "append_decode_attend", "attend_ex", "split_decode", "combine",
     "cache_bytes",
     "lib", "LIB_PATH",
 ]
 
-INT8, INT4, FP8_E4M3FN = 1, 2, 3
-PER_ROW, PER_TENSOR, PER_CHANNEL = 1, 2, 3
+INT8, INT4, FP8_E4M3FN, BF16 = 1, 2, 3, 4
+NO_SCALE, PER_ROW, PER_TENSOR, PER_CHANNEL = 0, 1, 2, 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
@@ -126,26 +126,31 @@ class KVCache:
     """One layer's quantized cache in device memory owned by torch.
 
     codes  uint8 [num_blocks, Hkv, block_size, row_bytes] for K and for V
-           (row_bytes = D, or D/2 for packed int4);
+           (row_bytes = D, D/2 for packed int4, 2D for the unquantized BF16);
     scales fp32 [num_blocks, Hkv, block_size] per-row, or the static
            per-tensor [1] / per-channel [Hkv, D] tables given at construction.
     scale_mode is the K side's mode and v_scale_mode the V side's (0: the same).
+    A BF16 cache has no scales: its modes are NO_SCALE whatever is passed.
     A contiguous [B, Hkv, T, D] cache is num_blocks = B, block_size = T.
     """
 
     def __init__(self, dtype: int, scale_mode: int, num_kv_heads: int, head_dim: int,
                  block_size: int, num_blocks: int, k_static=None, v_static=None,
                  device="cuda", v_scale_mode: int = 0):
+        if dtype == BF16:
+            scale_mode, v_scale_mode = NO_SCALE, NO_SCALE
         self.dtype, self.scale_mode = dtype, scale_mode
         self.v_scale_mode = v_scale_mode
         vmode = v_scale_mode or scale_mode
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.block_size, self.num_blocks = block_size, num_blocks
-        rb = head_dim // 2 if dtype == INT4 else head_dim
+        rb = head_dim // 2 if dtype == INT4 else 2 * head_dim if dtype == BF16 else head_dim
         shape = (num_blocks, num_kv_heads, block_size, rb)
         self.k_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
         self.v_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
         def scales(mode, static, side):
+            if mode == NO_SCALE:  # never read; a 16-byte placeholder keeps the pointer valid
+                return torch.zeros(4, dtype=torch.float32, device=device)
             if mode == PER_ROW:
                 return torch.zeros(shape[:3], dtype=torch.float32, device=device)
             if static is None:

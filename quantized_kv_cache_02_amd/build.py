@@ -2,8 +2,9 @@
 
     python -m quantized_kv_cache_02_amd.build        # or build() from Python
 
-The split-decode kernel source is compiled once per (cache dtype, scale mode)
-so the 108 kernel variants build in parallel translation units.
+The split-decode kernel source is compiled once per (cache dtype, K scale
+mode, V scales per row or static), plus once for the unquantized bf16 cache,
+so its variants build in parallel translation units.
 """
 from __future__ import annotations
 
@@ -43,6 +44,9 @@ def _units():
             for vr in (0, 1):
                 units.append((f"kvq_split_{dt}_{md}_{vr}.o", os.path.join(CSRC, "kvq_split.hip"),
                               [f"-DKVQ_DTYPE={dt}", f"-DKVQ_MODE={md}", f"-DKVQ_VROW={vr}"]))
+    # the unquantized bf16 cache: no scales
+    units.append(("kvq_split_4_0_0.o", os.path.join(CSRC, "kvq_split.hip"),
+                  ["-DKVQ_DTYPE=4", "-DKVQ_MODE=0", "-DKVQ_VROW=0"]))
     return units
 
 

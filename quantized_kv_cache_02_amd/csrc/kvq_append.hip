@@ -1,6 +1,6 @@
 // kvq_append.hip -- quantize-on-write of newly appended K/V rows: one
 // wavefront per (sequence, token, KV head, K|V) row; the arithmetic of a row
-// is in kvq_quant.h.
+// is in kvq_quant.h.  A bf16 cache stores the rows unchanged.
 
 #include "kvq_quant.h"
 
@@ -62,7 +62,10 @@ hipError_t launch_dt(int D, const AppendArgs& a, hipStream_t st) {
 hipError_t launch_append(int dtype, int kmode, int vmode, int D, const AppendArgs& a,
                          hipStream_t st) {
   auto ok = [](int m) { return m == kPerRow || m == kPerTensor || m == kPerChannel; };
-  if (!ok(kmode) || !ok(vmode) || a.kmode != kmode || a.vmode != vmode) return hipErrorInvalidValue;
+  if (a.kmode != kmode || a.vmode != vmode) return hipErrorInvalidValue;
+  if (dtype == kBf16)  // unquantized rows, no scales
+    return (kmode == kNoScale && vmode == kNoScale) ? launch_dt<kBf16>(D, a, st) : hipErrorInvalidValue;
+  if (!ok(kmode) || !ok(vmode)) return hipErrorInvalidValue;
   switch (dtype) {
     case kInt8: return launch_dt<kInt8>(D, a, st);
     case kInt4: return launch_dt<kInt4>(D, a, st);

@@ -165,6 +165,7 @@ hipError_t launch_mode(int D, const CombineArgs& a, dim3 grid, hipStream_t st) {
 hipError_t launch_combine(int mode, int D, const CombineArgs& a, int B, hipStream_t st) {
   dim3 grid(D / 64, a.R, B * a.Hkv);
   switch (mode) {
+    case kNoScale:  // unquantized cache: nothing to apply
     case kPerRow: return launch_mode<kPerRow>(D, a, grid, st);
     case kPerTensor: return launch_mode<kPerTensor>(D, a, grid, st);
     case kPerChannel: return launch_mode<kPerChannel>(D, a, grid, st);

@@ -117,6 +117,19 @@ __device__ __forceinline__ float4_t mfma32(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// bf16 MFMAs (same lane layouts as the fp16 ones above).  The operands travel
+// as bit containers of the same width and are reinterpreted here.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4_t mfma32_bf16(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma16_bf16(u32x2_t a, u32x2_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
+                                                   __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ half4_t u2_to_h4(uint32_t a, uint32_t b) {
   u32x2_t v = {a, b};
   return __builtin_bit_cast(half4_t, v);

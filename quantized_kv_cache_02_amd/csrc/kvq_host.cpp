@@ -25,23 +25,30 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int check_cache(const kvq_cache* c) {
   if (c == nullptr) return KVQ_EINVAL;
-  if (c->dtype != KVQ_INT8 && c->dtype != KVQ_INT4 && c->dtype != KVQ_FP8_E4M3FN)
+  if (c->dtype != KVQ_INT8 && c->dtype != KVQ_INT4 && c->dtype != KVQ_FP8_E4M3FN &&
+      c->dtype != KVQ_BF16)
     return KVQ_EUNSUPPORTED;
-  if (c->scale_mode != KVQ_PER_ROW && c->scale_mode != KVQ_PER_TENSOR &&
-      c->scale_mode != KVQ_PER_CHANNEL)
-    return KVQ_EUNSUPPORTED;
-  if (c->v_scale_mode != 0 && c->v_scale_mode != KVQ_PER_ROW && c->v_scale_mode != KVQ_PER_TENSOR &&
-      c->v_scale_mode != KVQ_PER_CHANNEL)
-    return KVQ_EUNSUPPORTED;
+  const bool scaled = c->dtype != KVQ_BF16;
+  if (!scaled) {
+    // unquantized: no scale of either side
+    if (c->scale_mode != KVQ_NO_SCALE || c->v_scale_mode != KVQ_NO_SCALE) return KVQ_EUNSUPPORTED;
+  } else {
+    if (c->scale_mode != KVQ_PER_ROW && c->scale_mode != KVQ_PER_TENSOR &&
+        c->scale_mode != KVQ_PER_CHANNEL)
+      return KVQ_EUNSUPPORTED;
+    if (c->v_scale_mode != 0 && c->v_scale_mode != KVQ_PER_ROW &&
+        c->v_scale_mode != KVQ_PER_TENSOR && c->v_scale_mode != KVQ_PER_CHANNEL)
+      return KVQ_EUNSUPPORTED;
+  }
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return KVQ_EUNSUPPORTED;
   if (c->num_kv_heads < 1 || c->block_size < 16 || c->block_size % 16 != 0 || c->num_blocks < 1)
     return KVQ_EINVAL;
-  if (c->k_codes == nullptr || c->v_codes == nullptr || c->k_scales == nullptr ||
-      c->v_scales == nullptr)
-    return KVQ_EINVAL;
-  if (!aligned16(c->k_codes) || !aligned16(c->v_codes) || !aligned16(c->k_scales) ||
-      !aligned16(c->v_scales))
-    return KVQ_EINVAL;
+  if (c->k_codes == nullptr || c->v_codes == nullptr) return KVQ_EINVAL;
+  if (!aligned16(c->k_codes) || !aligned16(c->v_codes)) return KVQ_EINVAL;
+  if (scaled) {
+    if (c->k_scales == nullptr || c->v_scales == nullptr) return KVQ_EINVAL;
+    if (!aligned16(c->k_scales) || !aligned16(c->v_scales)) return KVQ_EINVAL;
+  }
   return KVQ_OK;
 }
 
@@ -49,10 +56,11 @@ int v_mode_of(const kvq_cache* c) { return c->v_scale_mode != 0 ? c->v_scale_mod
 
 CacheArgs cache_args(const kvq_cache* c, const int32_t* table, int32_t max_blocks) {
   CacheArgs a;
+  const bool scaled = c->dtype != KVQ_BF16;  // an unquantized cache's scales are never read
   a.k_codes = static_cast<uint8_t*>(c->k_codes);
   a.v_codes = static_cast<uint8_t*>(c->v_codes);
-  a.k_scales = c->k_scales;
-  a.v_scales = c->v_scales;
+  a.k_scales = scaled ? c->k_scales : nullptr;
+  a.v_scales = scaled ? c->v_scales : nullptr;
   a.Hkv = c->num_kv_heads;
   a.block_size = c->block_size;
   a.num_blocks = c->num_blocks;
@@ -177,6 +185,7 @@ hipError_t dispatch_split(int dt, int md, bool vrow, int D, int RB, const kvq::S
   KVQ_CASE(3, 2)
   KVQ_CASE(3, 3)
 #undef KVQ_CASE
+  if (dt == KVQ_BF16 && md == KVQ_NO_SCALE && !vrow) return kvq::launch_split_4_0_0(D, RB, a, B, st);
   return hipErrorInvalidValue;
 }
 
@@ -238,7 +247,8 @@ int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, cons
   a.ws_o = o;
   a.ws_m = m;
   a.ws_l = l;
-  a.v_static = v_mode_of(c) == KVQ_PER_ROW ? nullptr : c->v_scales;
+  const int vmode = v_mode_of(c);
+  a.v_static = (vmode == KVQ_PER_TENSOR || vmode == KVQ_PER_CHANNEL) ? c->v_scales : nullptr;
   a.sink = sink;
   a.out = static_cast<uint16_t*>(out);
   a.seq_lens = seq_lens;
@@ -251,7 +261,7 @@ int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, cons
   a.G = sh.G;
   a.R = sh.R;
   a.S = sh.NSLOT;
-  hipError_t e = kvq::launch_combine(v_mode_of(c), c->head_dim, a, batch,
+  hipError_t e = kvq::launch_combine(vmode, c->head_dim, a, batch,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
@@ -391,6 +401,9 @@ size_t kvq_cache_bytes(int32_t dtype, int32_t scale_mode, int32_t num_kv_heads, 
     case KVQ_INT8:
     case KVQ_FP8_E4M3FN: row = (size_t)head_dim; break;
     case KVQ_INT4: row = (size_t)(head_dim + 1) / 2; break;
+    case KVQ_BF16:
+      if (scale_mode != KVQ_NO_SCALE) return 0;
+      return 2 * (size_t)num_kv_heads * (2 * (size_t)head_dim) * (size_t)tokens;
     default: return 0;
   }
   if (scale_mode == KVQ_PER_ROW)

@@ -7,8 +7,10 @@
 
 namespace kvq {
 
-enum : int { kInt8 = 1, kInt4 = 2, kFp8 = 3 };
-enum : int { kPerRow = 1, kPerTensor = 2, kPerChannel = 3 };
+// kBf16: an unquantized cache whose rows are the bf16 values themselves (the
+// baseline of the quantized ones); it has no scales (scale mode kNoScale).
+enum : int { kInt8 = 1, kInt4 = 2, kFp8 = 3, kBf16 = 4 };
+enum : int { kNoScale = 0, kPerRow = 1, kPerTensor = 2, kPerChannel = 3 };
 
 // Tokens per decode tile: one MFMA M dimension (16 rows of K) per wavefront step.
 constexpr int kTile = 16;
@@ -120,5 +122,6 @@ KVQ_DECLARE_SPLIT(3, 1)
 KVQ_DECLARE_SPLIT(3, 2)
 KVQ_DECLARE_SPLIT(3, 3)
 #undef KVQ_DECLARE_SPLIT
+hipError_t launch_split_4_0_0(int D, int RB, const SplitArgs& a, int B, hipStream_t st);
 
 }  // namespace kvq

@@ -15,6 +15,7 @@
 //                                           gives saturation, signed zero kept
 //   s == 0 -> c = 0.
 // Per-row mode: s = max|x| / Qmax (fp32 division), written next to the row.
+// An unquantized bf16 cache stores the row's bf16 values as they are.
 #pragma once
 
 #include "kvq_device.h"
@@ -55,7 +56,7 @@ template <int DT, int D>
 struct RowGeo {
   static constexpr int EPL = (DT == kInt4 && D / 64 < 2) ? 2 : D / 64;
   static constexpr int ACTIVE = D / EPL;
-  static constexpr int ROWB = (DT == kInt4) ? D / 2 : D;
+  static constexpr int ROWB = (DT == kInt4) ? D / 2 : (DT == kBf16) ? 2 * D : D;
 };
 
 // Load the lane's bf16 elements of a row (unconditional; idle lanes read element 0).
@@ -74,9 +75,9 @@ __device__ __forceinline__ void load_row(const uint16_t* x, int lane,
 //   static_s     per-tensor: [1]; per-channel: this KV head's [D] table
 // Every lane of the wavefront must call this (the per-row max is a wave reduction).
 template <int DT, int MODE, int D>
-__device__ __forceinline__ void quantize_store_row(const uint16_t (&raw)[RowGeo<DT, D>::EPL], int lane,
-                                                   uint8_t* codes, float* scale_out,
-                                                   const float* static_s) {
+__device__ __forceinline__ void quantize_store_row_q(const uint16_t (&raw)[RowGeo<DT, D>::EPL], int lane,
+                                                     uint8_t* codes, float* scale_out,
+                                                     const float* static_s) {
   using R = RowGeo<DT, D>;
   constexpr int EPL = R::EPL;
   const bool active = lane < R::ACTIVE;
@@ -125,13 +126,30 @@ __device__ __forceinline__ void quantize_store_row(const uint16_t (&raw)[RowGeo<
   }
 }
 
+template <int DT, int MODE, int D>
+__device__ __forceinline__ void quantize_store_row(const uint16_t (&raw)[RowGeo<DT, D>::EPL], int lane,
+                                                   uint8_t* codes, float* scale_out,
+                                                   const float* static_s) {
+  if constexpr (DT == kBf16) {  // unquantized: the row itself, no scale
+    (void)scale_out;
+    (void)static_s;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(codes);
+#pragma unroll
+    for (int e = 0; e < RowGeo<DT, D>::EPL; ++e) dst[lane * RowGeo<DT, D>::EPL + e] = raw[e];
+  } else {
+    quantize_store_row_q<DT, MODE, D>(raw, lane, codes, scale_out, static_s);
+  }
+}
+
 // The same with the scale mode chosen at run time (uniform over the wavefront).
 template <int DT, int D>
 __device__ __forceinline__ void quantize_store_row_mode(int mode,
                                                         const uint16_t (&raw)[RowGeo<DT, D>::EPL],
                                                         int lane, uint8_t* codes, float* scale_out,
                                                         const float* static_s) {
-  if (mode == kPerRow)
+  if constexpr (DT == kBf16)
+    quantize_store_row<DT, kNoScale, D>(raw, lane, codes, scale_out, static_s);
+  else if (mode == kPerRow)
     quantize_store_row<DT, kPerRow, D>(raw, lane, codes, scale_out, static_s);
   else if (mode == kPerTensor)
     quantize_store_row<DT, kPerTensor, D>(raw, lane, codes, scale_out, static_s);

@@ -1,7 +1,7 @@
 // kvq_split.hip -- split-KV decode attention over a quantized (int8 / packed
-// int4 / fp8 E4M3FN) cache for gfx950.  Compiled once per (KVQ_DTYPE,
-// KVQ_MODE) pair; each translation unit instantiates head_dim x row-block
-// variants.
+// int4 / fp8 E4M3FN) cache, or an unquantized bf16 one, for gfx950.  Compiled
+// once per (KVQ_DTYPE, KVQ_MODE, KVQ_VROW); each translation unit instantiates
+// head_dim x row-block variants.
 //
 // Method (kernel page "kv-quant-attn", "Method"; ORT PR "[CUDA] PagedAttention:
 // quantized KV cache ...", "CUDA kernels": split-KV, block-table-aware decode
@@ -30,6 +30,11 @@
 //                 with byte permutes and unpacked to fp16.
 //   The softmax weights are fp16 in [0, 1] (relative rounding 2^-11); the
 //   accumulators are fp32.
+//   An unquantized bf16 cache (the baseline the kernel page compares against,
+//   "Performance") takes the same path with the bf16 MFMAs: K rows and q rows
+//   enter v_mfma_f32_16x16x32_bf16 as they are; for P . V each weight is split
+//   into two bf16 terms hi + lo (hi = bf16(p), lo = bf16(p - hi), together
+//   within 2^-17 of p) and both go through v_mfma_f32_16x16x16_bf16.
 
 #include "kvq_quant.h"
 #include "kvq_sched.h"
@@ -54,7 +59,8 @@ constexpr bool kVRow = KVQ_VROW != 0;
 
 template <int DT, int D>
 struct Geo {
-  static constexpr int ROWB = (DT == kInt4) ? D / 2 : D;  // bytes per cached row
+  // bytes per cached row
+  static constexpr int ROWB = (DT == kInt4) ? D / 2 : (DT == kBf16) ? 2 * D : D;
   // K tile, lane (token i = l%16, group g = l/16): the lane's quarter of the row
   // is read as chunks of KCH bytes at row offsets KCH*(4c+g), so the 4 lanes of
   // a row read one contiguous 4*KCH-byte span per load instruction.
@@ -63,9 +69,12 @@ struct Geo {
   static constexpr int KNCH = KLB / KCH;
   static constexpr int KDW = KLB / 4;      // dwords of K codes per lane
   static constexpr int KSTEPS = D / 32;    // 16x16x32 MFMAs per row block
-  // V tile, lane (column j = l%16, group g = l/16): rows 4g..4g+3, bytes
-  // [VLB*j, VLB*(j+1)) of each row; a load instruction covers 4 whole rows.
+  // V tile, lane (column j = l%16, group g = l/16): rows 4g..4g+3, VLB bytes
+  // of each row, read as VNCH chunks of VCH bytes at row offsets VCH*(j+16c);
+  // a load instruction covers 4 whole rows (or 4 whole 256-byte spans).
   static constexpr int VLB = ROWB / 16;
+  static constexpr int VCH = VLB < 16 ? VLB : 16;
+  static constexpr int VNCH = VLB / VCH;
   static constexpr int VDW = VLB >= 4 ? VLB / 4 : 1;
   static constexpr int NCOL = D / 16;      // 16x16x16 MFMAs per row block
 };
@@ -81,6 +90,10 @@ __device__ __forceinline__ int k_channel(int ks, int g, int e) {
     const int byteoff = G_::KCH * (4 * (w / DPC) + g) + 4 * (w % DPC);
     const int nib = e < 4 ? 2 * e : 2 * (e - 4) + 1;
     return 2 * byteoff + nib;
+  } else if constexpr (DT == kBf16) {  // two channels per dword
+    const int w = 4 * ks + (e >> 1);
+    const int byteoff = G_::KCH * (4 * (w / DPC) + g) + 4 * (w % DPC);
+    return byteoff / 2 + (e & 1);
   } else {
     const int w = 2 * ks + (e >> 2);
     return G_::KCH * (4 * (w / DPC) + g) + 4 * (w % DPC) + (e & 3);
@@ -96,6 +109,9 @@ __device__ __forceinline__ int v_channel(int c, int j) {
     const int w = c / (2 * nb), r = c % (2 * nb);
     const int k = r % nb, odd = r / nb;
     return 2 * G_::VLB * j + 2 * (4 * w + k) + odd;
+  } else if constexpr (DT == kBf16) {
+    constexpr int CPC = G_::VCH / 2;  // channels per chunk
+    return CPC * (j + 16 * (c / CPC)) + c % CPC;
   } else {
     return G_::VLB * j + c;
   }
@@ -113,6 +129,25 @@ __device__ __forceinline__ constexpr int col_of(int o) {
     return 2 * nb * w + odd * nb + k;
   } else {
     return o;
+  }
+}
+
+// The merge writes each lane's accumulator columns in groups of 4 consecutive
+// channels: group k of lane column n holds columns col_of(4k) .. col_of(4k+3),
+// which are channels NCOL*n + 4k .. +3 (bf16: v_channel(4k, n) .. +3).
+// group_owner is the inverse: the lane column and group of channel d (a
+// multiple of 4).
+template <int DT, int D>
+__device__ __forceinline__ void group_owner(int d, int& n, int& k) {
+  using G_ = Geo<DT, D>;
+  if constexpr (DT == kBf16) {
+    constexpr int CPC = G_::VCH / 2;
+    const int q = d / CPC;
+    n = q % 16;
+    k = (q / 16) * (CPC / 4) + (d % CPC) / 4;
+  } else {
+    n = d / G_::NCOL;
+    k = (d % G_::NCOL) / 4;
   }
 }
 
@@ -152,7 +187,9 @@ __device__ __forceinline__ void load_bytes(__amdgpu_buffer_rsrc_t r, int off, ui
 template <int DT, int D>
 __device__ __forceinline__ half8_t k_operand(const uint32_t* kw, int ks) {
   uint32_t h[4];
-  if constexpr (DT == kInt4) {
+  if constexpr (DT == kBf16) {  // the bf16 values themselves (a bit container here)
+    return u4_to_h8(kw[4 * ks], kw[4 * ks + 1], kw[4 * ks + 2], kw[4 * ks + 3]);
+  } else if constexpr (DT == kInt4) {
     int4x8_to_h(kw[ks], h);
   } else if constexpr (DT == kInt8) {
     int8x4_to_h(kw[2 * ks], h[0], h[1]);
@@ -257,9 +294,12 @@ __device__ __forceinline__ void load_tile(const SplitArgs& a, int hkv, int t, bo
 #pragma unroll
   for (int c = 0; c < G_::KNCH; ++c)
     load_bytes<G_::KCH>(kr, koff + c * 4 * G_::KCH, T.kw + c * (G_::KCH / 4));
-  const int voff = 4 * g * ROWB + G_::VLB * n;
+  const int voff = 4 * g * ROWB + G_::VCH * n;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) load_bytes<G_::VLB>(vr, voff + e * ROWB, T.vw[e]);
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int c = 0; c < G_::VNCH; ++c)
+      load_bytes<G_::VCH>(vr, voff + e * ROWB + c * 16 * G_::VCH, T.vw[e] + c * (G_::VCH / 4));
   if constexpr (MODE == kPerRow) {
     uint32_t w[4];
     load_bytes<16>(make_rsrc(a.c.k_scales + row0, rows * 4), 16 * g, w);
@@ -274,6 +314,11 @@ __device__ __forceinline__ void load_tile(const SplitArgs& a, int hkv, int t, bo
   }
 }
 
+// Query rows staged in LDS as bf16, one row every kQStride elements: the 16
+// bytes of padding put the 16 rows of a k-step read in different banks.
+template <int D>
+constexpr int kQStride = D + 8;
+
 // Per-wavefront online-softmax state over its tiles.
 template <int DT, int D, int RB>
 struct WaveState {
@@ -286,6 +331,7 @@ struct WaveState {
 template <int DT, int MODE, int D, int RB, bool CAP>
 __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L, int n, int g,
                                              const half8_t (&qb)[RB][Geo<DT, D>::KSTEPS],
+                                             const uint16_t* qrow,
                                              const float (&rowmul)[RB], const int (&lim)[RB],
                                              const int (&lo)[RB], float cap2, float icap2,
                                              WaveState<DT, D, RB>& W) {
@@ -329,6 +375,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
   }
 
   half4_t pa[RB];
+  u32x2_t phi[RB], plo[RB];  // bf16 cache: p = hi + lo, each a bf16 A operand
   float alpha[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -336,8 +383,21 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
     float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < G_::KSTEPS; ks += 2) {
-      s0 = mfma32(k_operand<DT, D>(T.kw, ks), qb[rb][ks], s0);
-      if (ks + 1 < G_::KSTEPS) s1 = mfma32(k_operand<DT, D>(T.kw, ks + 1), qb[rb][ks + 1], s1);
+      if constexpr (DT == kBf16) {
+        // q from LDS (the bf16 tiles leave no registers for it): row rb*16+n,
+        // channels 8(4k+g) .. +7 for k-step k.  The offset is made opaque so the
+        // compiler cannot hoist these reads out of the tile loop into registers.
+        int qo = rb * 16 * kQStride<D> + k_channel<DT, D>(0, g, 0);
+        asm volatile("" : "+v"(qo));
+        auto qop = [&](int k) {
+          return __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(qrow + qo + 32 * k));
+        };
+        s0 = mfma32_bf16(k_operand<DT, D>(T.kw, ks), qop(ks), s0);
+        if (ks + 1 < G_::KSTEPS) s1 = mfma32_bf16(k_operand<DT, D>(T.kw, ks + 1), qop(ks + 1), s1);
+      } else {
+        s0 = mfma32(k_operand<DT, D>(T.kw, ks), qb[rb][ks], s0);
+        if (ks + 1 < G_::KSTEPS) s1 = mfma32(k_operand<DT, D>(T.kw, ks + 1), qb[rb][ks + 1], s1);
+      }
     }
     float z[4];
     bool up = false;
@@ -370,6 +430,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
     }
     const float msafe = (W.m[rb] == -INFINITY) ? 0.0f : W.m[rb];
     half4_t ph;
+    float pf[4];
     float psum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -378,9 +439,20 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
       float pv = p;
       if constexpr (kVRow) pv = valid[e] ? p * vsn[e] : 0.0f;
       ph[e] = (_Float16)pv;
+      pf[e] = pv;
     }
     W.l[rb] += psum;
     pa[rb] = ph;
+    if constexpr (DT == kBf16) {
+      uint16_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = f32_to_bf16(pf[e]);
+        l[e] = f32_to_bf16(pf[e] - bf16_to_f32(h[e]));  // exact difference
+      }
+      phi[rb] = u32x2_t{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+      plo[rb] = u32x2_t{l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16)};
+    }
   }
   // Rescale the accumulators when some row's max grew or the V reference moved
   // (rare after the first tiles).  Accumulator rows 4g+e belong to the P rows
@@ -420,6 +492,17 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
           W.acc[rb][2 * nb * w + k] = mfma16(pa[rb], vb[k], W.acc[rb][2 * nb * w + k]);
           W.acc[rb][2 * nb * w + nb + k] = mfma16(pa[rb], vb[4 + k], W.acc[rb][2 * nb * w + nb + k]);
         }
+    } else if constexpr (DT == kBf16) {
+      // dword w of the lane's span holds channel columns 2w (low half) and 2w+1
+      const u32x2_t b0 = {perm(vw[1][w], vw[0][w], 0x05040100u), perm(vw[3][w], vw[2][w], 0x05040100u)};
+      const u32x2_t b1 = {perm(vw[1][w], vw[0][w], 0x07060302u), perm(vw[3][w], vw[2][w], 0x07060302u)};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        W.acc[rb][2 * w] = mfma16_bf16(phi[rb], b0, W.acc[rb][2 * w]);
+        W.acc[rb][2 * w] = mfma16_bf16(plo[rb], b0, W.acc[rb][2 * w]);
+        W.acc[rb][2 * w + 1] = mfma16_bf16(phi[rb], b1, W.acc[rb][2 * w + 1]);
+        W.acc[rb][2 * w + 1] = mfma16_bf16(plo[rb], b1, W.acc[rb][2 * w + 1]);
+      }
     } else if constexpr (DT == kInt8) {
       v_transpose4<0>(vw[0][w] ^ 0x80808080u, vw[1][w] ^ 0x80808080u, vw[2][w] ^ 0x80808080u,
                       vw[3][w] ^ 0x80808080u, vb);
@@ -594,7 +677,7 @@ split_decode_kernel(SplitArgs a) {
     const int u = tid + 256 * i;
     if (u < RP * QU) {
       const u32x4_t v = (u / QU < Rw) ? qreg[i] : u32x4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t*>(qs + (u / QU) * D + (u % QU) * 8) = v;
+      *reinterpret_cast<u32x4_t*>(qs + (u / QU) * kQStride<D> + (u % QU) * 8) = v;
     }
   }
   __syncthreads();
@@ -610,13 +693,22 @@ split_decode_kernel(SplitArgs a) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int r = rb * 16 + n;
+      lim[rb] = (r < Rw) ? (L - a.Tq + (row0 + r) / a.G + 1) : 0;
+      if (lim[rb] > L) lim[rb] = L;
+      lo[rb] = a.window > 0 ? lim[rb] - a.window : 0;
+      if constexpr (DT == kBf16) {
+        // the q rows stay in LDS as they are (bf16 products are exact in the
+        // fp32 accumulation); the tile loop reads them there
+        rowmul[rb] = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
+        continue;
+      }
       float qv[G_::KSTEPS][8];
       float amax = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < G_::KSTEPS; ++ks) {
         // the 8 channels of a k-step are 8 consecutive channels (permuted for int4)
         const int base = k_channel<DT, D>(ks, g, 0);
-        u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qs + r * D + base);
+        u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base);
         float x8[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -646,9 +738,6 @@ split_decode_kernel(SplitArgs a) {
       if constexpr (MODE == kPerTensor) mul *= kst[0];
       if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
       rowmul[rb] = ldexpf(mul, ex);
-      lim[rb] = (r < Rw) ? (L - a.Tq + (row0 + r) / a.G + 1) : 0;
-      if (lim[rb] > L) lim[rb] = L;
-      lo[rb] = a.window > 0 ? lim[rb] - a.window : 0;
     }
   }
 
@@ -669,7 +758,8 @@ split_decode_kernel(SplitArgs a) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (t < te)
-        process_tile<DT, MODE, D, RB, CAP>(buf[i], t, L, n, g, qb, rowmul, lim, lo, cap2, icap2, W);
+        process_tile<DT, MODE, D, RB, CAP>(buf[i], t, L, n, g, qb, qs + n * kQStride<D>, rowmul, lim, lo,
+                                           cap2, icap2, W);
       load_tile<DT, MODE, D>(a, hkv, t + NB * kWaves, t + NB * kWaves < te,
                              paged ? table_entry(tbl, k + NB) : b, L, n, g, buf[i]);
       t += kWaves;
@@ -710,9 +800,10 @@ split_decode_kernel(SplitArgs a) {
     }
 
   // each wavefront writes its weighted rows; the sum runs in wave order.
-  // Lane column n owns the NCOL consecutive channels [NCOL*n, NCOL*(n+1)); they
-  // go to LDS as 16-byte chunks whose order is rotated by n / (64 / NCOL) so the
-  // 16 lanes of a pass hit distinct banks.
+  // Lane column n owns NCOL channels, NCOL / 4 groups of 4 consecutive ones
+  // (see group_owner); they go to the lane's NCOL-float LDS slot as 16-byte
+  // chunks whose order is rotated by n / (64 / NCOL) so the 16 lanes of a pass
+  // hit distinct banks.
   constexpr int NCH = G_::NCOL / 4;                 // 16-byte chunks per lane and row
   constexpr int ROT = G_::NCOL >= 16 ? 4 : (G_::NCOL == 8 ? 8 : 16);
   const int nbuf = K_::MERGE_BUFS;
@@ -746,7 +837,8 @@ split_decode_kernel(SplitArgs a) {
 
   for (int idx = tid * 4; idx < Rw * D; idx += 256 * 4) {
     const int r = idx / D, d = idx % D;
-    const int jn = d / G_::NCOL, k = (d % G_::NCOL) / 4;
+    int jn, k;
+    group_owner<DT, D>(d, jn, k);
     const int off = r * D + G_::NCOL * jn + 4 * ((k + jn / ROT) % NCH);
     float4_t v = *reinterpret_cast<const float4_t*>(smem + off);
 #pragma unroll

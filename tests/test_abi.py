@@ -65,6 +65,25 @@ def test_invalid_cache_rejected(kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
+    (dict(scale_mode=1), -2), (dict(v_scale_mode=1), -2), (dict(scale_mode=3), -2),
+    (dict(k_codes=None), -1), (dict(head_dim=96), -2),
+])
+def test_invalid_bf16_cache_rejected(kw, status):
+    # the unquantized cache has no scales: its modes must be KVQ_NO_SCALE
+    c = dict(dtype=kvq.BF16, scale_mode=kvq.NO_SCALE, k_scales=None, v_scales=None)
+    c.update(kw)
+    assert _decode(_cache(**c)) == status
+
+
+def test_bf16_cache_needs_no_scale_pointers():
+    # scale pointers are not validated for bf16: the call gets as far as the
+    # shape checks (here a workspace that is too small)
+    c = _cache(dtype=kvq.BF16, scale_mode=kvq.NO_SCALE, k_scales=None, v_scales=None)
+    assert _decode(c, ws_bytes=16) == -1
+    assert kvq.lib().kvq_workspace_bytes(ctypes.byref(c), 1, 24, 1, 4096) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
     (dict(hq=25), -1),            # Hq % Hkv != 0
     (dict(hq=36), -2),            # group of 9 query heads per KV head
     (dict(tq=9), -2),             # more than 8 query tokens
@@ -144,6 +163,11 @@ def test_cache_bytes_matches_pages_and_oracle(oracle_lib):
     toks = 1024 * 256
     assert 16 * kvq.cache_bytes(kvq.INT8, kvq.PER_CHANNEL, 4, 256, toks) == 8192 * 2 ** 20
     assert 16 * kvq.cache_bytes(kvq.INT4, kvq.PER_CHANNEL, 4, 256, toks) == 4096 * 2 ** 20
+    # bf16: the page's unquantized 64 KiB per token for 16 layers x 4 KV heads x D 256
+    assert 16 * kvq.cache_bytes(kvq.BF16, kvq.NO_SCALE, 4, 256, 1) == 64 * 1024
+    assert kvq.cache_bytes(kvq.BF16, kvq.PER_ROW, 4, 256, 1) == 0
+    assert kvq.cache_bytes(kvq.BF16, kvq.NO_SCALE, 8, 128, 1000) == \
+        oracle_lib.cache_bytes_per_token(16, False, 1, 8, 128) * 1000
     for dt, bits in ((kvq.INT8, 8), (kvq.INT4, 4), (kvq.FP8_E4M3FN, 8)):
         for md in (kvq.PER_ROW, kvq.PER_TENSOR, kvq.PER_CHANNEL):
             want = oracle_lib.cache_bytes_per_token(bits, md == kvq.PER_ROW, 1, 8, 128) * 1000

@@ -523,3 +523,63 @@ def test_attend_ex_fused_append_with_window():
     ref, _, ocache = oracle.reference(w)
     gu.compare_codes(w, cache, ocache)
     gu.check_output(out, ref, "fused append, window 50, softcap 3")
+
+
+# ------------------------------------------------ unquantized bf16 cache
+# kv-quant-attn page, "Performance": the quantized decode is measured against a
+# bf16 cache.  The same kernel runs it on the bf16 MFMAs; rows are stored as
+# given, so the codes compare bit-exactly and the output meets the same bound.
+BF16 = ki.BF16
+
+
+def test_bf16_append_every_value_bit_exact():
+    x = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).view(256, 256)
+    cache, oc, N = _append_rows(BF16, 0, x)
+    assert cache.k_codes.shape[-1] == 512
+    assert np.array_equal(cache.k_codes[0, 0, :N].cpu().numpy(), oc.k_codes[0, 0, :N])
+    assert np.array_equal(cache.v_codes[0, 0, :N].cpu().numpy(), oc.v_codes[0, 0, :N])
+    # the stored row is the input's own bits
+    assert np.array_equal(cache.k_codes[0, 0, :N].cpu().numpy().view("<u2"),
+                          x.view(torch.int16).numpy().view(np.uint16))
+
+
+BF16_CASES = [
+    # paged, lens, Tq, G, D, sink
+    (True, [1, 37, 300], 2, 3, 64, True),
+    (False, [17, 129], 1, 4, 128, False),
+    (False, [4100], 1, 6, 256, False),
+    (True, [3000, 64], 8, 3, 256, True),     # 24 query rows: one workgroup per 16-row block
+    (True, [0, 5, 2000], 4, 8, 128, False),  # 32 rows, two row blocks in one workgroup
+    (False, [700], 8, 8, 64, True),          # 64 rows, four row blocks
+    (True, [15, 16, 17, 4097], 1, 1, 256, False),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=[f"case{i}" for i in range(len(BF16_CASES))])
+def test_bf16_cache(case):
+    paged, lens, Tq, G, D, sink = case
+    w = ki.random_workload(7000 + sum(lens) + Tq + D, B=len(lens), Hkv=2, G=G, D=D, Tq=Tq,
+                           lens=lens, dtype=BF16, mode=0, block_size=16 if paged else None,
+                           sink=sink)
+    gu.run_and_check(w, f"bf16 {case}")
+
+
+def test_bf16_cache_64k_workload3():
+    gu.run_and_check(ki.make_workload(3, ctx=65536, dtype="bf16"), "bf16 64K B1 Hq24 Hkv4 D256")
+
+
+def test_bf16_cache_paged_workload4_geometry():
+    gu.run_and_check(ki.make_workload(4, max_len=3000, dtype="bf16"), "bf16 paged B4 Hq32 Hkv8 D128")
+
+
+def test_bf16_fused_append_decode():
+    _fused_vs_separate(ki.make_workload(3, ctx=4096, dtype="bf16"), "fused bf16 4K")
+    w = ki.random_workload(7100, B=3, Hkv=2, G=3, D=256, Tq=8, lens=[9, 1000, 31], dtype=BF16,
+                           mode=0, block_size=16)
+    _fused_vs_separate(w, "fused bf16 paged drafts")
+
+
+def test_bf16_softcap_and_window():
+    w = ki.random_workload(7200, B=2, Hkv=2, G=6, D=256, Tq=3, lens=[5000, 300], dtype=BF16,
+                           mode=0, block_size=16, sink=True, softcap=20.0, window=1000)
+    _attend_ex_and_check(w, "bf16 softcap 20 window 1000")
