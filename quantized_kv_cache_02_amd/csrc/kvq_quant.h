@@ -59,14 +59,24 @@ struct RowGeo {
   static constexpr int ROWB = (DT == kInt4) ? D / 2 : (DT == kBf16) ? 2 * D : D;
 };
 
-// Load the lane's bf16 elements of a row (unconditional; idle lanes read element 0).
+// Load the lane's bf16 elements of a row (unconditional; idle lanes read
+// element 0) as one 4- or 8-byte load.
 template <int DT, int D>
 __device__ __forceinline__ void load_row(const uint16_t* x, int lane,
                                          uint16_t (&raw)[RowGeo<DT, D>::EPL]) {
   using R = RowGeo<DT, D>;
-  const bool active = lane < R::ACTIVE;
-#pragma unroll
-  for (int e = 0; e < R::EPL; ++e) raw[e] = x[active ? lane * R::EPL + e : 0];
+  static_assert(R::EPL == 1 || R::EPL == 2 || R::EPL == 4, "row elements per lane");
+  const int i = lane < R::ACTIVE ? lane * R::EPL : 0;
+  if constexpr (R::EPL == 4) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(x + i);
+    raw[0] = (uint16_t)v[0]; raw[1] = (uint16_t)(v[0] >> 16);
+    raw[2] = (uint16_t)v[1]; raw[3] = (uint16_t)(v[1] >> 16);
+  } else if constexpr (R::EPL == 2) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(x + i);
+    raw[0] = (uint16_t)v; raw[1] = (uint16_t)(v >> 16);
+  } else {
+    raw[0] = x[i];
+  }
 }
 
 // Quantize the row held in `raw` and store its codes (and, per-row, its scale).

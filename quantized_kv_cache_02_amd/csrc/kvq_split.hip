@@ -328,10 +328,10 @@ struct WaveState {
   float vref;                          // per-row V: weights carry 1/vref, a power of two
 };
 
-template <int DT, int MODE, int D, int RB, bool CAP>
+template <int DT, int MODE, int D, int RB, bool CAP, bool QLDS>
 __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L, int n, int g,
                                              const half8_t (&qb)[RB][Geo<DT, D>::KSTEPS],
-                                             const uint16_t* qrow,
+                                             const half8_t* qlds,
                                              const float (&rowmul)[RB], const int (&lim)[RB],
                                              const int (&lo)[RB], float cap2, float icap2,
                                              WaveState<DT, D, RB>& W) {
@@ -381,22 +381,20 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
   for (int rb = 0; rb < RB; ++rb) {
     // S^T: two independent accumulation chains over the k-steps
     float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // the q operand of k-step k: registers, or this wavefront's LDS copy (lane-
+    // linear, so conflict-free).  The LDS offset is made opaque so the compiler
+    // cannot hoist those reads out of the tile loop back into registers.
+    int qo = rb * G_::KSTEPS * 64;
+    if constexpr (QLDS) asm volatile("" : "+v"(qo));
+    auto qop = [&](int k) { return QLDS ? qlds[qo + 64 * k] : qb[rb][k]; };
 #pragma unroll
     for (int ks = 0; ks < G_::KSTEPS; ks += 2) {
       if constexpr (DT == kBf16) {
-        // q from LDS (the bf16 tiles leave no registers for it): row rb*16+n,
-        // channels 8(4k+g) .. +7 for k-step k.  The offset is made opaque so the
-        // compiler cannot hoist these reads out of the tile loop into registers.
-        int qo = rb * 16 * kQStride<D> + k_channel<DT, D>(0, g, 0);
-        asm volatile("" : "+v"(qo));
-        auto qop = [&](int k) {
-          return __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(qrow + qo + 32 * k));
-        };
         s0 = mfma32_bf16(k_operand<DT, D>(T.kw, ks), qop(ks), s0);
         if (ks + 1 < G_::KSTEPS) s1 = mfma32_bf16(k_operand<DT, D>(T.kw, ks + 1), qop(ks + 1), s1);
       } else {
-        s0 = mfma32(k_operand<DT, D>(T.kw, ks), qb[rb][ks], s0);
-        if (ks + 1 < G_::KSTEPS) s1 = mfma32(k_operand<DT, D>(T.kw, ks + 1), qb[rb][ks + 1], s1);
+        s0 = mfma32(k_operand<DT, D>(T.kw, ks), qop(ks), s0);
+        if (ks + 1 < G_::KSTEPS) s1 = mfma32(k_operand<DT, D>(T.kw, ks + 1), qop(ks + 1), s1);
       }
     }
     float z[4];
@@ -524,11 +522,15 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
 // of the next NB-1 are in flight.
 template <int DT, int MODE, int D, int RB>
 struct Knobs {
+  // q operand from LDS instead of registers: the bf16 tiles need those
+  // registers.  (For the 8-bit caches this measured slower on MI355X: 64K int8
+  // 28.9 -> 30.5 us, and 3 tiles in flight with it 33.6 us, with spills.)
+  static constexpr bool QLDS = DT == kBf16;
   static constexpr int NB = kSplitTilesInFlight;
   static constexpr int WAVES_PER_EU = kSplitWavesPerSimd;
-  // merge buffers: one per wavefront when they fit in 64 KiB of LDS, else one
-  // shared buffer the wavefronts add into in turn
-  static constexpr int MERGE_BUFS = (kWaves * 16 * RB * D * 4 <= 65536) ? kWaves : 1;
+  // merge buffers: one per wavefront (RB * D <= 256 keeps them within 64 KiB)
+  static constexpr int MERGE_BUFS = kWaves;
+  static_assert(MERGE_BUFS * 16 * RB * D * 4 <= 65536, "merge buffers exceed 64 KiB");
 };
 
 template <int DT, int MODE, int D, int RB, bool CAP>
@@ -540,9 +542,17 @@ split_decode_kernel(SplitArgs a) {
   constexpr int RP = 16 * RB;  // padded query rows
   constexpr int NB = K_::NB;
 
-  __shared__ __attribute__((aligned(16))) float smem[K_::MERGE_BUFS * RP * D];  // q staging (as bf16), then merge buffers
+  // q rows staged as bf16 (and, with QLDS, each wavefront's copy of its q
+  // operand after them), then the merge buffers
+  __shared__ __attribute__((aligned(16))) float smem[K_::MERGE_BUFS * RP * D];
+  constexpr int kQStageBytes = (RP * kQStride<D> * 2 + 255) / 256 * 256;
+  constexpr int kQOpBytes = RB * G_::KSTEPS * 64 * 16;  // one wavefront's operand
+  static_assert(!K_::QLDS || kQStageBytes + kWaves * kQOpBytes <= (int)sizeof(smem),
+                "q operand copies do not fit the merge buffers");
   __shared__ float s_m[kWaves][RP];
   __shared__ float s_l[kWaves][RP];
+  __shared__ float s_f[kWaves][RP];  // merge weight of each wavefront's rows
+  __shared__ float s_vref[kWaves];
 
   const int hkv = blockIdx.y;
   // Row-split launches (RBN > 1) give each of a chunk's RBN row blocks its own
@@ -613,33 +623,39 @@ split_decode_kernel(SplitArgs a) {
   }
 
   // ---- fused append: the wavefront that will read the tile holding a new
-  // position quantizes and stores that row first (the same arithmetic as
-  // kvq_append), then waits for its stores before it issues any tile load.
-  // No other wavefront reads those rows in this launch.
-  if (a.k_new != nullptr) {
-    // Position L - Tq + j of query token j.  All of the wavefront's rows are
-    // loaded first (unconditional loads from clamped addresses), so their
-    // latencies overlap; then the owned ones are quantized and stored.
-    using RG = RowGeo<DT, D>;
-    uint16_t rk[kMaxQTokens][RG::EPL], rv[kMaxQTokens][RG::EPL];
-    int rblk[kMaxQTokens];
-    bool mine[kMaxQTokens];
+  // position quantizes and stores that row (the same arithmetic as
+  // kvq_append) and waits for its stores before it issues the load of that
+  // tile.  No other wavefront reads those rows in this launch.  Position
+  // L - Tq + j holds query token j's row.
+  const int t0 = tb + wave;  // the wavefront's tiles are t0, t0 + 4, ...
+  bool mine[kMaxQTokens];    // wave-uniform
+  bool any_mine = false, early_hit = false;
+#pragma unroll
+  for (int j = 0; j < kMaxQTokens; ++j) {
+    const int p = L - a.Tq + j;
+    const int t = p / kTile;
+    mine[j] = a.k_new != nullptr && j < a.Tq && p >= 0 && t >= tb && t < te && (t - tb) % kWaves == wave;
+    any_mine |= mine[j];
+    early_hit |= mine[j] && t < t0 + NB * kWaves;  // among the first NB tiles
+  }
+  using RG = RowGeo<DT, D>;
+  uint16_t rk[kMaxQTokens][RG::EPL], rv[kMaxQTokens][RG::EPL];
+  int rblk[kMaxQTokens];
+  if (any_mine) {
+    // the rows first, so their latency overlaps the tile loads
 #pragma unroll
     for (int j = 0; j < kMaxQTokens; ++j) {
+      if (!mine[j]) continue;
       const int p = L - a.Tq + j;
-      const int t = p / kTile;
-      mine[j] = j < a.Tq && p >= 0 && t >= tb && t < te && (t - tb) % kWaves == wave;  // wave-uniform
-      const int jj = j < a.Tq ? j : 0;
-      const size_t xi = (((size_t)b * a.Tq + jj) * a.c.Hkv + hkv) * D;
+      const size_t xi = (((size_t)b * a.Tq + j) * a.c.Hkv + hkv) * D;
       load_row<DT, D>(a.k_new + xi, lane, rk[j]);
       load_row<DT, D>(a.v_new + xi, lane, rv[j]);
-      rblk[j] = b;
-      if (a.c.block_table != nullptr) {
-        const int pc = p < 0 ? 0 : p;
-        rblk[j] = a.c.block_table[(size_t)b * a.c.max_blocks + pc / a.c.block_size];
-      }
+      rblk[j] = a.c.block_table != nullptr
+                    ? a.c.block_table[(size_t)b * a.c.max_blocks + p / a.c.block_size]
+                    : b;
     }
-    bool wrote = false;
+  }
+  auto append_rows = [&]() {
 #pragma unroll
     for (int j = 0; j < kMaxQTokens; ++j) {
       if (!mine[j] || (unsigned)rblk[j] >= (unsigned)a.c.num_blocks) continue;
@@ -648,27 +664,34 @@ split_decode_kernel(SplitArgs a) {
           ((size_t)rblk[j] * a.c.Hkv + hkv) * a.c.block_size + (size_t)(p % a.c.block_size);
       quantize_store_row<DT, MODE, D>(rk[j], lane, a.c.k_codes + ri * RG::ROWB, a.c.k_scales + ri,
                                       MODE == kPerChannel ? a.c.k_scales + (size_t)hkv * D : a.c.k_scales);
-      quantize_store_row_mode<DT, D>(a.vmode, rv[j], lane, a.c.v_codes + ri * RG::ROWB,
-                                     a.c.v_scales + ri,
-                                     a.vmode == kPerChannel ? a.c.v_scales + (size_t)hkv * D : a.c.v_scales);
-      wrote = true;
+      if constexpr (kVRow)  // V per row: known at compile time
+        quantize_store_row<DT, kPerRow, D>(rv[j], lane, a.c.v_codes + ri * RG::ROWB, a.c.v_scales + ri,
+                                           a.c.v_scales);
+      else
+        quantize_store_row_mode<DT, D>(a.vmode, rv[j], lane, a.c.v_codes + ri * RG::ROWB,
+                                       a.c.v_scales + ri,
+                                       a.vmode == kPerChannel ? a.c.v_scales + (size_t)hkv * D : a.c.v_scales);
     }
-    if (wrote) __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before any load of those rows
-  }
+    __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before any load of those rows
+  };
 
-  // ---- the wavefront's tiles are tb + wave, tb + wave + 4, ...; start the
-  // loads of the first NB now so their latency overlaps the query prologue.
-  // Every load is issued unconditionally (tiles past the split read nothing),
-  // so no branch joins on in-flight loads and the waits stay exact.
-  const int t0 = tb + wave;
+  // ---- start the loads of the wavefront's first NB tiles now so their
+  // latency overlaps the query prologue (and the append).  Every load is
+  // issued unconditionally (tiles past the split read nothing).  A wavefront
+  // whose first tiles hold a new row appends first; any other appends after
+  // issuing them, so the stores overlap the loads.
   const bool paged = a.c.block_table != nullptr;
   TableRegs tbl;
   if (paged) tbl = load_table(a, b, t0, kWaves, lane);
   Tile<DT, D> buf[NB];
+  // (the loads stay at one program point, so the compiler's waits for them
+  // remain exact on the path every wavefront but one takes)
+  if (early_hit) append_rows();
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    load_tile<DT, MODE, D>(a, hkv, t0 + i * kWaves, t0 + i * kWaves < te, paged ? table_entry(tbl, i) : b,
-                           L, n, g, buf[i]);
+    load_tile<DT, MODE, D>(a, hkv, t0 + i * kWaves, t0 + i * kWaves < te,
+                           paged ? table_entry(tbl, i) : b, L, n, g, buf[i]);
+  if (any_mine && !early_hit) append_rows();
 
   // ---- stage the query rows in LDS (bf16), zero padding rows
   uint16_t* qs = reinterpret_cast<uint16_t*>(smem);
@@ -697,8 +720,11 @@ split_decode_kernel(SplitArgs a) {
       if (lim[rb] > L) lim[rb] = L;
       lo[rb] = a.window > 0 ? lim[rb] - a.window : 0;
       if constexpr (DT == kBf16) {
-        // the q rows stay in LDS as they are (bf16 products are exact in the
-        // fp32 accumulation); the tile loop reads them there
+        // the q rows as they are: bf16 products are exact in the fp32 accumulation
+#pragma unroll
+        for (int ks = 0; ks < G_::KSTEPS; ++ks)
+          qb[rb][ks] = __builtin_bit_cast(
+              half8_t, *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + k_channel<DT, D>(ks, g, 0)));
         rowmul[rb] = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
         continue;
       }
@@ -740,6 +766,16 @@ split_decode_kernel(SplitArgs a) {
       rowmul[rb] = ldexpf(mul, ex);
     }
   }
+  // With QLDS the operand goes to this wavefront's own LDS copy (lane-linear),
+  // which only its own lanes read back: no barrier needed.
+  half8_t* qlds = reinterpret_cast<half8_t*>(reinterpret_cast<char*>(smem) + kQStageBytes +
+                                             wave * kQOpBytes) + lane;
+  if constexpr (K_::QLDS) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < G_::KSTEPS; ++ks) qlds[(rb * G_::KSTEPS + ks) * 64] = qb[rb][ks];
+  }
 
   // soft cap in log2 units (the CAP variant is launched when softcap > 0)
   const float cap2 = CAP ? a.softcap * 1.4426950408889634f : 0.0f;
@@ -758,8 +794,8 @@ split_decode_kernel(SplitArgs a) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (t < te)
-        process_tile<DT, MODE, D, RB, CAP>(buf[i], t, L, n, g, qb, qs + n * kQStride<D>, rowmul, lim, lo,
-                                           cap2, icap2, W);
+        process_tile<DT, MODE, D, RB, CAP, K_::QLDS>(buf[i], t, L, n, g, qb, qlds, rowmul, lim, lo,
+                                                     cap2, icap2, W);
       load_tile<DT, MODE, D>(a, hkv, t + NB * kWaves, t + NB * kWaves < te,
                              paged ? table_entry(tbl, k + NB) : b, L, n, g, buf[i]);
       t += kWaves;
@@ -767,7 +803,13 @@ split_decode_kernel(SplitArgs a) {
     }
   }
 
-  // ---- merge the 4 wavefronts in fixed order, write the split partial
+  // ---- merge the 4 wavefronts in fixed order, write the split partial.
+  // Each wavefront publishes its row statistics; after the barrier (every loop
+  // has ended, so the q staging area is free) it writes its raw accumulator
+  // rows to its own LDS buffer while one lane per row turns the statistics into
+  // the four per-wavefront weights; the readback then sums the weighted buffers
+  // in wave order.  The weight chain runs on a few lanes beside the writes
+  // rather than in front of them.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float lsum = group_sum4(W.l[rb]);
@@ -776,84 +818,73 @@ split_decode_kernel(SplitArgs a) {
       s_l[wave][rb * 16 + n] = lsum;
     }
   }
+  if constexpr (kVRow)
+    if (lane == 0) s_vref[wave] = W.vref;
   __syncthreads();
 
-  float fac[RB][4];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = rb * 16 + 4 * g + e;
-      float M = s_m[0][r];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
-      float f = 0.0f;
-      if (M != -INFINITY) {
-        float Lt = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) Lt += s_l[w][r] * exp2f(s_m[w][r] - M);
-        f = exp2f(s_m[wave][r] - M) / Lt;
-        if constexpr (kVRow) f *= W.vref;
-        if constexpr (DT == kInt4) f *= 0.0625f;  // V operand holds 16 * code
-      }
-      fac[rb][e] = f;
-    }
-
-  // each wavefront writes its weighted rows; the sum runs in wave order.
   // Lane column n owns NCOL channels, NCOL / 4 groups of 4 consecutive ones
   // (see group_owner); they go to the lane's NCOL-float LDS slot as 16-byte
   // chunks whose order is rotated by n / (64 / NCOL) so the 16 lanes of a pass
   // hit distinct banks.
   constexpr int NCH = G_::NCOL / 4;                 // 16-byte chunks per lane and row
   constexpr int ROT = G_::NCOL >= 16 ? 4 : (G_::NCOL == 8 ? 8 : 16);
-  const int nbuf = K_::MERGE_BUFS;
-  for (int round = 0; round < kWaves / nbuf; ++round) {
-    const int w_act = round * nbuf;  // first wave writing this round
-    if (wave >= w_act && wave < w_act + nbuf) {
-      float* ob = smem + (size_t)(wave - w_act) * RP * D;
+  {
+    float* ob = smem + (size_t)wave * RP * D;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rb * 16 + 4 * g + e;
-          if (r < Rw) {
+      for (int e = 0; e < 4; ++e) {
+        const int r = rb * 16 + 4 * g + e;
+        if (r < Rw) {
 #pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-              float4_t v;
+          for (int k = 0; k < NCH; ++k) {
+            float4_t v;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) v[i] = W.acc[rb][col_of<DT, D>(4 * k + i)][e] * fac[rb][e];
-              const int slot = (k + n / ROT) % NCH;
-              float4_t* dst = reinterpret_cast<float4_t*>(ob + r * D + G_::NCOL * n + 4 * slot);
-              if (round == 0)
-                *dst = v;
-              else
-                *dst += v;
-            }
+            for (int i = 0; i < 4; ++i) v[i] = W.acc[rb][col_of<DT, D>(4 * k + i)][e];
+            const int slot = (k + n / ROT) % NCH;
+            *reinterpret_cast<float4_t*>(ob + r * D + G_::NCOL * n + 4 * slot) = v;
           }
         }
-    }
-    __syncthreads();
+      }
   }
+  // the chunk's statistics of row r (log2 units) and the weight of each
+  // wavefront's rows: exp2(m_w - M) / L (times its V reference; 1/16 for int4,
+  // whose V operand holds 16 * code)
+  constexpr int kStatWave = kWaves - 1;
+  if (wave == kStatWave && lane < Rw) {
+    const int r = lane;
+    float M = s_m[0][r];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+    float Lt = 0.0f;
+    float ew[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      ew[w] = M != -INFINITY ? exp2f(s_m[w][r] - M) : 0.0f;
+      Lt += s_l[w][r] * ew[w];
+    }
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      float f = Lt > 0.0f ? ew[w] / Lt : 0.0f;
+      if constexpr (kVRow) f *= s_vref[w];
+      if constexpr (DT == kInt4) f *= 0.0625f;
+      s_f[w][r] = f;
+    }
+    a.ws_m[((size_t)hkv * a.R + row0 + r) * a.S + slot] = M;
+    a.ws_l[((size_t)hkv * a.R + row0 + r) * a.S + slot] = Lt;
+  }
+  __syncthreads();
 
   for (int idx = tid * 4; idx < Rw * D; idx += 256 * 4) {
     const int r = idx / D, d = idx % D;
     int jn, k;
     group_owner<DT, D>(d, jn, k);
     const int off = r * D + G_::NCOL * jn + 4 * ((k + jn / ROT) % NCH);
-    float4_t v = *reinterpret_cast<const float4_t*>(smem + off);
+    float4_t v = s_f[0][r] * *reinterpret_cast<const float4_t*>(smem + off);
 #pragma unroll
-    for (int w = 1; w < nbuf; ++w) v += *reinterpret_cast<const float4_t*>(smem + (size_t)w * RP * D + off);
+    for (int w = 1; w < kWaves; ++w)
+      v += s_f[w][r] * *reinterpret_cast<const float4_t*>(smem + (size_t)w * RP * D + off);
     *reinterpret_cast<float4_t*>(a.ws_o + (((size_t)hkv * a.R + row0 + r) * a.S + slot) * D + d) = v;
-  }
-  if (tid < Rw) {
-    const int r = tid;
-    float M = s_m[0][r];
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
-    float Lt = 0.0f;
-    if (M != -INFINITY)
-      for (int w = 0; w < kWaves; ++w) Lt += s_l[w][r] * exp2f(s_m[w][r] - M);
-    a.ws_m[((size_t)hkv * a.R + row0 + r) * a.S + slot] = M;
-    a.ws_l[((size_t)hkv * a.R + row0 + r) * a.S + slot] = Lt;
   }
 }
 
