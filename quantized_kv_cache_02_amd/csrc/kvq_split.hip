@@ -420,7 +420,9 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
       const float tmax = group_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
       const float mnew = fmaxf(W.m[rb], tmax);
       if (mnew > W.m[rb]) {
-        alpha[rb] = exp2f(W.m[rb] - mnew);  // 0 when the old max was -inf
+        // hardware exp2 (results below 2^-126 flush to 0: such weights vanish
+        // in the fp16 operand anyway); 0 when the old max was -inf
+        alpha[rb] = __builtin_amdgcn_exp2f(W.m[rb] - mnew);
         W.l[rb] *= alpha[rb];
         W.m[rb] = mnew;
         rescale = true;
@@ -432,7 +434,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
     float psum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float p = exp2f(z[e] - msafe);
+      const float p = __builtin_amdgcn_exp2f(z[e] - msafe);
       psum += p;
       float pv = p;
       if constexpr (kVRow) pv = valid[e] ? p * vsn[e] : 0.0f;
