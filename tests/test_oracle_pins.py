@@ -325,11 +325,13 @@ def _sdpa_ref(q, K, V, lens, scale, Tq):
     return out
 
 
-@pytest.mark.parametrize("G,Tq", [(1, 1), (4, 1), (6, 3), (8, 8)])
+@pytest.mark.parametrize("G,Tq", [(1, 1), (4, 1), (6, 3), (8, 8), (6, 37), (3, 90)])
 def test_attend_matches_torch_sdpa_fp64(oracle_lib, G, Tq):
+    """Causal attention of Tq query tokens ending at each sequence's length; the
+    larger Tq are a chunked prefill (the chunk attends the cache and itself)."""
     rng = np.random.default_rng(G * 10 + Tq)
     B, Hkv, D = 2, 2, 64
-    lens = np.array([37, 90], np.int32)
+    lens = np.array([max(37, Tq), 90], np.int32)
     K = rng.standard_normal((B, Hkv, 90, D)).astype(np.float32)
     V = rng.standard_normal((B, Hkv, 90, D)).astype(np.float32)
     q = ki.randn_bf16((B, Tq, G * Hkv, D), 11 + G)
