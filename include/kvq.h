@@ -274,6 +274,36 @@ int kvq_combine(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int3
                 const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvq_prefill_attend -- chunked prefill: q_tokens new tokens per sequence (a
+ * prompt chunk) are quantized into the cache and attend causally to every
+ * cached token up to their own ([K] "Requirements and limits": prefill runs a
+ * tiled attention kernel, its keys and values go through the append; [F]
+ * "Testing": prefill and chunked prefill over the paged quantized cache).
+ *
+ *   k_new, v_new  bf16 [batch, q_tokens, num_kv_heads, head_dim], both or
+ *                 neither: written first, like kvq_append, at positions
+ *                 seq_lens[b] - q_tokens + j; NULL when the chunk is already in
+ *                 the cache
+ *   q             bf16 [batch, q_tokens, num_q_heads, head_dim]
+ *   seq_lens      int32 [batch] (device): tokens of each sequence after the chunk
+ *   out           bf16 [batch, q_tokens, num_q_heads, head_dim]
+ *   options       soft cap / sliding window as kvq_attend_ex, or NULL
+ *   Everything else as kvq_attend_ex.  Query token j of sequence b sits at
+ *   position seq_lens[b] - q_tokens + j and attends every cached token at or
+ *   before it (inside the window); the output is exact softmax attention over
+ *   the dequantized cache, like the decode, so a chunk of one token is a
+ *   decode step.  Tokens before position 0 output zeros.  q_tokens has no
+ *   upper bound beyond G * q_tokens < 2^30; no workspace is needed (one
+ *   workgroup owns 64 query rows of one KV head over all its tokens).
+ *   Two launches on `stream` (append, attention); graph-capturable.
+ */
+int kvq_prefill_attend(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                       int32_t batch, int32_t num_q_heads, int32_t q_tokens, const int32_t* seq_lens,
+                       int32_t max_seq_len, float softmax_scale, const float* head_sink,
+                       const int32_t* block_table, int32_t max_blocks,
+                       const kvq_attn_options* options, void* out, void* stream);
+
+/*
  * kvq_cache_bytes -- host-only footprint of one layer's cache: codes of K and
  * V plus, for KVQ_PER_ROW, one fp32 scale per row ([K] opening paragraphs
  * and "Cache footprint"; [F] "Motivation and Context": static per-channel

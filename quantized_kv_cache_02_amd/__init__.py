@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "INT8", "INT4", "FP8_E4M3FN", "BF16", "NO_SCALE", "PER_ROW", "PER_TENSOR", "PER_CHANNEL",
     "KVCache", "KvqError", "append", "num_splits", "workspace_bytes", "decode_attend",
-    "paged_decode_attend", "append_decode_attend", "attend_ex", "split_decode", "combine",
+    "paged_decode_attend", "append_decode_attend", "attend_ex", "prefill_attend", "split_decode",
+    "combine",
     "cache_bytes",
     "lib", "LIB_PATH",
 ]
@@ -29,7 +30,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 EXPORTS = (
     "kvq_append", "kvq_num_splits", "kvq_workspace_bytes", "kvq_decode_attend",
-    "kvq_paged_decode_attend", "kvq_append_decode_attend", "kvq_attend_ex", "kvq_split_decode",
+    "kvq_paged_decode_attend", "kvq_append_decode_attend", "kvq_attend_ex", "kvq_prefill_attend",
+    "kvq_split_decode",
     "kvq_combine", "kvq_cache_bytes",
     "kvq_status_string",
 )
@@ -83,6 +85,9 @@ def lib():
         L.kvq_attend_ex.argtypes = [CP, P, P, P, I32, I32, I32, P, I32, F, P, P, I32,
                                     ctypes.POINTER(_Options), P, P, SZ, P]
         L.kvq_attend_ex.restype = ctypes.c_int
+        L.kvq_prefill_attend.argtypes = [CP, P, P, P, I32, I32, I32, P, I32, F, P, P, I32,
+                                         ctypes.POINTER(_Options), P, P]
+        L.kvq_prefill_attend.restype = ctypes.c_int
         L.kvq_split_decode.argtypes = [CP, P, I32, I32, I32, P, I32, F, P, I32, P, SZ, P]
         L.kvq_split_decode.restype = ctypes.c_int
         L.kvq_combine.argtypes = [CP, I32, I32, I32, P, I32, P, P, P, SZ, P]
@@ -294,6 +299,33 @@ def attend_ex(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_l
                                _ptr(block_table), mb, ctypes.byref(opts), _ptr(out), _ptr(ws),
                                nbytes, _stream(stream)),
            "kvq_attend_ex")
+    return out
+
+
+def prefill_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                   softmax_scale: float, k_new: Optional[torch.Tensor] = None,
+                   v_new: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+                   head_sink: Optional[torch.Tensor] = None, softcap: float = 0.0, window: int = 0,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Chunked prefill: the Tq = q.shape[1] tokens of a chunk (k_new, v_new bf16
+    [B, Tq, Hkv, D], appended first unless None) attend causally to the cache."""
+    _want(q, torch.bfloat16, "q")
+    _want(seq_lens, torch.int32, "seq_lens")
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        if t is not None:
+            _want(t, torch.bfloat16, nm)
+    B, Tq, Hq, _ = q.shape
+    mb = 0
+    if block_table is not None:
+        _want(block_table, torch.int32, "block_table")
+        mb = block_table.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    opts = _Options(float(softcap), int(window))
+    _check(lib().kvq_prefill_attend(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, Tq,
+                                    _ptr(seq_lens), max_seq_len, float(softmax_scale),
+                                    _ptr(head_sink), _ptr(block_table), mb, ctypes.byref(opts),
+                                    _ptr(out), _stream(stream)),
+           "kvq_prefill_attend")
     return out
 
 

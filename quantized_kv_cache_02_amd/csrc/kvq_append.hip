@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   uint16_t raw[R::EPL];
   load_row<DT, D>((side ? a.v : a.k) + (((size_t)b * a.Tn + j) * Hkv + h) * D, lane, raw);
 
-  const int pos = a.positions[b] + j;
+  const int pos = (a.positions != nullptr ? a.positions[b] : a.seq_lens[b] - a.Tn) + j;
   if (pos < 0 || pos >= a.capacity) return;
   const int bs = a.c.block_size;
   int blk = b;

@@ -139,4 +139,35 @@ __device__ __forceinline__ half8_t u4_to_h8(uint32_t a, uint32_t b, uint32_t c, 
   return __builtin_bit_cast(half8_t, v);
 }
 
+// Transpose 4 token rows x 4 bytes (one dword each) into MFMA B operands:
+// out[q] = (token0, token1, token2, token3) of byte q, q = 0..3, as fp16.
+template <int KIND>  // 0: biased magic bytes (int8 after xor, int4 nibbles), 1: fp8
+__device__ __forceinline__ void v_transpose4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                             half4_t out[4]) {
+  const uint32_t s01lo = perm(r1, r0, 0x05010400u);  // (r0.b0, r1.b0, r0.b1, r1.b1)
+  const uint32_t s01hi = perm(r1, r0, 0x07030602u);  // (r0.b2, r1.b2, r0.b3, r1.b3)
+  const uint32_t s23lo = perm(r3, r2, 0x05010400u);
+  const uint32_t s23hi = perm(r3, r2, 0x07030602u);
+  if constexpr (KIND == 1) {
+    out[0] = u2_to_h4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s01lo, 1.0f, false)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s23lo, 1.0f, false)));
+    out[1] = u2_to_h4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s01lo, 1.0f, true)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s23lo, 1.0f, true)));
+    out[2] = u2_to_h4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s01hi, 1.0f, false)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s23hi, 1.0f, false)));
+    out[3] = u2_to_h4(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s01hi, 1.0f, true)),
+                      as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s23hi, 1.0f, true)));
+  } else {
+    const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    out[0] = u2_to_h4(pk_add_h(perm(kMagic, s01lo, 0x04010400u), bias),
+                      pk_add_h(perm(kMagic, s23lo, 0x04010400u), bias));
+    out[1] = u2_to_h4(pk_add_h(perm(kMagic, s01lo, 0x04030402u), bias),
+                      pk_add_h(perm(kMagic, s23lo, 0x04030402u), bias));
+    out[2] = u2_to_h4(pk_add_h(perm(kMagic, s01hi, 0x04010400u), bias),
+                      pk_add_h(perm(kMagic, s23hi, 0x04010400u), bias));
+    out[3] = u2_to_h4(pk_add_h(perm(kMagic, s01hi, 0x04030402u), bias),
+                      pk_add_h(perm(kMagic, s23hi, 0x04030402u), bias));
+  }
+}
+
 }  // namespace kvq

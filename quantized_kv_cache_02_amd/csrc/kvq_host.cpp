@@ -189,6 +189,26 @@ hipError_t dispatch_split(int dt, int md, bool vrow, int D, int RB, const kvq::S
   return hipErrorInvalidValue;
 }
 
+hipError_t dispatch_prefill(int dt, int md, bool vrow, int D, const kvq::PrefillArgs& a, int B,
+                            hipStream_t st) {
+#define KVQ_CASE(DT, MD)                                                                        \
+  if (dt == DT && md == MD)                                                                     \
+    return vrow ? kvq::launch_prefill_##DT##_##MD##_1(D, a, B, st)                              \
+                : kvq::launch_prefill_##DT##_##MD##_0(D, a, B, st);
+  KVQ_CASE(1, 1)
+  KVQ_CASE(1, 2)
+  KVQ_CASE(1, 3)
+  KVQ_CASE(2, 1)
+  KVQ_CASE(2, 2)
+  KVQ_CASE(2, 3)
+  KVQ_CASE(3, 1)
+  KVQ_CASE(3, 2)
+  KVQ_CASE(3, 3)
+#undef KVQ_CASE
+  if (dt == KVQ_BF16 && md == KVQ_NO_SCALE && !vrow) return kvq::launch_prefill_4_0_0(D, a, B, st);
+  return hipErrorInvalidValue;
+}
+
 int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int32_t tq,
                const int32_t* seq_lens, int32_t max_seq_len, float scale, const int32_t* table,
                int32_t max_blocks, void* ws, size_t ws_bytes, void* stream,
@@ -292,6 +312,7 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t bat
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.positions = positions;
+  a.seq_lens = nullptr;
   a.B = batch;
   a.Tn = tokens;
   a.capacity = (int32_t)capacity;
@@ -391,6 +412,70 @@ int kvq_attend_ex(const kvq_cache* cache, const void* k_new, const void* v_new, 
   if (st != KVQ_OK) return st;
   return combine_impl(cache, batch, num_q_heads, q_tokens, seq_lens, max_seq_len, head_sink, out,
                       workspace, workspace_bytes, stream, options ? options->window : 0);
+}
+
+int kvq_prefill_attend(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                       int32_t batch, int32_t num_q_heads, int32_t q_tokens, const int32_t* seq_lens,
+                       int32_t max_seq_len, float softmax_scale, const float* head_sink,
+                       const int32_t* block_table, int32_t max_blocks,
+                       const kvq_attn_options* options, void* out, void* stream) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (batch < 1 || num_q_heads < 1 || q_tokens < 1 || max_seq_len < 1) return KVQ_EINVAL;
+  if (num_q_heads % cache->num_kv_heads != 0) return KVQ_EINVAL;
+  const int G = num_q_heads / cache->num_kv_heads;
+  if (G > kMaxGroup) return KVQ_EUNSUPPORTED;
+  if (batch > 65535 || cache->num_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+  if ((int64_t)G * q_tokens > INT32_MAX / 2) return KVQ_EUNSUPPORTED;
+  st = check_layout(cache, batch, max_seq_len, block_table, max_blocks);
+  if (st != KVQ_OK) return st;
+  if (q == nullptr || seq_lens == nullptr || out == nullptr || !aligned16(q) || !aligned16(out))
+    return KVQ_EINVAL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return KVQ_EINVAL;
+  if (k_new != nullptr && (!aligned16(k_new) || !aligned16(v_new))) return KVQ_EINVAL;
+  if (options != nullptr) {
+    const float cap = options->softcap;
+    if (!(cap >= 0.0f) || cap > 3.0e38f || options->window < 0) return KVQ_EINVAL;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (k_new != nullptr) {
+    // the chunk's rows first, at positions seq_lens[b] - q_tokens + j
+    kvq::AppendArgs ap;
+    ap.c = cache_args(cache, block_table, max_blocks);
+    ap.k = static_cast<const uint16_t*>(k_new);
+    ap.v = static_cast<const uint16_t*>(v_new);
+    ap.positions = nullptr;
+    ap.seq_lens = seq_lens;
+    ap.B = batch;
+    ap.Tn = q_tokens;
+    const int64_t capacity =
+        block_table == nullptr ? cache->block_size : (int64_t)max_blocks * cache->block_size;
+    if (capacity > INT32_MAX) return KVQ_EUNSUPPORTED;
+    ap.capacity = (int32_t)capacity;
+    ap.kmode = cache->scale_mode;
+    ap.vmode = v_mode_of(cache);
+    hipError_t e = kvq::launch_append(cache->dtype, ap.kmode, ap.vmode, cache->head_dim, ap, hs);
+    if (e != hipSuccess) return KVQ_EHIP;
+  }
+  kvq::PrefillArgs a;
+  a.c = cache_args(cache, block_table, max_blocks);
+  a.q = static_cast<const uint16_t*>(q);
+  a.seq_lens = seq_lens;
+  a.Hq = num_q_heads;
+  a.Tq = q_tokens;
+  a.G = G;
+  a.R = G * q_tokens;
+  a.max_seq_len = max_seq_len;
+  a.sm_scale = softmax_scale;
+  a.vmode = v_mode_of(cache);
+  a.softcap = options ? options->softcap : 0.0f;
+  a.window = options ? options->window : 0;
+  a.v_static = (a.vmode == KVQ_PER_TENSOR || a.vmode == KVQ_PER_CHANNEL) ? cache->v_scales : nullptr;
+  a.sink = head_sink;
+  a.out = static_cast<uint16_t*>(out);
+  hipError_t e = dispatch_prefill(cache->dtype, cache->scale_mode, a.vmode == KVQ_PER_ROW,
+                                  cache->head_dim, a, batch, hs);
+  return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
 
 size_t kvq_cache_bytes(int32_t dtype, int32_t scale_mode, int32_t num_kv_heads, int32_t head_dim,

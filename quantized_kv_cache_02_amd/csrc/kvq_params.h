@@ -53,7 +53,8 @@ struct AppendArgs {
   CacheArgs c;
   const uint16_t* k;  // bf16 [B, Tn, Hkv, D]
   const uint16_t* v;
-  const int32_t* positions;  // [B]
+  const int32_t* positions;  // [B], or nullptr: position seq_lens[b] - Tn
+  const int32_t* seq_lens;   // used when positions is nullptr
   int32_t B;
   int32_t Tn;
   int32_t capacity;  // tokens addressable per sequence
@@ -101,6 +102,23 @@ struct CombineArgs {
   int32_t Hkv, Hq, Tq, G, R, S;
 };
 
+// Chunked prefill: Tq query tokens per sequence (the chunk, already appended
+// at positions seq_len - Tq + j) attend causally to the cache.
+struct PrefillArgs {
+  CacheArgs c;
+  const uint16_t* q;  // bf16 [B, Tq, Hq, D]
+  const int32_t* seq_lens;
+  int32_t Hq, Tq, G, R;  // R = G * Tq query rows per (sequence, KV head)
+  int32_t max_seq_len;
+  float sm_scale;
+  int32_t vmode;          // V scale mode
+  float softcap;          // > 0: logits z -> softcap * tanh(z / softcap)
+  int32_t window;         // > 0: a query at position p sees tokens p - window + 1 .. p
+  const float* v_static;  // per-tensor [1] / per-channel [Hkv, D] / nullptr
+  const float* sink;      // [Hq] or nullptr
+  uint16_t* out;          // bf16 [B, Tq, Hq, D]
+};
+
 hipError_t launch_append(int dtype, int kmode, int vmode, int D, const AppendArgs& a,
                          hipStream_t st);
 hipError_t launch_split(int dtype, int mode, int D, int RB, const SplitArgs& a, int B,
@@ -123,5 +141,21 @@ KVQ_DECLARE_SPLIT(3, 2)
 KVQ_DECLARE_SPLIT(3, 3)
 #undef KVQ_DECLARE_SPLIT
 hipError_t launch_split_4_0_0(int D, int RB, const SplitArgs& a, int B, hipStream_t st);
+
+// prefill translation units, the same split by (dtype, K mode, V per row)
+#define KVQ_DECLARE_PREFILL(DT, MD)                                                             \
+  hipError_t launch_prefill_##DT##_##MD##_0(int D, const PrefillArgs& a, int B, hipStream_t st); \
+  hipError_t launch_prefill_##DT##_##MD##_1(int D, const PrefillArgs& a, int B, hipStream_t st);
+KVQ_DECLARE_PREFILL(1, 1)
+KVQ_DECLARE_PREFILL(1, 2)
+KVQ_DECLARE_PREFILL(1, 3)
+KVQ_DECLARE_PREFILL(2, 1)
+KVQ_DECLARE_PREFILL(2, 2)
+KVQ_DECLARE_PREFILL(2, 3)
+KVQ_DECLARE_PREFILL(3, 1)
+KVQ_DECLARE_PREFILL(3, 2)
+KVQ_DECLARE_PREFILL(3, 3)
+#undef KVQ_DECLARE_PREFILL
+hipError_t launch_prefill_4_0_0(int D, const PrefillArgs& a, int B, hipStream_t st);
 
 }  // namespace kvq

@@ -1,0 +1,548 @@
+// kvq_prefill.hip -- chunked prefill: the Tq tokens of a chunk (already
+// quantized into the cache at positions seq_len - Tq .. seq_len - 1) attend
+// causally to every cached token up to their own, on gfx950.  Compiled once per
+// (KVQ_DTYPE, KVQ_MODE, KVQ_VROW) like the decode kernel.
+//
+// Kernel page "kv-quant-attn", "Requirements and limits": prefill is a tiled
+// attention kernel whose keys and values are then handed to the append; ORT
+// PR "[CUDA] Add INT4 paged KV cache ...", "Testing": prefill and chunked
+// prefill over the paged quantized cache.  Here the chunk is appended first
+// (the same quantize-on-write as every other row) and then attended through
+// the cache, so a chunk sees exactly the cache a later decode sees.
+//
+// Work assignment: one workgroup per (sequence, KV head, 64 query rows), the
+// rows being the G grouped heads times the chunk's tokens (row = token * G +
+// head).  Each of the 4 wavefronts owns 16 rows.  The workgroup walks the
+// 64-token tiles its rows can see; per tile all 256 threads load the codes
+// (the next tile's loads are issued before this tile's math), unpack them once
+// into LDS -- K as fp16 rows, V transposed to channel-major -- and every
+// wavefront then runs
+//   S^T = K . Q^T   v_mfma_f32_16x16x32_f16 (A: K rows from LDS, B: its q rows),
+//   online softmax over the tile's 64 tokens per row,
+//   O  += P . V     v_mfma_f32_16x16x16_f16 (A: the weights where S^T left
+//                   them, B: 4 tokens of one channel read from the transposed V).
+// Scales enter as in the decode kernel: a per-row K scale multiplies the
+// logit, a per-row V scale the weight (over a power-of-two reference),
+// per-channel K is folded into q, static V scales are applied at the output.
+// A bf16 cache runs on the bf16 MFMAs with the weights split hi + lo.
+
+#include "kvq_device.h"
+#include "kvq_sched.h"
+
+#ifndef KVQ_DTYPE
+#error "KVQ_DTYPE must be defined"
+#endif
+#ifndef KVQ_VROW
+#error "KVQ_VROW must be defined (1: V scales per row, 0: static)"
+#endif
+#ifndef KVQ_MODE
+#error "KVQ_MODE must be defined"
+#endif
+
+namespace kvq {
+namespace {
+
+constexpr bool kVRow = KVQ_VROW != 0;
+constexpr int kPT = 64;                // tokens per KV tile
+constexpr int kPRows = 16 * kWaves;    // query rows per workgroup
+
+template <int DT, int D>
+struct PGeo {
+  static constexpr int ROWB = (DT == kInt4) ? D / 2 : (DT == kBf16) ? 2 * D : D;
+  static constexpr int KST = D + 8;      // K tile row stride in LDS (16-bit elements)
+  static constexpr int VST = kPT + 8;    // transposed V row stride (16-bit elements)
+  static constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per S^T sub-tile
+  static constexpr int NCOL = D / 16;    // 16-channel output column blocks
+  // K load: thread -> token tid / 4, bytes [KQB * (tid % 4), +KQB) of its row
+  static constexpr int KQB = ROWB / 4;
+  // V load: thread -> channel chunk tid / 16 (D / 16 channels), tokens 4 * (tid % 16) + 0..3
+  static constexpr int VCB = ROWB / 16;  // bytes of one token in one chunk
+  static constexpr int VCW = VCB >= 4 ? VCB / 4 : 1;
+  static constexpr int CPD = (DT == kInt4) ? 8 : (DT == kBf16) ? 2 : 4;  // channels per dword
+};
+
+// Load N (2, 4, 8 or 16) bytes from a device address into dwords.
+template <int N>
+__device__ __forceinline__ void gload(const uint8_t* p, uint32_t* out) {
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int i = 0; i < N / 16; ++i) {
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + i);
+      out[4 * i] = v[0]; out[4 * i + 1] = v[1]; out[4 * i + 2] = v[2]; out[4 * i + 3] = v[3];
+    }
+  } else if constexpr (N == 8) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    out[0] = v[0]; out[1] = v[1];
+  } else if constexpr (N == 4) {
+    out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  } else {
+    static_assert(N == 2, "unsupported load");
+    out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+  }
+}
+
+// Codes (and per-row scales) of one tile as this thread loads them.
+template <int DT, int D>
+struct PTile {
+  uint32_t k[PGeo<DT, D>::KQB / 4];
+  uint32_t v[4][PGeo<DT, D>::VCW];
+  float ks, vs;  // per-row scales of token tid (threads 0..63)
+};
+
+// Cache row index of position p of sequence b (-1: not readable).
+__device__ __forceinline__ long row_of(const PrefillArgs& a, int b, int hkv, int p, int L) {
+  if (p < 0 || p >= L) return -1;
+  int blk = b;
+  if (a.c.block_table != nullptr) {
+    blk = a.c.block_table[(size_t)b * a.c.max_blocks + p / a.c.block_size];
+    if ((unsigned)blk >= (unsigned)a.c.num_blocks) return -1;
+  }
+  return ((long)blk * a.c.Hkv + hkv) * a.c.block_size + p % a.c.block_size;
+}
+
+template <int DT, int MODE, int D>
+__device__ __forceinline__ void load_ptile(const PrefillArgs& a, int b, int hkv, int kt, int L, int tid,
+                                           PTile<DT, D>& T) {
+  using P = PGeo<DT, D>;
+  // K: one row quarter per thread; unreadable rows load row 0 and are zeroed
+  {
+    const long ri = row_of(a, b, hkv, kt * kPT + tid / 4, L);
+    gload<P::KQB>(a.c.k_codes + (ri < 0 ? 0 : ri) * P::ROWB + P::KQB * (tid % 4), T.k);
+    if (ri < 0)
+#pragma unroll
+      for (int i = 0; i < P::KQB / 4; ++i) T.k[i] = 0u;
+  }
+  // V: 4 tokens of one channel chunk
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const long ri = row_of(a, b, hkv, kt * kPT + 4 * (tid % 16) + e, L);
+    uint32_t w[P::VCW] = {};
+    gload<P::VCB>(a.c.v_codes + (ri < 0 ? 0 : ri) * P::ROWB + P::VCB * (tid / 16), w);
+#pragma unroll
+    for (int i = 0; i < P::VCW; ++i) T.v[e][i] = ri < 0 ? 0u : w[i];
+  }
+  T.ks = 0.0f;
+  T.vs = 0.0f;
+  if (tid < kPT) {
+    const long ri = row_of(a, b, hkv, kt * kPT + tid, L);
+    if constexpr (MODE == kPerRow) T.ks = ri < 0 ? 0.0f : a.c.k_scales[ri];
+    if constexpr (kVRow) T.vs = ri < 0 ? 0.0f : a.c.v_scales[ri];
+  }
+}
+
+// int4: one dword of 8 nibbles -> 16 * n as fp16 in natural channel order.
+__device__ __forceinline__ void int4x8_to_h_ordered(uint32_t w, uint32_t out[4]) {
+  const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t ev = (x << 4) & 0xF0F0F0F0u;  // 16 (n_even + 8) per byte
+  const uint32_t od = x & 0xF0F0F0F0u;         // 16 (n_odd + 8)
+  const uint32_t lo = perm(od, ev, 0x05010400u);  // (n0, n1, n2, n3)
+  const uint32_t hi = perm(od, ev, 0x07030602u);  // (n4, n5, n6, n7)
+  out[0] = pk_add_h(perm(kMagic, lo, 0x04010400u), bias);
+  out[1] = pk_add_h(perm(kMagic, lo, 0x04030402u), bias);
+  out[2] = pk_add_h(perm(kMagic, hi, 0x04010400u), bias);
+  out[3] = pk_add_h(perm(kMagic, hi, 0x04030402u), bias);
+}
+
+// Unpack a loaded tile into LDS: K rows as fp16 (bf16 as is), V transposed to
+// [channel][token], per-row scales.
+template <int DT, int MODE, int D>
+__device__ __forceinline__ void stage_ptile(const PTile<DT, D>& T, int tid, uint16_t* ks_lds,
+                                            uint16_t* vt_lds, float* ksc, float* vsc) {
+  using P = PGeo<DT, D>;
+  {
+    // this thread's quarter of its row: channels (D / 4) * (tid % 4) .. + D / 4
+    uint16_t* dst = ks_lds + (tid / 4) * P::KST + (D / 4) * (tid % 4);
+    constexpr int NW = P::KQB / 4;  // dwords loaded
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      if constexpr (DT == kBf16) {
+        reinterpret_cast<uint32_t*>(dst)[i] = T.k[i];
+      } else if constexpr (DT == kInt4) {
+        uint32_t h[4];
+        int4x8_to_h_ordered(T.k[i], h);
+        *reinterpret_cast<u32x4_t*>(dst + 8 * i) = u32x4_t{h[0], h[1], h[2], h[3]};
+      } else {
+        uint32_t lo, hi;
+        if constexpr (DT == kInt8)
+          int8x4_to_h(T.k[i], lo, hi);
+        else
+          fp8x4_to_h(T.k[i], lo, hi);
+        *reinterpret_cast<u32x2_t*>(dst + 4 * i) = u32x2_t{lo, hi};
+      }
+    }
+  }
+  {
+    // channels [cb0, cb0 + D / 16) of tokens t0 .. t0 + 3
+    const int cb0 = (D / 16) * (tid / 16), t0 = 4 * (tid % 16);
+    constexpr int NCH = D / 16;  // channels of this thread
+#pragma unroll
+    for (int w = 0; w < P::VCW; ++w) {
+      if constexpr (DT == kBf16) {
+        // dword w holds channels 2w, 2w + 1
+        const u32x2_t lo = {perm(T.v[1][w], T.v[0][w], 0x05040100u), perm(T.v[3][w], T.v[2][w], 0x05040100u)};
+        const u32x2_t hi = {perm(T.v[1][w], T.v[0][w], 0x07060302u), perm(T.v[3][w], T.v[2][w], 0x07060302u)};
+        *reinterpret_cast<u32x2_t*>(vt_lds + (cb0 + 2 * w) * P::VST + t0) = lo;
+        *reinterpret_cast<u32x2_t*>(vt_lds + (cb0 + 2 * w + 1) * P::VST + t0) = hi;
+      } else if constexpr (DT == kInt4) {
+        // dword w holds channels 8w .. 8w + 7 (even in the low nibbles)
+        uint32_t ev4[4], od4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = T.v[e][w] ^ 0x88888888u;
+          ev4[e] = (x << 4) & 0xF0F0F0F0u;
+          od4[e] = x & 0xF0F0F0F0u;
+        }
+        half4_t ve[4], vo[4];
+        v_transpose4<0>(ev4[0], ev4[1], ev4[2], ev4[3], ve);
+        v_transpose4<0>(od4[0], od4[1], od4[2], od4[3], vo);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (8 * w + 2 * q < NCH)
+            *reinterpret_cast<half4_t*>(vt_lds + (cb0 + 8 * w + 2 * q) * P::VST + t0) = ve[q];
+          if (8 * w + 2 * q + 1 < NCH)
+            *reinterpret_cast<half4_t*>(vt_lds + (cb0 + 8 * w + 2 * q + 1) * P::VST + t0) = vo[q];
+        }
+      } else {
+        half4_t vb[4];
+        if constexpr (DT == kInt8)
+          v_transpose4<0>(T.v[0][w] ^ 0x80808080u, T.v[1][w] ^ 0x80808080u, T.v[2][w] ^ 0x80808080u,
+                          T.v[3][w] ^ 0x80808080u, vb);
+        else
+          v_transpose4<1>(T.v[0][w], T.v[1][w], T.v[2][w], T.v[3][w], vb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (4 * w + q < NCH) *reinterpret_cast<half4_t*>(vt_lds + (cb0 + 4 * w + q) * P::VST + t0) = vb[q];
+      }
+    }
+  }
+  if (tid < kPT) {
+    ksc[tid] = T.ks;
+    vsc[tid] = T.vs;
+  }
+}
+
+template <int DT, int MODE, int D, bool CAP>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  using P = PGeo<DT, D>;
+  constexpr int KSTEPS = P::KSTEPS;
+  constexpr int NCOL = P::NCOL;
+  constexpr int KTILE_ELEMS = kPT * P::KST;
+  constexpr int VTILE_ELEMS = D * P::VST;
+  // K tile, transposed V tile; after the loop the output staging reuses them
+  __shared__ __attribute__((aligned(16))) uint16_t lds[KTILE_ELEMS + VTILE_ELEMS];
+  __shared__ float ksc[kPT], vsc[kPT];
+  __shared__ float rowf[kWaves][16], rowsink[kWaves][16];
+  static_assert(kWaves * 16 * (D + 4) * 4 <= (int)sizeof(lds), "output staging does not fit");
+  uint16_t* ks_lds = lds;
+  uint16_t* vt_lds = lds + KTILE_ELEMS;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int hkv = blockIdx.y, b = blockIdx.z;
+  const int rbase = blockIdx.x * kPRows;       // first row of the workgroup
+  const int r = rbase + 16 * wave + n;         // this lane's query row (S^T column / P row)
+  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int pos0 = L - a.Tq;                   // position of query token 0
+
+  // rows of this lane: visible tokens lo <= t < lim
+  int lim = 0, lo = 0;
+  if (r < a.R) {
+    lim = min(pos0 + r / a.G + 1, L);
+    lo = a.window > 0 ? lim - a.window : 0;
+  }
+
+  // q operand: row r, channels 32 ks + 8 g + 0..7 (zero rows past R)
+  half8_t qb[KSTEPS];
+  float rowmul;
+  {
+    const int rr = r < a.R ? r : 0;
+    const uint16_t* src = a.q + (((size_t)b * a.Tq + rr / a.G) * a.Hq + (size_t)hkv * a.G + rr % a.G) * D;
+    u32x4_t raw[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      raw[ks] = *reinterpret_cast<const u32x4_t*>(src + 32 * ks + 8 * g);
+      if (r >= a.R) raw[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
+    if constexpr (DT == kBf16) {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = __builtin_bit_cast(half8_t, raw[ks]);
+    } else {
+      // fp16 after a power-of-two row normalization (every element in (-1, 1))
+      float qv[KSTEPS][8];
+      float amax = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x0 = __uint_as_float(raw[ks][i] << 16), x1 = __uint_as_float(raw[ks][i] & 0xFFFF0000u);
+          if constexpr (MODE == kPerChannel) {
+            const float* kst = a.c.k_scales + (size_t)hkv * D + 32 * ks + 8 * g + 2 * i;
+            x0 *= kst[0];
+            x1 *= kst[1];
+          }
+          qv[ks][2 * i] = x0;
+          qv[ks][2 * i + 1] = x1;
+          amax = fmaxf(amax, fmaxf(fabsf(x0), fabsf(x1)));
+        }
+      amax = group_max4(amax);
+      int ex = 0;
+      if (amax > 0.0f) (void)frexpf(amax, &ex);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        half8_t h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)ldexpf(qv[ks][e], -ex);
+        qb[ks] = h;
+      }
+      if constexpr (MODE == kPerTensor) mul *= a.c.k_scales[0];
+      if constexpr (DT == kInt4) mul *= 0.0625f;  // K tile holds 16 * code
+      mul = ldexpf(mul, ex);
+    }
+    rowmul = mul;
+  }
+
+  // tiles any row of the workgroup can see
+  const int rlast = min(rbase + kPRows, a.R) - 1;
+  const int pos_hi = min(pos0 + rlast / a.G, L - 1);
+  int kt_end = pos_hi >= 0 ? pos_hi / kPT + 1 : 0;
+  int kt_begin = 0;
+  if (a.window > 0) {
+    const int first = pos0 + rbase / a.G - a.window + 1;
+    kt_begin = first > 0 ? first / kPT : 0;
+  }
+  if (kt_begin > kt_end) kt_begin = kt_end;
+
+  const float cap2 = CAP ? a.softcap * 1.4426950408889634f : 0.0f;
+  const float icap2 = CAP ? 2.0f / a.softcap : 0.0f;
+  float m = -INFINITY, l = 0.0f, vref = 0x1p-126f;
+  float4_t acc[NCOL];
+#pragma unroll
+  for (int c = 0; c < NCOL; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  PTile<DT, D> T;
+  if (kt_begin < kt_end) load_ptile<DT, MODE, D>(a, b, hkv, kt_begin, L, tid, T);
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    stage_ptile<DT, MODE, D>(T, tid, ks_lds, vt_lds, ksc, vsc);
+    __syncthreads();
+    if (kt + 1 < kt_end) load_ptile<DT, MODE, D>(a, b, hkv, kt + 1, L, tid, T);
+
+    // ---- S^T for the 4 sub-tiles of 16 tokens: lane (n, g) gets tokens 4g + e of row n
+    float z[4][4];
+    bool up = false;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow = ks_lds + (16 * s + n) * P::KST + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ks += 2) {
+        const half8_t k0 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(krow + 32 * ks));
+        if constexpr (DT == kBf16) s0 = mfma32_bf16(k0, qb[ks], s0);
+        else s0 = mfma32(k0, qb[ks], s0);
+        if (ks + 1 < KSTEPS) {
+          const half8_t k1 =
+              __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(krow + 32 * (ks + 1)));
+          if constexpr (DT == kBf16) s1 = mfma32_bf16(k1, qb[ks + 1], s1);
+          else s1 = mfma32(k1, qb[ks + 1], s1);
+        }
+      }
+      const float4_t ks4 = MODE == kPerRow ? *reinterpret_cast<const float4_t*>(ksc + 16 * s + 4 * g)
+                                           : float4_t{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = kt * kPT + 16 * s + 4 * g + e;
+        float zz = (s0[e] + s1[e]) * rowmul;
+        if constexpr (MODE == kPerRow) zz *= ks4[e];
+        if constexpr (CAP) {
+          const float ex = __builtin_amdgcn_exp2f(zz * icap2);
+          zz = cap2 - 2.0f * cap2 * __builtin_amdgcn_rcpf(ex + 1.0f);
+        }
+        z[s][e] = (t < lim && t >= lo) ? zz : -INFINITY;
+        up |= z[s][e] > m;
+      }
+    }
+
+    // ---- online softmax over the tile's 64 tokens (per row n: lanes n, n+16, n+32, n+48)
+    float alpha = 1.0f, vfac = 1.0f;
+    bool rescale = false;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        tmax = fmaxf(tmax, fmaxf(fmaxf(z[s][0], z[s][1]), fmaxf(z[s][2], z[s][3])));
+      tmax = group_max4(tmax);
+      const float mnew = fmaxf(m, tmax);
+      if (mnew > m) {
+        alpha = __builtin_amdgcn_exp2f(m - mnew);
+        l *= alpha;
+        m = mnew;
+        rescale = true;
+      }
+    }
+    float vsn[4][4] = {};
+    if constexpr (kVRow) {
+      // weights carry v_scale / vref with vref a power of two >= every scale seen
+      bool vup = false;
+      float4_t vs4[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        vs4[s] = *reinterpret_cast<const float4_t*>(vsc + 16 * s + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vup |= vs4[s][e] > vref;
+      }
+      if (__builtin_amdgcn_ballot_w64(vup) != 0) {
+        float vmax = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vmax = fmaxf(vmax, vs4[s][e]);
+        vmax = wave_max(vmax);
+        int en;
+        (void)frexpf(vmax, &en);
+        const float nref = ldexpf(1.0f, en);
+        if (nref > vref) {
+          vfac = vref / nref;
+          vref = nref;
+          rescale = true;
+        }
+      }
+      const float inv = 1.0f / vref;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vsn[s][e] = vs4[s][e] * inv;
+    }
+    if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = __shfl(alpha, 4 * g + e) * vfac;
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[c][e] *= f[e];
+    }
+    const float msafe = m == -INFINITY ? 0.0f : m;
+
+    // ---- O += P . V per sub-tile
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float pf[4];
+      float psum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(z[s][e] - msafe);
+        psum += p;
+        if constexpr (kVRow)
+          pf[e] = p * vsn[s][e];
+        else
+          pf[e] = p;
+      }
+      l += psum;
+      const uint16_t* vcol = vt_lds + 16 * s + 4 * g;
+      if constexpr (DT == kBf16) {
+        uint16_t hh[4], ll[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hh[e] = f32_to_bf16(pf[e]);
+          ll[e] = f32_to_bf16(pf[e] - bf16_to_f32(hh[e]));
+        }
+        const u32x2_t phi = {hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16)};
+        const u32x2_t plo = {ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16)};
+#pragma unroll
+        for (int c = 0; c < NCOL; ++c) {
+          const u32x2_t vb = *reinterpret_cast<const u32x2_t*>(vcol + (16 * c + n) * P::VST);
+          acc[c] = mfma16_bf16(phi, vb, acc[c]);
+          acc[c] = mfma16_bf16(plo, vb, acc[c]);
+        }
+      } else {
+        half4_t ph;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ph[e] = (_Float16)pf[e];
+#pragma unroll
+        for (int c = 0; c < NCOL; ++c) {
+          const half4_t vb = *reinterpret_cast<const half4_t*>(vcol + (16 * c + n) * P::VST);
+          acc[c] = mfma16(ph, vb, acc[c]);
+        }
+      }
+    }
+    __syncthreads();  // every wavefront is done with this tile's LDS
+  }
+
+  // ---- epilogue: per row 1 / l (with the V reference and the int4 factor),
+  // the head sink, then the static V scale per channel, bf16 out
+  l = group_sum4(l);
+  if (g == 0) {
+    float f = 0.0f, sk = 1.0f;
+    if (l > 0.0f) {
+      f = 1.0f / l;
+      if constexpr (kVRow) f *= vref;           // weights carried v_scale / vref
+      if constexpr (DT == kInt4) f *= 0.0625f;  // V tile holds 16 * code
+      if (a.sink != nullptr && r < a.R) {
+        const int h = hkv * a.G + r % a.G;
+        const float lse = 0.6931471805599453f * (m + log2f(l));
+        sk = 1.0f / (1.0f + expf(a.sink[h] - lse));
+      }
+    }
+    rowf[wave][n] = f;
+    rowsink[wave][n] = sk;
+  }
+  // stage this wavefront's 16 x D block as fp32 (row stride D + 4)
+  float* ob = reinterpret_cast<float*>(lds) + wave * 16 * (D + 4);
+  __syncthreads();  // the last tile's LDS reads are done everywhere (no tile: nothing to wait for)
+#pragma unroll
+  for (int c = 0; c < NCOL; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ob[(4 * g + e) * (D + 4) + 16 * c + n] = acc[c][e];
+  __syncthreads();
+  constexpr int QPR = D / 4;  // float4 per row
+  for (int i = lane; i < 16 * QPR; i += 64) {
+    const int rr = i / QPR, d = 4 * (i % QPR);
+    const int row = rbase + 16 * wave + rr;
+    if (row >= a.R) continue;
+    const float f = rowf[wave][rr] * rowsink[wave][rr];
+    const float4_t v = *reinterpret_cast<const float4_t*>(ob + rr * (D + 4) + d);
+    uint16_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x = v[e] * f;
+      if (!kVRow && a.v_static != nullptr)
+        x *= a.vmode == kPerTensor ? a.v_static[0] : a.v_static[(size_t)hkv * D + d + e];
+      o[e] = f32_to_bf16(x);
+    }
+    const int jq = row / a.G, h = hkv * a.G + row % a.G;
+    *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.Tq + jq) * a.Hq + h) * D + d) =
+        u32x2_t{(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+  }
+}
+
+template <int DT, int MODE, int D>
+hipError_t launch_d(const PrefillArgs& a, int B, hipStream_t st) {
+  const long nx = ((long)a.R + kPRows - 1) / kPRows;
+  if (nx > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nx, a.c.Hkv, B);
+  if (a.softcap > 0.0f)
+    hipLaunchKernelGGL((prefill_kernel<DT, MODE, D, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<DT, MODE, D, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#define KVQ_PCAT2(a, b, c, d) a##b##_##c##_##d
+#define KVQ_PCAT(a, b, c, d) KVQ_PCAT2(a, b, c, d)
+
+hipError_t KVQ_PCAT(launch_prefill_, KVQ_DTYPE, KVQ_MODE, KVQ_VROW)(int D, const PrefillArgs& a, int B,
+                                                                    hipStream_t st) {
+  switch (D) {
+    case 64: return launch_d<KVQ_DTYPE, KVQ_MODE, 64>(a, B, st);
+    case 128: return launch_d<KVQ_DTYPE, KVQ_MODE, 128>(a, B, st);
+    case 256: return launch_d<KVQ_DTYPE, KVQ_MODE, 256>(a, B, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

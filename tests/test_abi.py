@@ -136,6 +136,27 @@ def test_invalid_attend_options_rejected():
                            None, 0, o, FAKE, FAKE, 1 << 30, None) == -1
 
 
+def test_invalid_prefill_rejected():
+    L = kvq.lib()
+    c = _cache()
+
+    def call(batch=1, hq=24, tq=100, msl=4096, q=FAKE, out=FAKE, k_new=FAKE, v_new=FAKE, opts=None):
+        o = None if opts is None else ctypes.byref(kvq._Options(*opts))
+        return L.kvq_prefill_attend(ctypes.byref(c), k_new, v_new, q, batch, hq, tq, FAKE, msl, 0.1,
+                                    None, None, 0, o, out, None)
+
+    assert call(hq=25) == -1          # Hq % Hkv
+    assert call(hq=36) == -2          # group of 9
+    assert call(tq=0) == -1
+    assert call(batch=2) == -1        # contiguous cache holds one sequence
+    assert call(msl=4097) == -1       # beyond the capacity
+    assert call(q=None) == -1
+    assert call(out=ctypes.c_void_p(0x50002)) == -1
+    assert call(v_new=None) == -1     # one of the new-row tensors only
+    assert call(opts=(-1.0, 0)) == -1
+    assert call(opts=(0.0, -3)) == -1
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, 5):
         assert kvq.lib().kvq_status_string(s)
