@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode µs/step + KV-read HBM GB/s, Hq24/Hkv4/D256 int8 at 64K ctx"
 PEAK_HBM_GBPS = 8000.0
+PEAK_F16_FLOPS = 2.5e15  # MI355X dense fp16 / bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_decode_int8_64k_traffic.json")
 KERNEL_SOURCES = ["quantized_kv_cache_02_amd/csrc/kvq_split.hip",
                   "quantized_kv_cache_02_amd/csrc/kvq_device.h",
@@ -227,6 +228,69 @@ def time_sdpa_bf16(torch, ctx: int, layers: int, iters: int, dev, expanded: bool
     return ms
 
 
+def prefill_flops(w) -> int:
+    """MFMA work of one chunked-prefill attention: 2 D multiply-adds for Q.K^T and
+    2 D for P.V per (query row, visible key)."""
+    pairs = 0
+    for L in w.lens:
+        L = int(L)
+        for j in range(w.Tq):
+            p = L - w.Tq + j
+            lo = max(0, p - w.window + 1) if w.window > 0 else 0
+            pairs += max(0, p + 1 - lo)
+    return 4 * w.D * w.Hq * pairs
+
+
+def time_prefill(kvq, torch, ki, dtype: str, past: int, chunk: int, layers: int, reps: int, dev):
+    """Chunked prefill of `chunk` tokens after `past` cached ones (workload-3
+    geometry), over `layers` rotated caches: kvq_prefill_attend (append + tiled
+    attention) as HIP-graph replays, and the attention kernel alone (the chunk
+    already in the cache)."""
+    w = ki.make_workload(3, ctx=past + chunk, dtype=dtype)
+    w.Tq = chunk
+    w.q = ki.randn_bf16((1, chunk, w.Hq, w.D), 777)
+    caches, table, _, _ = build_layers(kvq, torch, w, layers, dev)
+    k = w.k.to(dev)
+    v = w.v.to(dev)
+    kn = k[:, past:past + chunk].contiguous()
+    vn = v[:, past:past + chunk].contiguous()
+    q = w.q.to(dev)
+    lens = torch.from_numpy(w.lens).to(dev)
+    msl = past + chunk
+    out = torch.empty_like(q)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    res = {}
+    with torch.cuda.stream(stream):
+        for name, fused in (("step", True), ("attend", False)):
+            def run(c):
+                kvq.prefill_attend(c, q, lens, msl, w.sm_scale, k_new=kn if fused else None,
+                                   v_new=vn if fused else None, out=out, stream=stream)
+            for c in caches:
+                run(c)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for c in caches:
+                    run(c)
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / (reps * layers)
+            del g
+    del caches
+    torch.cuda.empty_cache()
+    fl = prefill_flops(w)
+    return dict(dtype=dtype, past=past, chunk=chunk, step_ms=res["step"], attend_ms=res["attend"],
+                flops=fl, attend_TFLOPs=fl / (res["attend"] * 1e-3) / 1e12,
+                step_TFLOPs=fl / (res["step"] * 1e-3) / 1e12)
+
+
 def cpu_baseline(ki, w, seconds: float):
     """The oracle as it stands on the same workload: one step = dequantize the
     layer cache to fp32, then fp64 attention.  Runs whole steps until `seconds`
@@ -270,6 +334,10 @@ def main():
                     help="time the int8 step against the same step over an unquantized bf16 "
                          "cache (this library's kernel) and torch bf16 SDPA, over the context "
                          "sweep, and write JSON lines to this file")
+    ap.add_argument("--prefill", default="",
+                    help="time chunked prefill (workload-3 geometry, int8 / int4 / bf16 "
+                         "caches, several past lengths and chunk sizes) and write JSON lines to this "
+                         "file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 20 times "
                          "(reference dispatch for HBM byte counters)")
@@ -314,6 +382,19 @@ def main():
                 f.write(json.dumps(line) + "\n")
                 f.flush()
                 print(f"[crossover] {line}", file=sys.stderr, flush=True)
+        return
+
+    if args.prefill:
+        with open(args.prefill, "w") as f:
+            for dt in ("int8", "int4", "bf16"):
+                for past, chunk in ((0, 2048), (16384, 2048), (32768, 1024), (4096, 512)):
+                    r = time_prefill(kvq, torch, ki, dt, past, chunk, 4, 8, dev)
+                    r["attend_frac_of_fp16_peak"] = r["attend_TFLOPs"] * 1e12 / PEAK_F16_FLOPS
+                    f.write(json.dumps(r) + "\n")
+                    f.flush()
+                    print(f"[prefill] {dt} past={past} chunk={chunk} step {r['step_ms']:.3f} ms "
+                          f"attend {r['attend_ms']:.3f} ms {r['attend_TFLOPs']:.0f} TFLOP/s",
+                          file=sys.stderr, flush=True)
         return
 
     if args.copy_probe_mib:
