@@ -10,13 +10,14 @@
 // (the same quantize-on-write as every other row) and then attended through
 // the cache, so a chunk sees exactly the cache a later decode sees.
 //
-// Work assignment: one workgroup per (sequence, KV head, 64 query rows), the
+// Work assignment: one workgroup per (sequence, KV head, 128 query rows), the
 // rows being the G grouped heads times the chunk's tokens (row = token * G +
-// head).  Each of the 4 wavefronts owns 16 rows.  The workgroup walks the
-// 64-token tiles its rows can see; per tile all 256 threads load the codes
-// (the next tile's loads are issued before this tile's math), unpack them once
-// into LDS -- K as fp16 rows, V transposed to channel-major -- and every
-// wavefront then runs
+// head).  Each of the 4 wavefronts owns 32 rows (two 16-row MFMA blocks, so
+// every operand read from LDS feeds two MFMAs).  The workgroup walks the
+// 64-token tiles its rows can see; per tile all 256 threads load the codes and
+// unpack them once into LDS -- K as fp16 rows, V transposed to channel-major --
+// into one of two buffers, so the next tile is loaded and unpacked while this
+// one is used (one barrier per tile), and every wavefront runs
 //   S^T = K . Q^T   v_mfma_f32_16x16x32_f16 (A: K rows from LDS, B: its q rows),
 //   online softmax over the tile's 64 tokens per row,
 //   O  += P . V     v_mfma_f32_16x16x16_f16 (A: the weights where S^T left
@@ -43,8 +44,15 @@ namespace kvq {
 namespace {
 
 constexpr bool kVRow = KVQ_VROW != 0;
-constexpr int kPT = 64;                // tokens per KV tile
-constexpr int kPRows = 16 * kWaves;    // query rows per workgroup
+constexpr int kPT = 64;  // tokens per KV tile
+// 16-row blocks per wavefront: two (every operand read from LDS feeds two
+// MFMAs) where the accumulators fit the registers beside the q operands; at
+// D = 256 two blocks pushed the accumulators into the accumulation registers
+// and the compiler copied them back and forth every tile.
+template <int D>
+constexpr int kPRowBlocks = D >= 256 ? 1 : 2;
+template <int D>
+constexpr int kPRows = 16 * kPRowBlocks<D> * kWaves;  // query rows per workgroup
 
 template <int DT, int D>
 struct PGeo {
@@ -81,52 +89,82 @@ __device__ __forceinline__ void gload(const uint8_t* p, uint32_t* out) {
   }
 }
 
-// Codes (and per-row scales) of one tile as this thread loads them.
+// Codes (and per-row scales) of one tile as this thread loads them.  Rows
+// that cannot be read are loaded from row 0 and flagged; the flags are applied
+// when the tile is unpacked, so nothing between the loads and that point waits
+// for the loaded values (the next tile's loads stay in flight under this
+// tile's math).
 template <int DT, int D>
 struct PTile {
   uint32_t k[PGeo<DT, D>::KQB / 4];
   uint32_t v[4][PGeo<DT, D>::VCW];
   float ks, vs;  // per-row scales of token tid (threads 0..63)
+  bool kok, vok[4], sok;
 };
 
-// Cache row index of position p of sequence b (-1: not readable).
-__device__ __forceinline__ long row_of(const PrefillArgs& a, int b, int hkv, int p, int L) {
-  if (p < 0 || p >= L) return -1;
-  int blk = b;
-  if (a.c.block_table != nullptr) {
-    blk = a.c.block_table[(size_t)b * a.c.max_blocks + p / a.c.block_size];
-    if ((unsigned)blk >= (unsigned)a.c.num_blocks) return -1;
+// Cache rows of one 64-token tile: block sizes are multiples of 16, so each
+// aligned group of 16 tokens lies in one block; base[sg] is the cache row of
+// token 16 * sg of the tile (-1: past the length or outside the pool).
+// Computed once per tile from uniform values (no per-token division).
+struct TileRows {
+  long base[4];
+};
+
+__device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int b, int hkv, int kt, int L) {
+  TileRows tr;
+#pragma unroll
+  for (int sg = 0; sg < 4; ++sg) {
+    const int p = kt * kPT + 16 * sg;
+    long r = -1;
+    if (p < L) {
+      if (a.c.block_table == nullptr) {
+        r = ((long)b * a.c.Hkv + hkv) * a.c.block_size + p;  // contiguous: p < L <= block_size
+      } else {
+        const int blk = a.c.block_table[(size_t)b * a.c.max_blocks + p / a.c.block_size];
+        if ((unsigned)blk < (unsigned)a.c.num_blocks)
+          r = ((long)blk * a.c.Hkv + hkv) * a.c.block_size + p % a.c.block_size;
+      }
+    }
+    tr.base[sg] = r;
   }
-  return ((long)blk * a.c.Hkv + hkv) * a.c.block_size + p % a.c.block_size;
+  return tr;
+}
+
+// Row of tile token tk (0..63), or -1.
+__device__ __forceinline__ long tile_row(const TileRows& tr, int kt, int tk, int L) {
+  const int sg = tk >> 4;
+  const long base = sg == 0 ? tr.base[0] : sg == 1 ? tr.base[1] : sg == 2 ? tr.base[2] : tr.base[3];
+  return (base < 0 || kt * kPT + tk >= L) ? -1 : base + (tk & 15);
 }
 
 template <int DT, int MODE, int D>
 __device__ __forceinline__ void load_ptile(const PrefillArgs& a, int b, int hkv, int kt, int L, int tid,
                                            PTile<DT, D>& T) {
   using P = PGeo<DT, D>;
-  // K: one row quarter per thread; unreadable rows load row 0 and are zeroed
+  const TileRows tr = tile_rows(a, b, hkv, kt, L);
+  // K: one row quarter per thread
   {
-    const long ri = row_of(a, b, hkv, kt * kPT + tid / 4, L);
+    const long ri = tile_row(tr, kt, tid / 4, L);
+    T.kok = ri >= 0;
     gload<P::KQB>(a.c.k_codes + (ri < 0 ? 0 : ri) * P::ROWB + P::KQB * (tid % 4), T.k);
-    if (ri < 0)
-#pragma unroll
-      for (int i = 0; i < P::KQB / 4; ++i) T.k[i] = 0u;
   }
   // V: 4 tokens of one channel chunk
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const long ri = row_of(a, b, hkv, kt * kPT + 4 * (tid % 16) + e, L);
-    uint32_t w[P::VCW] = {};
-    gload<P::VCB>(a.c.v_codes + (ri < 0 ? 0 : ri) * P::ROWB + P::VCB * (tid / 16), w);
-#pragma unroll
-    for (int i = 0; i < P::VCW; ++i) T.v[e][i] = ri < 0 ? 0u : w[i];
+    const long ri = tile_row(tr, kt, 4 * (tid % 16) + e, L);
+    T.vok[e] = ri >= 0;
+    if constexpr (P::VCB < 4) T.v[e][0] = 0u;  // the load fills the low bytes only
+    gload<P::VCB>(a.c.v_codes + (ri < 0 ? 0 : ri) * P::ROWB + P::VCB * (tid / 16), T.v[e]);
   }
-  T.ks = 0.0f;
-  T.vs = 0.0f;
-  if (tid < kPT) {
-    const long ri = row_of(a, b, hkv, kt * kPT + tid, L);
-    if constexpr (MODE == kPerRow) T.ks = ri < 0 ? 0.0f : a.c.k_scales[ri];
-    if constexpr (kVRow) T.vs = ri < 0 ? 0.0f : a.c.v_scales[ri];
+  // per-row scales of token tid % 64 (every thread loads; threads 0..63 store)
+  {
+    const long ri = tile_row(tr, kt, tid % kPT, L);
+    T.sok = ri >= 0;
+    const long rs = ri < 0 ? 0 : ri;
+    T.ks = 0.0f;
+    T.vs = 0.0f;
+    if constexpr (MODE == kPerRow) T.ks = __builtin_nontemporal_load(a.c.k_scales + rs);
+    if constexpr (kVRow) T.vs = __builtin_nontemporal_load(a.c.v_scales + rs);
   }
 }
 
@@ -156,18 +194,19 @@ __device__ __forceinline__ void stage_ptile(const PTile<DT, D>& T, int tid, uint
     constexpr int NW = P::KQB / 4;  // dwords loaded
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
+      const uint32_t kw = T.kok ? T.k[i] : 0u;
       if constexpr (DT == kBf16) {
-        reinterpret_cast<uint32_t*>(dst)[i] = T.k[i];
+        reinterpret_cast<uint32_t*>(dst)[i] = kw;
       } else if constexpr (DT == kInt4) {
         uint32_t h[4];
-        int4x8_to_h_ordered(T.k[i], h);
+        int4x8_to_h_ordered(kw, h);
         *reinterpret_cast<u32x4_t*>(dst + 8 * i) = u32x4_t{h[0], h[1], h[2], h[3]};
       } else {
         uint32_t lo, hi;
         if constexpr (DT == kInt8)
-          int8x4_to_h(T.k[i], lo, hi);
+          int8x4_to_h(kw, lo, hi);
         else
-          fp8x4_to_h(T.k[i], lo, hi);
+          fp8x4_to_h(kw, lo, hi);
         *reinterpret_cast<u32x2_t*>(dst + 4 * i) = u32x2_t{lo, hi};
       }
     }
@@ -176,12 +215,17 @@ __device__ __forceinline__ void stage_ptile(const PTile<DT, D>& T, int tid, uint
     // channels [cb0, cb0 + D / 16) of tokens t0 .. t0 + 3
     const int cb0 = (D / 16) * (tid / 16), t0 = 4 * (tid % 16);
     constexpr int NCH = D / 16;  // channels of this thread
+    uint32_t vv[4][P::VCW];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < P::VCW; ++i) vv[e][i] = T.vok[e] ? T.v[e][i] : 0u;
 #pragma unroll
     for (int w = 0; w < P::VCW; ++w) {
       if constexpr (DT == kBf16) {
         // dword w holds channels 2w, 2w + 1
-        const u32x2_t lo = {perm(T.v[1][w], T.v[0][w], 0x05040100u), perm(T.v[3][w], T.v[2][w], 0x05040100u)};
-        const u32x2_t hi = {perm(T.v[1][w], T.v[0][w], 0x07060302u), perm(T.v[3][w], T.v[2][w], 0x07060302u)};
+        const u32x2_t lo = {perm(vv[1][w], vv[0][w], 0x05040100u), perm(vv[3][w], vv[2][w], 0x05040100u)};
+        const u32x2_t hi = {perm(vv[1][w], vv[0][w], 0x07060302u), perm(vv[3][w], vv[2][w], 0x07060302u)};
         *reinterpret_cast<u32x2_t*>(vt_lds + (cb0 + 2 * w) * P::VST + t0) = lo;
         *reinterpret_cast<u32x2_t*>(vt_lds + (cb0 + 2 * w + 1) * P::VST + t0) = hi;
       } else if constexpr (DT == kInt4) {
@@ -189,7 +233,7 @@ __device__ __forceinline__ void stage_ptile(const PTile<DT, D>& T, int tid, uint
         uint32_t ev4[4], od4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t x = T.v[e][w] ^ 0x88888888u;
+          const uint32_t x = vv[e][w] ^ 0x88888888u;
           ev4[e] = (x << 4) & 0xF0F0F0F0u;
           od4[e] = x & 0xF0F0F0F0u;
         }
@@ -206,10 +250,10 @@ __device__ __forceinline__ void stage_ptile(const PTile<DT, D>& T, int tid, uint
       } else {
         half4_t vb[4];
         if constexpr (DT == kInt8)
-          v_transpose4<0>(T.v[0][w] ^ 0x80808080u, T.v[1][w] ^ 0x80808080u, T.v[2][w] ^ 0x80808080u,
-                          T.v[3][w] ^ 0x80808080u, vb);
+          v_transpose4<0>(vv[0][w] ^ 0x80808080u, vv[1][w] ^ 0x80808080u, vv[2][w] ^ 0x80808080u,
+                          vv[3][w] ^ 0x80808080u, vb);
         else
-          v_transpose4<1>(T.v[0][w], T.v[1][w], T.v[2][w], T.v[3][w], vb);
+          v_transpose4<1>(vv[0][w], vv[1][w], vv[2][w], vv[3][w], vb);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (4 * w + q < NCH) *reinterpret_cast<half4_t*>(vt_lds + (cb0 + 4 * w + q) * P::VST + t0) = vb[q];
@@ -217,47 +261,76 @@ __device__ __forceinline__ void stage_ptile(const PTile<DT, D>& T, int tid, uint
     }
   }
   if (tid < kPT) {
-    ksc[tid] = T.ks;
-    vsc[tid] = T.vs;
+    ksc[tid] = T.sok ? T.ks : 0.0f;
+    vsc[tid] = T.sok ? T.vs : 0.0f;
   }
 }
 
 template <int DT, int MODE, int D, bool CAP>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) void prefill_kernel(
+    PrefillArgs a) {
   using P = PGeo<DT, D>;
   constexpr int KSTEPS = P::KSTEPS;
   constexpr int NCOL = P::NCOL;
+  constexpr int RBW = kPRowBlocks<D>;
+  constexpr int kRows = kPRows<D>;
   constexpr int KTILE_ELEMS = kPT * P::KST;
   constexpr int VTILE_ELEMS = D * P::VST;
-  // K tile, transposed V tile; after the loop the output staging reuses them
-  __shared__ __attribute__((aligned(16))) uint16_t lds[KTILE_ELEMS + VTILE_ELEMS];
-  __shared__ float ksc[kPT], vsc[kPT];
-  __shared__ float rowf[kWaves][16], rowsink[kWaves][16];
-  static_assert(kWaves * 16 * (D + 4) * 4 <= (int)sizeof(lds), "output staging does not fit");
-  uint16_t* ks_lds = lds;
-  uint16_t* vt_lds = lds + KTILE_ELEMS;
+  constexpr int BUF_ELEMS = KTILE_ELEMS + VTILE_ELEMS;
+  // two tile buffers (K rows, transposed V): one is read while the next tile
+  // is unpacked into the other; after the loop the output staging reuses them
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF_ELEMS];
+  __shared__ float ksc[2][kPT], vsc[2][kPT];
+  __shared__ float rowf[kWaves][16 * RBW], rowsink[kWaves][16 * RBW];
+  static_assert(kWaves * 16 * RBW * (D + 4) * 4 <= (int)sizeof(lds), "output staging does not fit");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
   const int hkv = blockIdx.y, b = blockIdx.z;
-  const int rbase = blockIdx.x * kPRows;       // first row of the workgroup
-  const int r = rbase + 16 * wave + n;         // this lane's query row (S^T column / P row)
+  const int rbase = blockIdx.x * kRows;        // first row of the workgroup
+  const int rwave = rbase + 16 * RBW * wave;   // first row of this wavefront
   const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
   const int pos0 = L - a.Tq;                   // position of query token 0
 
-  // rows of this lane: visible tokens lo <= t < lim
-  int lim = 0, lo = 0;
-  if (r < a.R) {
-    lim = min(pos0 + r / a.G + 1, L);
-    lo = a.window > 0 ? lim - a.window : 0;
+  // rows rwave + 16 rb + n of this lane: visible tokens lo <= t < lim
+  int lim[RBW], lo[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    const int r = rwave + 16 * rb + n;
+    lim[rb] = 0;
+    lo[rb] = 0;
+    if (r < a.R) {
+      lim[rb] = min(pos0 + r / a.G + 1, L);
+      lo[rb] = a.window > 0 ? lim[rb] - a.window : 0;
+    }
   }
 
+  // the wavefront's tightest bounds over its rows (rows past R are never
+  // written, so they do not constrain it): a tile inside [wlo_max, wlim_min)
+  // needs no mask
+  int wlim_min = 0x7FFFFFFF, wlo_max = 0;
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    const bool valid = rwave + 16 * rb + n < a.R;
+    wlim_min = min(wlim_min, valid ? lim[rb] : 0x7FFFFFFF);
+    wlo_max = max(wlo_max, valid ? lo[rb] : 0);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    wlim_min = min(wlim_min, __shfl_xor(wlim_min, o));
+    wlo_max = max(wlo_max, __shfl_xor(wlo_max, o));
+  }
+  wlim_min = __builtin_amdgcn_readfirstlane(wlim_min);
+  wlo_max = __builtin_amdgcn_readfirstlane(wlo_max);
+
   // q operand: row r, channels 32 ks + 8 g + 0..7 (zero rows past R)
-  half8_t qb[KSTEPS];
-  float rowmul;
-  {
+  half8_t qb[RBW][KSTEPS];
+  float rowmul[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    const int r = rwave + 16 * rb + n;
     const int rr = r < a.R ? r : 0;
     const uint16_t* src = a.q + (((size_t)b * a.Tq + rr / a.G) * a.Hq + (size_t)hkv * a.G + rr % a.G) * D;
     u32x4_t raw[KSTEPS];
@@ -269,7 +342,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
     if constexpr (DT == kBf16) {
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) qb[ks] = __builtin_bit_cast(half8_t, raw[ks]);
+      for (int ks = 0; ks < KSTEPS; ++ks) qb[rb][ks] = __builtin_bit_cast(half8_t, raw[ks]);
     } else {
       // fp16 after a power-of-two row normalization (every element in (-1, 1))
       float qv[KSTEPS][8];
@@ -296,19 +369,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         half8_t h;
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = (_Float16)ldexpf(qv[ks][e], -ex);
-        qb[ks] = h;
+        qb[rb][ks] = h;
       }
       if constexpr (MODE == kPerTensor) mul *= a.c.k_scales[0];
       if constexpr (DT == kInt4) mul *= 0.0625f;  // K tile holds 16 * code
       mul = ldexpf(mul, ex);
     }
-    rowmul = mul;
+    rowmul[rb] = mul;
   }
 
   // tiles any row of the workgroup can see
-  const int rlast = min(rbase + kPRows, a.R) - 1;
+  const int rlast = min(rbase + kRows, a.R) - 1;
   const int pos_hi = min(pos0 + rlast / a.G, L - 1);
-  int kt_end = pos_hi >= 0 ? pos_hi / kPT + 1 : 0;
+  const int kt_end = pos_hi >= 0 ? pos_hi / kPT + 1 : 0;
   int kt_begin = 0;
   if (a.window > 0) {
     const int first = pos0 + rbase / a.G - a.window + 1;
@@ -318,68 +391,123 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
   const float cap2 = CAP ? a.softcap * 1.4426950408889634f : 0.0f;
   const float icap2 = CAP ? 2.0f / a.softcap : 0.0f;
-  float m = -INFINITY, l = 0.0f, vref = 0x1p-126f;
-  float4_t acc[NCOL];
+  float m[RBW], l[RBW];
+  float vref = 0x1p-126f;
+  float4_t acc[RBW][NCOL];
 #pragma unroll
-  for (int c = 0; c < NCOL; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RBW; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCOL; ++c) acc[rb][c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   PTile<DT, D> T;
-  if (kt_begin < kt_end) load_ptile<DT, MODE, D>(a, b, hkv, kt_begin, L, tid, T);
+  if (kt_begin < kt_end) {
+    load_ptile<DT, MODE, D>(a, b, hkv, kt_begin, L, tid, T);
+    stage_ptile<DT, MODE, D>(T, tid, lds, lds + KTILE_ELEMS, ksc[0], vsc[0]);
+  }
+  __syncthreads();
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    stage_ptile<DT, MODE, D>(T, tid, ks_lds, vt_lds, ksc, vsc);
-    __syncthreads();
-    if (kt + 1 < kt_end) load_ptile<DT, MODE, D>(a, b, hkv, kt + 1, L, tid, T);
+    const int cur = (kt - kt_begin) & 1;
+    const bool more = kt + 1 < kt_end;
+    if (more) load_ptile<DT, MODE, D>(a, b, hkv, kt + 1, L, tid, T);
+    const uint16_t* ks_lds = lds + cur * BUF_ELEMS;
+    const uint16_t* vt_lds = ks_lds + KTILE_ELEMS;
 
-    // ---- S^T for the 4 sub-tiles of 16 tokens: lane (n, g) gets tokens 4g + e of row n
-    float z[4][4];
+    // ---- S^T for the 4 sub-tiles of 16 tokens: lane (n, g) gets tokens 4g + e
+    // of its rows.  The K operands of sub-tile s + 1 are read from LDS before
+    // sub-tile s's MFMAs in source order (the compiler schedules them).
+    float z[RBW][4][4];
     bool up = false;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    half8_t kop[2][KSTEPS];
+    auto kread = [&](int s, half8_t (&dst)[KSTEPS]) {
       const uint16_t* krow = ks_lds + (16 * s + n) * P::KST + 8 * g;
 #pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        dst[ks] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(krow + 32 * ks));
+    };
+    kread(0, kop[0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s + 1 < 4) kread(s + 1, kop[(s + 1) & 1]);
+      float4_t s0[RBW], s1[RBW];
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        s0[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+        s1[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
       for (int ks = 0; ks < KSTEPS; ks += 2) {
-        const half8_t k0 = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(krow + 32 * ks));
-        if constexpr (DT == kBf16) s0 = mfma32_bf16(k0, qb[ks], s0);
-        else s0 = mfma32(k0, qb[ks], s0);
-        if (ks + 1 < KSTEPS) {
-          const half8_t k1 =
-              __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(krow + 32 * (ks + 1)));
-          if constexpr (DT == kBf16) s1 = mfma32_bf16(k1, qb[ks + 1], s1);
-          else s1 = mfma32(k1, qb[ks + 1], s1);
+        const half8_t k0 = kop[s & 1][ks];
+        const half8_t k1 = kop[s & 1][ks + 1 < KSTEPS ? ks + 1 : ks];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+          if constexpr (DT == kBf16) {
+            s0[rb] = mfma32_bf16(k0, qb[rb][ks], s0[rb]);
+            if (ks + 1 < KSTEPS) s1[rb] = mfma32_bf16(k1, qb[rb][ks + 1], s1[rb]);
+          } else {
+            s0[rb] = mfma32(k0, qb[rb][ks], s0[rb]);
+            if (ks + 1 < KSTEPS) s1[rb] = mfma32(k1, qb[rb][ks + 1], s1[rb]);
+          }
         }
       }
-      const float4_t ks4 = MODE == kPerRow ? *reinterpret_cast<const float4_t*>(ksc + 16 * s + 4 * g)
+      const float4_t ks4 = MODE == kPerRow ? *reinterpret_cast<const float4_t*>(&ksc[cur][16 * s + 4 * g])
                                            : float4_t{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = kt * kPT + 16 * s + 4 * g + e;
-        float zz = (s0[e] + s1[e]) * rowmul;
-        if constexpr (MODE == kPerRow) zz *= ks4[e];
-        if constexpr (CAP) {
-          const float ex = __builtin_amdgcn_exp2f(zz * icap2);
-          zz = cap2 - 2.0f * cap2 * __builtin_amdgcn_rcpf(ex + 1.0f);
+      for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float zz = (s0[rb][e] + s1[rb][e]) * rowmul[rb];
+          if constexpr (MODE == kPerRow) zz *= ks4[e];
+          if constexpr (CAP) {
+            const float ex = __builtin_amdgcn_exp2f(zz * icap2);
+            zz = cap2 - 2.0f * cap2 * __builtin_amdgcn_rcpf(ex + 1.0f);
+          }
+          z[rb][s][e] = zz;
         }
-        z[s][e] = (t < lim && t >= lo) ? zz : -INFINITY;
-        up |= z[s][e] > m;
-      }
     }
-
-    // ---- online softmax over the tile's 64 tokens (per row n: lanes n, n+16, n+32, n+48)
-    float alpha = 1.0f, vfac = 1.0f;
-    bool rescale = false;
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
-      float tmax = -INFINITY;
+    // causal / window / length mask, skipped on tiles every row of the
+    // wavefront sees whole
+    if (!(kt * kPT + kPT <= wlim_min && kt * kPT >= wlo_max)) {
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = kt * kPT + 16 * s + 4 * g + e;
+            if (!(t < lim[rb] && t >= lo[rb])) z[rb][s][e] = -INFINITY;
+          }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        tmax = fmaxf(tmax, fmaxf(fmaxf(z[s][0], z[s][1]), fmaxf(z[s][2], z[s][3])));
-      tmax = group_max4(tmax);
-      const float mnew = fmaxf(m, tmax);
-      if (mnew > m) {
-        alpha = __builtin_amdgcn_exp2f(m - mnew);
-        l *= alpha;
-        m = mnew;
-        rescale = true;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) up |= z[rb][s][e] > m[rb];
+
+    // ---- online softmax over the tile's 64 tokens (row n: lanes n, n+16, n+32, n+48)
+    float alpha[RBW];
+    float vfac = 1.0f;
+    bool rescale = false;
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) alpha[rb] = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          tmax = fmaxf(tmax, fmaxf(fmaxf(z[rb][s][0], z[rb][s][1]), fmaxf(z[rb][s][2], z[rb][s][3])));
+        tmax = group_max4(tmax);
+        const float mnew = fmaxf(m[rb], tmax);
+        if (mnew > m[rb]) {
+          alpha[rb] = __builtin_amdgcn_exp2f(m[rb] - mnew);
+          l[rb] *= alpha[rb];
+          m[rb] = mnew;
+          rescale = true;
+        }
       }
     }
     float vsn[4][4] = {};
@@ -389,7 +517,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       float4_t vs4[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        vs4[s] = *reinterpret_cast<const float4_t*>(vsc + 16 * s + 4 * g);
+        vs4[s] = *reinterpret_cast<const float4_t*>(&vsc[cur][16 * s + 4 * g]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) vup |= vs4[s][e] > vref;
       }
@@ -416,91 +544,118 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         for (int e = 0; e < 4; ++e) vsn[s][e] = vs4[s][e] * inv;
     }
     if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
-      float f[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] = __shfl(alpha, 4 * g + e) * vfac;
+      for (int rb = 0; rb < RBW; ++rb) {
+        float f[4];
 #pragma unroll
-      for (int c = 0; c < NCOL; ++c)
+        for (int e = 0; e < 4; ++e) f[e] = __shfl(alpha[rb], 4 * g + e) * vfac;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[c][e] *= f[e];
+        for (int c = 0; c < NCOL; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rb][c][e] *= f[e];
+      }
     }
-    const float msafe = m == -INFINITY ? 0.0f : m;
 
     // ---- O += P . V per sub-tile
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      float pf[4];
-      float psum = 0.0f;
+      half4_t ph[RBW];
+      u32x2_t phi[RBW], plo[RBW];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(z[s][e] - msafe);
-        psum += p;
-        if constexpr (kVRow)
-          pf[e] = p * vsn[s][e];
-        else
-          pf[e] = p;
-      }
-      l += psum;
-      const uint16_t* vcol = vt_lds + 16 * s + 4 * g;
-      if constexpr (DT == kBf16) {
-        uint16_t hh[4], ll[4];
+      for (int rb = 0; rb < RBW; ++rb) {
+        const float msafe = m[rb] == -INFINITY ? 0.0f : m[rb];
+        float pf[4];
+        float psum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          hh[e] = f32_to_bf16(pf[e]);
-          ll[e] = f32_to_bf16(pf[e] - bf16_to_f32(hh[e]));
+          const float p = __builtin_amdgcn_exp2f(z[rb][s][e] - msafe);
+          psum += p;
+          if constexpr (kVRow)
+            pf[e] = p * vsn[s][e];
+          else
+            pf[e] = p;
         }
-        const u32x2_t phi = {hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16)};
-        const u32x2_t plo = {ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16)};
+        l[rb] += psum;
+        if constexpr (DT == kBf16) {
+          uint16_t hh[4], ll[4];
 #pragma unroll
-        for (int c = 0; c < NCOL; ++c) {
-          const u32x2_t vb = *reinterpret_cast<const u32x2_t*>(vcol + (16 * c + n) * P::VST);
-          acc[c] = mfma16_bf16(phi, vb, acc[c]);
-          acc[c] = mfma16_bf16(plo, vb, acc[c]);
+          for (int e = 0; e < 4; ++e) {
+            hh[e] = f32_to_bf16(pf[e]);
+            ll[e] = f32_to_bf16(pf[e] - bf16_to_f32(hh[e]));
+          }
+          phi[rb] = u32x2_t{hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16)};
+          plo[rb] = u32x2_t{ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16)};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ph[rb][e] = (_Float16)pf[e];
         }
-      } else {
-        half4_t ph;
+      }
+      // all of the sub-tile's V operands first, so their LDS latencies overlap
+      const uint16_t* vcol = vt_lds + 16 * s + 4 * g;
+      u32x2_t vop[NCOL];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ph[e] = (_Float16)pf[e];
+      for (int c = 0; c < NCOL; ++c) vop[c] = *reinterpret_cast<const u32x2_t*>(vcol + (16 * c + n) * P::VST);
 #pragma unroll
-        for (int c = 0; c < NCOL; ++c) {
-          const half4_t vb = *reinterpret_cast<const half4_t*>(vcol + (16 * c + n) * P::VST);
-          acc[c] = mfma16(ph, vb, acc[c]);
+      for (int c = 0; c < NCOL; ++c) {
+        if constexpr (DT == kBf16) {
+          const u32x2_t vb = vop[c];
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+            acc[rb][c] = mfma16_bf16(phi[rb], vb, acc[rb][c]);
+            acc[rb][c] = mfma16_bf16(plo[rb], vb, acc[rb][c]);
+          }
+        } else {
+          const half4_t vb = __builtin_bit_cast(half4_t, vop[c]);
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) acc[rb][c] = mfma16(ph[rb], vb, acc[rb][c]);
         }
       }
     }
-    __syncthreads();  // every wavefront is done with this tile's LDS
+
+    // unpack the next tile into the other buffer (nobody reads it during this
+    // tile), then one barrier: it is complete, and this tile's buffer is free
+    if (more)
+      stage_ptile<DT, MODE, D>(T, tid, lds + (cur ^ 1) * BUF_ELEMS, lds + (cur ^ 1) * BUF_ELEMS + KTILE_ELEMS,
+                               ksc[cur ^ 1], vsc[cur ^ 1]);
+    __syncthreads();
   }
 
   // ---- epilogue: per row 1 / l (with the V reference and the int4 factor),
   // the head sink, then the static V scale per channel, bf16 out
-  l = group_sum4(l);
-  if (g == 0) {
-    float f = 0.0f, sk = 1.0f;
-    if (l > 0.0f) {
-      f = 1.0f / l;
-      if constexpr (kVRow) f *= vref;           // weights carried v_scale / vref
-      if constexpr (DT == kInt4) f *= 0.0625f;  // V tile holds 16 * code
-      if (a.sink != nullptr && r < a.R) {
-        const int h = hkv * a.G + r % a.G;
-        const float lse = 0.6931471805599453f * (m + log2f(l));
-        sk = 1.0f / (1.0f + expf(a.sink[h] - lse));
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    const float lt = group_sum4(l[rb]);
+    if (g == 0) {
+      const int r = rwave + 16 * rb + n;
+      float f = 0.0f, sk = 1.0f;
+      if (lt > 0.0f) {
+        f = 1.0f / lt;
+        if constexpr (kVRow) f *= vref;           // weights carried v_scale / vref
+        if constexpr (DT == kInt4) f *= 0.0625f;  // V tile holds 16 * code
+        if (a.sink != nullptr && r < a.R) {
+          const int h = hkv * a.G + r % a.G;
+          const float lse = 0.6931471805599453f * (m[rb] + log2f(lt));
+          sk = 1.0f / (1.0f + expf(a.sink[h] - lse));
+        }
       }
+      rowf[wave][16 * rb + n] = f;
+      rowsink[wave][16 * rb + n] = sk;
     }
-    rowf[wave][n] = f;
-    rowsink[wave][n] = sk;
   }
-  // stage this wavefront's 16 x D block as fp32 (row stride D + 4)
-  float* ob = reinterpret_cast<float*>(lds) + wave * 16 * (D + 4);
-  __syncthreads();  // the last tile's LDS reads are done everywhere (no tile: nothing to wait for)
+  // stage this wavefront's rows as fp32 (row stride D + 4); the loop ended
+  // with a barrier, so the tile buffers are free
+  float* ob = reinterpret_cast<float*>(lds) + wave * 16 * RBW * (D + 4);
 #pragma unroll
-  for (int c = 0; c < NCOL; ++c)
+  for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ob[(4 * g + e) * (D + 4) + 16 * c + n] = acc[c][e];
+    for (int c = 0; c < NCOL; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ob[(16 * rb + 4 * g + e) * (D + 4) + 16 * c + n] = acc[rb][c][e];
   __syncthreads();
   constexpr int QPR = D / 4;  // float4 per row
-  for (int i = lane; i < 16 * QPR; i += 64) {
+  for (int i = lane; i < 16 * RBW * QPR; i += 64) {
     const int rr = i / QPR, d = 4 * (i % QPR);
-    const int row = rbase + 16 * wave + rr;
+    const int row = rwave + rr;
     if (row >= a.R) continue;
     const float f = rowf[wave][rr] * rowsink[wave][rr];
     const float4_t v = *reinterpret_cast<const float4_t*>(ob + rr * (D + 4) + d);
@@ -520,7 +675,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
 template <int DT, int MODE, int D>
 hipError_t launch_d(const PrefillArgs& a, int B, hipStream_t st) {
-  const long nx = ((long)a.R + kPRows - 1) / kPRows;
+  const long nx = ((long)a.R + kPRows<D> - 1) / kPRows<D>;
   if (nx > 0x7FFFFFFFL) return hipErrorInvalidValue;
   dim3 grid((unsigned)nx, a.c.Hkv, B);
   if (a.softcap > 0.0f)
