@@ -148,3 +148,55 @@ def test_prefill_large_chunk_sampled():
         ref, _ = oracle.attend(qb[:, j:j + 1], K, V, np.array([p + 1], np.int32), w.sm_scale, None,
                                w.Hkv)
         gu.check_output(out[:, j:j + 1], ref, f"large chunk, token {j}")
+
+
+def test_prefill_attend_only_after_append():
+    """kvq_prefill_attend without new rows: the chunk was written by kvq_append."""
+    w = ki.random_workload(8600, B=2, Hkv=2, G=4, D=128, Tq=50, lens=[400, 60], dtype=INT8,
+                           mode=PER_ROW, block_size=16, sink=True)
+    cache = gu.gpu_cache(w)
+    table = gu.gpu_build(w, cache)  # every row, the chunk included
+    out = kvq.prefill_attend(cache, w.q.cuda(), torch.from_numpy(w.lens).cuda(), int(w.lens.max()),
+                             w.sm_scale, block_table=table, head_sink=torch.from_numpy(w.sink).cuda())
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.reference(w)
+    gu.check_output(out, ref, "prefill, attention only")
+
+
+def test_prefill_graph_replays_equal_eager():
+    """Append + prefill captured in a HIP graph and replayed: every replay writes
+    the same cache bytes and the same output as the eager call (the append of
+    the chunk is idempotent)."""
+    w = ki.random_workload(8700, B=2, Hkv=2, G=3, D=256, Tq=40, lens=[500, 45], dtype=FP8,
+                           mode=PER_TENSOR, block_size=16)
+    eager, cache = _run_prefill(w)
+    codes = cache.k_codes.clone()
+    dev = "cuda"
+    table = torch.from_numpy(w.block_table).to(dev)
+    kn = torch.zeros(w.B, w.Tq, w.Hkv, w.D, dtype=torch.bfloat16)
+    vn = torch.zeros_like(kn)
+    for b in range(w.B):
+        L = int(w.lens[b])
+        kn[b] = w.k[b, L - w.Tq:L]
+        vn[b] = w.v[b, L - w.Tq:L]
+    kn, vn = kn.to(dev), vn.to(dev)
+    q = w.q.to(dev)
+    lens = torch.from_numpy(w.lens).to(dev)
+    out = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kvq.prefill_attend(cache, q, lens, int(w.lens.max()), w.sm_scale, k_new=kn, v_new=vn,
+                           block_table=table, out=out, stream=s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            kvq.prefill_attend(cache, q, lens, int(w.lens.max()), w.sm_scale, k_new=kn, v_new=vn,
+                               block_table=table, out=out, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(cache.k_codes, codes), f"replay {rep} cache"
