@@ -130,6 +130,14 @@ __device__ __forceinline__ float4_t mfma16_bf16(u32x2_t a, u32x2_t b, float4_t c
                                                    __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
 }
 
+// Integer MFMA 16x16x64 i8: each lane holds 16 bytes of A (row l%16) and of B
+// (column l%16); within a lane group l/16 the A and B bytes at the same
+// position meet the same k (checked on gfx950), and C has the f32 layout.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t mfma64_i8(i32x4_t a, i32x4_t b, i32x4_t c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ half4_t u2_to_h4(uint32_t a, uint32_t b) {
   u32x2_t v = {a, b};
   return __builtin_bit_cast(half4_t, v);

@@ -69,6 +69,11 @@ struct Geo {
   static constexpr int KNCH = KLB / KCH;
   static constexpr int KDW = KLB / 4;      // dwords of K codes per lane
   static constexpr int KSTEPS = D / 32;    // 16x16x32 MFMAs per row block
+  // The integer caches take S^T on the int8 MFMA: the K codes are its A operand
+  // as loaded (int4 nibbles moved to the high half of a byte, 16 * code), q the
+  // B operand in two int8 halves.  16x16x64 steps per row block (and half):
+  static constexpr bool IQK = DT == kInt8 || DT == kInt4;
+  static constexpr int ISTEPS = D / 64;
   // V tile, lane (column j = l%16, group g = l/16): rows 4g..4g+3, VLB bytes
   // of each row, read as VNCH chunks of VCH bytes at row offsets VCH*(j+16c);
   // a load instruction covers 4 whole rows (or 4 whole 256-byte spans).
@@ -97,6 +102,24 @@ __device__ __forceinline__ int k_channel(int ks, int g, int e) {
   } else {
     const int w = 2 * ks + (e >> 2);
     return G_::KCH * (4 * (w / DPC) + g) + 4 * (w % DPC) + (e & 3);
+  }
+}
+
+// Channel d that byte p (0..15) of integer k-step s holds in lane group g, for
+// both operands of the int8 S^T MFMA.  int8: the 16 bytes are the lane's K
+// dwords 4s..4s+3; int4: the even and odd nibbles of dwords 2s and 2s+1, as
+// (even 2s, odd 2s, even 2s+1, odd 2s+1).  Either way 16 consecutive channels.
+template <int DT, int D>
+__device__ __forceinline__ int k_channel_i8(int s, int g, int p) {
+  using G_ = Geo<DT, D>;
+  constexpr int DPC = G_::KCH / 4;  // dwords per chunk
+  if constexpr (DT == kInt4) {
+    const int j = p / 4, w = 2 * s + j / 2;
+    const int byteoff = G_::KCH * (4 * (w / DPC) + g) + 4 * (w % DPC) + p % 4;
+    return 2 * byteoff + (j & 1);
+  } else {
+    const int w = 4 * s + p / 4;
+    return G_::KCH * (4 * (w / DPC) + g) + 4 * (w % DPC) + p % 4;
   }
 }
 
@@ -199,6 +222,20 @@ __device__ __forceinline__ half8_t k_operand(const uint32_t* kw, int ks) {
     fp8x4_to_h(kw[2 * ks + 1], h[2], h[3]);
   }
   return u4_to_h8(h[0], h[1], h[2], h[3]);
+}
+
+// The lane's K codes of integer k-step s as the int8 A operand: int8 codes as
+// they are; int4 nibbles n as the bytes 16 n (two's complement nibble in the
+// high half), even nibbles then odd ones of each dword.
+template <int DT, int D>
+__device__ __forceinline__ i32x4_t k_operand_i8(const uint32_t* kw, int s) {
+  if constexpr (DT == kInt4) {
+    const uint32_t x = kw[2 * s], y = kw[2 * s + 1];
+    return i32x4_t{(int)((x << 4) & 0xF0F0F0F0u), (int)(x & 0xF0F0F0F0u),
+                   (int)((y << 4) & 0xF0F0F0F0u), (int)(y & 0xF0F0F0F0u)};
+  } else {
+    return i32x4_t{(int)kw[4 * s], (int)kw[4 * s + 1], (int)kw[4 * s + 2], (int)kw[4 * s + 3]};
+  }
 }
 
 // Codes and scales of one 16-token tile as this lane holds them.
@@ -356,21 +393,38 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
     int qo = rb * G_::KSTEPS * 64;
     if constexpr (QLDS) asm volatile("" : "+v"(qo));
     auto qop = [&](int k) { return QLDS ? qlds[qo + 64 * k] : qb[rb][k]; };
+    float dot[4];
+    if constexpr (G_::IQK) {
+      // exact integer dot products with the high and low query halves
+      // (qb[rb][2s], qb[rb][2s+1]); their sum hi * 256 + lo stays below 2^30
+      i32x4_t h = {0, 0, 0, 0}, l = {0, 0, 0, 0};
 #pragma unroll
-    for (int ks = 0; ks < G_::KSTEPS; ks += 2) {
-      if constexpr (DT == kBf16) {
-        s0 = mfma32_bf16(k_operand<DT, D>(T.kw, ks), qop(ks), s0);
-        if (ks + 1 < G_::KSTEPS) s1 = mfma32_bf16(k_operand<DT, D>(T.kw, ks + 1), qop(ks + 1), s1);
-      } else {
-        s0 = mfma32(k_operand<DT, D>(T.kw, ks), qop(ks), s0);
-        if (ks + 1 < G_::KSTEPS) s1 = mfma32(k_operand<DT, D>(T.kw, ks + 1), qop(ks + 1), s1);
+      for (int st = 0; st < G_::ISTEPS; ++st) {
+        const i32x4_t ka = k_operand_i8<DT, D>(T.kw, st);
+        h = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qb[rb][2 * st]), h);
+        l = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qb[rb][2 * st + 1]), l);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot[e] = (float)(h[e] * 256 + l[e]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < G_::KSTEPS; ks += 2) {
+        if constexpr (DT == kBf16) {
+          s0 = mfma32_bf16(k_operand<DT, D>(T.kw, ks), qop(ks), s0);
+          if (ks + 1 < G_::KSTEPS) s1 = mfma32_bf16(k_operand<DT, D>(T.kw, ks + 1), qop(ks + 1), s1);
+        } else {
+          s0 = mfma32(k_operand<DT, D>(T.kw, ks), qop(ks), s0);
+          if (ks + 1 < G_::KSTEPS) s1 = mfma32(k_operand<DT, D>(T.kw, ks + 1), qop(ks + 1), s1);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot[e] = s0[e] + s1[e];
     }
     float z[4];
     bool up = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float zz = (s0[e] + s1[e]) * rowmul[rb];
+      float zz = dot[e] * rowmul[rb];
       if constexpr (MODE == kPerRow) zz *= T.ks4[e];
       // soft cap in log2 units: with x = z / softcap, z2 = z log2(e), cap2 =
       // softcap log2(e): cap2 tanh(x) = cap2 (1 - 2 / (1 + 2^(2 z2 / softcap)))
@@ -677,7 +731,8 @@ split_decode_kernel(SplitArgs a) {
   __syncthreads();
 
   // ---- B operands of S^T: q rows in this lane's channel order, normalized by a
-  // power of two so every element lies in (-1, 1); the row multiplier restores it.
+  // power of two so every element lies in (-1, 1) (integer caches: the int8
+  // halves of the row scaled to 15 bits); the row multiplier restores it.
   half8_t qb[RB][G_::KSTEPS];
   float rowmul[RB];  // logit (log2 units) = dot * rowmul * per-row K scale
   int lim[RB];       // tokens visible to this lane's row n: lo <= t < lim
@@ -697,6 +752,57 @@ split_decode_kernel(SplitArgs a) {
           qb[rb][ks] = __builtin_bit_cast(
               half8_t, *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + k_channel<DT, D>(ks, g, 0)));
         rowmul[rb] = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
+        continue;
+      }
+      if constexpr (G_::IQK) {
+        // The row as a 15-bit integer vector: qi = rne(q 2^(14 - ex)) with
+        // |q| < 2^ex, |qi| <= 2^14, split as qi = 256 hi + lo, hi in [-64, 64],
+        // lo in [-128, 127], each an int8 B operand.
+        float qv[G_::ISTEPS][16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int st = 0; st < G_::ISTEPS; ++st) {
+          const int base = k_channel_i8<DT, D>(st, g, 0);
+          const u32x4_t r0 = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base);
+          const u32x4_t r1 = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base + 8);
+          float x16[16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x16[2 * i] = __uint_as_float(r0[i] << 16);
+            x16[2 * i + 1] = __uint_as_float(r0[i] & 0xFFFF0000u);
+            x16[8 + 2 * i] = __uint_as_float(r1[i] << 16);
+            x16[8 + 2 * i + 1] = __uint_as_float(r1[i] & 0xFFFF0000u);
+          }
+#pragma unroll
+          for (int p = 0; p < 16; ++p) {
+            const int off = k_channel_i8<DT, D>(st, g, p) - base;  // 0..15
+            float x = x16[off];
+            if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
+            qv[st][p] = x;
+            amax = fmaxf(amax, fabsf(x));
+          }
+        }
+        amax = group_max4(amax);
+        int ex = 0;
+        if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
+#pragma unroll
+        for (int st = 0; st < G_::ISTEPS; ++st) {
+          u32x4_t hw = {0u, 0u, 0u, 0u}, lw = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int p = 0; p < 16; ++p) {
+            const int qi = (int)__builtin_rintf(ldexpf(qv[st][p], 14 - ex));
+            const int hi = (qi + 128) >> 8;
+            const int lo8 = qi - hi * 256;
+            hw[p / 4] |= ((uint32_t)hi & 0xFFu) << (8 * (p % 4));
+            lw[p / 4] |= ((uint32_t)lo8 & 0xFFu) << (8 * (p % 4));
+          }
+          qb[rb][2 * st] = __builtin_bit_cast(half8_t, hw);
+          qb[rb][2 * st + 1] = __builtin_bit_cast(half8_t, lw);
+        }
+        float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
+        if constexpr (MODE == kPerTensor) mul *= kst[0];
+        if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
+        rowmul[rb] = ldexpf(mul, ex - 14);
         continue;
       }
       float qv[G_::KSTEPS][8];
