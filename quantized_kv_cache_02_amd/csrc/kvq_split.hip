@@ -332,6 +332,7 @@ struct WaveState {
   float l[RB];                         // this lane's share of the running sum
   float4_t acc[RB][Geo<DT, D>::NCOL];  // O rows rb*16+4g+e, column c of lane n
   float vref;                          // per-row V: weights carry 1/vref, a power of two
+  float ivref;                         // 1 / vref (exact)
 };
 
 template <int DT, int MODE, int D, int RB, bool CAP, bool QLDS>
@@ -345,11 +346,11 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
   const int tok0 = t * kTile;
   const int tbase = tok0 + 4 * g;
   const bool ok = T.ok != 0;
-  bool valid[4];  // token tbase+e exists (row-independent)
-#pragma unroll
-  for (int e = 0; e < 4; ++e) valid[e] = ok && tbase + e < L;
+  (void)L;
 
-  // (rows past the sequence were read as zero by the bounded loads)
+  // Rows past the sequence and tiles outside the pool were read as zero by the
+  // bounded loads (codes and scales), so only the logits need masking: those
+  // tokens then get weight 0 and add nothing.
   const auto& vw = T.vw;
 
   // Per-row V scales: keep vref a power of two >= every scale seen, so the
@@ -359,25 +360,18 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
   bool rescale = false;
   float vsn[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (kVRow) {
-    bool vup = false;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vup |= valid[e] && T.vs4[e] > W.vref;
-    if (__builtin_amdgcn_ballot_w64(vup) != 0) {
-      float vmax = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (valid[e]) vmax = fmaxf(vmax, T.vs4[e]);
-      vmax = group_max4(vmax);
+    const float vmax4 = fmaxf(fmaxf(T.vs4[0], T.vs4[1]), fmaxf(T.vs4[2], T.vs4[3]));
+    if (__builtin_amdgcn_ballot_w64(vmax4 > W.vref) != 0) {
+      const float vmax = group_max4(vmax4);
       int en;
       (void)frexpf(vmax, &en);  // vmax < 2^en
-      const float nref = ldexpf(1.0f, en);
-      vfac = W.vref / nref;
-      W.vref = nref;
+      W.ivref = ldexpf(1.0f, -en);
+      vfac = W.vref * W.ivref;  // both powers of two: exact
+      W.vref = ldexpf(1.0f, en);
       rescale = true;
     }
-    const float inv = 1.0f / W.vref;  // exact: a power of two
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vsn[e] = T.vs4[e] * inv;
+    for (int e = 0; e < 4; ++e) vsn[e] = T.vs4[e] * W.ivref;
   }
 
   half4_t pa[RB];
@@ -422,6 +416,9 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
     }
     float z[4];
     bool up = false;
+    // token tbase + e is visible to this lane's row iff lo <= it < lim
+    const unsigned span = ok ? (unsigned)(lim[rb] - lo[rb]) : 0u;
+    const int rel = tbase - lo[rb];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float zz = dot[e] * rowmul[rb];
@@ -433,7 +430,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
         const float ex = __builtin_amdgcn_exp2f(zz * icap2);
         zz = cap2 - 2.0f * cap2 * __builtin_amdgcn_rcpf(ex + 1.0f);
       }
-      z[e] = (ok && tbase + e < lim[rb] && tbase + e >= lo[rb]) ? zz : -INFINITY;
+      z[e] = (unsigned)(rel + e) < span ? zz : -INFINITY;
       up |= z[e] > W.m[rb];
     }
     // The running max changes only if some logit exceeds it; the cross-lane
@@ -460,7 +457,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
       const float p = __builtin_amdgcn_exp2f(z[e] - msafe);
       psum += p;
       float pv = p;
-      if constexpr (kVRow) pv = valid[e] ? p * vsn[e] : 0.0f;
+      if constexpr (kVRow) pv = p * vsn[e];
       ph[e] = (_Float16)pv;
       pf[e] = pv;
     }
@@ -745,6 +742,7 @@ split_decode_kernel(SplitArgs a) {
       lim[rb] = (r < Rw) ? (L - a.Tq + (row0 + r) / a.G + 1) : 0;
       if (lim[rb] > L) lim[rb] = L;
       lo[rb] = a.window > 0 ? lim[rb] - a.window : 0;
+      if (lim[rb] < lo[rb]) lim[rb] = lo[rb];  // a query before the first token sees none
       if constexpr (DT == kBf16) {
         // the q rows as they are: bf16 products are exact in the fp32 accumulation
 #pragma unroll
@@ -866,6 +864,7 @@ split_decode_kernel(SplitArgs a) {
     for (int c = 0; c < G_::NCOL; ++c) W.acc[rb][c] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
   W.vref = 0x1p-126f;  // smallest normal: any nonzero scale above it raises the reference
+  W.ivref = 0x1p126f;
 
   for (int t = t0, k = 0; t < te;) {
 #pragma unroll
