@@ -90,6 +90,8 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   const int G = hq / c->num_kv_heads;
   if (G > kMaxGroup || tq > kvq::kMaxQTokens) return KVQ_EUNSUPPORTED;
   if (batch > 65535 || c->num_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+  // the split kernel addresses a tile by its first pool row over 16 in an int
+  if ((int64_t)c->num_blocks * c->num_kv_heads * c->block_size / 16 > INT32_MAX) return KVQ_EUNSUPPORTED;
   const int64_t ntiles = ((int64_t)max_seq_len + 15) / 16;
   const int64_t Hkv = c->num_kv_heads;
   // Balanced schedule: the tiles of all sequences of a KV head are cut into

@@ -247,29 +247,41 @@ struct Tile {
   int ok;                           // block-table entry inside the pool
 };
 
-// Block-table entries of a wavefront's tiles.  The wavefront's k-th tile is
-// t0 + kWaves * k; its entry sits in lane k % 64 of register k / 64.  Loaded
-// once before the first tile, so the tile loop never waits on a table read.
+// First cache row of each of a wavefront's tiles, in units of 16 rows (a
+// tile's 16 rows are consecutive: block sizes are multiples of 16), or -1 for a
+// tile whose block-table entry lies outside the pool.  The wavefront's k-th
+// tile is t0 + kWaves * k; its value sits in lane k % 64 of register k / 64.
+// Computed once before the first tile (the block-table reads included), so
+// the tile loop neither waits on a table read nor does row arithmetic beyond
+// one shift.  The host bounds the pool so that every value fits an int.
 struct TableRegs {
   int e0, e1, e2, e3;  // kTableRegs == 4 (named, not an array: stays in registers)
 };
 static_assert(kTableRegs == 4, "TableRegs holds four registers");
 
-__device__ __forceinline__ int table_load_one(const int32_t* row, const SplitArgs& a, int t0,
-                                              int waves, int j, int lane) {
+__device__ __forceinline__ int tile_row16(const SplitArgs& a, int b, int hkv, int t0, int waves,
+                                          int j, int lane) {
   const int64_t t = (int64_t)t0 + (int64_t)waves * (64 * j + lane);
-  const int64_t idx = t * kTile / a.c.block_size;  // clamped: dead tiles stay in range
-  return row[idx < a.c.max_blocks ? idx : a.c.max_blocks - 1];
+  const int64_t tok0 = t * kTile;
+  const int64_t bs = a.c.block_size;
+  int64_t blk = b, off = tok0 < bs ? tok0 : 0;  // (tiles past a contiguous sequence read nothing)
+  if (a.c.block_table != nullptr) {
+    int64_t idx = tok0 / bs;
+    idx = idx < a.c.max_blocks ? idx : a.c.max_blocks - 1;  // dead tiles stay in range
+    blk = a.c.block_table[(size_t)b * a.c.max_blocks + idx];
+    off = tok0 % bs;
+  }
+  if ((uint64_t)blk >= (uint64_t)a.c.num_blocks) return -1;
+  return (int)(((blk * a.c.Hkv + hkv) * bs + off) / kTile);
 }
 
-__device__ __forceinline__ TableRegs load_table(const SplitArgs& a, int b, int t0, int waves,
+__device__ __forceinline__ TableRegs load_table(const SplitArgs& a, int b, int hkv, int t0, int waves,
                                                 int lane) {
-  const int32_t* row = a.c.block_table + (size_t)b * a.c.max_blocks;
-  return TableRegs{table_load_one(row, a, t0, waves, 0, lane), table_load_one(row, a, t0, waves, 1, lane),
-                   table_load_one(row, a, t0, waves, 2, lane), table_load_one(row, a, t0, waves, 3, lane)};
+  return TableRegs{tile_row16(a, b, hkv, t0, waves, 0, lane), tile_row16(a, b, hkv, t0, waves, 1, lane),
+                   tile_row16(a, b, hkv, t0, waves, 2, lane), tile_row16(a, b, hkv, t0, waves, 3, lane)};
 }
 
-// Entry of the wavefront's k-th tile (k wave-uniform, k < kTableRegs * 64 for
+// Value of the wavefront's k-th tile (k wave-uniform, k < kTableRegs * 64 for
 // every live tile; larger k only occurs for dead tiles, which read nothing).
 __device__ __forceinline__ int table_entry(const TableRegs& r, int k) {
   const int j = k >> 6;
@@ -277,23 +289,19 @@ __device__ __forceinline__ int table_entry(const TableRegs& r, int k) {
   return __builtin_amdgcn_readlane(v, k & 63);
 }
 
-// Issue the loads of tile t (tokens 16t..16t+15) of block `blk` (the table
-// entry of a paged cache, the sequence index of a contiguous one).  `live` is
-// false for the tiles a wavefront loads past the end of its split; those read
-// nothing.
+// Issue the loads of tile t (tokens 16t..16t+15), whose first cache row is
+// 16 * row16 (row16 < 0: outside the pool).  `live` is false for the tiles a
+// wavefront loads past the end of its split; those read nothing.
 template <int DT, int MODE, int D>
-__device__ __forceinline__ void load_tile(const SplitArgs& a, int hkv, int t, bool live, int blk,
-                                          int L, int n, int g, Tile<DT, D>& T) {
+__device__ __forceinline__ void load_tile(const SplitArgs& a, int t, bool live, int row16, int L,
+                                          int n, int g, Tile<DT, D>& T) {
   using G_ = Geo<DT, D>;
   constexpr int ROWB = G_::ROWB;
-  const int bs = a.c.block_size;
   const int tok0 = t * kTile;
-  const int ok = (unsigned)blk < (unsigned)a.c.num_blocks;
-  blk = __builtin_amdgcn_readfirstlane(ok ? blk : 0);
-  T.ok = __builtin_amdgcn_readfirstlane(ok);
-  int rows = (live && ok) ? min(kTile, L - tok0) : 0;
-  rows = __builtin_amdgcn_readfirstlane(rows);
-  const size_t row0 = ((size_t)blk * a.c.Hkv + hkv) * (size_t)bs + (size_t)(tok0 % bs);
+  const int ok = row16 >= 0;
+  T.ok = ok;
+  const int rows = (live && ok) ? min(kTile, L - tok0) : 0;
+  const size_t row0 = (size_t)(uint32_t)(ok ? row16 : 0) * kTile;
   const auto kr = make_rsrc(a.c.k_codes + row0 * ROWB, rows * ROWB);
   const auto vr = make_rsrc(a.c.v_codes + row0 * ROWB, rows * ROWB);
   const int koff = n * ROWB + G_::KCH * g;
@@ -702,17 +710,15 @@ split_decode_kernel(SplitArgs a) {
   // issued unconditionally (tiles past the split read nothing).  A wavefront
   // whose first tiles hold a new row appends first; any other appends after
   // issuing them, so the stores overlap the loads.
-  const bool paged = a.c.block_table != nullptr;
-  TableRegs tbl;
-  if (paged) tbl = load_table(a, b, t0, kWaves, lane);
+  const TableRegs tbl = load_table(a, b, hkv, t0, kWaves, lane);
   Tile<DT, D> buf[NB];
   // (the loads stay at one program point, so the compiler's waits for them
   // remain exact on the path every wavefront but one takes)
   if (early_hit) append_rows();
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    load_tile<DT, MODE, D>(a, hkv, t0 + i * kWaves, t0 + i * kWaves < te,
-                           paged ? table_entry(tbl, i) : b, L, n, g, buf[i]);
+    load_tile<DT, MODE, D>(a, t0 + i * kWaves, t0 + i * kWaves < te, table_entry(tbl, i), L, n, g,
+                           buf[i]);
   if (any_mine && !early_hit) append_rows();
 
   // ---- stage the query rows in LDS (bf16), zero padding rows
@@ -872,8 +878,8 @@ split_decode_kernel(SplitArgs a) {
       if (t < te)
         process_tile<DT, MODE, D, RB, CAP, K_::QLDS>(buf[i], t, L, n, g, qb, qlds, rowmul, lim, lo,
                                                      cap2, icap2, W);
-      load_tile<DT, MODE, D>(a, hkv, t + NB * kWaves, t + NB * kWaves < te,
-                             paged ? table_entry(tbl, k + NB) : b, L, n, g, buf[i]);
+      load_tile<DT, MODE, D>(a, t + NB * kWaves, t + NB * kWaves < te, table_entry(tbl, k + NB), L, n,
+                             g, buf[i]);
       t += kWaves;
       ++k;
     }

@@ -274,6 +274,17 @@ def test_balanced_schedule_many_sequences():
     gu.run_and_check(w, "balanced 150 sequences")
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_wavefront_reads_more_than_64_tiles(paged):
+    """256 KV heads fill the CUs with one workgroup each: every wavefront reads
+    129 tiles, so the first rows of its tiles come from three of its table
+    registers (64 tiles per register)."""
+    w = ki.random_workload(4700 + int(paged), B=1, Hkv=256, G=1, D=64, Tq=1, lens=[8200],
+                           dtype=INT8, mode=PER_ROW, block_size=16 if paged else None)
+    assert kvq.num_splits(gu.gpu_cache(w), 1, 256, 1, 8200) == 1
+    gu.run_and_check(w, f"129 tiles per wavefront paged={paged}")
+
+
 def test_query_tokens_beyond_length():
     """Tq larger than the cached length: early drafts see nothing and output zeros."""
     w = ki.random_workload(77, B=1, Hkv=1, G=2, D=64, Tq=6, lens=[3], dtype=INT8, mode=PER_ROW,
