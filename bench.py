@@ -190,6 +190,40 @@ def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fuse
                 split_ms=split_ms, wall_s=wall_s, bytes=algorithmic_bytes(w), splits=S)
 
 
+STREAM_GRIDS = (256, 512, 1024, 2048)
+
+
+def time_stream_floor(kvq, torch, nbytes: int, layers: int, dev, reps: int = 8):
+    """The HBM floor for reading `nbytes` once: kvq_stream_read (the decode's
+    non-temporal 16-byte loads, nothing else) over `layers` rotated buffers of
+    that size, back to back on one stream, timed with HIP events on it; the
+    fastest of a few workgroup counts."""
+    nbytes = nbytes // 16 * 16
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(layers)]
+    sink = torch.empty(max(STREAM_GRIDS) * 4096, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    best = None
+    with torch.cuda.stream(stream):
+        for wg in STREAM_GRIDS:
+            for b in bufs:
+                kvq.stream_read(b, wg, sink, stream=stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                for b in bufs:
+                    kvq.stream_read(b, wg, sink, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * layers)
+            if best is None or us < best[0]:
+                best = (us, wg)
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return best
+
+
 def time_config(kvq, torch, ki, dtype: str, ctx: int, layers: int, steps: int, warmup: int, dev,
                 fused: bool = True):
     w = ki.make_workload(3, ctx=ctx, dtype=dtype)
@@ -461,6 +495,15 @@ def main():
             "traffic": traffic,
         },
     }
+    fl_us, fl_wg = time_stream_floor(kvq, torch, r["bytes"], args.layers, dev)
+    line["stream_floor"] = {
+        "us": round(fl_us, 2),
+        "GB/s": round(r["bytes"] / (fl_us * 1e-6) / 1e9, 1),
+        "frac_of_peak": round(r["bytes"] / (fl_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "workgroups": fl_wg,
+        "split_kernel_over_floor": round(r["split_ms"] * 1e3 / fl_us, 3),
+        "what": "kvq_stream_read of the same bytes: the decode's loads and nothing else",
+    }
     if not args.no_cpu_baseline:
         n, sec, threads = cpu_baseline(ki, w, args.cpu_seconds)
         line["cpu_baseline"] = {
@@ -484,6 +527,9 @@ def main():
                     s["step_GBps"] = s["bytes"] / (s["step_ms"] * 1e-3) / 1e9
                     s["split_GBps"] = s["bytes"] / (s["split_ms"] * 1e-3) / 1e9
                     s["split_frac_of_peak"] = s["split_GBps"] / PEAK_HBM_GBPS
+                    fl_us, fl_wg = time_stream_floor(kvq, torch, s["bytes"], layers, dev)
+                    s["stream_floor_us"] = fl_us
+                    s["stream_floor_workgroups"] = fl_wg
                     f.write(json.dumps(s) + "\n")
                     f.flush()
                     print(f"[sweep] {dt} ctx={ctx} step {s['step_ms'] * 1e3:.2f} us "

@@ -313,6 +313,19 @@ int kvq_prefill_attend(const kvq_cache* cache, const void* k_new, const void* v_
 size_t kvq_cache_bytes(int32_t dtype, int32_t scale_mode, int32_t num_kv_heads, int32_t head_dim,
                        int64_t tokens);
 
+/*
+ * kvq_stream_read -- a measurement aid, no part of attention: reads `bytes`
+ * (a multiple of 16) at `src` once with the loads the decode uses
+ * (non-temporal, 16 bytes per lane), `workgroups` workgroups of 256 threads
+ * each reading one contiguous slice, and does nothing else.  Its duration is
+ * the HBM floor for reading that many bytes, the reference the decode's
+ * KV-read rate is set against.  `sink` must hold workgroups * 4096 bytes; a
+ * thread stores there only if the XOR of what it read equals one fixed 64-bit
+ * pattern.  KVQ_EINVAL for a NULL pointer, bytes % 16 != 0 or workgroups
+ * outside [1, 65535].
+ */
+int kvq_stream_read(const void* src, size_t bytes, int32_t workgroups, void* sink, void* stream);
+
 /* Human-readable name of a kvq_status (host, static storage). */
 const char* kvq_status_string(int status);
 

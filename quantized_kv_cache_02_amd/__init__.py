@@ -32,7 +32,7 @@ EXPORTS = (
     "kvq_append", "kvq_num_splits", "kvq_workspace_bytes", "kvq_decode_attend",
     "kvq_paged_decode_attend", "kvq_append_decode_attend", "kvq_attend_ex", "kvq_prefill_attend",
     "kvq_split_decode",
-    "kvq_combine", "kvq_cache_bytes",
+    "kvq_combine", "kvq_cache_bytes", "kvq_stream_read",
     "kvq_status_string",
 )
 
@@ -94,6 +94,8 @@ def lib():
         L.kvq_combine.restype = ctypes.c_int
         L.kvq_cache_bytes.argtypes = [I32, I32, I32, I32, ctypes.c_int64]
         L.kvq_cache_bytes.restype = SZ
+        L.kvq_stream_read.argtypes = [P, SZ, I32, P, P]
+        L.kvq_stream_read.restype = ctypes.c_int
         L.kvq_status_string.argtypes = [ctypes.c_int]
         L.kvq_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -356,3 +358,16 @@ def combine(cache: KVCache, batch: int, num_q_heads: int, q_tokens: int, seq_len
 def cache_bytes(dtype: int, scale_mode: int, num_kv_heads: int, head_dim: int, tokens: int) -> int:
     """Footprint of one layer's K+V cache (codes plus per-row scales)."""
     return lib().kvq_cache_bytes(dtype, scale_mode, num_kv_heads, head_dim, tokens)
+
+
+def stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of `src` once with the decode's load instructions and
+    nothing else (kvq_stream_read): the HBM floor a KV read is compared with.
+    `sink` holds at least workgroups * 4096 bytes."""
+    if not src.is_contiguous() or not sink.is_contiguous():
+        raise KvqError("stream_read: src and sink must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() * sink.element_size() < workgroups * 4096:
+        raise KvqError("stream_read: sink smaller than workgroups * 4096 bytes")
+    _check(lib().kvq_stream_read(_ptr(src), nbytes, workgroups, _ptr(sink), _stream(stream)),
+           "kvq_stream_read")

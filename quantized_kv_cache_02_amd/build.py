@@ -37,6 +37,7 @@ def _units():
         ("kvq_host.o", os.path.join(CSRC, "kvq_host.cpp"), []),
         ("kvq_append.o", os.path.join(CSRC, "kvq_append.hip"), []),
         ("kvq_combine.o", os.path.join(CSRC, "kvq_combine.hip"), []),
+        ("kvq_probe.o", os.path.join(CSRC, "kvq_probe.hip"), []),
     ]
     # one unit per (dtype, K scale mode, V scales per row or static)
     for dt in (1, 2, 3):

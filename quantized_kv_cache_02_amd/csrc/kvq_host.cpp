@@ -52,6 +52,11 @@ int check_cache(const kvq_cache* c) {
   return KVQ_OK;
 }
 
+// Bytes of one cached row of codes (int4: two per byte; bf16: two bytes each).
+int64_t row_bytes(const kvq_cache* c) {
+  return c->dtype == KVQ_INT4 ? c->head_dim / 2 : c->dtype == KVQ_BF16 ? 2 * c->head_dim : c->head_dim;
+}
+
 int v_mode_of(const kvq_cache* c) { return c->v_scale_mode != 0 ? c->v_scale_mode : c->scale_mode; }
 
 CacheArgs cache_args(const kvq_cache* c, const int32_t* table, int32_t max_blocks) {
@@ -108,15 +113,17 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   // share its bytes through L2.
   const int RB = (G * tq + 15) / 16;
   const int RBN = (RB > 1 && RB * c->head_dim > kvq::kSplitMaxAccColumns) ? RB : 1;
-  // Compute-bound variants (packed int4, whose tiles carry half the bytes, and
-  // row-split launches) run two workgroups per CU -- two wavefronts per SIMD
-  // hide each other's dependency stalls (measured on MI355X: int4 at 256K
-  // tokens 78.1 -> 68.6 us, workload 5 173.6 -> 90.7 us) -- as long as a chunk
-  // keeps at least 2 * kMinTilesPerSplit tiles.
+  // Compute-bound variants (rows of at most 128 bytes, whose tiles carry less
+  // data per instruction: packed int4 at D 256, the 8-bit caches at D 128 and
+  // below; and row-split launches) run two workgroups per CU -- two
+  // wavefronts per SIMD hide each other's dependency stalls (measured on
+  // MI355X: int4 at 256K tokens 78.1 -> 68.6 us, workload 5 173.6 -> 90.7 us,
+  // paged fp8 at D 128 28.9 -> 27.9 us per step) -- as long as a chunk keeps
+  // at least 2 * kMinTilesPerSplit tiles.
   const int64_t per_head = std::max<int64_t>(kNumCUs / (Hkv * RBN), 1);
   const int64_t all_tiles = (int64_t)batch * ntiles;
   int64_t NW = per_head - (batch - 1);
-  if ((RBN > 1 || c->dtype == KVQ_INT4) && 2 * per_head - (batch - 1) <= all_tiles / (2 * kvq::kMinTilesPerSplit))
+  if ((RBN > 1 || row_bytes(c) <= 128) && 2 * per_head - (batch - 1) <= all_tiles / (2 * kvq::kMinTilesPerSplit))
     NW = 2 * per_head - (batch - 1);
   NW = std::min<int64_t>(NW, all_tiles / kvq::kMinTilesPerSplit);
   NW = std::max<int64_t>(NW, 1);

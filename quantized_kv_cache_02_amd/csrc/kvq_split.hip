@@ -123,6 +123,14 @@ __device__ __forceinline__ int k_channel_i8(int s, int g, int p) {
   }
 }
 
+// k_channel_i8(s, g, p) - k_channel_i8(s, g, 0), which depends on p alone:
+// int8 0..15 in order; int4 the even channels 0, 2, 4, 6, the odd ones, then
+// the same 8 higher.
+template <int DT>
+__device__ __forceinline__ constexpr int k_offset_i8(int p) {
+  return DT == kInt4 ? 8 * (p / 8) + 2 * (p % 4) + ((p / 4) & 1) : p;
+}
+
 // Channel d of column c (0..NCOL-1) of the P.V MFMA in lane column j.
 template <int DT, int D>
 __device__ __forceinline__ int v_channel(int c, int j) {
@@ -779,7 +787,7 @@ split_decode_kernel(SplitArgs a) {
           }
 #pragma unroll
           for (int p = 0; p < 16; ++p) {
-            const int off = k_channel_i8<DT, D>(st, g, p) - base;  // 0..15
+            const int off = k_offset_i8<DT>(p);  // 0..15
             float x = x16[off];
             if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
             qv[st][p] = x;

@@ -157,6 +157,16 @@ def test_invalid_prefill_rejected():
     assert call(opts=(0.0, -3)) == -1
 
 
+def test_invalid_stream_read_rejected():
+    L = kvq.lib()
+    buf = ctypes.c_void_p(0x1000)  # never dereferenced: every call below is rejected first
+    assert L.kvq_stream_read(None, 4096, 1, buf, None) == -1
+    assert L.kvq_stream_read(buf, 4096, 1, None, None) == -1
+    assert L.kvq_stream_read(buf, 4100, 1, buf, None) == -1
+    assert L.kvq_stream_read(buf, 4096, 0, buf, None) == -1
+    assert L.kvq_stream_read(buf, 4096, 65536, buf, None) == -1
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, 5):
         assert kvq.lib().kvq_status_string(s)

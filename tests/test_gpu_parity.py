@@ -276,13 +276,17 @@ def test_balanced_schedule_many_sequences():
 
 @pytest.mark.parametrize("paged", [False, True])
 def test_wavefront_reads_more_than_64_tiles(paged):
-    """256 KV heads fill the CUs with one workgroup each: every wavefront reads
-    129 tiles, so the first rows of its tiles come from three of its table
-    registers (64 tiles per register)."""
-    w = ki.random_workload(4700 + int(paged), B=1, Hkv=256, G=1, D=64, Tq=1, lens=[8200],
+    """256 KV heads fill the CUs with one or two workgroups each: every
+    wavefront reads more than 128 tiles, so the first rows of its tiles come
+    from three of its table registers (64 tiles per register)."""
+    L = 16400
+    w = ki.random_workload(4700 + int(paged), B=1, Hkv=256, G=1, D=64, Tq=1, lens=[L],
                            dtype=INT8, mode=PER_ROW, block_size=16 if paged else None)
-    assert kvq.num_splits(gu.gpu_cache(w), 1, 256, 1, 8200) == 1
-    gu.run_and_check(w, f"129 tiles per wavefront paged={paged}")
+    S = kvq.num_splits(gu.gpu_cache(w), 1, 256, 1, L)
+    tiles = -(-L // 16)
+    per_wave = -(-max(-(-tiles // S), 8) // 4)
+    assert per_wave > 128, (S, per_wave)
+    gu.run_and_check(w, f"{per_wave} tiles per wavefront paged={paged}")
 
 
 def test_query_tokens_beyond_length():
