@@ -551,6 +551,9 @@ def main():
                 s["step_GBps"] = s["bytes"] / (s["step_ms"] * 1e-3) / 1e9
                 s["split_GBps"] = s["bytes"] / (s["split_ms"] * 1e-3) / 1e9
                 s["split_frac_of_peak"] = s["split_GBps"] / PEAK_HBM_GBPS
+                fl_us, fl_wg = time_stream_floor(kvq, torch, s["bytes"], args.layers, dev)
+                s["stream_floor_us"] = fl_us
+                s["stream_floor_workgroups"] = fl_wg
                 f.write(json.dumps(s) + "\n")
                 f.flush()
                 print(f"[sweep] cfg{cfg} {w.name} step {s['step_ms'] * 1e3:.2f} us "
