@@ -48,14 +48,18 @@ def _units():
     # the unquantized bf16 cache: no scales
     units.append(("kvq_split_4_0_0.o", os.path.join(CSRC, "kvq_split.hip"),
                   ["-DKVQ_DTYPE=4", "-DKVQ_MODE=0", "-DKVQ_VROW=0"]))
-    # the chunked-prefill kernel, split the same way
+    # the chunked-prefill kernel, split the same way.  Its accumulators stay in
+    # ordinary vector registers: left to itself the backend parks them in the
+    # accumulation registers and copies all of them in and out on every tile
+    # (160 copies per tile at D 256).
+    pf = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
     for dt in (1, 2, 3):
         for md in (1, 2, 3):
             for vr in (0, 1):
                 units.append((f"kvq_prefill_{dt}_{md}_{vr}.o", os.path.join(CSRC, "kvq_prefill.hip"),
-                              [f"-DKVQ_DTYPE={dt}", f"-DKVQ_MODE={md}", f"-DKVQ_VROW={vr}"]))
+                              [f"-DKVQ_DTYPE={dt}", f"-DKVQ_MODE={md}", f"-DKVQ_VROW={vr}", *pf]))
     units.append(("kvq_prefill_4_0_0.o", os.path.join(CSRC, "kvq_prefill.hip"),
-                  ["-DKVQ_DTYPE=4", "-DKVQ_MODE=0", "-DKVQ_VROW=0"]))
+                  ["-DKVQ_DTYPE=4", "-DKVQ_MODE=0", "-DKVQ_VROW=0", *pf]))
     return units
 
 
