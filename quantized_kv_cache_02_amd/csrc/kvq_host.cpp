@@ -18,7 +18,6 @@ namespace {
 using kvq::CacheArgs;
 
 constexpr int kMaxGroup = 8;     // query heads per KV head
-constexpr int kNumCUs = 256;  // MI355X
 constexpr int kMaxSplits = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -120,7 +119,7 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   // MI355X: int4 at 256K tokens 78.1 -> 68.6 us, workload 5 173.6 -> 90.7 us,
   // paged fp8 at D 128 28.9 -> 27.9 us per step) -- as long as a chunk keeps
   // at least 2 * kMinTilesPerSplit tiles.
-  const int64_t per_head = std::max<int64_t>(kNumCUs / (Hkv * RBN), 1);
+  const int64_t per_head = std::max<int64_t>(kvq::kNumCUs / (Hkv * RBN), 1);
   const int64_t all_tiles = (int64_t)batch * ntiles;
   int64_t NW = per_head - (batch - 1);
   if ((RBN > 1 || row_bytes(c) <= 128) && 2 * per_head - (batch - 1) <= all_tiles / (2 * kvq::kMinTilesPerSplit))

@@ -16,6 +16,7 @@ enum : int { kNoScale = 0, kPerRow = 1, kPerTensor = 2, kPerChannel = 3 };
 constexpr int kTile = 16;
 // Wavefronts per decode workgroup; each owns a private online-softmax state.
 constexpr int kWaves = 4;
+constexpr int kNumCUs = 256;  // compute units of an MI355X
 
 // Block-table entries of a paged cache are read once per decode workgroup, in
 // its prologue, and held in registers: a wavefront keeps the entries of up to

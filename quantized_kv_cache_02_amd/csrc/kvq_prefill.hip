@@ -12,10 +12,11 @@
 //
 // Work assignment: one workgroup per (sequence, KV head, 128 query rows), the
 // rows being the G grouped heads times the chunk's tokens (row = token * G +
-// head).  Each of the 4 wavefronts owns 32 rows (two 16-row MFMA blocks, so
-// every operand read from LDS feeds two MFMAs).  The workgroup walks the
-// 64-token tiles its rows can see; per tile all 256 threads load the codes and
-// unpack them once into LDS -- K as fp16 rows, V transposed to channel-major --
+// head).  Below D = 256 each of 4 wavefronts owns 32 rows (two 16-row MFMA
+// blocks, so every operand read from LDS feeds two MFMAs); at D = 256 each of
+// 8 wavefronts owns 16.  The workgroup walks the 64-token tiles its rows can
+// see; per tile all its threads load the codes and unpack them once into LDS
+// -- K as fp16 rows, V transposed to channel-major --
 // into one of two buffers, so the next tile is loaded and unpacked while this
 // one is used (one barrier per tile), and every wavefront runs
 //   S^T = K . Q^T   v_mfma_f32_16x16x32_f16 (A: K rows from LDS, B: its q rows),
@@ -51,20 +52,28 @@ constexpr int kPT = 64;  // tokens per KV tile
 // and the compiler copied them back and forth every tile.
 template <int D>
 constexpr int kPRowBlocks = D >= 256 ? 1 : 2;
-template <int D>
-constexpr int kPRows = 16 * kPRowBlocks<D> * kWaves;  // query rows per workgroup
+// Wavefronts per workgroup (W): 4, or at D = 256 also 8 (one row block each,
+// so the tile's unpack is shared by 128 rows and two wavefronts per SIMD hide
+// each other's stalls; the two tile buffers still fit the LDS) when that still
+// gives every CU a workgroup.
+template <int D, int W>
+constexpr int kPRows = 16 * kPRowBlocks<D> * W;  // query rows per workgroup
 
-template <int DT, int D>
+template <int DT, int D, int W>
 struct PGeo {
   static constexpr int ROWB = (DT == kInt4) ? D / 2 : (DT == kBf16) ? 2 * D : D;
   static constexpr int KST = D + 8;      // K tile row stride in LDS (16-bit elements)
   static constexpr int VST = kPT + 8;    // transposed V row stride (16-bit elements)
   static constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per S^T sub-tile
   static constexpr int NCOL = D / 16;    // 16-channel output column blocks
-  // K load: thread -> token tid / 4, bytes [KQB * (tid % 4), +KQB) of its row
-  static constexpr int KQB = ROWB / 4;
-  // V load: thread -> channel chunk tid / 16 (D / 16 channels), tokens 4 * (tid % 16) + 0..3
-  static constexpr int VCB = ROWB / 16;  // bytes of one token in one chunk
+  static constexpr int NT = 64 * W;
+  // K load: thread -> token tid / KP, bytes [KQB * (tid % KP), +KQB) of its row
+  static constexpr int KP = NT / kPT;    // threads per K row
+  static constexpr int KQB = ROWB / KP;
+  // V load: thread -> channel chunk tid / 16 (VNC chunks of D / VNC channels),
+  // tokens 4 * (tid % 16) + 0..3
+  static constexpr int VNC = NT / 16;
+  static constexpr int VCB = ROWB / VNC;  // bytes of one token in one chunk
   static constexpr int VCW = VCB >= 4 ? VCB / 4 : 1;
   static constexpr int CPD = (DT == kInt4) ? 8 : (DT == kBf16) ? 2 : 4;  // channels per dword
 };
@@ -94,10 +103,10 @@ __device__ __forceinline__ void gload(const uint8_t* p, uint32_t* out) {
 // when the tile is unpacked, so nothing between the loads and that point waits
 // for the loaded values (the next tile's loads stay in flight under this
 // tile's math).
-template <int DT, int D>
+template <int DT, int D, int W>
 struct PTile {
-  uint32_t k[PGeo<DT, D>::KQB / 4];
-  uint32_t v[4][PGeo<DT, D>::VCW];
+  uint32_t k[PGeo<DT, D, W>::KQB / 4];
+  uint32_t v[4][PGeo<DT, D, W>::VCW];
   float ks, vs;  // per-row scales of token tid (threads 0..63)
   bool kok, vok[4], sok;
 };
@@ -137,16 +146,16 @@ __device__ __forceinline__ long tile_row(const TileRows& tr, int kt, int tk, int
   return (base < 0 || kt * kPT + tk >= L) ? -1 : base + (tk & 15);
 }
 
-template <int DT, int MODE, int D>
+template <int DT, int MODE, int D, int W>
 __device__ __forceinline__ void load_ptile(const PrefillArgs& a, int b, int hkv, int kt, int L, int tid,
-                                           PTile<DT, D>& T) {
-  using P = PGeo<DT, D>;
+                                           PTile<DT, D, W>& T) {
+  using P = PGeo<DT, D, W>;
   const TileRows tr = tile_rows(a, b, hkv, kt, L);
   // K: one row quarter per thread
   {
-    const long ri = tile_row(tr, kt, tid / 4, L);
+    const long ri = tile_row(tr, kt, tid / P::KP, L);
     T.kok = ri >= 0;
-    gload<P::KQB>(a.c.k_codes + (ri < 0 ? 0 : ri) * P::ROWB + P::KQB * (tid % 4), T.k);
+    gload<P::KQB>(a.c.k_codes + (ri < 0 ? 0 : ri) * P::ROWB + P::KQB * (tid % P::KP), T.k);
   }
   // V: 4 tokens of one channel chunk
 #pragma unroll
@@ -184,13 +193,13 @@ __device__ __forceinline__ void int4x8_to_h_ordered(uint32_t w, uint32_t out[4])
 
 // Unpack a loaded tile into LDS: K rows as fp16 (bf16 as is), V transposed to
 // [channel][token], per-row scales.
-template <int DT, int MODE, int D>
-__device__ __forceinline__ void stage_ptile(const PTile<DT, D>& T, int tid, uint16_t* ks_lds,
+template <int DT, int MODE, int D, int W>
+__device__ __forceinline__ void stage_ptile(const PTile<DT, D, W>& T, int tid, uint16_t* ks_lds,
                                             uint16_t* vt_lds, float* ksc, float* vsc) {
-  using P = PGeo<DT, D>;
+  using P = PGeo<DT, D, W>;
   {
-    // this thread's quarter of its row: channels (D / 4) * (tid % 4) .. + D / 4
-    uint16_t* dst = ks_lds + (tid / 4) * P::KST + (D / 4) * (tid % 4);
+    // this thread's part of its row: channels (D / KP) * (tid % KP) .. + D / KP
+    uint16_t* dst = ks_lds + (tid / P::KP) * P::KST + (D / P::KP) * (tid % P::KP);
     constexpr int NW = P::KQB / 4;  // dwords loaded
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
@@ -213,8 +222,8 @@ __device__ __forceinline__ void stage_ptile(const PTile<DT, D>& T, int tid, uint
   }
   {
     // channels [cb0, cb0 + D / 16) of tokens t0 .. t0 + 3
-    const int cb0 = (D / 16) * (tid / 16), t0 = 4 * (tid % 16);
-    constexpr int NCH = D / 16;  // channels of this thread
+    constexpr int NCH = D / P::VNC;  // channels of this thread
+    const int cb0 = NCH * (tid / 16), t0 = 4 * (tid % 16);
     uint32_t vv[4][P::VCW];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -266,14 +275,14 @@ __device__ __forceinline__ void stage_ptile(const PTile<DT, D>& T, int tid, uint
   }
 }
 
-template <int DT, int MODE, int D, bool CAP>
-__global__ __launch_bounds__(256) void prefill_kernel(
+template <int DT, int MODE, int D, int W, bool CAP>
+__global__ __launch_bounds__(64 * W) void prefill_kernel(
     PrefillArgs a) {
-  using P = PGeo<DT, D>;
+  using P = PGeo<DT, D, W>;
   constexpr int KSTEPS = P::KSTEPS;
   constexpr int NCOL = P::NCOL;
   constexpr int RBW = kPRowBlocks<D>;
-  constexpr int kRows = kPRows<D>;
+  constexpr int kRows = kPRows<D, W>;
   constexpr int KTILE_ELEMS = kPT * P::KST;
   constexpr int VTILE_ELEMS = D * P::VST;
   constexpr int BUF_ELEMS = KTILE_ELEMS + VTILE_ELEMS;
@@ -281,8 +290,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   // is unpacked into the other; after the loop the output staging reuses them
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF_ELEMS];
   __shared__ float ksc[2][kPT], vsc[2][kPT];
-  __shared__ float rowf[kWaves][16 * RBW], rowsink[kWaves][16 * RBW];
-  static_assert(kWaves * 16 * RBW * (D + 4) * 4 <= (int)sizeof(lds), "output staging does not fit");
+  __shared__ float rowf[W][16 * RBW], rowsink[W][16 * RBW];
+  static_assert(W * 16 * RBW * (D + 4) * 4 <= (int)sizeof(lds), "output staging does not fit");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -402,16 +411,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     for (int c = 0; c < NCOL; ++c) acc[rb][c] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  PTile<DT, D> T;
+  PTile<DT, D, W> T;
   if (kt_begin < kt_end) {
-    load_ptile<DT, MODE, D>(a, b, hkv, kt_begin, L, tid, T);
-    stage_ptile<DT, MODE, D>(T, tid, lds, lds + KTILE_ELEMS, ksc[0], vsc[0]);
+    load_ptile<DT, MODE, D, W>(a, b, hkv, kt_begin, L, tid, T);
+    stage_ptile<DT, MODE, D, W>(T, tid, lds, lds + KTILE_ELEMS, ksc[0], vsc[0]);
   }
   __syncthreads();
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int cur = (kt - kt_begin) & 1;
     const bool more = kt + 1 < kt_end;
-    if (more) load_ptile<DT, MODE, D>(a, b, hkv, kt + 1, L, tid, T);
+    if (more) load_ptile<DT, MODE, D, W>(a, b, hkv, kt + 1, L, tid, T);
     const uint16_t* ks_lds = lds + cur * BUF_ELEMS;
     const uint16_t* vt_lds = ks_lds + KTILE_ELEMS;
 
@@ -420,17 +429,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     // sub-tile s's MFMAs in source order (the compiler schedules them).
     float z[RBW][4][4];
     bool up = false;
-    half8_t kop[2][KSTEPS];
+    // (one sub-tile's K operands at a time at D = 256: two in flight cost 32
+    // more registers than two wavefronts per SIMD leave)
+    constexpr int KB = W > 4 ? 1 : 2;
+    half8_t kop[KB][KSTEPS];
     auto kread = [&](int s, half8_t (&dst)[KSTEPS]) {
       const uint16_t* krow = ks_lds + (16 * s + n) * P::KST + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
         dst[ks] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(krow + 32 * ks));
     };
-    kread(0, kop[0]);
+    if constexpr (KB == 2) kread(0, kop[0]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (s + 1 < 4) kread(s + 1, kop[(s + 1) & 1]);
+      if constexpr (KB == 2) {
+        if (s + 1 < 4) kread(s + 1, kop[(s + 1) & 1]);
+      } else {
+        kread(s, kop[0]);
+      }
       float4_t s0[RBW], s1[RBW];
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) {
@@ -439,8 +455,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       }
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ks += 2) {
-        const half8_t k0 = kop[s & 1][ks];
-        const half8_t k1 = kop[s & 1][ks + 1 < KSTEPS ? ks + 1 : ks];
+        const half8_t k0 = kop[s % KB][ks];
+        const half8_t k1 = kop[s % KB][ks + 1 < KSTEPS ? ks + 1 : ks];
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
           if constexpr (DT == kBf16) {
@@ -590,24 +606,31 @@ __global__ __launch_bounds__(256) void prefill_kernel(
           for (int e = 0; e < 4; ++e) ph[rb][e] = (_Float16)pf[e];
         }
       }
-      // all of the sub-tile's V operands first, so their LDS latencies overlap
+      // the sub-tile's V operands in groups read ahead of their MFMAs, so their
+      // LDS latencies overlap (all at once with 4 wavefronts; two halves with
+      // 8, whose registers are shared by two wavefronts per SIMD)
       const uint16_t* vcol = vt_lds + 16 * s + 4 * g;
-      u32x2_t vop[NCOL];
+      constexpr int VG = W > 4 ? NCOL / 2 : NCOL;
 #pragma unroll
-      for (int c = 0; c < NCOL; ++c) vop[c] = *reinterpret_cast<const u32x2_t*>(vcol + (16 * c + n) * P::VST);
+      for (int c0 = 0; c0 < NCOL; c0 += VG) {
+        u32x2_t vop[VG];
 #pragma unroll
-      for (int c = 0; c < NCOL; ++c) {
-        if constexpr (DT == kBf16) {
-          const u32x2_t vb = vop[c];
+        for (int c = 0; c < VG; ++c)
+          vop[c] = *reinterpret_cast<const u32x2_t*>(vcol + (16 * (c0 + c) + n) * P::VST);
 #pragma unroll
-          for (int rb = 0; rb < RBW; ++rb) {
-            acc[rb][c] = mfma16_bf16(phi[rb], vb, acc[rb][c]);
-            acc[rb][c] = mfma16_bf16(plo[rb], vb, acc[rb][c]);
+        for (int c = 0; c < VG; ++c) {
+          if constexpr (DT == kBf16) {
+            const u32x2_t vb = vop[c];
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+              acc[rb][c0 + c] = mfma16_bf16(phi[rb], vb, acc[rb][c0 + c]);
+              acc[rb][c0 + c] = mfma16_bf16(plo[rb], vb, acc[rb][c0 + c]);
+            }
+          } else {
+            const half4_t vb = __builtin_bit_cast(half4_t, vop[c]);
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) acc[rb][c0 + c] = mfma16(ph[rb], vb, acc[rb][c0 + c]);
           }
-        } else {
-          const half4_t vb = __builtin_bit_cast(half4_t, vop[c]);
-#pragma unroll
-          for (int rb = 0; rb < RBW; ++rb) acc[rb][c] = mfma16(ph[rb], vb, acc[rb][c]);
         }
       }
     }
@@ -615,7 +638,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     // unpack the next tile into the other buffer (nobody reads it during this
     // tile), then one barrier: it is complete, and this tile's buffer is free
     if (more)
-      stage_ptile<DT, MODE, D>(T, tid, lds + (cur ^ 1) * BUF_ELEMS, lds + (cur ^ 1) * BUF_ELEMS + KTILE_ELEMS,
+      stage_ptile<DT, MODE, D, W>(T, tid, lds + (cur ^ 1) * BUF_ELEMS, lds + (cur ^ 1) * BUF_ELEMS + KTILE_ELEMS,
                                ksc[cur ^ 1], vsc[cur ^ 1]);
     __syncthreads();
   }
@@ -673,16 +696,33 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   }
 }
 
-template <int DT, int MODE, int D>
-hipError_t launch_d(const PrefillArgs& a, int B, hipStream_t st) {
-  const long nx = ((long)a.R + kPRows<D> - 1) / kPRows<D>;
+template <int DT, int MODE, int D, int W>
+hipError_t launch_w(const PrefillArgs& a, int B, hipStream_t st) {
+  const long nx = ((long)a.R + kPRows<D, W> - 1) / kPRows<D, W>;
   if (nx > 0x7FFFFFFFL) return hipErrorInvalidValue;
   dim3 grid((unsigned)nx, a.c.Hkv, B);
   if (a.softcap > 0.0f)
-    hipLaunchKernelGGL((prefill_kernel<DT, MODE, D, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<DT, MODE, D, W, true>), grid, dim3(64 * W), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<DT, MODE, D, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<DT, MODE, D, W, false>), grid, dim3(64 * W), 0, st, a);
   return hipGetLastError();
+}
+
+template <int DT, int MODE, int D>
+hipError_t launch_d(const PrefillArgs& a, int B, hipStream_t st) {
+  if constexpr (D == 256) {
+    // An 8-wavefront workgroup (128 rows) gets through its rows S times faster
+    // than a 4-wavefront one (measured on MI355X at 32K + 1K tokens: S = 1.66
+    // int4, 1.63 bf16, 1.27 int8, whose unpack weighs more).  Rows per CU in
+    // rounds of one workgroup per CU: 8 wavefronts when 2 r8 / S < r4.
+    const long nx8 = ((long)a.R + kPRows<D, 8> - 1) / kPRows<D, 8>;
+    const long nx4 = ((long)a.R + kPRows<D, 4> - 1) / kPRows<D, 4>;
+    const long r8 = (nx8 * a.c.Hkv * B + kNumCUs - 1) / kNumCUs;
+    const long r4 = (nx4 * a.c.Hkv * B + kNumCUs - 1) / kNumCUs;
+    constexpr long S100 = (DT == kInt4 || DT == kBf16) ? 160 : 125;
+    if (2 * r8 * 100 < r4 * S100) return launch_w<DT, MODE, D, 8>(a, B, st);
+  }
+  return launch_w<DT, MODE, D, 4>(a, B, st);
 }
 
 }  // namespace

@@ -110,6 +110,29 @@ def test_prefill_bf16_cache():
     _check(w, "prefill bf16 cache")
 
 
+def _eight_wave_rounds(R: int, hkv: int, B: int, s100: int) -> bool:
+    """The library's choice at D = 256: 8 wavefronts (128 rows) per workgroup
+    when 2 r8 / S < r4, r = workgroups per CU rounded up (256 CUs)."""
+    r8 = -(-(-(-R // 128)) * hkv * B // 256)
+    r4 = -(-(-(-R // 64)) * hkv * B // 256)
+    return 2 * r8 * 100 < r4 * s100
+
+
+@pytest.mark.parametrize("dtype,mode,vmode,extra", [
+    (INT8, PER_ROW, None, {}), (INT4, PER_CHANNEL, None, {}), (FP8, PER_TENSOR, None, {"sink": True}),
+    (BF16, 0, None, {}), (INT8, PER_CHANNEL, PER_ROW, {"softcap": 10.0, "window": 200}),
+    (INT4, PER_ROW, PER_TENSOR, {})])
+def test_prefill_eight_wavefront_workgroups(dtype, mode, vmode, extra):
+    """Head dim 256 with enough rows that the kernel runs 128-row workgroups
+    of 8 wavefronts: 8 KV heads x 8 grouped heads x a 272-token chunk."""
+    s100 = 160 if dtype in (INT4, BF16) else 125
+    assert _eight_wave_rounds(8 * 272, 8, 1, s100)
+    w = ki.random_workload(8800 + 10 * dtype + mode, B=1, Hkv=8, G=8, D=256, Tq=272, lens=[340],
+                           dtype=dtype, mode=mode, v_mode=vmode, block_size=16 if dtype != INT8 else None,
+                           **extra)
+    _check(w, f"prefill 8 wavefronts dt={dtype} md={mode} vmd={vmode} {extra}")
+
+
 @pytest.mark.parametrize("cap,win", [(20.0, 0), (0.0, 50), (5.0, 300)])
 def test_prefill_softcap_window(cap, win):
     w = ki.random_workload(8400 + win, B=2, Hkv=2, G=3, D=128, Tq=90, lens=[600, 95], dtype=INT8,
