@@ -62,7 +62,12 @@ constexpr int kPRows = 16 * kPRowBlocks<D> * W;  // query rows per workgroup
 template <int DT, int D, int W>
 struct PGeo {
   static constexpr int ROWB = (DT == kInt4) ? D / 2 : (DT == kBf16) ? 2 * D : D;
-  static constexpr int KST = D + 8;      // K tile row stride in LDS (16-bit elements)
+  // The integer caches take S^T on the int8 MFMA: their K tile holds the codes
+  // as bytes (int4: 16 n), rows of D + 16 bytes; the others hold fp16 rows of
+  // D + 8 elements.  KST is the row stride in 16-bit elements either way.
+  static constexpr bool IQK = DT == kInt8 || DT == kInt4;
+  static constexpr int KST = IQK ? (D + 16) / 2 : D + 8;
+  static constexpr int ISTEPS = D / 64;  // 16x16x64 int8 MFMAs per S^T sub-tile (and q half)
   static constexpr int VST = kPT + 8;    // transposed V row stride (16-bit elements)
   static constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per S^T sub-tile
   static constexpr int NCOL = D / 16;    // 16-channel output column blocks
@@ -177,45 +182,32 @@ __device__ __forceinline__ void load_ptile(const PrefillArgs& a, int b, int hkv,
   }
 }
 
-// int4: one dword of 8 nibbles -> 16 * n as fp16 in natural channel order.
-__device__ __forceinline__ void int4x8_to_h_ordered(uint32_t w, uint32_t out[4]) {
-  const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  const uint32_t x = w ^ 0x88888888u;
-  const uint32_t ev = (x << 4) & 0xF0F0F0F0u;  // 16 (n_even + 8) per byte
-  const uint32_t od = x & 0xF0F0F0F0u;         // 16 (n_odd + 8)
-  const uint32_t lo = perm(od, ev, 0x05010400u);  // (n0, n1, n2, n3)
-  const uint32_t hi = perm(od, ev, 0x07030602u);  // (n4, n5, n6, n7)
-  out[0] = pk_add_h(perm(kMagic, lo, 0x04010400u), bias);
-  out[1] = pk_add_h(perm(kMagic, lo, 0x04030402u), bias);
-  out[2] = pk_add_h(perm(kMagic, hi, 0x04010400u), bias);
-  out[3] = pk_add_h(perm(kMagic, hi, 0x04030402u), bias);
-}
-
-// Unpack a loaded tile into LDS: K rows as fp16 (bf16 as is), V transposed to
-// [channel][token], per-row scales.
+// Unpack a loaded tile into LDS: K rows as int8 bytes (int8, int4 as 16 n) or
+// fp16 (fp8; bf16 as is), V transposed to [channel][token] as fp16 (bf16),
+// per-row scales.
 template <int DT, int MODE, int D, int W>
 __device__ __forceinline__ void stage_ptile(const PTile<DT, D, W>& T, int tid, uint16_t* ks_lds,
                                             uint16_t* vt_lds, float* ksc, float* vsc) {
   using P = PGeo<DT, D, W>;
   {
     // this thread's part of its row: channels (D / KP) * (tid % KP) .. + D / KP
-    uint16_t* dst = ks_lds + (tid / P::KP) * P::KST + (D / P::KP) * (tid % P::KP);
+    uint16_t* dst = ks_lds + (tid / P::KP) * P::KST + (P::IQK ? (D / P::KP) / 2 : (D / P::KP)) * (tid % P::KP);
     constexpr int NW = P::KQB / 4;  // dwords loaded
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const uint32_t kw = T.kok ? T.k[i] : 0u;
-      if constexpr (DT == kBf16) {
+      if constexpr (DT == kInt8) {
+        reinterpret_cast<uint32_t*>(dst)[i] = kw;  // the codes as they are
+      } else if constexpr (P::IQK) {
+        // 8 nibbles -> the bytes 16 n in channel order
+        const uint32_t ev = (kw << 4) & 0xF0F0F0F0u, od = kw & 0xF0F0F0F0u;
+        *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint32_t*>(dst) + 2 * i) =
+            u32x2_t{perm(od, ev, 0x05010400u), perm(od, ev, 0x07030602u)};
+      } else if constexpr (DT == kBf16) {
         reinterpret_cast<uint32_t*>(dst)[i] = kw;
-      } else if constexpr (DT == kInt4) {
-        uint32_t h[4];
-        int4x8_to_h_ordered(kw, h);
-        *reinterpret_cast<u32x4_t*>(dst + 8 * i) = u32x4_t{h[0], h[1], h[2], h[3]};
-      } else {
+      } else {  // fp8 -> fp16
         uint32_t lo, hi;
-        if constexpr (DT == kInt8)
-          int8x4_to_h(kw, lo, hi);
-        else
-          fp8x4_to_h(kw, lo, hi);
+        fp8x4_to_h(kw, lo, hi);
         *reinterpret_cast<u32x2_t*>(dst + 4 * i) = u32x2_t{lo, hi};
       }
     }
@@ -288,7 +280,8 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
   constexpr int BUF_ELEMS = KTILE_ELEMS + VTILE_ELEMS;
   // two tile buffers (K rows, transposed V): one is read while the next tile
   // is unpacked into the other; after the loop the output staging reuses them
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF_ELEMS];
+  constexpr int OUT_ELEMS = W * 16 * RBW * (D + 4) * 2;  // the output staging, fp32
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF_ELEMS > OUT_ELEMS ? 2 * BUF_ELEMS : OUT_ELEMS];
   __shared__ float ksc[2][kPT], vsc[2][kPT];
   __shared__ float rowf[W][16 * RBW], rowsink[W][16 * RBW];
   static_assert(W * 16 * RBW * (D + 4) * 4 <= (int)sizeof(lds), "output staging does not fit");
@@ -334,7 +327,11 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
   wlim_min = __builtin_amdgcn_readfirstlane(wlim_min);
   wlo_max = __builtin_amdgcn_readfirstlane(wlo_max);
 
-  // q operand: row r, channels 32 ks + 8 g + 0..7 (zero rows past R)
+  // q operand: row r, channels 32 ks + 8 g + 0..7 (zero rows past R).
+  // Integer caches: channels 64 st + 16 g + 0..15 of the row as a 15-bit
+  // integer vector qi = rne(q 2^(14 - ex)), |q| < 2^ex, split as qi = 256 hi +
+  // lo (hi in [-64, 64], lo in [-128, 127]); qb[rb][2 st] holds hi,
+  // qb[rb][2 st + 1] lo, as int8 bytes.
   half8_t qb[RBW][KSTEPS];
   float rowmul[RBW];
 #pragma unroll
@@ -342,6 +339,51 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
     const int r = rwave + 16 * rb + n;
     const int rr = r < a.R ? r : 0;
     const uint16_t* src = a.q + (((size_t)b * a.Tq + rr / a.G) * a.Hq + (size_t)hkv * a.G + rr % a.G) * D;
+    if constexpr (P::IQK) {
+      float qv[P::ISTEPS][16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int st = 0; st < P::ISTEPS; ++st) {
+        const int c0 = 64 * st + 16 * g;
+        u32x4_t r0 = *reinterpret_cast<const u32x4_t*>(src + c0);
+        u32x4_t r1 = *reinterpret_cast<const u32x4_t*>(src + c0 + 8);
+        if (r >= a.R) r0 = r1 = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qv[st][2 * i] = __uint_as_float(r0[i] << 16);
+          qv[st][2 * i + 1] = __uint_as_float(r0[i] & 0xFFFF0000u);
+          qv[st][8 + 2 * i] = __uint_as_float(r1[i] << 16);
+          qv[st][8 + 2 * i + 1] = __uint_as_float(r1[i] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+          if constexpr (MODE == kPerChannel) qv[st][p] *= a.c.k_scales[(size_t)hkv * D + c0 + p];
+          amax = fmaxf(amax, fabsf(qv[st][p]));
+        }
+      }
+      amax = group_max4(amax);
+      int ex = 0;
+      if (amax > 0.0f) (void)frexpf(amax, &ex);
+#pragma unroll
+      for (int st = 0; st < P::ISTEPS; ++st) {
+        u32x4_t hw = {0u, 0u, 0u, 0u}, lw = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+          const int qi = (int)__builtin_rintf(ldexpf(qv[st][p], 14 - ex));
+          const int hi = (qi + 128) >> 8;
+          const int lo8 = qi - hi * 256;
+          hw[p / 4] |= ((uint32_t)hi & 0xFFu) << (8 * (p % 4));
+          lw[p / 4] |= ((uint32_t)lo8 & 0xFFu) << (8 * (p % 4));
+        }
+        qb[rb][2 * st] = __builtin_bit_cast(half8_t, hw);
+        qb[rb][2 * st + 1] = __builtin_bit_cast(half8_t, lw);
+      }
+      float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
+      if constexpr (MODE == kPerTensor) mul *= a.c.k_scales[0];
+      if constexpr (DT == kInt4) mul *= 0.0625f;  // K tile holds 16 * code
+      rowmul[rb] = ldexpf(mul, ex - 14);
+      continue;
+    }
     u32x4_t raw[KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -434,10 +476,18 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
     constexpr int KB = W > 4 ? 1 : 2;
     half8_t kop[KB][KSTEPS];
     auto kread = [&](int s, half8_t (&dst)[KSTEPS]) {
-      const uint16_t* krow = ks_lds + (16 * s + n) * P::KST + 8 * g;
+      if constexpr (P::IQK) {
+        // 16 code bytes of channels 64 st + 16 g .. + 15 per integer step
+        const uint8_t* krow = reinterpret_cast<const uint8_t*>(ks_lds + (16 * s + n) * P::KST) + 16 * g;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        dst[ks] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(krow + 32 * ks));
+        for (int st = 0; st < P::ISTEPS; ++st)
+          dst[st] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(krow + 64 * st));
+      } else {
+        const uint16_t* krow = ks_lds + (16 * s + n) * P::KST + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+          dst[ks] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(krow + 32 * ks));
+      }
     };
     if constexpr (KB == 2) kread(0, kop[0]);
 #pragma unroll
@@ -453,8 +503,24 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
         s0[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
         s1[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
       }
+      if constexpr (P::IQK) {
+        // exact integer dot products with the two q halves (hi * 256 + lo stays
+        // below 2^30), as floats in s0
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ks += 2) {
+        for (int rb = 0; rb < RBW; ++rb) {
+          i32x4_t h = {0, 0, 0, 0}, l = {0, 0, 0, 0};
+#pragma unroll
+          for (int st = 0; st < P::ISTEPS; ++st) {
+            const i32x4_t ka = __builtin_bit_cast(i32x4_t, kop[s % KB][st]);
+            h = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qb[rb][2 * st]), h);
+            l = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qb[rb][2 * st + 1]), l);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s0[rb][e] = (float)(h[e] * 256 + l[e]);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < (P::IQK ? 0 : KSTEPS); ks += 2) {
         const half8_t k0 = kop[s % KB][ks];
         const half8_t k1 = kop[s % KB][ks + 1 < KSTEPS ? ks + 1 : ks];
 #pragma unroll
