@@ -289,6 +289,19 @@ def test_wavefront_reads_more_than_64_tiles(paged):
     gu.run_and_check(w, f"{per_wave} tiles per wavefront paged={paged}")
 
 
+def test_more_than_256_chunks_per_sequence():
+    """One KV head over 140,000 tokens with 128-byte rows (int8 at D 128: two
+    workgroups per CU once a chunk keeps 16 tiles): the sequence gets more than
+    256 chunks, so each of the combine's threads merges the statistics of
+    several chunks."""
+    L = 140000
+    w = ki.random_workload(4800, B=1, Hkv=1, G=4, D=128, Tq=1, lens=[L], dtype=INT8, mode=PER_ROW,
+                           block_size=None)
+    S = kvq.num_splits(gu.gpu_cache(w), 1, 4, 1, L)
+    assert S > 256, S
+    gu.run_and_check(w, f"{S} chunks, one KV head")
+
+
 def test_query_tokens_beyond_length():
     """Tq larger than the cached length: early drafts see nothing and output zeros."""
     w = ki.random_workload(77, B=1, Hkv=1, G=2, D=64, Tq=6, lens=[3], dtype=INT8, mode=PER_ROW,
