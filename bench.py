@@ -472,7 +472,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("bf16 MFMA, f32 accumulate" if args.dtype == "bf16"
-                  else "f16 MFMA, f32 accumulate"),
+                  else "i8 MFMA (Q.K, i32 accumulate) + f16 MFMA (P.V, f32 accumulate)"),
         "data": "synthetic",
         "config": {
             "workload": f"decode B1 Hq24 Hkv4 D256, "
