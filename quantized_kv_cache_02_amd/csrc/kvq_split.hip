@@ -896,10 +896,10 @@ split_decode_kernel(SplitArgs a) {
   // ---- merge the 4 wavefronts in fixed order, write the split partial.
   // Each wavefront publishes its row statistics; after the barrier (every loop
   // has ended, so the q staging area is free) it writes its raw accumulator
-  // rows to its own LDS buffer while one lane per row turns the statistics into
-  // the four per-wavefront weights; the readback then sums the weighted buffers
-  // in wave order.  The weight chain runs on a few lanes beside the writes
-  // rather than in front of them.
+  // rows to its own LDS buffer while one lane per row of the last wavefront
+  // turns the statistics into the four per-wavefront weights (first, so the
+  // chain overlaps the other wavefronts' writes); the readback then sums the
+  // weighted buffers in wave order.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float lsum = group_sum4(W.l[rb]);
@@ -912,6 +912,35 @@ split_decode_kernel(SplitArgs a) {
     if (lane == 0) s_vref[wave] = W.vref;
   __syncthreads();
 
+  // the chunk's statistics of row r (log2 units) and the weight of each
+  // wavefront's rows: exp2(m_w - M) / L (times its V reference; 1/16 for int4,
+  // whose V operand holds 16 * code), computed before this wavefront's own
+  // accumulator writes so that the chain does not wait behind them
+  constexpr int kStatWave = kWaves - 1;
+  if (wave == kStatWave && lane < Rw) {
+    const int r = lane;
+    float M = s_m[0][r];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+    float Lt = 0.0f;
+    float ew[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      // the hardware exp2, as in the tile loop (results below 2^-126 flush to 0)
+      ew[w] = M != -INFINITY ? __builtin_amdgcn_exp2f(s_m[w][r] - M) : 0.0f;
+      Lt += s_l[w][r] * ew[w];
+    }
+    const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      float f = ew[w] * inv;
+      if constexpr (kVRow) f *= s_vref[w];
+      if constexpr (DT == kInt4) f *= 0.0625f;
+      s_f[w][r] = f;
+    }
+    a.ws_m[((size_t)hkv * a.R + row0 + r) * a.S + slot] = M;
+    a.ws_l[((size_t)hkv * a.R + row0 + r) * a.S + slot] = Lt;
+  }
   // Lane column n owns NCOL channels, NCOL / 4 groups of 4 consecutive ones
   // (see group_owner); they go to the lane's NCOL-float LDS slot as 16-byte
   // chunks whose order is rotated by n / (64 / NCOL) so the 16 lanes of a pass
@@ -936,32 +965,6 @@ split_decode_kernel(SplitArgs a) {
           }
         }
       }
-  }
-  // the chunk's statistics of row r (log2 units) and the weight of each
-  // wavefront's rows: exp2(m_w - M) / L (times its V reference; 1/16 for int4,
-  // whose V operand holds 16 * code)
-  constexpr int kStatWave = kWaves - 1;
-  if (wave == kStatWave && lane < Rw) {
-    const int r = lane;
-    float M = s_m[0][r];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
-    float Lt = 0.0f;
-    float ew[kWaves];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      ew[w] = M != -INFINITY ? exp2f(s_m[w][r] - M) : 0.0f;
-      Lt += s_l[w][r] * ew[w];
-    }
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      float f = Lt > 0.0f ? ew[w] / Lt : 0.0f;
-      if constexpr (kVRow) f *= s_vref[w];
-      if constexpr (DT == kInt4) f *= 0.0625f;
-      s_f[w][r] = f;
-    }
-    a.ws_m[((size_t)hkv * a.R + row0 + r) * a.S + slot] = M;
-    a.ws_l[((size_t)hkv * a.R + row0 + r) * a.S + slot] = Lt;
   }
   __syncthreads();
 
