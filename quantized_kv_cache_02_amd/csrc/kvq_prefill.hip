@@ -68,11 +68,11 @@ struct PGeo {
   static constexpr bool IQK = DT == kInt8 || DT == kInt4;
   static constexpr int KST = IQK ? (D + 16) / 2 : D + 8;
   static constexpr int ISTEPS = D / 64;  // 16x16x64 int8 MFMAs per S^T sub-tile (and q half)
-  // transposed V row stride (16-bit elements), chosen by measurement on MI355X:
-  // kPT + 4 for int4 (chunked prefill after 16K-32K tokens 13-14 % faster than
-  // with kPT + 8), kPT + 8 for the others (kPT + 4 made int8 5 % and bf16 over
-  // 2x slower there)
-  static constexpr int VST = DT == kInt4 ? kPT + 4 : kPT + 8;
+  // transposed V row stride (16-bit elements): 42 dwords.  Measured on MI355X
+  // (chunked prefill, 1-2K tokens after 16-32K): 84 beats 72 by 12 % for int8
+  // and 22 % for bf16 and ties the best int4 stride; 76 does about as well,
+  // 72 and 80 (multiples of 4 dwords) are slow, and 68 was fast for int4 only.
+  static constexpr int VST = kPT + 20;
   static constexpr int KSTEPS = D / 32;  // 16x16x32 MFMAs per S^T sub-tile
   static constexpr int NCOL = D / 16;    // 16-channel output column blocks
   static constexpr int NT = 64 * W;
