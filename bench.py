@@ -420,7 +420,7 @@ def main():
 
     if args.prefill:
         with open(args.prefill, "w") as f:
-            for dt in ("int8", "int4", "bf16"):
+            for dt in ("int8", "int4", "fp8", "bf16"):
                 for past, chunk in ((0, 2048), (16384, 2048), (32768, 1024), (4096, 512)):
                     r = time_prefill(kvq, torch, ki, dt, past, chunk, 4, 8, dev)
                     r["attend_frac_of_fp16_peak"] = r["attend_TFLOPs"] * 1e12 / PEAK_F16_FLOPS
