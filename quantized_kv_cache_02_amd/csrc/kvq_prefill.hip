@@ -783,14 +783,14 @@ hipError_t launch_d(const PrefillArgs& a, int B, hipStream_t st) {
   if constexpr (D == 256) {
     // An 8-wavefront workgroup (128 rows) gets through its rows S times faster
     // than a 4-wavefront one (measured on MI355X at 32K + 1K tokens: S = 1.66
-    // int4, 1.63 bf16; 1.27 for int8 while its K tile was unpacked to fp16,
-    // the value kept for fp8, whose K tile still is).  Rows per CU in rounds
-    // of one workgroup per CU: 8 wavefronts when 2 r8 / S < r4.
+    // int4, 1.63 bf16; taken as 1.6 for every cache: with the 84-half V stride
+    // it put fp8 at 16K + 2K on 8 wavefronts, 282 -> 360 TFLOP/s).  Rows per
+    // CU in rounds of one workgroup per CU: 8 wavefronts when 2 r8 / S < r4.
     const long nx8 = ((long)a.R + kPRows<D, 8> - 1) / kPRows<D, 8>;
     const long nx4 = ((long)a.R + kPRows<D, 4> - 1) / kPRows<D, 4>;
     const long r8 = (nx8 * a.c.Hkv * B + kNumCUs - 1) / kNumCUs;
     const long r4 = (nx4 * a.c.Hkv * B + kNumCUs - 1) / kNumCUs;
-    constexpr long S100 = DT == kFp8 ? 125 : 160;
+    constexpr long S100 = 160;
     if (2 * r8 * 100 < r4 * S100) return launch_w<DT, MODE, D, 8>(a, B, st);
   }
   return launch_w<DT, MODE, D, 4>(a, B, st);

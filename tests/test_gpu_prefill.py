@@ -112,7 +112,8 @@ def test_prefill_bf16_cache():
 
 def _eight_wave_rounds(R: int, hkv: int, B: int, s100: int) -> bool:
     """The library's choice at D = 256: 8 wavefronts (128 rows) per workgroup
-    when 2 r8 / S < r4, r = workgroups per CU rounded up (256 CUs)."""
+    when 2 r8 / S < r4 (S = 1.6 for every cache), r = workgroups per CU rounded
+    up (256 CUs)."""
     r8 = -(-(-(-R // 128)) * hkv * B // 256)
     r4 = -(-(-(-R // 64)) * hkv * B // 256)
     return 2 * r8 * 100 < r4 * s100
@@ -125,8 +126,7 @@ def _eight_wave_rounds(R: int, hkv: int, B: int, s100: int) -> bool:
 def test_prefill_eight_wavefront_workgroups(dtype, mode, vmode, extra):
     """Head dim 256 with enough rows that the kernel runs 128-row workgroups
     of 8 wavefronts: 8 KV heads x 8 grouped heads x a 272-token chunk."""
-    s100 = 160 if dtype in (INT4, BF16) else 125
-    assert _eight_wave_rounds(8 * 272, 8, 1, s100)
+    assert _eight_wave_rounds(8 * 272, 8, 1, 160)
     w = ki.random_workload(8800 + 10 * dtype + mode, B=1, Hkv=8, G=8, D=256, Tq=272, lens=[340],
                            dtype=dtype, mode=mode, v_mode=vmode, block_size=16 if dtype != INT8 else None,
                            **extra)
