@@ -64,6 +64,98 @@ def test_fp8_encoder_every_bf16_value(oracle_lib, scale):
     np.testing.assert_array_equal(codes[0].astype(np.int64), want)
 
 
+# --------------------------------------------------- per-channel static scales
+# "[CUDA] Add INT4 paged KV cache with per-channel scales", opening description
+# and "Motivation and Context": static per-channel scales are per-(KV head,
+# side) tables, element d of a row divided by its own channel's scale.
+
+def _channel_table(D: int, seed: int) -> np.ndarray:
+    """D distinct scales spanning 2^-20 .. 2^20, with 0, 2^-130 (subnormal),
+    2^100, 1 and 3/7 among them."""
+    rng = np.random.default_rng(seed)
+    s = (2.0 ** rng.uniform(-20, 20, size=D)).astype(np.float32)
+    s[[3, 17, 40, 41, 60]] = [0.0, 2.0 ** -130, 2.0 ** 100, 1.0, 3.0 / 7.0]
+    assert len(np.unique(s)) == D
+    return s
+
+
+@pytest.mark.parametrize("dtype,qmax", [(INT8, 127), (INT4, 7), (FP8, 448)])
+def test_per_channel_encoder_every_bf16_value(oracle_lib, dtype, qmax):
+    """Every finite bf16 value quantized under a per-channel table: element d's code
+    is the brute-force nearest code to fp32(x_d / s_d), 0 where s_d = 0.  The values
+    are laid out in rows of D = 256 and rotated 4 times, so each value meets 4
+    channels (4 different scales)."""
+    bits, f = bf.all_finite_bf16()
+    D = 256
+    n = len(bits) // D * D
+    table = _channel_table(D, 31 + dtype)
+    for rot in (0, 1, 97, 200):
+        rb = np.roll(bits[:n], rot).reshape(-1, D)
+        rf = np.roll(f[:n], rot).reshape(-1, D)
+        codes, scales = oracle_lib.quantize_rows(rb, dtype, PER_CHANNEL, table)
+        assert not scales.any()  # a static mode writes no row scale
+        with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+            y = (rf / table[None, :]).astype(np.float32)
+        y = np.where(table[None, :] == 0, np.float32(0), y)
+        if dtype == FP8:
+            want = bf.fp8_codes_argmin(y.ravel()).reshape(y.shape)
+            want = np.where(table[None, :] == 0, 0, want)  # s = 0 gives code 0x00
+            got = codes.astype(np.int64)
+        else:
+            want = bf.int_codes_argmin(y.ravel(), qmax).reshape(y.shape)
+            got = codes.view(np.int8).astype(np.int64) if dtype == INT8 else _unpack_int4(codes)
+        np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype,qmax", [(INT8, 127), (INT4, 7), (FP8, 448)])
+@pytest.mark.parametrize("paged", [False, True])
+def test_per_channel_append_and_dequantize_per_head(oracle_lib, dtype, qmax, paged):
+    """Three KV heads with different per-channel tables (K and V tables differ
+    too): every appended row's codes are the brute-force codes under its own
+    head's table, and dequantize returns code x s[h, d] with the code read
+    straight from the cache bytes."""
+    Hkv, D, B, L = 3, 64, 2, 37
+    rng = np.random.default_rng(90 + dtype + 10 * paged)
+    kt = np.stack([_channel_table(D, 500 + h) for h in range(Hkv)]) * np.float32(0.01)
+    vt = np.stack([_channel_table(D, 600 + h) for h in range(Hkv)]) * np.float32(0.02)
+    kt, vt = kt.astype(np.float32), vt.astype(np.float32)
+    # data of the size of each channel's scale, so codes spread over the grid
+    k = torch.from_numpy((rng.standard_normal((B, L, Hkv, D)) * qmax / 3 * kt[None, None])
+                         .astype(np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy((rng.standard_normal((B, L, Hkv, D)) * qmax / 3 * vt[None, None])
+                         .astype(np.float32)).to(torch.bfloat16)
+    bs = 16 if paged else 48
+    mb = (L + bs - 1) // bs if paged else 1
+    nb = B * mb
+    table = rng.permutation(nb).astype(np.int32).reshape(B, mb) if paged else None
+    c = oracle_lib.Cache(dtype, PER_CHANNEL, Hkv, D, bs, nb, kt, vt)
+    c.append(_bits(k), _bits(v), np.zeros(B, np.int32), table)
+    lens = np.full(B, L, np.int32)
+    Kd, Vd = c.dequantize(lens, table)
+    kf, vf = k.float().numpy(), v.float().numpy()
+    for b in range(B):
+        for p in range(L):
+            blk = b if table is None else table[b, p // bs]
+            for h in range(Hkv):
+                for side, x, tab, codes, deq in (("K", kf, kt, c.k_codes, Kd), ("V", vf, vt, c.v_codes, Vd)):
+                    row = codes[blk, h, p % bs]
+                    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+                        y = (x[b, p, h] / tab[h]).astype(np.float32)
+                    y = np.where(tab[h] == 0, np.float32(0), y)
+                    if dtype == FP8:
+                        want = np.where(tab[h] == 0, 0, bf.fp8_codes_argmin(y))
+                        got = row.astype(np.int64)
+                        val = bf.fp8_value_table()[row]
+                    else:
+                        want = bf.int_codes_argmin(y, qmax)
+                        got = row.view(np.int8).astype(np.int64) if dtype == INT8 else _unpack_int4(row[None])[0]
+                        val = got.astype(np.float64)
+                    np.testing.assert_array_equal(got, want, err_msg=f"{side} b={b} p={p} h={h}")
+                    # x-hat = float(c) * s, one fp32 multiply
+                    xh = (val.astype(np.float32) * tab[h]).astype(np.float32)
+                    np.testing.assert_array_equal(deq[b, h, p], xh, err_msg=f"{side} dequant h={h}")
+
+
 def test_fp8_encoder_matches_torch_cast_in_range(oracle_lib):
     """torch's float32 -> float8_e4m3fn cast (round to nearest even) agrees with the
     oracle wherever no saturation is involved."""
