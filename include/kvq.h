@@ -172,8 +172,10 @@ size_t kvq_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_
  *               INCLUDING the q_tokens query tokens, which are the last ones.
  *               Query j sits at position seq_lens[b] - q_tokens + j and sees the
  *               tokens at or before it (causal among speculative drafts, [F]
- *               int4 XQA speculative decode).  Values above max_seq_len are
- *               treated as max_seq_len; 0 gives a zero output.
+ *               int4 XQA speculative decode).  A value above max_seq_len is
+ *               treated as max_seq_len by every entry point, for reading and
+ *               (fused append, prefill) for writing alike; 0 or less gives a
+ *               zero output.
  *   max_seq_len host upper bound on seq_lens, <= the capacity; sizes the grid.
  *   softmax_scale logits are softmax_scale * q . k (usually 1/sqrt(head_dim)).
  *   head_sink   fp32 [num_q_heads] or NULL: per-head sink logit in post-scale
@@ -213,14 +215,16 @@ int kvq_paged_decode_attend(const kvq_cache* cache, const void* q, int32_t batch
  * runs the paged decode; [K] "Usage": append(k, v) followed by attend(q)).
  *
  *   k_new, v_new  bf16 [batch, q_tokens, num_kv_heads, head_dim]: row j of
- *                 sequence b is written at position seq_lens[b] - q_tokens + j
- *                 (the query tokens are the last tokens of the sequence).
+ *                 sequence b is written at position L_b - q_tokens + j, with
+ *                 L_b = min(seq_lens[b], max_seq_len) (the query tokens are the
+ *                 last tokens of the sequence); rows before position 0 are not
+ *                 written.
  *   block_table   int32 [batch, max_blocks], or NULL for the contiguous cache.
  *   Everything else as kvq_decode_attend / kvq_paged_decode_attend.
  *
  * The cache afterwards holds exactly what kvq_append(k_new, v_new,
- * positions = seq_lens - q_tokens) would have written, and `out` equals that
- * append followed by the decode.  The new rows are quantized inside the decode
+ * positions = min(seq_lens, max_seq_len) - q_tokens) would have written, and
+ * `out` equals that append followed by the decode.  The new rows are quantized inside the decode
  * kernel by the wavefront that reads them, which saves a launch per step.
  */
 int kvq_append_decode_attend(const kvq_cache* cache, const void* k_new, const void* v_new,
@@ -282,10 +286,11 @@ int kvq_combine(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int3
  *
  *   k_new, v_new  bf16 [batch, q_tokens, num_kv_heads, head_dim], both or
  *                 neither: written first, like kvq_append, at positions
- *                 seq_lens[b] - q_tokens + j; NULL when the chunk is already in
- *                 the cache
+ *                 min(seq_lens[b], max_seq_len) - q_tokens + j; NULL when the
+ *                 chunk is already in the cache
  *   q             bf16 [batch, q_tokens, num_q_heads, head_dim]
- *   seq_lens      int32 [batch] (device): tokens of each sequence after the chunk
+ *   seq_lens      int32 [batch] (device): tokens of each sequence after the
+ *                 chunk; a value above max_seq_len is treated as max_seq_len
  *   out           bf16 [batch, q_tokens, num_q_heads, head_dim]
  *   options       soft cap / sliding window as kvq_attend_ex, or NULL
  *   Everything else as kvq_attend_ex.  Query token j of sequence b sits at
@@ -294,7 +299,7 @@ int kvq_combine(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int3
  *   the dequantized cache, like the decode, so a chunk of one token is a
  *   decode step.  Tokens before position 0 output zeros.  q_tokens has no
  *   upper bound beyond G * q_tokens < 2^30; no workspace is needed (one
- *   workgroup owns 64 query rows of one KV head over all its tokens).
+ *   workgroup owns 64 or 128 query rows of one KV head over all its tokens).
  *   Two launches on `stream` (append, attention); graph-capturable.
  */
 int kvq_prefill_attend(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
@@ -312,19 +317,6 @@ int kvq_prefill_attend(const kvq_cache* cache, const void* k_new, const void* v_
  */
 size_t kvq_cache_bytes(int32_t dtype, int32_t scale_mode, int32_t num_kv_heads, int32_t head_dim,
                        int64_t tokens);
-
-/*
- * kvq_stream_read -- a measurement aid, no part of attention: reads `bytes`
- * (a multiple of 16) at `src` once with the loads the decode uses
- * (non-temporal, 16 bytes per lane), `workgroups` workgroups of 256 threads
- * each reading one contiguous slice, and does nothing else.  Its duration is
- * the HBM floor for reading that many bytes, the reference the decode's
- * KV-read rate is set against.  `sink` must hold workgroups * 4096 bytes; a
- * thread stores there only if the XOR of what it read equals one fixed 64-bit
- * pattern.  KVQ_EINVAL for a NULL pointer, bytes % 16 != 0 or workgroups
- * outside [1, 65535].
- */
-int kvq_stream_read(const void* src, size_t bytes, int32_t workgroups, void* sink, void* stream);
 
 /* Human-readable name of a kvq_status (host, static storage). */
 const char* kvq_status_string(int status);

@@ -32,7 +32,7 @@ EXPORTS = (
     "kvq_append", "kvq_num_splits", "kvq_workspace_bytes", "kvq_decode_attend",
     "kvq_paged_decode_attend", "kvq_append_decode_attend", "kvq_attend_ex", "kvq_prefill_attend",
     "kvq_split_decode",
-    "kvq_combine", "kvq_cache_bytes", "kvq_stream_read",
+    "kvq_combine", "kvq_cache_bytes",
     "kvq_status_string",
 )
 
@@ -94,8 +94,6 @@ def lib():
         L.kvq_combine.restype = ctypes.c_int
         L.kvq_cache_bytes.argtypes = [I32, I32, I32, I32, ctypes.c_int64]
         L.kvq_cache_bytes.restype = SZ
-        L.kvq_stream_read.argtypes = [P, SZ, I32, P, P]
-        L.kvq_stream_read.restype = ctypes.c_int
         L.kvq_status_string.argtypes = [ctypes.c_int]
         L.kvq_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -106,6 +104,16 @@ def _check(status: int, what: str):
     if status != 0:
         msg = lib().kvq_status_string(status).decode()
         raise KvqError(f"{what}: {msg} ({status})")
+
+
+_STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL: invalid argument",
+           -2: "KVQ_EUNSUPPORTED: unsupported shape or type", -3: "KVQ_EHIP: HIP runtime error"}
+
+
+def _check_status_with(status: int, what: str):
+    """The same as _check for libraries other than libkvq (same status codes)."""
+    if status != 0:
+        raise KvqError(f"{what}: {_STATUS.get(status, 'unknown kvq status')} ({status})")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -122,11 +130,69 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _want(t: torch.Tensor, dtype, name: str):
+def _want(t, dtype, name: str, shape=None, numel=None):
+    """Check a tensor before its pointer crosses the C ABI, which cannot see
+    sizes: dtype, exact shape (or element count) and contiguity (the device is
+    checked by _on_gpu once every shape has passed).  A mismatch raises here
+    instead of making a kernel read or write past the end of an allocation."""
+    if not isinstance(t, torch.Tensor):
+        raise KvqError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
     if t.dtype != dtype:
         raise KvqError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise KvqError(f"{name} must be on the GPU")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise KvqError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise KvqError(f"{name} must hold {numel} elements, got {t.numel()}")
+    if not t.is_contiguous():
+        raise KvqError(f"{name} must be contiguous")
+
+
+def _query(cache: "KVCache", q):
+    """q bf16 [B, Tq, Hq, D] with D the cache's head_dim and Hq a multiple of Hkv."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise KvqError("q must be a 4-D tensor [batch, q_tokens, num_q_heads, head_dim]")
+    B, Tq, Hq, D = q.shape
+    if D != cache.head_dim:
+        raise KvqError(f"q has head_dim {D}, the cache {cache.head_dim}")
+    if Hq % cache.num_kv_heads != 0:
+        raise KvqError(f"num_q_heads {Hq} is not a multiple of num_kv_heads {cache.num_kv_heads}")
+    _want(q, torch.bfloat16, "q")
+    return B, Tq, Hq
+
+
+def _table(block_table, B: int) -> int:
+    """int32 [B, max_blocks] or None (contiguous); returns max_blocks (0 for None)."""
+    if block_table is None:
+        return 0
+    if not isinstance(block_table, torch.Tensor) or block_table.dim() != 2:
+        raise KvqError("block_table must be a 2-D int32 tensor [batch, max_blocks]")
+    _want(block_table, torch.int32, "block_table", shape=(B, block_table.shape[1]))
+    return block_table.shape[1]
+
+
+def _common(cache, B, Tq, Hq, seq_lens, head_sink=None, k_new=None, v_new=None, out=None):
+    """seq_lens int32 [B]; head_sink fp32 [Hq]; k_new, v_new bf16 [B, Tq, Hkv, D]
+    (both or neither); out bf16 [B, Tq, Hq, D]."""
+    _want(seq_lens, torch.int32, "seq_lens", numel=B)
+    if head_sink is not None:
+        _want(head_sink, torch.float32, "head_sink", numel=Hq)
+    if (k_new is None) != (v_new is None):
+        raise KvqError("k_new and v_new go together: pass both or neither")
+    if k_new is not None:
+        rows = (B, Tq, cache.num_kv_heads, cache.head_dim)
+        _want(k_new, torch.bfloat16, "k_new", shape=rows)
+        _want(v_new, torch.bfloat16, "v_new", shape=rows)
+    if out is not None:
+        _want(out, torch.bfloat16, "out", shape=(B, Tq, Hq, cache.head_dim))
+
+
+def _on_gpu(cache: "KVCache", **tensors):
+    """Every tensor that crosses the ABI, and the cache, live on the GPU."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise KvqError(f"{name} must be on the GPU")
+    if not cache.k_codes.is_cuda:
+        raise KvqError("the cache must live on the GPU")
 
 
 class KVCache:
@@ -146,6 +212,11 @@ class KVCache:
                  device="cuda", v_scale_mode: int = 0):
         if dtype == BF16:
             scale_mode, v_scale_mode = NO_SCALE, NO_SCALE
+        if dtype not in (INT8, INT4, FP8_E4M3FN, BF16):
+            raise KvqError(f"unknown cache dtype {dtype}")
+        if dtype != BF16 and (scale_mode not in (PER_ROW, PER_TENSOR, PER_CHANNEL)
+                              or v_scale_mode not in (0, PER_ROW, PER_TENSOR, PER_CHANNEL)):
+            raise KvqError(f"unknown scale mode {scale_mode} / {v_scale_mode}")
         self.dtype, self.scale_mode = dtype, scale_mode
         self.v_scale_mode = v_scale_mode
         vmode = v_scale_mode or scale_mode
@@ -162,7 +233,16 @@ class KVCache:
                 return torch.zeros(shape[:3], dtype=torch.float32, device=device)
             if static is None:
                 raise KvqError(f"a static {side} scale mode needs {side}_static")
-            return torch.as_tensor(static, dtype=torch.float32).reshape(-1).to(device)
+            t = torch.as_tensor(static, dtype=torch.float32).reshape(-1)
+            want = 1 if mode == PER_TENSOR else num_kv_heads * head_dim
+            if t.numel() != want:
+                raise KvqError(f"{side}_static must hold {want} scales "
+                               f"({'per-tensor: 1' if mode == PER_TENSOR else 'per-channel: Hkv * D'}), "
+                               f"got {t.numel()}")
+            tc = t.cpu()
+            if not bool(torch.isfinite(tc).all()) or bool((tc < 0).any()):
+                raise KvqError(f"{side}_static scales must be finite and >= 0")
+            return t.to(device).contiguous()
 
         self.k_scales = scales(scale_mode, k_static, "k")
         self.v_scales = scales(vmode, v_static, "v")
@@ -178,14 +258,15 @@ class KVCache:
 def append(cache: KVCache, k: torch.Tensor, v: torch.Tensor, positions: torch.Tensor,
            block_table: Optional[torch.Tensor] = None, stream=None) -> None:
     """Quantize and store k, v (bf16 [B, Tn, Hkv, D]) at positions[b] + j."""
-    _want(k, torch.bfloat16, "k")
-    _want(v, torch.bfloat16, "v")
-    _want(positions, torch.int32, "positions")
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise KvqError("k must be a 4-D tensor [batch, tokens, num_kv_heads, head_dim]")
     B, Tn = k.shape[0], k.shape[1]
-    mb = 0
-    if block_table is not None:
-        _want(block_table, torch.int32, "block_table")
-        mb = block_table.shape[1]
+    rows = (B, Tn, cache.num_kv_heads, cache.head_dim)
+    _want(k, torch.bfloat16, "k", shape=rows)
+    _want(v, torch.bfloat16, "v", shape=rows)
+    _want(positions, torch.int32, "positions", numel=B)
+    mb = _table(block_table, B)
+    _on_gpu(cache, k=k, v=v, positions=positions, block_table=block_table)
     _check(lib().kvq_append(cache.struct, _ptr(k), _ptr(v), B, Tn, _ptr(positions),
                             _ptr(block_table), mb, _stream(stream)), "kvq_append")
 
@@ -209,7 +290,19 @@ def _workspace(cache, B, Hq, Tq, max_seq_len, workspace, device):
     need = workspace_bytes(cache, B, Hq, Tq, max_seq_len)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    return workspace, workspace.numel() * workspace.element_size()
+    elif not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous() or not workspace.is_cuda:
+        raise KvqError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise KvqError(f"workspace holds {nbytes} bytes, the call needs {need}")
+    return workspace, nbytes
+
+
+def _out(q, out, cache, B, Tq, Hq):
+    if out is None:
+        return torch.empty_like(q)
+    _want(out, torch.bfloat16, "out", shape=(B, Tq, Hq, cache.head_dim))
+    return out
 
 
 def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
@@ -217,10 +310,10 @@ def decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_s
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
     """Decode attention over a contiguous cache.  q bf16 [B, Tq, Hq, D] -> out bf16."""
-    _want(q, torch.bfloat16, "q")
-    _want(seq_lens, torch.int32, "seq_lens")
-    B, Tq, Hq, _ = q.shape
-    out = torch.empty_like(q) if out is None else out
+    B, Tq, Hq = _query(cache, q)
+    _common(cache, B, Tq, Hq, seq_lens, head_sink)
+    out = _out(q, out, cache, B, Tq, Hq)
+    _on_gpu(cache, q=q, seq_lens=seq_lens, head_sink=head_sink, out=out)
     ws, nbytes = _workspace(cache, B, Hq, Tq, max_seq_len, workspace, q.device)
     _check(lib().kvq_decode_attend(cache.struct, _ptr(q), B, Hq, Tq, _ptr(seq_lens), max_seq_len,
                                    float(softmax_scale), _ptr(head_sink), _ptr(out), _ptr(ws),
@@ -234,15 +327,18 @@ def paged_decode_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor,
                         out: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Decode attention over a block-paged cache (block_table int32 [B, max_blocks])."""
-    _want(q, torch.bfloat16, "q")
-    _want(seq_lens, torch.int32, "seq_lens")
-    _want(block_table, torch.int32, "block_table")
-    B, Tq, Hq, _ = q.shape
-    out = torch.empty_like(q) if out is None else out
+    B, Tq, Hq = _query(cache, q)
+    _common(cache, B, Tq, Hq, seq_lens, head_sink)
+    if block_table is None:
+        raise KvqError("paged_decode_attend needs a block_table")
+    mb = _table(block_table, B)
+    out = _out(q, out, cache, B, Tq, Hq)
+    _on_gpu(cache, q=q, seq_lens=seq_lens, head_sink=head_sink, block_table=block_table,
+            out=out)
     ws, nbytes = _workspace(cache, B, Hq, Tq, max_seq_len, workspace, q.device)
     _check(lib().kvq_paged_decode_attend(cache.struct, _ptr(q), B, Hq, Tq, _ptr(seq_lens),
                                          max_seq_len, float(softmax_scale), _ptr(head_sink),
-                                         _ptr(block_table), block_table.shape[1], _ptr(out),
+                                         _ptr(block_table), mb, _ptr(out),
                                          _ptr(ws), nbytes, _stream(stream)),
            "kvq_paged_decode_attend")
     return out
@@ -255,16 +351,16 @@ def append_decode_attend(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tenso
                          out: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """One decode step: write the query tokens' K/V rows (bf16 [B, Tq, Hkv, D]) at
-    positions seq_lens - Tq + j, then attend.  block_table None = contiguous cache."""
-    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (q, "q")):
-        _want(t, torch.bfloat16, nm)
-    _want(seq_lens, torch.int32, "seq_lens")
-    B, Tq, Hq, _ = q.shape
-    mb = 0
-    if block_table is not None:
-        _want(block_table, torch.int32, "block_table")
-        mb = block_table.shape[1]
-    out = torch.empty_like(q) if out is None else out
+    positions min(seq_lens, max_seq_len) - Tq + j, then attend.  block_table None =
+    contiguous cache."""
+    B, Tq, Hq = _query(cache, q)
+    if k_new is None or v_new is None:
+        raise KvqError("append_decode_attend needs k_new and v_new")
+    _common(cache, B, Tq, Hq, seq_lens, head_sink, k_new, v_new)
+    mb = _table(block_table, B)
+    out = _out(q, out, cache, B, Tq, Hq)
+    _on_gpu(cache, q=q, seq_lens=seq_lens, head_sink=head_sink, block_table=block_table,
+            k_new=k_new, v_new=v_new, out=out)
     ws, nbytes = _workspace(cache, B, Hq, Tq, max_seq_len, workspace, q.device)
     _check(lib().kvq_append_decode_attend(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq,
                                           Tq, _ptr(seq_lens), max_seq_len, float(softmax_scale),
@@ -283,17 +379,12 @@ def attend_ex(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_l
     """The decode step with every option: optional fused append (k_new, v_new bf16
     [B, Tq, Hkv, D]), contiguous or paged cache, optional sink, logit soft cap and
     sliding window (0 = off)."""
-    _want(q, torch.bfloat16, "q")
-    _want(seq_lens, torch.int32, "seq_lens")
-    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
-        if t is not None:
-            _want(t, torch.bfloat16, nm)
-    B, Tq, Hq, _ = q.shape
-    mb = 0
-    if block_table is not None:
-        _want(block_table, torch.int32, "block_table")
-        mb = block_table.shape[1]
-    out = torch.empty_like(q) if out is None else out
+    B, Tq, Hq = _query(cache, q)
+    _common(cache, B, Tq, Hq, seq_lens, head_sink, k_new, v_new)
+    mb = _table(block_table, B)
+    out = _out(q, out, cache, B, Tq, Hq)
+    _on_gpu(cache, q=q, seq_lens=seq_lens, head_sink=head_sink, block_table=block_table,
+            k_new=k_new, v_new=v_new, out=out)
     ws, nbytes = _workspace(cache, B, Hq, Tq, max_seq_len, workspace, q.device)
     opts = _Options(float(softcap), int(window))
     _check(lib().kvq_attend_ex(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, Tq,
@@ -311,17 +402,12 @@ def prefill_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_
                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Chunked prefill: the Tq = q.shape[1] tokens of a chunk (k_new, v_new bf16
     [B, Tq, Hkv, D], appended first unless None) attend causally to the cache."""
-    _want(q, torch.bfloat16, "q")
-    _want(seq_lens, torch.int32, "seq_lens")
-    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
-        if t is not None:
-            _want(t, torch.bfloat16, nm)
-    B, Tq, Hq, _ = q.shape
-    mb = 0
-    if block_table is not None:
-        _want(block_table, torch.int32, "block_table")
-        mb = block_table.shape[1]
-    out = torch.empty_like(q) if out is None else out
+    B, Tq, Hq = _query(cache, q)
+    _common(cache, B, Tq, Hq, seq_lens, head_sink, k_new, v_new)
+    mb = _table(block_table, B)
+    out = _out(q, out, cache, B, Tq, Hq)
+    _on_gpu(cache, q=q, seq_lens=seq_lens, head_sink=head_sink, block_table=block_table,
+            k_new=k_new, v_new=v_new, out=out)
     opts = _Options(float(softcap), int(window))
     _check(lib().kvq_prefill_attend(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, Tq,
                                     _ptr(seq_lens), max_seq_len, float(softmax_scale),
@@ -335,11 +421,16 @@ def split_decode(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_se
                  softmax_scale: float, workspace: torch.Tensor,
                  block_table: Optional[torch.Tensor] = None, stream=None) -> None:
     """Phase 1 of decode: per-split partials into `workspace`."""
-    B, Tq, Hq, _ = q.shape
-    mb = 0 if block_table is None else block_table.shape[1]
+    B, Tq, Hq = _query(cache, q)
+    _common(cache, B, Tq, Hq, seq_lens)
+    mb = _table(block_table, B)
+    if workspace is None:
+        raise KvqError("split_decode needs a workspace (kvq.workspace_bytes)")
+    _on_gpu(cache, q=q, seq_lens=seq_lens, block_table=block_table)
+    ws, nbytes = _workspace(cache, B, Hq, Tq, max_seq_len, workspace, q.device)
     _check(lib().kvq_split_decode(cache.struct, _ptr(q), B, Hq, Tq, _ptr(seq_lens), max_seq_len,
-                                  float(softmax_scale), _ptr(block_table), mb, _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream)),
+                                  float(softmax_scale), _ptr(block_table), mb, _ptr(ws), nbytes,
+                                  _stream(stream)),
            "kvq_split_decode")
 
 
@@ -347,10 +438,17 @@ def combine(cache: KVCache, batch: int, num_q_heads: int, q_tokens: int, seq_len
             max_seq_len: int, workspace: torch.Tensor, out: torch.Tensor,
             head_sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Phase 2 of decode: fixed-order merge of the chunks into bf16 `out`."""
-    _want(seq_lens, torch.int32, "seq_lens")
+    _common(cache, batch, q_tokens, num_q_heads, seq_lens, head_sink)
+    if out is None:
+        raise KvqError("combine needs an output tensor")
+    _want(out, torch.bfloat16, "out", shape=(batch, q_tokens, num_q_heads, cache.head_dim))
+    if workspace is None:
+        raise KvqError("combine needs the workspace of the preceding split_decode")
+    _on_gpu(cache, seq_lens=seq_lens, head_sink=head_sink, out=out)
+    ws, nbytes = _workspace(cache, batch, num_q_heads, q_tokens, max_seq_len, workspace, out.device)
     _check(lib().kvq_combine(cache.struct, batch, num_q_heads, q_tokens, _ptr(seq_lens),
-                             max_seq_len, _ptr(head_sink), _ptr(out), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(stream)),
+                             max_seq_len, _ptr(head_sink), _ptr(out), _ptr(ws), nbytes,
+                             _stream(stream)),
            "kvq_combine")
     return out
 
@@ -358,16 +456,3 @@ def combine(cache: KVCache, batch: int, num_q_heads: int, q_tokens: int, seq_len
 def cache_bytes(dtype: int, scale_mode: int, num_kv_heads: int, head_dim: int, tokens: int) -> int:
     """Footprint of one layer's K+V cache (codes plus per-row scales)."""
     return lib().kvq_cache_bytes(dtype, scale_mode, num_kv_heads, head_dim, tokens)
-
-
-def stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=None) -> None:
-    """Read every byte of `src` once with the decode's load instructions and
-    nothing else (kvq_stream_read): the HBM floor a KV read is compared with.
-    `sink` holds at least workgroups * 4096 bytes."""
-    if not src.is_contiguous() or not sink.is_contiguous():
-        raise KvqError("stream_read: src and sink must be contiguous")
-    nbytes = src.numel() * src.element_size()
-    if sink.numel() * sink.element_size() < workgroups * 4096:
-        raise KvqError("stream_read: sink smaller than workgroups * 4096 bytes")
-    _check(lib().kvq_stream_read(_ptr(src), nbytes, workgroups, _ptr(sink), _stream(stream)),
-           "kvq_stream_read")

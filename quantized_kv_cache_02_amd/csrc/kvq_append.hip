@@ -27,7 +27,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   uint16_t raw[R::EPL];
   load_row<DT, D>((side ? a.v : a.k) + (((size_t)b * a.Tn + j) * Hkv + h) * D, lane, raw);
 
-  const int pos = (a.positions != nullptr ? a.positions[b] : a.seq_lens[b] - a.Tn) + j;
+  // with seq_lens, the length is clamped to the host bound exactly as the
+  // attention that follows clamps it, so the rows land where it reads them
+  int base;
+  if (a.positions != nullptr) {
+    base = a.positions[b];
+  } else {
+    const int L = a.seq_lens[b];
+    base = (L < 0 ? 0 : L > a.max_len ? a.max_len : L) - a.Tn;
+  }
+  const int pos = base + j;
   if (pos < 0 || pos >= a.capacity) return;
   const int bs = a.c.block_size;
   int blk = b;

@@ -321,6 +321,7 @@ int kvq_append(const kvq_cache* cache, const void* k, const void* v, int32_t bat
   a.v = static_cast<const uint16_t*>(v);
   a.positions = positions;
   a.seq_lens = nullptr;
+  a.max_len = 0;
   a.B = batch;
   a.Tn = tokens;
   a.capacity = (int32_t)capacity;
@@ -454,6 +455,7 @@ int kvq_prefill_attend(const kvq_cache* cache, const void* k_new, const void* v_
     ap.v = static_cast<const uint16_t*>(v_new);
     ap.positions = nullptr;
     ap.seq_lens = seq_lens;
+    ap.max_len = max_seq_len;
     ap.B = batch;
     ap.Tn = q_tokens;
     const int64_t capacity =

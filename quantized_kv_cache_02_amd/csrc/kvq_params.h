@@ -54,8 +54,9 @@ struct AppendArgs {
   CacheArgs c;
   const uint16_t* k;  // bf16 [B, Tn, Hkv, D]
   const uint16_t* v;
-  const int32_t* positions;  // [B], or nullptr: position seq_lens[b] - Tn
+  const int32_t* positions;  // [B], or nullptr: position min(seq_lens[b], max_len) - Tn
   const int32_t* seq_lens;   // used when positions is nullptr
+  int32_t max_len;           // bound on seq_lens (as the attention clamps it)
   int32_t B;
   int32_t Tn;
   int32_t capacity;  // tokens addressable per sequence

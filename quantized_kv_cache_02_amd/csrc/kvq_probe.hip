@@ -1,11 +1,12 @@
-// kvq_probe.hip -- a plain streaming read, as the floor the decode's KV reads
-// are compared with: the same non-temporal 16-byte loads, every byte read once,
-// no arithmetic beyond an XOR that keeps the loads alive.
+// kvq_probe.hip -- libkvq_probe (include/kvq_probe.h): a plain streaming read,
+// as the floor the decode's KV reads are compared with: the same non-temporal
+// 16-byte loads, every byte read once, no arithmetic beyond an XOR that keeps
+// the loads alive.  Built as its own library; the attention path never loads it.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "kvq.h"
+#include "kvq_probe.h"
 
 namespace kvq {
 namespace {

@@ -10,13 +10,15 @@ import re
 import pytest
 
 import quantized_kv_cache_02_amd as kvq
+from quantized_kv_cache_02_amd import probe as kprobe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvq.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "kvq_probe.h")
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(kvq_[a-z_0-9]+)\s*\(", src)))
 
@@ -26,12 +28,22 @@ def test_header_declares_the_boundary():
     for must in ("kvq_append", "kvq_decode_attend", "kvq_paged_decode_attend"):
         assert must in names
     assert set(names) == set(kvq.EXPORTS)
+    # the streaming-read probe is a measurement aid in a library of its own
+    assert "kvq_stream_read" not in names
+    assert set(declared_functions(PROBE_HEADER)) == set(kprobe.EXPORTS)
+
+
+def test_every_header_is_covered():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["kvq.h", "kvq_probe.h"]
 
 
 def test_library_exports_every_declared_symbol():
     L = kvq.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
+    P = kprobe.lib()
+    for name in declared_functions(PROBE_HEADER):
+        assert hasattr(P, name), name
 
 
 def _cache(**kw):
@@ -158,7 +170,7 @@ def test_invalid_prefill_rejected():
 
 
 def test_invalid_stream_read_rejected():
-    L = kvq.lib()
+    L = kprobe.lib()
     buf = ctypes.c_void_p(0x1000)  # never dereferenced: every call below is rejected first
     assert L.kvq_stream_read(None, 4096, 1, buf, None) == -1
     assert L.kvq_stream_read(buf, 4096, 1, None, None) == -1
@@ -203,3 +215,135 @@ def test_cache_bytes_matches_pages_and_oracle(oracle_lib):
         for md in (kvq.PER_ROW, kvq.PER_TENSOR, kvq.PER_CHANNEL):
             want = oracle_lib.cache_bytes_per_token(bits, md == kvq.PER_ROW, 1, 8, 128) * 1000
             assert kvq.cache_bytes(dt, md, 8, 128, 1000) == want
+
+
+# ------------------------------------------------ binding argument checks
+# The C ABI takes plain pointers and cannot see a tensor's size, so the
+# binding checks every tensor against the cache before a pointer crosses it.
+# These run without a GPU: every call below must raise KvqError before any
+# device work (a well-formed call on CPU tensors stops at the device check).
+
+import torch  # noqa: E402
+
+
+def _cpu_cache(dtype=kvq.INT8, mode=kvq.PER_ROW, Hkv=2, D=64, bs=64, nb=2, **kw):
+    return kvq.KVCache(dtype, mode, Hkv, D, bs, nb, device="cpu", **kw)
+
+
+def _args(B=2, Tq=1, Hq=4, D=64, Hkv=2):
+    bf = torch.bfloat16
+    return dict(q=torch.zeros(B, Tq, Hq, D, dtype=bf), lens=torch.ones(B, dtype=torch.int32),
+                k_new=torch.zeros(B, Tq, Hkv, D, dtype=bf), v_new=torch.zeros(B, Tq, Hkv, D, dtype=bf),
+                out=torch.zeros(B, Tq, Hq, D, dtype=bf), sink=torch.zeros(Hq),
+                table=torch.zeros(B, 1, dtype=torch.int32))
+
+
+def _raises(match, fn, *a, **kw):
+    with pytest.raises(kvq.KvqError, match=match):
+        fn(*a, **kw)
+
+
+def test_binding_accepts_well_formed_arguments_up_to_the_device():
+    c, a = _cpu_cache(), _args()
+    _raises("on the GPU", kvq.decode_attend, c, a["q"], a["lens"], 64, 0.1, head_sink=a["sink"],
+            out=a["out"])
+    _raises("on the GPU", kvq.attend_ex, c, a["q"], a["lens"], 64, 0.1, block_table=a["table"],
+            head_sink=a["sink"], k_new=a["k_new"], v_new=a["v_new"], out=a["out"])
+    _raises("on the GPU", kvq.prefill_attend, c, a["q"], a["lens"], 64, 0.1, k_new=a["k_new"],
+            v_new=a["v_new"], out=a["out"])
+    _raises("on the GPU", kvq.append, c, a["k_new"], a["v_new"], a["lens"])
+
+
+@pytest.mark.parametrize("what", ["q_head_dim", "q_heads", "q_dtype", "q_rank", "out_shape",
+                                  "out_dtype", "lens_numel", "lens_dtype", "sink_numel",
+                                  "sink_dtype", "k_new_shape", "v_new_shape", "one_new",
+                                  "table_rows", "table_rank", "q_noncontig"])
+def test_binding_rejects_mismatched_tensors(what):
+    c, a = _cpu_cache(), _args()
+    bf = torch.bfloat16
+    kw = dict(block_table=a["table"], head_sink=a["sink"], k_new=a["k_new"], v_new=a["v_new"],
+              out=a["out"])
+    q, lens = a["q"], a["lens"]
+    match = {"q_head_dim": "head_dim", "q_heads": "multiple of num_kv_heads", "q_dtype": "q must be",
+             "q_rank": "4-D", "out_shape": "out must have shape", "out_dtype": "out must be",
+             "lens_numel": "seq_lens must hold", "lens_dtype": "seq_lens must be",
+             "sink_numel": "head_sink must hold", "sink_dtype": "head_sink must be",
+             "k_new_shape": "k_new must have shape", "v_new_shape": "v_new must have shape",
+             "one_new": "both or neither", "table_rows": "block_table must have shape",
+             "table_rank": "2-D", "q_noncontig": "contiguous"}[what]
+    if what == "q_head_dim":
+        q = torch.zeros(2, 1, 4, 128, dtype=bf)
+    elif what == "q_heads":
+        q = torch.zeros(2, 1, 5, 64, dtype=bf)
+    elif what == "q_dtype":
+        q = torch.zeros(2, 1, 4, 64)
+    elif what == "q_rank":
+        q = torch.zeros(2, 4, 64, dtype=bf)
+    elif what == "out_shape":
+        kw["out"] = torch.zeros(2, 1, 4, 32, dtype=bf)
+    elif what == "out_dtype":
+        kw["out"] = torch.zeros(2, 1, 4, 64)
+    elif what == "lens_numel":
+        lens = torch.ones(3, dtype=torch.int32)
+    elif what == "lens_dtype":
+        lens = torch.ones(2, dtype=torch.int64)
+    elif what == "sink_numel":
+        kw["head_sink"] = torch.zeros(2)
+    elif what == "sink_dtype":
+        kw["head_sink"] = torch.zeros(4, dtype=bf)
+    elif what == "k_new_shape":
+        kw["k_new"] = torch.zeros(2, 1, 4, 64, dtype=bf)  # Hq heads instead of Hkv
+    elif what == "v_new_shape":
+        kw["v_new"] = torch.zeros(2, 2, 2, 64, dtype=bf)  # two tokens for one query token
+    elif what == "one_new":
+        kw["v_new"] = None
+    elif what == "table_rows":
+        kw["block_table"] = torch.zeros(1, 4, dtype=torch.int32)
+    elif what == "table_rank":
+        kw["block_table"] = torch.zeros(8, dtype=torch.int32)
+    elif what == "q_noncontig":
+        q = torch.zeros(2, 1, 64, 4, dtype=bf).transpose(2, 3)
+    _raises(match, kvq.attend_ex, c, q, lens, 64, 0.1, **kw)
+    pf = {k: v for k, v in kw.items() if k != "block_table" or what.startswith("table")}
+    _raises(match, kvq.prefill_attend, c, q, lens, 64, 0.1, **pf)
+
+
+def test_binding_rejects_mismatched_append_and_split_tensors():
+    c, a = _cpu_cache(), _args()
+    bf = torch.bfloat16
+    _raises("k must have shape", kvq.append, c, torch.zeros(2, 1, 2, 32, dtype=bf), a["v_new"], a["lens"])
+    _raises("v must have shape", kvq.append, c, a["k_new"], torch.zeros(2, 3, 2, 64, dtype=bf), a["lens"])
+    _raises("positions must hold", kvq.append, c, a["k_new"], a["v_new"], torch.zeros(1, dtype=torch.int32))
+    _raises("positions must be", kvq.append, c, a["k_new"], a["v_new"], torch.zeros(2))
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    _raises("head_dim", kvq.split_decode, c, torch.zeros(2, 1, 4, 32, dtype=bf), a["lens"], 64, 0.1, ws)
+    _raises("seq_lens must hold", kvq.split_decode, c, a["q"], torch.ones(5, dtype=torch.int32), 64, 0.1, ws)
+    _raises("out must have shape", kvq.combine, c, 2, 4, 1, a["lens"], 64, ws,
+            torch.zeros(2, 1, 4, 63, dtype=bf))
+    _raises("head_sink must hold", kvq.combine, c, 2, 4, 1, a["lens"], 64, ws, a["out"],
+            head_sink=torch.zeros(3))
+    _raises("workspace", kvq.split_decode, c, a["q"], a["lens"], 64, 0.1, None)
+
+
+@pytest.mark.parametrize("mode,table,match", [
+    (kvq.PER_TENSOR, [1.0, 2.0], "must hold 1 scales"),
+    (kvq.PER_CHANNEL, [1.0] * 64, r"must hold 128 scales"),  # [D] with Hkv = 2
+    (kvq.PER_CHANNEL, [1.0] * 129, r"must hold 128 scales"),
+    (kvq.PER_TENSOR, [-1.0], "finite and >= 0"),
+    (kvq.PER_CHANNEL, [float("nan")] * 128, "finite and >= 0"),
+    (kvq.PER_TENSOR, [float("inf")], "finite and >= 0"),
+])
+def test_cache_rejects_bad_static_tables(mode, table, match):
+    with pytest.raises(kvq.KvqError, match=match):
+        _cpu_cache(mode=mode, k_static=table, v_static=[1.0] * (1 if mode == kvq.PER_TENSOR else 128))
+    with pytest.raises(kvq.KvqError, match=match.replace("k_", "v_")):
+        _cpu_cache(mode=kvq.PER_ROW, v_scale_mode=mode, v_static=table)
+
+
+def test_cache_accepts_well_sized_static_tables():
+    c = _cpu_cache(mode=kvq.PER_CHANNEL, k_static=[[0.5] * 64] * 2, v_static=[0.0] * 128)
+    assert c.k_scales.numel() == 128 and c.v_scales.numel() == 128
+    c = _cpu_cache(mode=kvq.PER_TENSOR, k_static=[0.25], v_static=[2.0 ** -130])
+    assert c.k_scales.numel() == 1
+    with pytest.raises(kvq.KvqError, match="dtype"):
+        kvq.KVCache(7, kvq.PER_ROW, 2, 64, 64, 2, device="cpu")
