@@ -138,6 +138,39 @@ __device__ __forceinline__ i32x4_t mfma64_i8(i32x4_t a, i32x4_t b, i32x4_t c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// Folded query of the integer caches: a row x (q times the per-channel K scale)
+// with |x| < 2^ex becomes the integer vector qi = rne(x 2^(8 NSL - 2 - ex)),
+// |qi| <= 2^(8 NSL - 2), written as NSL signed bytes, qi = sum_k 256^k s_k
+// (balanced digits: s_0 .. s_{NSL-2} in [-128, 127], the top one in
+// [-65, 64]).  Each byte is an int8 B operand; the integer dot products of the
+// slices with the K codes are exact in int32 (|s| <= 128, |k| <= 127, 256
+// channels) and combine into one float per logit (q_dot).  Two slices keep 15
+// bits of the row's largest element, three 23: a channel 2^r below the largest
+// keeps 15 - r or 23 - r bits.
+template <int NSL>
+__device__ __forceinline__ void q_slices(float x, int ex, int (&sl)[NSL]) {
+  static_assert(NSL == 2 || NSL == 3, "two or three slices");
+  int qi = (int)__builtin_rintf(ldexpf(x, 8 * NSL - 2 - ex));
+#pragma unroll
+  for (int k = 0; k < NSL - 1; ++k) {
+    const int d = ((qi + 128) & 255) - 128;
+    sl[k] = d;
+    qi = (qi - d) >> 8;  // exact: qi - d is a multiple of 256
+  }
+  sl[NSL - 1] = qi;
+}
+
+// The dot product of the folded query with the codes from the per-slice int32
+// dot products (dots[k] for slice k): exact integers, one rounding to fp32 at
+// the end (two slices: the sum is below 2^30 and exact in int32).
+template <int NSL>
+__device__ __forceinline__ float q_dot(const int (&dots)[NSL]) {
+  if constexpr (NSL == 2)
+    return (float)(dots[1] * 256 + dots[0]);
+  else
+    return (float)dots[2] * 65536.0f + (float)(dots[1] * 256 + dots[0]);
+}
+
 __device__ __forceinline__ half4_t u2_to_h4(uint32_t a, uint32_t b) {
   u32x2_t v = {a, b};
   return __builtin_bit_cast(half4_t, v);

@@ -332,11 +332,13 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
   wlo_max = __builtin_amdgcn_readfirstlane(wlo_max);
 
   // q operand: row r, channels 32 ks + 8 g + 0..7 (zero rows past R).
-  // Integer caches: channels 64 st + 16 g + 0..15 of the row as a 15-bit
-  // integer vector qi = rne(q 2^(14 - ex)), |q| < 2^ex, split as qi = 256 hi +
-  // lo (hi in [-64, 64], lo in [-128, 127]); qb[rb][2 st] holds hi,
-  // qb[rb][2 st + 1] lo, as int8 bytes.
-  half8_t qb[RBW][KSTEPS];
+  // Integer caches: channels 64 st + 16 g + 0..15 of the row as a fixed-point
+  // integer vector in NSL int8 slices (q_slices: 15 bits of the row's largest
+  // element, 23 with a per-channel K scale folded in); qb[rb][NSL st + k]
+  // holds slice k.
+  constexpr int NSL = MODE == kPerChannel ? 3 : 2;
+  constexpr int QOPS = P::IQK ? NSL * P::ISTEPS : KSTEPS;
+  half8_t qb[RBW][QOPS];
   float rowmul[RBW];
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
@@ -370,22 +372,23 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
       if (amax > 0.0f) (void)frexpf(amax, &ex);
 #pragma unroll
       for (int st = 0; st < P::ISTEPS; ++st) {
-        u32x4_t hw = {0u, 0u, 0u, 0u}, lw = {0u, 0u, 0u, 0u};
+        u32x4_t wq[NSL];
+#pragma unroll
+        for (int k = 0; k < NSL; ++k) wq[k] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
-          const int qi = (int)__builtin_rintf(ldexpf(qv[st][p], 14 - ex));
-          const int hi = (qi + 128) >> 8;
-          const int lo8 = qi - hi * 256;
-          hw[p / 4] |= ((uint32_t)hi & 0xFFu) << (8 * (p % 4));
-          lw[p / 4] |= ((uint32_t)lo8 & 0xFFu) << (8 * (p % 4));
+          int sl[NSL];
+          q_slices<NSL>(qv[st][p], ex, sl);
+#pragma unroll
+          for (int k = 0; k < NSL; ++k) wq[k][p / 4] |= ((uint32_t)sl[k] & 0xFFu) << (8 * (p % 4));
         }
-        qb[rb][2 * st] = __builtin_bit_cast(half8_t, hw);
-        qb[rb][2 * st + 1] = __builtin_bit_cast(half8_t, lw);
+#pragma unroll
+        for (int k = 0; k < NSL; ++k) qb[rb][NSL * st + k] = __builtin_bit_cast(half8_t, wq[k]);
       }
       float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
       if constexpr (MODE == kPerTensor) mul *= a.c.k_scales[0];
       if constexpr (DT == kInt4) mul *= 0.0625f;  // K tile holds 16 * code
-      rowmul[rb] = ldexpf(mul, ex - 14);
+      rowmul[rb] = ldexpf(mul, ex - (8 * NSL - 2));
       continue;
     }
     u32x4_t raw[KSTEPS];
@@ -508,19 +511,27 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
         s1[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
       }
       if constexpr (P::IQK) {
-        // exact integer dot products with the two q halves (hi * 256 + lo stays
-        // below 2^30), as floats in s0
+        // exact integer dot products with each q slice, combined into one
+        // float per logit in s0
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
-          i32x4_t h = {0, 0, 0, 0}, l = {0, 0, 0, 0};
+          i32x4_t acc[NSL];
+#pragma unroll
+          for (int k = 0; k < NSL; ++k) acc[k] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
           for (int st = 0; st < P::ISTEPS; ++st) {
             const i32x4_t ka = __builtin_bit_cast(i32x4_t, kop[s % KB][st]);
-            h = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qb[rb][2 * st]), h);
-            l = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qb[rb][2 * st + 1]), l);
+#pragma unroll
+            for (int k = NSL - 1; k >= 0; --k)
+              acc[k] = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qb[rb][NSL * st + k]), acc[k]);
           }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s0[rb][e] = (float)(h[e] * 256 + l[e]);
+          for (int e = 0; e < 4; ++e) {
+            int dd[NSL];
+#pragma unroll
+            for (int k = 0; k < NSL; ++k) dd[k] = acc[k][e];
+            s0[rb][e] = q_dot<NSL>(dd);
+          }
         }
       }
 #pragma unroll

@@ -84,6 +84,15 @@ struct Geo {
   static constexpr int NCOL = D / 16;      // 16x16x16 MFMAs per row block
 };
 
+// Query slices of the integer S^T (see q_slices): three for a per-channel K
+// scale, whose folded query spans the table's range, two otherwise.  The q
+// operand array holds NSL slices per integer k-step (integer caches) or one
+// fp16 / bf16 operand per k-step.
+template <int DT, int MODE>
+constexpr int kQSlices = (MODE == kPerChannel) ? 3 : 2;
+template <int DT, int MODE, int D>
+constexpr int kQOps = Geo<DT, D>::IQK ? kQSlices<DT, MODE> * Geo<DT, D>::ISTEPS : Geo<DT, D>::KSTEPS;
+
 // Channel d that element e (0..7) of k-step `ks` holds in lane group g, for both
 // MFMA operands of S^T (the K codes and the q rows use the same map).
 template <int DT, int D>
@@ -353,7 +362,7 @@ struct WaveState {
 
 template <int DT, int MODE, int D, int RB, bool CAP, bool QLDS>
 __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L, int n, int g,
-                                             const half8_t (&qb)[RB][Geo<DT, D>::KSTEPS],
+                                             const half8_t (&qb)[RB][kQOps<DT, MODE, D>],
                                              const half8_t* qlds,
                                              const float (&rowmul)[RB], const int (&lim)[RB],
                                              const int (&lo)[RB], float cap2, float icap2,
@@ -400,22 +409,31 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
     // the q operand of k-step k: registers, or this wavefront's LDS copy (lane-
     // linear, so conflict-free).  The LDS offset is made opaque so the compiler
     // cannot hoist those reads out of the tile loop back into registers.
-    int qo = rb * G_::KSTEPS * 64;
+    int qo = rb * kQOps<DT, MODE, D> * 64;
     if constexpr (QLDS) asm volatile("" : "+v"(qo));
     auto qop = [&](int k) { return QLDS ? qlds[qo + 64 * k] : qb[rb][k]; };
     float dot[4];
     if constexpr (G_::IQK) {
-      // exact integer dot products with the high and low query halves
-      // (qb[rb][2s], qb[rb][2s+1]); their sum hi * 256 + lo stays below 2^30
-      i32x4_t h = {0, 0, 0, 0}, l = {0, 0, 0, 0};
+      // exact integer dot products with each query slice (qb[rb][NSL st + k]
+      // is slice k of integer step st), combined into one float per logit
+      constexpr int NSL = kQSlices<DT, MODE>;
+      i32x4_t acc[NSL];
+#pragma unroll
+      for (int k = 0; k < NSL; ++k) acc[k] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
       for (int st = 0; st < G_::ISTEPS; ++st) {
         const i32x4_t ka = k_operand_i8<DT, D>(T.kw, st);
-        h = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qb[rb][2 * st]), h);
-        l = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qb[rb][2 * st + 1]), l);
+#pragma unroll
+        for (int k = NSL - 1; k >= 0; --k)
+          acc[k] = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st + k)), acc[k]);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dot[e] = (float)(h[e] * 256 + l[e]);
+      for (int e = 0; e < 4; ++e) {
+        int dd[NSL];
+#pragma unroll
+        for (int k = 0; k < NSL; ++k) dd[k] = acc[k][e];
+        dot[e] = q_dot<NSL>(dd);
+      }
     } else {
 #pragma unroll
       for (int ks = 0; ks < G_::KSTEPS; ks += 2) {
@@ -561,9 +579,13 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
 template <int DT, int MODE, int D, int RB>
 struct Knobs {
   // q operand from LDS instead of registers: the bf16 tiles need those
-  // registers.  (For the 8-bit caches this measured slower on MI355X: 64K int8
+  // registers, and so do the three query slices of an int8 cache with a
+  // per-channel K scale once the accumulators fill a wavefront (RB * D = 256:
+  // in registers they spilled 13-45 of them to scratch).  (For the 8-bit
+  // caches with two slices this measured slower on MI355X: 64K int8
   // 28.9 -> 30.5 us, and 3 tiles in flight with it 33.6 us, with spills.)
-  static constexpr bool QLDS = DT == kBf16;
+  static constexpr bool QLDS =
+      DT == kBf16 || (DT == kInt8 && MODE == kPerChannel && RB * D >= kSplitMaxAccColumns);
   static constexpr int NB = kSplitTilesInFlight;
   static constexpr int WAVES_PER_EU = kSplitWavesPerSimd;
   // merge buffers: one per wavefront (RB * D <= 256 keeps them within 64 KiB)
@@ -584,7 +606,7 @@ split_decode_kernel(SplitArgs a) {
   // operand after them), then the merge buffers
   __shared__ __attribute__((aligned(16))) float smem[K_::MERGE_BUFS * RP * D];
   constexpr int kQStageBytes = (RP * kQStride<D> * 2 + 255) / 256 * 256;
-  constexpr int kQOpBytes = RB * G_::KSTEPS * 64 * 16;  // one wavefront's operand
+  constexpr int kQOpBytes = RB * kQOps<DT, MODE, D> * 64 * 16;  // one wavefront's operand
   static_assert(!K_::QLDS || kQStageBytes + kWaves * kQOpBytes <= (int)sizeof(smem),
                 "q operand copies do not fit the merge buffers");
   __shared__ float s_m[kWaves][RP];
@@ -744,7 +766,7 @@ split_decode_kernel(SplitArgs a) {
   // ---- B operands of S^T: q rows in this lane's channel order, normalized by a
   // power of two so every element lies in (-1, 1) (integer caches: the int8
   // halves of the row scaled to 15 bits); the row multiplier restores it.
-  half8_t qb[RB][G_::KSTEPS];
+  half8_t qb[RB][kQOps<DT, MODE, D>];
   float rowmul[RB];  // logit (log2 units) = dot * rowmul * per-row K scale
   int lim[RB];       // tokens visible to this lane's row n: lo <= t < lim
   int lo[RB];
@@ -767,9 +789,10 @@ split_decode_kernel(SplitArgs a) {
         continue;
       }
       if constexpr (G_::IQK) {
-        // The row as a 15-bit integer vector: qi = rne(q 2^(14 - ex)) with
-        // |q| < 2^ex, |qi| <= 2^14, split as qi = 256 hi + lo, hi in [-64, 64],
-        // lo in [-128, 127], each an int8 B operand.
+        // The row as a fixed-point integer vector in NSL int8 slices (see
+        // q_slices): 15 bits of the row's largest element, 23 with a
+        // per-channel K scale folded in.
+        constexpr int NSL = kQSlices<DT, MODE>;
         float qv[G_::ISTEPS][16];
         float amax = 0.0f;
 #pragma unroll
@@ -799,22 +822,23 @@ split_decode_kernel(SplitArgs a) {
         if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
 #pragma unroll
         for (int st = 0; st < G_::ISTEPS; ++st) {
-          u32x4_t hw = {0u, 0u, 0u, 0u}, lw = {0u, 0u, 0u, 0u};
+          u32x4_t w[NSL];
+#pragma unroll
+          for (int k = 0; k < NSL; ++k) w[k] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
           for (int p = 0; p < 16; ++p) {
-            const int qi = (int)__builtin_rintf(ldexpf(qv[st][p], 14 - ex));
-            const int hi = (qi + 128) >> 8;
-            const int lo8 = qi - hi * 256;
-            hw[p / 4] |= ((uint32_t)hi & 0xFFu) << (8 * (p % 4));
-            lw[p / 4] |= ((uint32_t)lo8 & 0xFFu) << (8 * (p % 4));
+            int sl[NSL];
+            q_slices<NSL>(qv[st][p], ex, sl);
+#pragma unroll
+            for (int k = 0; k < NSL; ++k) w[k][p / 4] |= ((uint32_t)sl[k] & 0xFFu) << (8 * (p % 4));
           }
-          qb[rb][2 * st] = __builtin_bit_cast(half8_t, hw);
-          qb[rb][2 * st + 1] = __builtin_bit_cast(half8_t, lw);
+#pragma unroll
+          for (int k = 0; k < NSL; ++k) qb[rb][NSL * st + k] = __builtin_bit_cast(half8_t, w[k]);
         }
         float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
         if constexpr (MODE == kPerTensor) mul *= kst[0];
         if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
-        rowmul[rb] = ldexpf(mul, ex - 14);
+        rowmul[rb] = ldexpf(mul, ex - (8 * NSL - 2));
         continue;
       }
       float qv[G_::KSTEPS][8];
@@ -860,10 +884,11 @@ split_decode_kernel(SplitArgs a) {
   half8_t* qlds = reinterpret_cast<half8_t*>(reinterpret_cast<char*>(smem) + kQStageBytes +
                                              wave * kQOpBytes) + lane;
   if constexpr (K_::QLDS) {
+    constexpr int QO = kQOps<DT, MODE, D>;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int ks = 0; ks < G_::KSTEPS; ++ks) qlds[(rb * G_::KSTEPS + ks) * 64] = qb[rb][ks];
+      for (int ks = 0; ks < QO; ++ks) qlds[(rb * QO + ks) * 64] = qb[rb][ks];
   }
 
   // soft cap in log2 units (the CAP variant is launched when softcap > 0)
