@@ -65,10 +65,14 @@ def lib():
         L.kvo_attend.restype = None
         L.kvo_attend_ex.argtypes = [P, P, P, I, I, I, I, I, I, P, F, P, F, I, P, P]
         L.kvo_attend_ex.restype = None
+        L.kvo_attend_ex2.argtypes = [P, P, P, I, I, I, I, I, I, P, F, P, F, I, P, P, P]
+        L.kvo_attend_ex2.restype = None
         L.kvo_cache_bytes_per_token.argtypes = [I, I, I, I, I]
         L.kvo_cache_bytes_per_token.restype = D
         L.kvo_num_threads.argtypes = []
         L.kvo_num_threads.restype = I
+        L.kvo_set_num_threads.argtypes = [I]
+        L.kvo_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -185,11 +189,12 @@ class Cache:
 
 def attend(q_bits: np.ndarray, K: np.ndarray, V: np.ndarray, lens, scale: float,
            sink: Optional[np.ndarray] = None, Hkv: Optional[int] = None, softcap: float = 0.0,
-           window: int = 0):
+           window: int = 0, return_max: bool = False):
     """fp64 softmax attention.  q_bits bf16 bits [B, Tq, Hq, D]; K, V fp32
     [B, Hkv, Lmax, D].  softcap > 0 caps every scaled logit as c tanh(z / c);
     window > 0 lets a query at position p see tokens p - window + 1 .. p only.
-    Returns (out fp64 [B, Tq, Hq, D], lse fp64 [B, Tq, Hq])."""
+    Returns (out fp64 [B, Tq, Hq, D], lse fp64 [B, Tq, Hq]), and with
+    return_max also the largest logit of each row, fp64 [B, Tq, Hq]."""
     q_bits = np.ascontiguousarray(q_bits, np.uint16)
     K = np.ascontiguousarray(K, np.float32)
     V = np.ascontiguousarray(V, np.float32)
@@ -199,13 +204,18 @@ def attend(q_bits: np.ndarray, K: np.ndarray, V: np.ndarray, lens, scale: float,
     out = np.empty((B, Tq, Hq, D), np.float64)
     lse = np.empty((B, Tq, Hq), np.float64)
     sk = _c(sink, np.float32)
-    lib().kvo_attend_ex(_p(q_bits), _p(K), _p(V), B, Tq, Hq, hkv, D, K.shape[2], _p(lens),
-                        float(scale), _p(sk), float(softcap), int(window), _p(out), _p(lse))
-    return out, lse
+    m = np.empty((B, Tq, Hq), np.float64)
+    lib().kvo_attend_ex2(_p(q_bits), _p(K), _p(V), B, Tq, Hq, hkv, D, K.shape[2], _p(lens),
+                         float(scale), _p(sk), float(softcap), int(window), _p(out), _p(lse), _p(m))
+    return (out, lse, m) if return_max else (out, lse)
 
 
 def num_threads() -> int:
     return lib().kvo_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().kvo_set_num_threads(int(n))
 
 
 def cache_bytes_per_token(bits: int, per_row_scales: bool, layers: int, Hkv: int, D: int) -> float:

@@ -279,7 +279,9 @@ void kvo_dequantize(int dtype, int k_mode, int v_mode, int Hkv, int D, int block
  *   z_t = scale * sum_d q_d K_td; o = sum_t softmax(z)_t V_t; lse = log sum_t exp(z_t)
  *   sink (if given, [Hq] fp32): o *= 1 / (1 + exp(sink[h] - lse))
  *   no visible token: o = 0 and lse = -inf
- * out fp64 [B, Tq, Hq, D]; lse_out fp64 [B, Tq, Hq] (may be NULL).
+ * out fp64 [B, Tq, Hq, D]; lse_out fp64 [B, Tq, Hq] (may be NULL); m_out fp64
+ * [B, Tq, Hq], the largest logit of each row (may be NULL; -inf with no
+ * visible token), so that lse - m = ln of the row's normalizer.
  */
 /* Logit of query row qd against key row k: z = scale * q . k, then, with a
  * soft cap c > 0, z -> c * tanh(z / c) ([P] "CUDA kernels": the paged decode
@@ -299,9 +301,9 @@ static double kvo_logit(const double* qd, const float* k, int D, float scale, fl
  * [P] "CUDA kernels": sliding-window decode), an optional logit soft cap and an
  * optional per-head sink (o *= 1 / (1 + exp(sink[h] - lse)), [P] ApplyHeadSink).
  * A query with no visible token outputs zeros. */
-void kvo_attend_ex(const uint16_t* q, const float* K, const float* V, int B, int Tq, int Hq, int Hkv,
-                   int D, int Lmax, const int32_t* lens, float scale, const float* sink,
-                   float softcap, int window, double* out, double* lse_out) {
+void kvo_attend_ex2(const uint16_t* q, const float* K, const float* V, int B, int Tq, int Hq, int Hkv,
+                    int D, int Lmax, const int32_t* lens, float scale, const float* sink,
+                    float softcap, int window, double* out, double* lse_out, double* m_out) {
   int G = Hq / Hkv;
 #pragma omp parallel for collapse(3) schedule(dynamic)
   for (int b = 0; b < B; ++b)
@@ -317,6 +319,7 @@ void kvo_attend_ex(const uint16_t* q, const float* K, const float* V, int B, int
         if (lo < 0) lo = 0;
         if (hi <= lo) {
           if (lse_out) lse_out[((size_t)b * Tq + j) * Hq + h] = -INFINITY;
+          if (m_out) m_out[((size_t)b * Tq + j) * Hq + h] = -INFINITY;
           continue;
         }
         const float* Kb = K + ((size_t)b * Hkv + hk) * Lmax * (size_t)D;
@@ -343,7 +346,16 @@ void kvo_attend_ex(const uint16_t* q, const float* K, const float* V, int B, int
           for (int d = 0; d < D; ++d) o[d] *= f;
         }
         if (lse_out) lse_out[((size_t)b * Tq + j) * Hq + h] = lse;
+        if (m_out) m_out[((size_t)b * Tq + j) * Hq + h] = m;
       }
+}
+
+/* The same without the largest logit of each row. */
+void kvo_attend_ex(const uint16_t* q, const float* K, const float* V, int B, int Tq, int Hq, int Hkv,
+                   int D, int Lmax, const int32_t* lens, float scale, const float* sink,
+                   float softcap, int window, double* out, double* lse_out) {
+  kvo_attend_ex2(q, K, V, B, Tq, Hq, Hkv, D, Lmax, lens, scale, sink, softcap, window, out, lse_out,
+                 NULL);
 }
 
 /* The same without soft cap or window. */
@@ -371,5 +383,15 @@ int kvo_num_threads(void) {
   return omp_get_max_threads();
 #else
   return 1;
+#endif
+}
+
+/* Run the OpenMP loops above on n threads from now on (timing the baseline on
+ * one core and on all of them). */
+void kvo_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
 #endif
 }

@@ -11,6 +11,8 @@ scales bit-exact; outputs within the decode's relative-L2 bound.
 """
 from __future__ import annotations
 
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -68,9 +70,9 @@ def _run_prefill(w: ki.Workload, dev="cuda"):
 def _check(w: ki.Workload, what: str):
     gu.log(what)
     out, cache = _run_prefill(w)
-    ref, _, ocache = oracle.reference(w)
+    ref, tol, ocache = gu.reference(w)
     gu.compare_codes(w, cache, ocache)
-    gu.check_output(out, ref, what)
+    gu.check_output(out, ref, what, tol)
 
 
 PREFILL_MATRIX = [(dt, md, D) for dt in (INT8, INT4, FP8) for md in (PER_ROW, PER_TENSOR, PER_CHANNEL)
@@ -147,9 +149,9 @@ def test_prefill_one_token_matches_decode():
     out, cache = _run_prefill(w)
     table = torch.from_numpy(w.block_table).cuda()
     dec = gu.gpu_decode(w, cache, table)
-    ref, _, _ = oracle.reference(w)
-    gu.check_output(out, ref, "prefill Tq=1")
-    gu.check_output(dec, ref, "decode of the same cache")
+    ref, tol, _ = gu.reference(w)
+    gu.check_output(out, ref, "prefill Tq=1", tol)
+    gu.check_output(dec, ref, "decode of the same cache", tol)
 
 
 def test_prefill_large_chunk_sampled():
@@ -162,15 +164,16 @@ def test_prefill_large_chunk_sampled():
     w.q = ki.randn_bf16((1, Tq, w.Hq, w.D), 345)
     out, cache = _run_prefill(w)
     ocache = oracle.build_cache(w)
-    compare = gu.compare_codes(w, cache, ocache)
-    K, V = ocache.dequantize(w.lens)
-    got = out.float().cpu().numpy().astype(np.float64)
-    qb = ki.bf16_bits(w.q)
+    gu.compare_codes(w, cache, ocache)
     for j in (0, 1, 63, 64, 500, Tq - 1):
-        p = L - Tq + j
-        ref, _ = oracle.attend(qb[:, j:j + 1], K, V, np.array([p + 1], np.int32), w.sm_scale, None,
-                               w.Hkv)
-        gu.check_output(out[:, j:j + 1], ref, f"large chunk, token {j}")
+        # query token j alone over its visible prefix: a one-token workload on
+        # the same oracle cache
+        wj = copy.copy(w)
+        wj.Tq = 1
+        wj.q = w.q[:, j:j + 1].contiguous()
+        wj.lens = np.array([L - Tq + j + 1], np.int32)
+        ref, tol, _ = gu.reference(wj, ocache)
+        gu.check_output(out[:, j:j + 1], ref, f"large chunk, token {j}", tol)
 
 
 def test_prefill_attend_only_after_append():
@@ -182,8 +185,8 @@ def test_prefill_attend_only_after_append():
     out = kvq.prefill_attend(cache, w.q.cuda(), torch.from_numpy(w.lens).cuda(), int(w.lens.max()),
                              w.sm_scale, block_table=table, head_sink=torch.from_numpy(w.sink).cuda())
     torch.cuda.synchronize()
-    ref, _, _ = oracle.reference(w)
-    gu.check_output(out, ref, "prefill, attention only")
+    ref, tol, _ = gu.reference(w)
+    gu.check_output(out, ref, "prefill, attention only", tol)
 
 
 def test_prefill_graph_replays_equal_eager():
@@ -223,3 +226,71 @@ def test_prefill_graph_replays_equal_eager():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
         assert torch.equal(cache.k_codes, codes), f"replay {rep} cache"
+
+
+# ------------------------------------------------- seq_lens above the bound
+# include/kvq.h: a seq_lens value above max_seq_len is treated as max_seq_len,
+# both for the chunk's rows the prefill appends and for the attention.
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_with_lengths_above_the_bound(paged):
+    w = ki.random_workload(8800 + paged, B=2, Hkv=2, G=3, D=128, Tq=24, lens=[700, 200],
+                           dtype=INT4, mode=PER_ROW, block_size=16 if paged else None)
+    dev = "cuda"
+    msl = 500
+    table = None if w.block_table is None else torch.from_numpy(w.block_table).to(dev)
+    clamped = np.minimum(w.lens, msl).astype(np.int32)
+    caches = [gu.gpu_cache(w), gu.gpu_cache(w)]
+    for b in range(w.B):
+        head = int(clamped[b]) - w.Tq
+        bt = (torch.tensor([[b]], dtype=torch.int32, device=dev) if table is None
+              else table[b:b + 1].contiguous())
+        for c in caches:
+            kvq.append(c, w.k[b:b + 1, :head].contiguous().to(dev), w.v[b:b + 1, :head].contiguous().to(dev),
+                       torch.zeros(1, dtype=torch.int32, device=dev), bt)
+    kn = ki.randn_bf16((w.B, w.Tq, w.Hkv, w.D), 8810).to(dev)
+    vn = ki.randn_bf16((w.B, w.Tq, w.Hkv, w.D), 8811).to(dev)
+    q = w.q.to(dev)
+    over = kvq.prefill_attend(caches[0], q, torch.from_numpy(w.lens).to(dev), msl, w.sm_scale,
+                              k_new=kn, v_new=vn, block_table=table)
+    exact = kvq.prefill_attend(caches[1], q, torch.from_numpy(clamped).to(dev), msl, w.sm_scale,
+                               k_new=kn, v_new=vn, block_table=table)
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0].k_codes, caches[1].k_codes)
+    assert torch.equal(caches[0].v_codes, caches[1].v_codes)
+    assert torch.equal(caches[0].k_scales, caches[1].k_scales)
+    assert torch.equal(over.view(torch.int16), exact.view(torch.int16))
+
+
+# ------------------------------------------------------- scale extremes
+# "[CUDA] Add INT4 paged KV cache with per-channel scales", "Testing": scale
+# extremes through prefill and chunked prefill over the paged cache.
+
+@pytest.mark.parametrize("dtype", [INT8, INT4, FP8])
+@pytest.mark.parametrize("vcase", ["channel", "tensor_tiny", "tensor_huge"])
+def test_prefill_at_scale_extremes(dtype, vcase):
+    v_mode, v_scalar = {"channel": (PER_CHANNEL, None), "tensor_tiny": (PER_TENSOR, 2.0 ** -130),
+                        "tensor_huge": (PER_TENSOR, 2.0 ** 100)}[vcase]
+    w, chan = gu.extreme_workload(dtype, 256, 8900 + 10 * dtype + len(vcase), v_mode, v_scalar,
+                                  lens=(300, 700), Tq=40)
+    what = f"prefill extremes dt={dtype} V={vcase}"
+    gu.log(what)
+    out, cache = _run_prefill(w)
+    ref, tol, ocache = gu.reference(w)
+    gu.compare_codes(w, cache, ocache)
+    gu.check_output_channels(out, ref, tol, chan, w.Hq // w.Hkv, what)
+
+
+@pytest.mark.parametrize("dtype", [INT8, INT4])
+def test_prefill_per_channel_k_table_spanning_2_pow_10(dtype):
+    qmax = {INT8: 127.0, INT4: 7.0}[dtype]
+    w = ki.random_workload(8950 + dtype, B=2, Hkv=2, G=6, D=256, Tq=33, lens=[900, 100],
+                           dtype=dtype, mode=PER_CHANNEL, v_mode=PER_ROW, block_size=16)
+    rng = np.random.default_rng(8951 + dtype)
+    kt = (2.0 ** rng.uniform(-5, 5, size=(2, 256))).astype(np.float32)
+    w.k_static = kt
+    w.k = (w.k.float() * torch.from_numpy(kt)[None, None] * (qmax / 3)).to(torch.bfloat16)
+    qs = w.q.float()[0, 0, 0] * torch.from_numpy(kt[0]) * (qmax / 3)
+    z = float(torch.sqrt((qs * qs).sum())) * w.sm_scale
+    w.q = (w.q.float() * (2.0 / z)).to(torch.bfloat16)
+    _check(w, f"prefill, K table over 2^-5..2^5, dt={dtype}")

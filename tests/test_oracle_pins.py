@@ -597,6 +597,28 @@ def test_head_sink_identity(oracle_lib):
     np.testing.assert_array_equal(off, plain)
 
 
+def test_max_logit_and_normalizer(oracle_lib):
+    """The largest logit the oracle reports is the max of the fp64 logits computed
+    here, and lse - m is the log of sum_t exp(z_t - m) (>= 0, 0 for one token)."""
+    rng = np.random.default_rng(14)
+    B, Hkv, G, D, L, Tq = 1, 2, 3, 32, 25, 2
+    K = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, L, D)).astype(np.float32)
+    q = ki.randn_bf16((B, Tq, G * Hkv, D), 15)
+    out, lse, m = oracle_lib.attend(_bits(q), K, V, np.array([L], np.int32), 0.3, window=7,
+                                    return_max=True)
+    qd = q.double().numpy()
+    for j in range(Tq):
+        pos = L - Tq + j
+        for h in range(G * Hkv):
+            # the softmax scale is an fp32 argument, widened
+            z = float(np.float32(0.3)) * (K[0, h // G, pos - 6:pos + 1].astype(np.float64) @ qd[0, j, h])
+            assert abs(m[0, j, h] - z.max()) <= 1e-13
+            assert abs(lse[0, j, h] - (z.max() + math.log(np.exp(z - z.max()).sum()))) <= 1e-13
+    _, lse1, m1 = oracle_lib.attend(_bits(q), K, V, np.array([1], np.int32), 0.3, return_max=True)
+    assert np.all(np.isneginf(m1[0, 0])) and np.all(lse1[0, 1] == m1[0, 1])
+
+
 def test_closed_forms(oracle_lib):
     rng = np.random.default_rng(10)
     D = 64
