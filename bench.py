@@ -5,10 +5,17 @@ Workload (default): batch 1, 24 query heads, 4 KV heads, head_dim 256, an int8
 cache with per-row absmax scales holding 65,536 tokens, one query token.  One
 step = quantize-on-append of the new token's K/V row + split-KV decode +
 fixed-order combine, i.e. the whole hot path, issued as kvq_append_decode_attend
-(the append runs inside the split kernel) unless --separate-append is given.  Steps rotate over 16 layer caches (16 x
-130 MiB) so the 256 MB Infinity Cache cannot serve the KV bytes, and run as
-HIP-graph replays of 16 steps.  Inputs are seeded synthetic tensors already
-resident in HBM when the timed region starts.
+(the append runs inside the split kernel) unless --separate-append is given.
+Steps rotate over 16 layer caches (16 x 130 MiB) so the 256 MB Infinity Cache
+cannot serve the KV bytes.  Inputs are seeded synthetic tensors already resident
+in HBM when the timed region starts.
+
+Timing: half a second of step replays settles the clocks whatever --warmup is,
+then --warmup untimed steps, then 5 back-to-back windows of exactly --steps
+steps (one HIP-graph replay each, step i on layer i % 16), each between two HIP
+events on its stream; ms_per_step is the median window.  The split kernel alone
+is timed the same way over 64 replays of a graph of 16 split launches per
+window.
 
 Prints ONE JSON line.  `value` is the effective KV-read bandwidth of the whole
 step: algorithmic bytes (K and V codes plus per-row scales of every cached
@@ -109,9 +116,27 @@ def build_layers(kvq, torch, w, layers: int, dev):
     return caches, table, kn, vn
 
 
+SETTLE_S = 0.5   # step-graph replays before any timing, whatever --warmup is
+WINDOWS = 5      # timed windows; the median is reported
+SPLIT_REPLAYS = 64  # replays of the 16-launch split-only graph per window
+
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
 def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fused: bool = True):
-    """Time `steps` decode steps of workload `w` rotated over `layers` caches, as
-    HIP-graph replays of one step per layer, and the split kernel alone."""
+    """Time decode steps of workload `w` rotated over `layers` caches.
+
+    Clocks are settled first by SETTLE_S seconds of replays of a graph of one
+    step per layer.  Then `warmup` untimed steps and WINDOWS timed windows of
+    exactly `steps` steps each (a graph of `steps` steps, step i on layer
+    i % layers), issued back to back after a synchronize and timed with HIP
+    events on their stream; the median window gives ms per step.  The split
+    kernel alone is timed the same way over SPLIT_REPLAYS replays of a graph of
+    one split launch per layer per window."""
     caches, table, kn, vn = build_layers(kvq, torch, w, layers, dev)
     q = w.q.to(dev)
     lens = torch.from_numpy(w.lens).to(dev)
@@ -150,50 +175,58 @@ def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fuse
     with torch.cuda.stream(stream):
         for c in caches:  # warm the kernels once outside capture
             step(c, stream)
-        for name, fn in (("step", step), ("split", split_only)):
+        plans = (("layers", step, layers), ("window", step, steps), ("split", split_only, layers))
+        for name, fn, n in plans:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
-                for c in caches:
-                    fn(c, stream)
+                for i in range(n):
+                    fn(caches[i % layers], stream)
             graphs[name] = g
     torch.cuda.synchronize()
 
-    reps = max(1, (steps + layers - 1) // layers)
-    wreps = max(1, (warmup + layers - 1) // layers)
+    def windows(graph, reps: int):
+        """WINDOWS back-to-back windows of `reps` replays, each between two events."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(WINDOWS + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for k in range(WINDOWS):
+            for _ in range(reps):
+                graph.replay()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        return [ev[k].elapsed_time(ev[k + 1]) for k in range(WINDOWS)]
+
     with torch.cuda.stream(stream):
-        for _ in range(wreps):
-            graphs["step"].replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        t_settle = time.perf_counter()
+        n_settle = 0
+        while time.perf_counter() - t_settle < SETTLE_S:
+            for _ in range(8):
+                graphs["layers"].replay()
+            n_settle += 8 * layers
+            torch.cuda.synchronize()
+        wsteps = 0
+        while wsteps < warmup:
+            graphs["layers"].replay()
+            wsteps += layers
         t0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(reps):
-            graphs["step"].replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
+        step_windows = windows(graphs["window"], 1)
         wall_s = time.perf_counter() - t0
-        step_ms = e0.elapsed_time(e1) / (reps * layers)
-        # dominant kernel alone: back-to-back split launches, timed on their stream
-        sreps = max(4, reps // 2)
-        graphs["split"].replay()
-        s0 = torch.cuda.Event(enable_timing=True)
-        s1 = torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for _ in range(sreps):
-            graphs["split"].replay()
-        s1.record(stream)
-        torch.cuda.synchronize()
-        split_ms = s0.elapsed_time(s1) / (sreps * layers)
+        step_ms = _median(step_windows) / steps
+        split_windows = windows(graphs["split"], SPLIT_REPLAYS)
+        split_ms = _median(split_windows) / (SPLIT_REPLAYS * layers)
     del graphs, caches
-    return dict(workload=w.name, steps=reps * layers, warmup=wreps * layers, step_ms=step_ms,
-                split_ms=split_ms, wall_s=wall_s, bytes=algorithmic_bytes(w), splits=S)
+    return dict(workload=w.name, steps=steps, warmup=wsteps, settle_steps=n_settle, step_ms=step_ms,
+                split_ms=split_ms, wall_s=wall_s, bytes=algorithmic_bytes(w), splits=S,
+                step_window_ms=[round(x / steps, 6) for x in step_windows],
+                split_window_ms=[round(x / (SPLIT_REPLAYS * layers), 6) for x in split_windows])
 
 
 STREAM_GRIDS = (256, 512, 1024, 2048)
 
 
 def time_stream_floor(kvq, torch, nbytes: int, layers: int, dev, reps: int = 8):
+    from quantized_kv_cache_02_amd import probe as kprobe
+
     """The HBM floor for reading `nbytes` once: kvq_stream_read (the decode's
     non-temporal 16-byte loads, nothing else) over `layers` rotated buffers of
     that size, back to back on one stream, timed with HIP events on it; the
@@ -207,13 +240,13 @@ def time_stream_floor(kvq, torch, nbytes: int, layers: int, dev, reps: int = 8):
     with torch.cuda.stream(stream):
         for wg in STREAM_GRIDS:
             for b in bufs:
-                kvq.stream_read(b, wg, sink, stream=stream)
+                kprobe.stream_read(b, wg, sink, stream=stream)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(reps):
                 for b in bufs:
-                    kvq.stream_read(b, wg, sink, stream=stream)
+                    kprobe.stream_read(b, wg, sink, stream=stream)
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / (reps * layers)
@@ -325,25 +358,46 @@ def time_prefill(kvq, torch, ki, dtype: str, past: int, chunk: int, layers: int,
                 step_TFLOPs=fl / (res["step"] * 1e-3) / 1e12)
 
 
-def cpu_baseline(ki, w, seconds: float):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(ki, w, seconds: float, seconds_1t: float):
     """The oracle as it stands on the same workload: one step = dequantize the
-    layer cache to fp32, then fp64 attention.  Runs whole steps until `seconds`
-    of CPU time have passed (at least one)."""
+    layer cache to fp32, then fp64 attention.  Whole steps until `seconds` of
+    wall time have passed (at least one) on the OpenMP threads the process has,
+    then on one thread for `seconds_1t`.  Returns both as (steps, s/step) with
+    the thread count."""
     import oracle
 
     oracle.build(force=False)
     ocache = oracle.build_cache(w)
     qb = ki.bf16_bits(w.q)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        K, V = ocache.dequantize(w.lens)
-        oracle.attend(qb, K, V, w.lens, w.sm_scale, None, w.Hkv)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or el / n * (n + 1) > 2.5 * seconds:
-            break
-    return n, el / n, oracle.num_threads()
+
+    def run(budget):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            K, V = ocache.dequantize(w.lens)
+            oracle.attend(qb, K, V, w.lens, w.sm_scale, None, w.Hkv)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget or el / n * (n + 1) > 2.5 * budget:
+                return n, el / n
+
+    threads = oracle.num_threads()
+    n, sec = run(seconds)
+    oracle.set_num_threads(1)
+    n1, sec1 = run(seconds_1t)
+    oracle.set_num_threads(threads)
+    return n, sec, threads, n1, sec1
 
 
 def main():
@@ -354,7 +408,10 @@ def main():
     ap.add_argument("--ctx", type=int, default=65536)
     ap.add_argument("--dtype", default="int8", choices=["int8", "int4", "bf16"])
     ap.add_argument("--layers", type=int, default=16)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall seconds of oracle steps on all OpenMP threads")
+    ap.add_argument("--cpu-seconds-1t", type=float, default=6.0,
+                    help="wall seconds of oracle steps on one thread")
     ap.add_argument("--separate-append", action="store_true",
                     help="run the step as three launches (kvq_append, split, combine) instead of "
                          "kvq_append_decode_attend (append fused into the split kernel, then combine)")
@@ -378,8 +435,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; the decode path is not run across "
-              "GPUs (see DESIGN.md for how it would shard). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the decode path is not run across GPUs, and the "
+              "figure is that GPU's throughput. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -468,6 +525,15 @@ def main():
         "ms_per_step": round(r["step_ms"], 5),
         "us_per_step": round(r["step_ms"] * 1e3, 2),
         "split_kernel_us": round(r["split_ms"] * 1e3, 2),
+        "timing": {
+            "settle_steps": r["settle_steps"],
+            "windows": WINDOWS,
+            "step_us_per_window": [round(x * 1e3, 2) for x in r["step_window_ms"]],
+            "split_replays_per_window": SPLIT_REPLAYS * args.layers,
+            "split_us_per_window": [round(x * 1e3, 2) for x in r["split_window_ms"]],
+            "how": "median of the windows; each window a HIP-graph replay timed with HIP events on "
+                   "its stream, after settle_steps steps of clock settling and the warmup steps",
+        },
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -505,14 +571,19 @@ def main():
         "what": "kvq_stream_read of the same bytes: the decode's loads and nothing else",
     }
     if not args.no_cpu_baseline:
-        n, sec, threads = cpu_baseline(ki, w, args.cpu_seconds)
+        n, sec, threads, n1, sec1 = cpu_baseline(ki, w, args.cpu_seconds, args.cpu_seconds_1t)
         line["cpu_baseline"] = {
             "value": round(r["bytes"] / sec / 1e9, 4),
             "unit": "GB/s",
             "cores": threads,
             "kind": "oracle",
             "sample": f"{n} oracle steps (dequantize the {args.ctx}-token layer cache to fp32, "
-                      f"then fp64 attention) on the same workload, {sec * 1e3:.0f} ms/step",
+                      f"then fp64 attention) on the same workload, {sec * 1e3:.0f} ms/step on "
+                      f"{threads} OpenMP threads; {n1} steps on 1 thread, {sec1 * 1e3:.0f} ms/step",
+            "cpu_model": cpu_model(),
+            "value_1_thread": round(r["bytes"] / sec1 / 1e9, 4),
+            "ms_per_step": round(sec * 1e3, 1),
+            "ms_per_step_1_thread": round(sec1 * 1e3, 1),
         }
     print(json.dumps(line), flush=True)
 
