@@ -80,7 +80,9 @@ typedef enum kvq_status {
   KVQ_OK = 0,
   KVQ_EINVAL = -1,       /* null required pointer, inconsistent sizes, workspace too small */
   KVQ_EUNSUPPORTED = -2, /* head_dim not in {64,128,256}, Hq/Hkv > 8, q_tokens > 8, unknown enum */
-  KVQ_EHIP = -3          /* the HIP runtime reported a launch error */
+  KVQ_EHIP = -3,         /* the HIP runtime reported a launch error */
+  KVQ_ESCRATCH = -4      /* kvq_attend_ex_noalloc: the call needs more workspace than
+                            KVQ_NOALLOC_SCRATCH_BYTES */
 } kvq_status;
 
 /* One layer's quantized cache.  K and V share the dtype; scale_mode is the K
@@ -248,6 +250,31 @@ int kvq_attend_ex(const kvq_cache* cache, const void* k_new, const void* v_new, 
                   int32_t max_seq_len, float softmax_scale, const float* head_sink,
                   const int32_t* block_table, int32_t max_blocks, const kvq_attn_options* options,
                   void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_attend_ex_noalloc -- kvq_attend_ex for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, whose
+ * place takes a scratch array of KVQ_NOALLOC_SCRATCH_BYTES that the library
+ * holds in device memory (one per GPU, kept until the process ends).  The
+ * call allocates nothing and computes exactly what kvq_attend_ex computes.
+ *
+ * Limit: a shape whose kvq_workspace_bytes exceeds KVQ_NOALLOC_SCRATCH_BYTES
+ * returns KVQ_ESCRATCH before anything is enqueued (use kvq_attend_ex with a
+ * caller workspace then).  Every call on one GPU uses that GPU's one array:
+ * calls that overlap on a GPU (two streams, or two host threads, without an
+ * order between them) race and give undefined results; calls ordered on one
+ * stream are safe.  No content of the array carries from one call to the
+ * next.  The first call whose stream belongs to a device looks up the
+ * array's address on that device (a host query, no allocation); KVQ_EHIP if
+ * the runtime refuses it.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int kvq_attend_ex_noalloc(const kvq_cache* cache, const void* k_new, const void* v_new,
+                          const void* q, int32_t batch, int32_t num_q_heads, int32_t q_tokens,
+                          const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                          const float* head_sink, const int32_t* block_table, int32_t max_blocks,
+                          const kvq_attn_options* options, void* out, void* stream);
 
 /*
  * The two phases the decode entry points are made of, for callers that

@@ -17,20 +17,23 @@ import torch
 __all__ = [
     "INT8", "INT4", "FP8_E4M3FN", "BF16", "NO_SCALE", "PER_ROW", "PER_TENSOR", "PER_CHANNEL",
     "KVCache", "KvqError", "append", "num_splits", "workspace_bytes", "decode_attend",
-    "paged_decode_attend", "append_decode_attend", "attend_ex", "prefill_attend", "split_decode",
+    "paged_decode_attend", "append_decode_attend", "attend_ex", "attend_ex_noalloc", "prefill_attend",
+    "split_decode", "NOALLOC_SCRATCH_BYTES",
     "combine",
     "cache_bytes",
     "lib", "LIB_PATH",
 ]
 
 INT8, INT4, FP8_E4M3FN, BF16 = 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 16 << 20  # KVQ_NOALLOC_SCRATCH_BYTES of include/kvq.h
 NO_SCALE, PER_ROW, PER_TENSOR, PER_CHANNEL = 0, 1, 2, 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 EXPORTS = (
     "kvq_append", "kvq_num_splits", "kvq_workspace_bytes", "kvq_decode_attend",
-    "kvq_paged_decode_attend", "kvq_append_decode_attend", "kvq_attend_ex", "kvq_prefill_attend",
+    "kvq_paged_decode_attend", "kvq_append_decode_attend", "kvq_attend_ex", "kvq_attend_ex_noalloc",
+    "kvq_prefill_attend",
     "kvq_split_decode",
     "kvq_combine", "kvq_cache_bytes",
     "kvq_status_string",
@@ -85,6 +88,9 @@ def lib():
         L.kvq_attend_ex.argtypes = [CP, P, P, P, I32, I32, I32, P, I32, F, P, P, I32,
                                     ctypes.POINTER(_Options), P, P, SZ, P]
         L.kvq_attend_ex.restype = ctypes.c_int
+        L.kvq_attend_ex_noalloc.argtypes = [CP, P, P, P, I32, I32, I32, P, I32, F, P, P, I32,
+                                            ctypes.POINTER(_Options), P, P]
+        L.kvq_attend_ex_noalloc.restype = ctypes.c_int
         L.kvq_prefill_attend.argtypes = [CP, P, P, P, I32, I32, I32, P, I32, F, P, P, I32,
                                          ctypes.POINTER(_Options), P, P]
         L.kvq_prefill_attend.restype = ctypes.c_int
@@ -107,7 +113,8 @@ def _check(status: int, what: str):
 
 
 _STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL: invalid argument",
-           -2: "KVQ_EUNSUPPORTED: unsupported shape or type", -3: "KVQ_EHIP: HIP runtime error"}
+           -2: "KVQ_EUNSUPPORTED: unsupported shape or type", -3: "KVQ_EHIP: HIP runtime error",
+           -4: "KVQ_ESCRATCH: the call needs more workspace than the static scratch"}
 
 
 def _check_status_with(status: int, what: str):
@@ -392,6 +399,31 @@ def attend_ex(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_l
                                _ptr(block_table), mb, ctypes.byref(opts), _ptr(out), _ptr(ws),
                                nbytes, _stream(stream)),
            "kvq_attend_ex")
+    return out
+
+
+def attend_ex_noalloc(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                      softmax_scale: float, out: torch.Tensor,
+                      block_table: Optional[torch.Tensor] = None,
+                      head_sink: Optional[torch.Tensor] = None,
+                      k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                      softcap: float = 0.0, window: int = 0, stream=None) -> torch.Tensor:
+    """attend_ex without a workspace and without allocating: the library's static
+    scratch (NOALLOC_SCRATCH_BYTES per GPU) holds the split partials, so `out`
+    must be given.  Calls that overlap on one GPU race."""
+    B, Tq, Hq = _query(cache, q)
+    if out is None:
+        raise KvqError("attend_ex_noalloc writes into a given out tensor (it allocates nothing)")
+    _common(cache, B, Tq, Hq, seq_lens, head_sink, k_new, v_new, out)
+    mb = _table(block_table, B)
+    _on_gpu(cache, q=q, seq_lens=seq_lens, head_sink=head_sink, block_table=block_table,
+            k_new=k_new, v_new=v_new, out=out)
+    opts = _Options(float(softcap), int(window))
+    _check(lib().kvq_attend_ex_noalloc(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, Tq,
+                                       _ptr(seq_lens), max_seq_len, float(softmax_scale),
+                                       _ptr(head_sink), _ptr(block_table), mb, ctypes.byref(opts),
+                                       _ptr(out), _stream(stream)),
+           "kvq_attend_ex_noalloc")
     return out
 
 

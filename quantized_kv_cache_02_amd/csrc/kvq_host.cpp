@@ -4,6 +4,7 @@
 // into a HIP graph.
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvq.h"
 
@@ -294,6 +295,42 @@ int combine_impl(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, cons
   return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
 
+// Scratch of kvq_attend_ex_noalloc: the decode workspace of callers that
+// cannot allocate.  One array per GPU (the runtime places a copy on every
+// device the library runs on); host code uses only the device address that
+// hipGetSymbolAddress returns for the current device, never the name.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The scratch address on the device the call's kernels run on (the stream's
+// device; the current one for the null stream), looked up once per device
+// with that device current.
+int scratch_for_stream(hipStream_t stream, void** ptr) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return KVQ_EHIP;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t sd;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return KVQ_EHIP;
+    dev = static_cast<int>(sd);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return KVQ_EHIP;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return KVQ_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return KVQ_EHIP;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -423,6 +460,24 @@ int kvq_attend_ex(const kvq_cache* cache, const void* k_new, const void* v_new, 
                       workspace, workspace_bytes, stream, options ? options->window : 0);
 }
 
+int kvq_attend_ex_noalloc(const kvq_cache* cache, const void* k_new, const void* v_new,
+                          const void* q, int32_t batch, int32_t num_q_heads, int32_t q_tokens,
+                          const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                          const float* head_sink, const int32_t* block_table, int32_t max_blocks,
+                          const kvq_attn_options* options, void* out, void* stream) {
+  // the shape's workspace must fit the scratch: checked on the host first
+  DecodeShape sh;
+  int st = decode_shape(cache, batch, num_q_heads, q_tokens, max_seq_len, &sh);
+  if (st != KVQ_OK) return st;
+  if (workspace_size(cache, batch, sh) > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ESCRATCH;
+  void* ws = nullptr;
+  st = scratch_for_stream(static_cast<hipStream_t>(stream), &ws);
+  if (st != KVQ_OK) return st;
+  return kvq_attend_ex(cache, k_new, v_new, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len,
+                       softmax_scale, head_sink, block_table, max_blocks, options, out, ws,
+                       KVQ_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int kvq_prefill_attend(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
                        int32_t batch, int32_t num_q_heads, int32_t q_tokens, const int32_t* seq_lens,
                        int32_t max_seq_len, float softmax_scale, const float* head_sink,
@@ -514,6 +569,9 @@ const char* kvq_status_string(int status) {
     case KVQ_EINVAL: return "KVQ_EINVAL: invalid argument";
     case KVQ_EUNSUPPORTED: return "KVQ_EUNSUPPORTED: unsupported shape or type";
     case KVQ_EHIP: return "KVQ_EHIP: HIP runtime error";
+    case KVQ_ESCRATCH:
+      return "KVQ_ESCRATCH: the call needs more workspace than the library's static scratch "
+             "(KVQ_NOALLOC_SCRATCH_BYTES); pass a workspace to kvq_attend_ex instead";
     default: return "unknown kvq status";
   }
 }

@@ -180,7 +180,7 @@ def test_invalid_stream_read_rejected():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, 5):
+    for s in (0, -1, -2, -3, -4, 5):
         assert kvq.lib().kvq_status_string(s)
 
 
@@ -347,3 +347,30 @@ def test_cache_accepts_well_sized_static_tables():
     assert c.k_scales.numel() == 1
     with pytest.raises(kvq.KvqError, match="dtype"):
         kvq.KVCache(7, kvq.PER_ROW, 2, 64, 64, 2, device="cpu")
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """kvq_attend_ex_noalloc checks the shape's workspace against the static
+    scratch on the host: a shape that needs more returns KVQ_ESCRATCH (-4), an
+    invalid cache the usual status, both before any HIP call."""
+    L = kvq.lib()
+    c = _cache(num_kv_heads=8, block_size=16, num_blocks=1 << 16)
+    need = L.kvq_workspace_bytes(ctypes.byref(c), 512, 64, 8, 4096)
+    assert need > kvq.NOALLOC_SCRATCH_BYTES
+    st = L.kvq_attend_ex_noalloc(ctypes.byref(c), None, None, FAKE, 512, 64, 8, FAKE, 4096, 0.1, None,
+                                 FAKE, 256, None, FAKE, None)
+    assert st == -4
+    assert b"KVQ_ESCRATCH" in L.kvq_status_string(-4)
+    bad = _cache(head_dim=96)
+    assert L.kvq_attend_ex_noalloc(ctypes.byref(bad), None, None, FAKE, 1, 24, 1, FAKE, 4096, 0.1,
+                                   None, None, 0, None, FAKE, None) == -2
+    assert L.kvq_attend_ex_noalloc(ctypes.byref(_cache()), None, None, FAKE, 1, 25, 1, FAKE, 4096,
+                                   0.1, None, None, 0, None, FAKE, None) == -1
+
+
+def test_noalloc_binding_needs_an_output():
+    c, a = _cpu_cache(), _args()
+    _raises("given out tensor", kvq.attend_ex_noalloc, c, a["q"], a["lens"], 64, 0.1, None)
+    _raises("out must have shape", kvq.attend_ex_noalloc, c, a["q"], a["lens"], 64, 0.1,
+            torch.zeros(2, 1, 4, 32, dtype=torch.bfloat16))
+    _raises("on the GPU", kvq.attend_ex_noalloc, c, a["q"], a["lens"], 64, 0.1, a["out"])
