@@ -116,7 +116,7 @@ def build_layers(kvq, torch, w, layers: int, dev):
     return caches, table, kn, vn
 
 
-SETTLE_S = 0.5   # step-graph replays before any timing, whatever --warmup is
+SETTLE_S = 0.5   # step-graph replays before any timing, whatever --warmup is (--settle-s)
 WINDOWS = 5      # timed windows; the median is reported
 SPLIT_REPLAYS = 64  # replays of the 16-launch split-only graph per window
 
@@ -127,7 +127,8 @@ def _median(xs):
     return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
 
-def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fused: bool = True):
+def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fused: bool = True,
+                  settle_s: float = SETTLE_S, split_replays: int = SPLIT_REPLAYS):
     """Time decode steps of workload `w` rotated over `layers` caches.
 
     Clocks are settled first by SETTLE_S seconds of replays of a graph of one
@@ -199,7 +200,7 @@ def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fuse
     with torch.cuda.stream(stream):
         t_settle = time.perf_counter()
         n_settle = 0
-        while time.perf_counter() - t_settle < SETTLE_S:
+        while time.perf_counter() - t_settle < settle_s:
             for _ in range(8):
                 graphs["layers"].replay()
             n_settle += 8 * layers
@@ -212,13 +213,13 @@ def time_workload(kvq, torch, w, layers: int, steps: int, warmup: int, dev, fuse
         step_windows = windows(graphs["window"], 1)
         wall_s = time.perf_counter() - t0
         step_ms = _median(step_windows) / steps
-        split_windows = windows(graphs["split"], SPLIT_REPLAYS)
-        split_ms = _median(split_windows) / (SPLIT_REPLAYS * layers)
+        split_windows = windows(graphs["split"], split_replays)
+        split_ms = _median(split_windows) / (split_replays * layers)
     del graphs, caches
     return dict(workload=w.name, steps=steps, warmup=wsteps, settle_steps=n_settle, step_ms=step_ms,
                 split_ms=split_ms, wall_s=wall_s, bytes=algorithmic_bytes(w), splits=S,
                 step_window_ms=[round(x / steps, 6) for x in step_windows],
-                split_window_ms=[round(x / (SPLIT_REPLAYS * layers), 6) for x in split_windows])
+                split_window_ms=[round(x / (split_replays * layers), 6) for x in split_windows])
 
 
 STREAM_GRIDS = (256, 512, 1024, 2048)
@@ -258,9 +259,9 @@ def time_stream_floor(kvq, torch, nbytes: int, layers: int, dev, reps: int = 8):
 
 
 def time_config(kvq, torch, ki, dtype: str, ctx: int, layers: int, steps: int, warmup: int, dev,
-                fused: bool = True):
+                fused: bool = True, **kw):
     w = ki.make_workload(3, ctx=ctx, dtype=dtype)
-    r = time_workload(kvq, torch, w, layers, steps, warmup, dev, fused)
+    r = time_workload(kvq, torch, w, layers, steps, warmup, dev, fused, **kw)
     r.update(ctx=ctx, dtype=dtype, workload=w)
     return r
 
@@ -416,6 +417,13 @@ def main():
                     help="run the step as three launches (kvq_append, split, combine) instead of "
                          "kvq_append_decode_attend (append fused into the split kernel, then combine)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-floor", action="store_true",
+                    help="skip the streaming-read floor (e.g. under a profiler)")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of step replays that settle the clocks before timing (0 under a "
+                         "profiler, which serializes every launch)")
+    ap.add_argument("--split-replays", type=int, default=SPLIT_REPLAYS,
+                    help="replays of the split-only graph per timed window")
     ap.add_argument("--sweep", default="", help="also time the context sweep for int8 and int4 "
                                                 "and write the lines to this JSON-lines file")
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5],
@@ -501,7 +509,8 @@ def main():
     fused = not args.separate_append
     if args.workload != 3:
         w = ki.make_workload(args.workload)
-        r = time_workload(kvq, torch, w, args.layers, args.steps, args.warmup, dev, fused)
+        r = time_workload(kvq, torch, w, args.layers, args.steps, args.warmup, dev, fused,
+                          settle_s=args.settle_s, split_replays=args.split_replays)
         r.pop("workload")
         print(json.dumps({"workload": w.name, "us_per_step": round(r["step_ms"] * 1e3, 2),
                           "split_kernel_us": round(r["split_ms"] * 1e3, 2),
@@ -510,7 +519,7 @@ def main():
               flush=True)
         return
     r = time_config(kvq, torch, ki, args.dtype, args.ctx, args.layers, args.steps, args.warmup, dev,
-                    fused)
+                    fused, settle_s=args.settle_s, split_replays=args.split_replays)
     w = r.pop("workload")
     achieved = r["bytes"] / (r["split_ms"] * 1e-3) / 1e9
     value = r["bytes"] / (r["step_ms"] * 1e-3) / 1e9
@@ -529,7 +538,7 @@ def main():
             "settle_steps": r["settle_steps"],
             "windows": WINDOWS,
             "step_us_per_window": [round(x * 1e3, 2) for x in r["step_window_ms"]],
-            "split_replays_per_window": SPLIT_REPLAYS * args.layers,
+            "split_replays_per_window": args.split_replays * args.layers,
             "split_us_per_window": [round(x * 1e3, 2) for x in r["split_window_ms"]],
             "how": "median of the windows; each window a HIP-graph replay timed with HIP events on "
                    "its stream, after settle_steps steps of clock settling and the warmup steps",
@@ -561,15 +570,17 @@ def main():
             "traffic": traffic,
         },
     }
-    fl_us, fl_wg = time_stream_floor(kvq, torch, r["bytes"], args.layers, dev)
-    line["stream_floor"] = {
-        "us": round(fl_us, 2),
-        "GB/s": round(r["bytes"] / (fl_us * 1e-6) / 1e9, 1),
-        "frac_of_peak": round(r["bytes"] / (fl_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-        "workgroups": fl_wg,
-        "split_kernel_over_floor": round(r["split_ms"] * 1e3 / fl_us, 3),
-        "what": "kvq_stream_read of the same bytes: the decode's loads and nothing else",
-    }
+    fl_us, fl_wg = (None, None) if args.no_stream_floor else time_stream_floor(kvq, torch, r["bytes"],
+                                                                                 args.layers, dev)
+    if fl_us is not None:
+        line["stream_floor"] = {
+            "us": round(fl_us, 2),
+            "GB/s": round(r["bytes"] / (fl_us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(r["bytes"] / (fl_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "workgroups": fl_wg,
+            "split_kernel_over_floor": round(r["split_ms"] * 1e3 / fl_us, 3),
+            "what": "kvq_stream_read of the same bytes: the decode's loads and nothing else",
+        }
     if not args.no_cpu_baseline:
         n, sec, threads, n1, sec1 = cpu_baseline(ki, w, args.cpu_seconds, args.cpu_seconds_1t)
         line["cpu_baseline"] = {

@@ -40,15 +40,20 @@ def _units():
         ("kvq_append.o", os.path.join(CSRC, "kvq_append.hip"), []),
         ("kvq_combine.o", os.path.join(CSRC, "kvq_combine.hip"), []),
     ]
-    # one unit per (dtype, K scale mode, V scales per row or static)
+    # one unit per (dtype, K scale mode, V scales per row or static).  The MFMA
+    # accumulators stay in ordinary VGPRs: the variants built for one wavefront
+    # per SIMD then keep what exceeds 256 registers in the accumulation
+    # registers (one-cycle copies), where the default form put the accumulators
+    # there and copied all of them around every rescale test.
+    vf = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
     for dt in (1, 2, 3):
         for md in (1, 2, 3):
             for vr in (0, 1):
                 units.append((f"kvq_split_{dt}_{md}_{vr}.o", os.path.join(CSRC, "kvq_split.hip"),
-                              [f"-DKVQ_DTYPE={dt}", f"-DKVQ_MODE={md}", f"-DKVQ_VROW={vr}"]))
+                              [f"-DKVQ_DTYPE={dt}", f"-DKVQ_MODE={md}", f"-DKVQ_VROW={vr}", *vf]))
     # the unquantized bf16 cache: no scales
     units.append(("kvq_split_4_0_0.o", os.path.join(CSRC, "kvq_split.hip"),
-                  ["-DKVQ_DTYPE=4", "-DKVQ_MODE=0", "-DKVQ_VROW=0"]))
+                  ["-DKVQ_DTYPE=4", "-DKVQ_MODE=0", "-DKVQ_VROW=0", *vf]))
     # the chunked-prefill kernel, split the same way.  Its accumulators stay in
     # ordinary vector registers: left to itself the backend parks them in the
     # accumulation registers and copies all of them in and out on every tile

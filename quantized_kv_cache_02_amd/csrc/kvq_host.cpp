@@ -81,6 +81,7 @@ struct DecodeShape {
   int RBK;          // row blocks per workgroup (the kernel variant)
   int SMAX;         // most chunks one sequence can get
   int NSLOT;        // chunk slots per KV head, NW + batch - 1
+  int one_per_cu;   // at most one live workgroup per CU (NW not doubled)
 };
 
 // Static decode shape: grouping, query rows, row blocks and the split count S,
@@ -123,8 +124,11 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   const int64_t per_head = std::max<int64_t>(kvq::kNumCUs / (Hkv * RBN), 1);
   const int64_t all_tiles = (int64_t)batch * ntiles;
   int64_t NW = per_head - (batch - 1);
-  if ((RBN > 1 || row_bytes(c) <= 128) && 2 * per_head - (batch - 1) <= all_tiles / (2 * kvq::kMinTilesPerSplit))
+  bool doubled = false;
+  if ((RBN > 1 || row_bytes(c) <= 128) && 2 * per_head - (batch - 1) <= all_tiles / (2 * kvq::kMinTilesPerSplit)) {
     NW = 2 * per_head - (batch - 1);
+    doubled = true;
+  }
   NW = std::min<int64_t>(NW, all_tiles / kvq::kMinTilesPerSplit);
   NW = std::max<int64_t>(NW, 1);
   const int64_t need = ((int64_t)batch * ntiles + kvq::kMaxTilesPerSplit - 1) / kvq::kMaxTilesPerSplit;
@@ -143,6 +147,9 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   sh->SMAX = (int)std::min<int64_t>(most, NW + batch - 1);
   sh->RBK = RBN > 1 ? 1 : RB;
   sh->NSLOT = (int)(NW + batch - 1);
+  // (the need-based minimum below can exceed the CU count for very long
+  // batches; then the grid holds more than one workgroup per CU)
+  sh->one_per_cu = !doubled && (int64_t)sh->NSLOT * Hkv * RBN <= kvq::kNumCUs;
   return KVQ_OK;
 }
 
@@ -244,6 +251,7 @@ int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int
   a.NW = sh.NW;
   a.S = sh.NSLOT;
   a.RBN = sh.RBN;
+  a.one_per_cu = sh.one_per_cu;
   a.sm_scale = scale;
   a.softcap = opts ? opts->softcap : 0.0f;
   a.window = opts ? opts->window : 0;

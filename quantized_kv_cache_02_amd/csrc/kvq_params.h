@@ -74,6 +74,8 @@ struct SplitArgs {
   int32_t S;   // chunk slots per KV head: NW + B - 1
   int32_t RBN; // workgroups per chunk, one per 16-row block of query rows (1: one
                // workgroup serves every row)
+  int32_t one_per_cu;  // the grid holds at most one workgroup per CU, so a variant
+                       // may use one wavefront per SIMD's register budget
   float sm_scale;
   int32_t vmode;   // V scale mode (the K mode is the kernel's template mode)
   float softcap;   // > 0: logits z -> softcap * tanh(z / softcap)

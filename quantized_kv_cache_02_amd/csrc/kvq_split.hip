@@ -350,10 +350,18 @@ __device__ __forceinline__ void load_tile(const SplitArgs& a, int t, bool live, 
 template <int D>
 constexpr int kQStride = D + 8;
 
+// The softmax weights of a row are exp2(z - m) for a reference m that moves
+// only when a logit exceeds it by more than this (log2 units): the weights stay
+// below 2^8 -- exact in the fp16 (and bf16 hi + lo) P operand up to its usual
+// rounding, far from fp16's 65504 -- and the accumulators are rescaled a few
+// times per wavefront instead of on a large share of tiles.  The merge and the
+// combine weigh each partial by its own reference, as before.
+constexpr float kLazyHeadroom = 8.0f;
+
 // Per-wavefront online-softmax state over its tiles.
 template <int DT, int D, int RB>
 struct WaveState {
-  float m[RB];                         // running max logit of row rb*16+n (log2 units)
+  float m[RB];                         // reference logit of row rb*16+n (log2 units)
   float l[RB];                         // this lane's share of the running sum
   float4_t acc[RB][Geo<DT, D>::NCOL];  // O rows rb*16+4g+e, column c of lane n
   float vref;                          // per-row V: weights carry 1/vref, a power of two
@@ -417,22 +425,24 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
       // exact integer dot products with each query slice (qb[rb][NSL st + k]
       // is slice k of integer step st), combined into one float per logit
       constexpr int NSL = kQSlices<DT, MODE>;
-      i32x4_t acc[NSL];
-#pragma unroll
-      for (int k = 0; k < NSL; ++k) acc[k] = i32x4_t{0, 0, 0, 0};
+      i32x4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
 #pragma unroll
       for (int st = 0; st < G_::ISTEPS; ++st) {
         const i32x4_t ka = k_operand_i8<DT, D>(T.kw, st);
-#pragma unroll
-        for (int k = NSL - 1; k >= 0; --k)
-          acc[k] = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st + k)), acc[k]);
+        if constexpr (NSL == 3)
+          acc2 = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st + 2)), acc2);
+        acc1 = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st + 1)), acc1);
+        acc0 = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st)), acc0);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        int dd[NSL];
-#pragma unroll
-        for (int k = 0; k < NSL; ++k) dd[k] = acc[k][e];
-        dot[e] = q_dot<NSL>(dd);
+        if constexpr (NSL == 3) {
+          const int dd[3] = {acc0[e], acc1[e], acc2[e]};
+          dot[e] = q_dot<3>(dd);
+        } else {
+          const int dd[2] = {acc0[e], acc1[e]};
+          dot[e] = q_dot<2>(dd);
+        }
       }
     } else {
 #pragma unroll
@@ -465,20 +475,21 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
         zz = cap2 - 2.0f * cap2 * __builtin_amdgcn_rcpf(ex + 1.0f);
       }
       z[e] = (unsigned)(rel + e) < span ? zz : -INFINITY;
-      up |= z[e] > W.m[rb];
+      up |= z[e] > W.m[rb] + kLazyHeadroom;
     }
-    // The running max changes only if some logit exceeds it; the cross-lane
-    // reduction runs only then (exactly the same result as reducing always).
+    // The reference m moves only when a logit exceeds it by more than
+    // kLazyHeadroom (a factor 2^8 in the weights); the cross-lane reduction and
+    // the accumulator rescale run only then.  m stays a logit of the row, so
+    // m <= the row's max logit <= m + kLazyHeadroom.
     alpha[rb] = 1.0f;
     if (__builtin_amdgcn_ballot_w64(up) != 0) {
       const float tmax = group_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-      const float mnew = fmaxf(W.m[rb], tmax);
-      if (mnew > W.m[rb]) {
+      if (tmax > W.m[rb] + kLazyHeadroom) {
         // hardware exp2 (results below 2^-126 flush to 0: such weights vanish
-        // in the fp16 operand anyway); 0 when the old max was -inf
-        alpha[rb] = __builtin_amdgcn_exp2f(W.m[rb] - mnew);
+        // in the fp16 operand anyway); 0 when the old reference was -inf
+        alpha[rb] = __builtin_amdgcn_exp2f(W.m[rb] - tmax);
         W.l[rb] *= alpha[rb];
-        W.m[rb] = mnew;
+        W.m[rb] = tmax;
         rescale = true;
       }
     }
@@ -576,7 +587,7 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
 
 // NB tiles of codes are held per wavefront: while one is processed, the loads
 // of the next NB-1 are in flight.
-template <int DT, int MODE, int D, int RB>
+template <int DT, int MODE, int D, int RB, int WPE = kSplitWavesPerSimd>
 struct Knobs {
   // q operand from LDS instead of registers: the bf16 tiles need those
   // registers, and so do the three query slices of an int8 cache with a
@@ -587,18 +598,27 @@ struct Knobs {
   static constexpr bool QLDS =
       DT == kBf16 || (DT == kInt8 && MODE == kPerChannel && RB * D >= kSplitMaxAccColumns);
   static constexpr int NB = kSplitTilesInFlight;
-  static constexpr int WAVES_PER_EU = kSplitWavesPerSimd;
+  static constexpr int WAVES_PER_EU = WPE;
   // merge buffers: one per wavefront (RB * D <= 256 keeps them within 64 KiB)
   static constexpr int MERGE_BUFS = kWaves;
   static_assert(MERGE_BUFS * 16 * RB * D * 4 <= 65536, "merge buffers exceed 64 KiB");
 };
 
-template <int DT, int MODE, int D, int RB, bool CAP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    Knobs<DT, MODE, D, RB>::WAVES_PER_EU, Knobs<DT, MODE, D, RB>::WAVES_PER_EU))) void
+// Variants whose accumulators fill a wavefront and whose rows exceed 128 bytes
+// sit at the 256-register budget of two wavefronts per SIMD (a spill there is a
+// scratch reload in the tile loop, which waits for every tile load before it).
+// Launches that place one workgroup per CU -- all of these but the row-split
+// ones -- run them with WPE = 1 instead: up to 512 registers, the MFMA
+// accumulators in ordinary VGPRs (the units build with -amdgpu-mfma-vgpr-form)
+// and any excess held in the accumulation registers, not in memory.
+template <int DT, int D, int RB>
+constexpr bool kHeavy = Geo<DT, D>::ROWB > 128 && RB * D >= kSplitMaxAccColumns;
+
+template <int DT, int MODE, int D, int RB, bool CAP, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
 split_decode_kernel(SplitArgs a) {
   using G_ = Geo<DT, D>;
-  using K_ = Knobs<DT, MODE, D, RB>;
+  using K_ = Knobs<DT, MODE, D, RB, WPE>;
   constexpr int RP = 16 * RB;  // padded query rows
   constexpr int NB = K_::NB;
 
@@ -1018,10 +1038,20 @@ hipError_t launch_one(const SplitArgs& a, int B, hipStream_t st) {
   } else {
     const int gx = a.RBN > 1 ? (a.S + 7) / 8 * 8 * a.RBN : a.S;
     dim3 grid(gx, a.c.Hkv, 1);
+    constexpr int W2 = kSplitWavesPerSimd;
+    if constexpr (kHeavy<DT, D, RB>) {
+      if (a.one_per_cu) {
+        if (a.softcap > 0.0f)
+          hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, true, 1>), grid, dim3(256), 0, st, a);
+        else
+          hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, false, 1>), grid, dim3(256), 0, st, a);
+        return hipGetLastError();
+      }
+    }
     if (a.softcap > 0.0f)
-      hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, true, W2>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, false>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, false, W2>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
 }
