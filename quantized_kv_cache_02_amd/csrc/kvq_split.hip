@@ -368,6 +368,240 @@ struct WaveState {
   float ivref;                         // 1 / vref (exact)
 };
 
+// Per-row V scales: keep vref a power of two >= every scale seen, so the
+// weights p * s / vref stay in [0, 1].  The reduction runs only on the rare
+// tiles where some scale exceeds the current reference; then vfac = old vref /
+// new vref (exact) multiplies the accumulators.
+__device__ __forceinline__ void v_reference(const float4_t& vs4, float& vref, float& ivref, float& vfac,
+                                            bool& rescale, float (&vsn)[4]) {
+  const float vmax4 = fmaxf(fmaxf(vs4[0], vs4[1]), fmaxf(vs4[2], vs4[3]));
+  if (__builtin_amdgcn_ballot_w64(vmax4 > vref) != 0) {
+    const float vmax = group_max4(vmax4);
+    int en;
+    (void)frexpf(vmax, &en);  // vmax < 2^en
+    ivref = ldexpf(1.0f, -en);
+    vfac = vref * ivref;  // both powers of two: exact
+    vref = ldexpf(1.0f, en);
+    rescale = true;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vsn[e] = vs4[e] * ivref;
+}
+
+// S^T of one tile for one 16-row block: this lane's 4 dot products (tokens
+// 4g..4g+3 of the tile, query row n) of the K codes with the row block's q
+// operand (qop(k): the operand of k-step k), in the operand's units.
+template <int DT, int MODE, int D, class QOp>
+__device__ __forceinline__ void tile_dots(const uint32_t* kw, QOp qop, float (&dot)[4]) {
+  using G_ = Geo<DT, D>;
+  // S^T: two independent accumulation chains over the k-steps
+  float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (G_::IQK) {
+    // exact integer dot products with each query slice (operand NSL st + k
+    // is slice k of integer step st), combined into one float per logit
+    constexpr int NSL = kQSlices<DT, MODE>;
+    i32x4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < G_::ISTEPS; ++st) {
+      const i32x4_t ka = k_operand_i8<DT, D>(kw, st);
+      if constexpr (NSL == 3)
+        acc2 = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st + 2)), acc2);
+      acc1 = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st + 1)), acc1);
+      acc0 = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st)), acc0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (NSL == 3) {
+        const int dd[3] = {acc0[e], acc1[e], acc2[e]};
+        dot[e] = q_dot<3>(dd);
+      } else {
+        const int dd[2] = {acc0[e], acc1[e]};
+        dot[e] = q_dot<2>(dd);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < G_::KSTEPS; ks += 2) {
+      if constexpr (DT == kBf16) {
+        s0 = mfma32_bf16(k_operand<DT, D>(kw, ks), qop(ks), s0);
+        if (ks + 1 < G_::KSTEPS) s1 = mfma32_bf16(k_operand<DT, D>(kw, ks + 1), qop(ks + 1), s1);
+      } else {
+        s0 = mfma32(k_operand<DT, D>(kw, ks), qop(ks), s0);
+        if (ks + 1 < G_::KSTEPS) s1 = mfma32(k_operand<DT, D>(kw, ks + 1), qop(ks + 1), s1);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dot[e] = s0[e] + s1[e];
+  }
+}
+
+// Logits (log2 units) of this lane's 4 tokens tbase..tbase+3 from their dot
+// products: the row multiplier, a per-row K scale, the soft cap, and -inf for
+// tokens outside the row's visible range lo <= t < lim (or a tile outside the
+// pool).  Rows past the sequence and tiles outside the pool were read as zero
+// by the bounded loads (codes and scales), so only the logits need masking:
+// those tokens then get weight 0 and add nothing.
+template <int MODE, bool CAP>
+__device__ __forceinline__ void tile_logits(const float (&dot)[4], const float4_t& ks4, bool ok, int tbase,
+                                            float rowmul, int lim, int lo, float cap2, float icap2,
+                                            float (&z)[4]) {
+  // token tbase + e is visible to this lane's row iff lo <= it < lim
+  const unsigned span = ok ? (unsigned)(lim - lo) : 0u;
+  const int rel = tbase - lo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float zz = dot[e] * rowmul;
+    if constexpr (MODE == kPerRow) zz *= ks4[e];
+    // soft cap in log2 units: with x = z / softcap, z2 = z log2(e), cap2 =
+    // softcap log2(e): cap2 tanh(x) = cap2 (1 - 2 / (1 + 2^(2 z2 / softcap)))
+    // (icap2 = 2 / softcap); the hardware exp2 and reciprocal, 1 ulp each
+    if constexpr (CAP) {
+      const float ex = __builtin_amdgcn_exp2f(zz * icap2);
+      zz = cap2 - 2.0f * cap2 * __builtin_amdgcn_rcpf(ex + 1.0f);
+    }
+    z[e] = (unsigned)(rel + e) < span ? zz : -INFINITY;
+  }
+}
+
+// One tile's logits and softmax weights for one 16-row block: S^T, the
+// logits, the lazily moved reference m, the running sum l and the P operand
+// (bf16 cache: its hi and lo parts).  alpha is the factor the row's
+// accumulators take when m moved (1 otherwise), and `rescale` is set then.
+template <int DT, int MODE, int D, bool CAP, class QOp>
+__device__ __forceinline__ void row_block_weights(const uint32_t* kw, const float4_t& ks4, bool ok,
+                                                  int tbase, QOp qop, float rowmul, int lim, int lo,
+                                                  float cap2, float icap2, const float (&vsn)[4],
+                                                  float& m, float& l, float& alpha, bool& rescale,
+                                                  half4_t& pa, u32x2_t& phi, u32x2_t& plo) {
+  float dot[4];
+  tile_dots<DT, MODE, D>(kw, qop, dot);
+  float z[4];
+  tile_logits<MODE, CAP>(dot, ks4, ok, tbase, rowmul, lim, lo, cap2, icap2, z);
+  bool up = false;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) up |= z[e] > m + kLazyHeadroom;
+  // The reference m moves only when a logit exceeds it by more than
+  // kLazyHeadroom (a factor 2^8 in the weights); the cross-lane reduction and
+  // the accumulator rescale run only then.  m stays a logit of the row, so
+  // m <= the row's max logit <= m + kLazyHeadroom.
+  alpha = 1.0f;
+  if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    const float tmax = group_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    if (tmax > m + kLazyHeadroom) {
+      // hardware exp2 (results below 2^-126 flush to 0: such weights vanish
+      // in the fp16 operand anyway); 0 when the old reference was -inf
+      alpha = __builtin_amdgcn_exp2f(m - tmax);
+      l *= alpha;
+      m = tmax;
+      rescale = true;
+    }
+  }
+  const float msafe = (m == -INFINITY) ? 0.0f : m;
+  half4_t ph;
+  float pf[4];
+  float psum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float p = __builtin_amdgcn_exp2f(z[e] - msafe);
+    psum += p;
+    float pv = p;
+    if constexpr (kVRow) pv = p * vsn[e];
+    ph[e] = (_Float16)pv;
+    pf[e] = pv;
+  }
+  l += psum;
+  pa = ph;
+  if constexpr (DT == kBf16) {
+    uint16_t h[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = f32_to_bf16(pf[e]);
+      lw[e] = f32_to_bf16(pf[e] - bf16_to_f32(h[e]));  // exact difference
+    }
+    phi = u32x2_t{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+    plo = u32x2_t{lw[0] | ((uint32_t)lw[1] << 16), lw[2] | ((uint32_t)lw[3] << 16)};
+  }
+}
+
+// O += P . V for one tile: unpack the lane's V column blocks (VD channels) and
+// accumulate every row block's weights into them.
+// The B operands of the P . V MFMA from dword w of the lane's V codes (tokens
+// 4g..4g+3 of the tile): vb[k] feeds accumulator column v_column(w, k), for k
+// < 8 (int4: both nibbles of the bytes of the dword, nb of them valid) or
+// k < 4 (the 8-bit caches).
+template <int DT, int VD>
+__device__ __forceinline__ void v_block(const uint32_t (&vw)[4][Geo<DT, VD>::VDW], int w, half4_t (&vb)[8]) {
+  if constexpr (DT == kInt4) {
+    uint32_t ev4[4], od4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t x = vw[e][w] ^ 0x88888888u;
+      ev4[e] = (x << 4) & 0xF0F0F0F0u;
+      od4[e] = x & 0xF0F0F0F0u;
+    }
+    v_transpose4<0>(ev4[0], ev4[1], ev4[2], ev4[3], vb);
+    v_transpose4<0>(od4[0], od4[1], od4[2], od4[3], vb + 4);
+  } else if constexpr (DT == kInt8) {
+    v_transpose4<0>(vw[0][w] ^ 0x80808080u, vw[1][w] ^ 0x80808080u, vw[2][w] ^ 0x80808080u,
+                    vw[3][w] ^ 0x80808080u, vb);
+  } else {
+    static_assert(DT == kFp8, "v_block: quantized caches");
+    v_transpose4<1>(vw[0][w], vw[1][w], vw[2][w], vw[3][w], vb);
+  }
+}
+
+// Operands of dword block w: how many, and the accumulator column of vb[k].
+template <int DT, int VD>
+constexpr int v_block_ops() {
+  return DT == kInt4 ? 2 * (Geo<DT, VD>::VLB >= 4 ? 4 : Geo<DT, VD>::VLB) : 4;
+}
+template <int DT, int VD>
+__device__ __forceinline__ constexpr int v_column(int w, int k) {
+  if constexpr (DT == kInt4) {
+    constexpr int nb = Geo<DT, VD>::VLB >= 4 ? 4 : Geo<DT, VD>::VLB;
+    return 2 * nb * w + (k < nb ? k : nb + (k - 4));
+  } else {
+    return 4 * w + k;
+  }
+}
+
+// O += P . V for one tile: unpack the lane's V column blocks (VD channels) and
+// accumulate every row block's weights into them.
+template <int DT, int VD, int RB>
+__device__ __forceinline__ void accumulate_pv(const uint32_t (&vw)[4][Geo<DT, VD>::VDW],
+                                              const half4_t (&pa)[RB], const u32x2_t (&phi)[RB],
+                                              const u32x2_t (&plo)[RB],
+                                              float4_t (&acc)[RB][Geo<DT, VD>::NCOL]) {
+  using GV = Geo<DT, VD>;
+#pragma unroll
+  for (int w = 0; w < GV::VDW; ++w) {
+    if constexpr (DT == kBf16) {
+      // dword w of the lane's span holds channel columns 2w (low half) and 2w+1
+      const u32x2_t b0 = {perm(vw[1][w], vw[0][w], 0x05040100u), perm(vw[3][w], vw[2][w], 0x05040100u)};
+      const u32x2_t b1 = {perm(vw[1][w], vw[0][w], 0x07060302u), perm(vw[3][w], vw[2][w], 0x07060302u)};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[rb][2 * w] = mfma16_bf16(phi[rb], b0, acc[rb][2 * w]);
+        acc[rb][2 * w] = mfma16_bf16(plo[rb], b0, acc[rb][2 * w]);
+        acc[rb][2 * w + 1] = mfma16_bf16(phi[rb], b1, acc[rb][2 * w + 1]);
+        acc[rb][2 * w + 1] = mfma16_bf16(plo[rb], b1, acc[rb][2 * w + 1]);
+      }
+    } else {
+      half4_t vb[8];
+      v_block<DT, VD>(vw, w, vb);
+      constexpr int NO = v_block_ops<DT, VD>();
+#pragma unroll
+      for (int k0 = 0; k0 < NO; ++k0) {
+        // int4: the even-nibble operand k and its odd partner, as before
+        const int k = DT == kInt4 ? (k0 % 2 == 0 ? k0 / 2 : 4 + k0 / 2) : k0;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc[rb][v_column<DT, VD>(w, k)] = mfma16(pa[rb], vb[k], acc[rb][v_column<DT, VD>(w, k)]);
+      }
+    }
+  }
+}
+
 template <int DT, int MODE, int D, int RB, bool CAP, bool QLDS>
 __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L, int n, int g,
                                              const half8_t (&qb)[RB][kQOps<DT, MODE, D>],
@@ -381,143 +615,25 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
   const bool ok = T.ok != 0;
   (void)L;
 
-  // Rows past the sequence and tiles outside the pool were read as zero by the
-  // bounded loads (codes and scales), so only the logits need masking: those
-  // tokens then get weight 0 and add nothing.
-  const auto& vw = T.vw;
-
-  // Per-row V scales: keep vref a power of two >= every scale seen, so the
-  // weights p * s / vref stay in [0, 1].  The reduction runs only on the rare
-  // tiles where some scale exceeds the current reference.
   float vfac = 1.0f;
   bool rescale = false;
   float vsn[4] = {1.f, 1.f, 1.f, 1.f};
-  if constexpr (kVRow) {
-    const float vmax4 = fmaxf(fmaxf(T.vs4[0], T.vs4[1]), fmaxf(T.vs4[2], T.vs4[3]));
-    if (__builtin_amdgcn_ballot_w64(vmax4 > W.vref) != 0) {
-      const float vmax = group_max4(vmax4);
-      int en;
-      (void)frexpf(vmax, &en);  // vmax < 2^en
-      W.ivref = ldexpf(1.0f, -en);
-      vfac = W.vref * W.ivref;  // both powers of two: exact
-      W.vref = ldexpf(1.0f, en);
-      rescale = true;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vsn[e] = T.vs4[e] * W.ivref;
-  }
+  if constexpr (kVRow) v_reference(T.vs4, W.vref, W.ivref, vfac, rescale, vsn);
 
   half4_t pa[RB];
   u32x2_t phi[RB], plo[RB];  // bf16 cache: p = hi + lo, each a bf16 A operand
   float alpha[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    // S^T: two independent accumulation chains over the k-steps
-    float4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     // the q operand of k-step k: registers, or this wavefront's LDS copy (lane-
     // linear, so conflict-free).  The LDS offset is made opaque so the compiler
     // cannot hoist those reads out of the tile loop back into registers.
     int qo = rb * kQOps<DT, MODE, D> * 64;
     if constexpr (QLDS) asm volatile("" : "+v"(qo));
     auto qop = [&](int k) { return QLDS ? qlds[qo + 64 * k] : qb[rb][k]; };
-    float dot[4];
-    if constexpr (G_::IQK) {
-      // exact integer dot products with each query slice (qb[rb][NSL st + k]
-      // is slice k of integer step st), combined into one float per logit
-      constexpr int NSL = kQSlices<DT, MODE>;
-      i32x4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
-#pragma unroll
-      for (int st = 0; st < G_::ISTEPS; ++st) {
-        const i32x4_t ka = k_operand_i8<DT, D>(T.kw, st);
-        if constexpr (NSL == 3)
-          acc2 = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st + 2)), acc2);
-        acc1 = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st + 1)), acc1);
-        acc0 = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qop(NSL * st)), acc0);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (NSL == 3) {
-          const int dd[3] = {acc0[e], acc1[e], acc2[e]};
-          dot[e] = q_dot<3>(dd);
-        } else {
-          const int dd[2] = {acc0[e], acc1[e]};
-          dot[e] = q_dot<2>(dd);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < G_::KSTEPS; ks += 2) {
-        if constexpr (DT == kBf16) {
-          s0 = mfma32_bf16(k_operand<DT, D>(T.kw, ks), qop(ks), s0);
-          if (ks + 1 < G_::KSTEPS) s1 = mfma32_bf16(k_operand<DT, D>(T.kw, ks + 1), qop(ks + 1), s1);
-        } else {
-          s0 = mfma32(k_operand<DT, D>(T.kw, ks), qop(ks), s0);
-          if (ks + 1 < G_::KSTEPS) s1 = mfma32(k_operand<DT, D>(T.kw, ks + 1), qop(ks + 1), s1);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dot[e] = s0[e] + s1[e];
-    }
-    float z[4];
-    bool up = false;
-    // token tbase + e is visible to this lane's row iff lo <= it < lim
-    const unsigned span = ok ? (unsigned)(lim[rb] - lo[rb]) : 0u;
-    const int rel = tbase - lo[rb];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float zz = dot[e] * rowmul[rb];
-      if constexpr (MODE == kPerRow) zz *= T.ks4[e];
-      // soft cap in log2 units: with x = z / softcap, z2 = z log2(e), cap2 =
-      // softcap log2(e): cap2 tanh(x) = cap2 (1 - 2 / (1 + 2^(2 z2 / softcap)))
-      // (icap2 = 2 / softcap); the hardware exp2 and reciprocal, 1 ulp each
-      if constexpr (CAP) {
-        const float ex = __builtin_amdgcn_exp2f(zz * icap2);
-        zz = cap2 - 2.0f * cap2 * __builtin_amdgcn_rcpf(ex + 1.0f);
-      }
-      z[e] = (unsigned)(rel + e) < span ? zz : -INFINITY;
-      up |= z[e] > W.m[rb] + kLazyHeadroom;
-    }
-    // The reference m moves only when a logit exceeds it by more than
-    // kLazyHeadroom (a factor 2^8 in the weights); the cross-lane reduction and
-    // the accumulator rescale run only then.  m stays a logit of the row, so
-    // m <= the row's max logit <= m + kLazyHeadroom.
-    alpha[rb] = 1.0f;
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
-      const float tmax = group_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-      if (tmax > W.m[rb] + kLazyHeadroom) {
-        // hardware exp2 (results below 2^-126 flush to 0: such weights vanish
-        // in the fp16 operand anyway); 0 when the old reference was -inf
-        alpha[rb] = __builtin_amdgcn_exp2f(W.m[rb] - tmax);
-        W.l[rb] *= alpha[rb];
-        W.m[rb] = tmax;
-        rescale = true;
-      }
-    }
-    const float msafe = (W.m[rb] == -INFINITY) ? 0.0f : W.m[rb];
-    half4_t ph;
-    float pf[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = __builtin_amdgcn_exp2f(z[e] - msafe);
-      psum += p;
-      float pv = p;
-      if constexpr (kVRow) pv = p * vsn[e];
-      ph[e] = (_Float16)pv;
-      pf[e] = pv;
-    }
-    W.l[rb] += psum;
-    pa[rb] = ph;
-    if constexpr (DT == kBf16) {
-      uint16_t h[4], l[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[e] = f32_to_bf16(pf[e]);
-        l[e] = f32_to_bf16(pf[e] - bf16_to_f32(h[e]));  // exact difference
-      }
-      phi[rb] = u32x2_t{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
-      plo[rb] = u32x2_t{l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16)};
-    }
+    row_block_weights<DT, MODE, D, CAP>(T.kw, T.ks4, ok, tbase, qop, rowmul[rb], lim[rb], lo[rb],
+                                        cap2, icap2, vsn, W.m[rb], W.l[rb], alpha[rb], rescale,
+                                        pa[rb], phi[rb], plo[rb]);
   }
   // Rescale the accumulators when some row's max grew or the V reference moved
   // (rare after the first tiles).  Accumulator rows 4g+e belong to the P rows
@@ -534,56 +650,203 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
         for (int e = 0; e < 4; ++e) W.acc[rb][c][e] *= f[e];
     }
   }
+  accumulate_pv<DT, D, RB>(T.vw, pa, phi, plo, W.acc);
+}
 
-  // V: unpack column blocks and accumulate O += P . V
+// B operand of S^T for query row r of the staged rows qs (bf16, kQStride
+// apart): the row in this lane's channel order, normalized by a power of two
+// so every element lies in (-1, 1) (integer caches: the row as a fixed-point
+// integer vector in int8 slices); returns the row multiplier that restores it
+// (logit in log2 units = dot * multiplier * per-row K scale).
+template <int DT, int MODE, int D>
+__device__ __forceinline__ float fold_q_row(const SplitArgs& a, const uint16_t* qs, int r, int g, int hkv,
+                                            half8_t (&qb)[kQOps<DT, MODE, D>]) {
+  using G_ = Geo<DT, D>;
+  const float* kst = a.c.k_scales;
+  if constexpr (DT == kBf16) {
+    // the q rows as they are: bf16 products are exact in the fp32 accumulation
 #pragma unroll
-  for (int w = 0; w < G_::VDW; ++w) {
-    half4_t vb[8];
-    if constexpr (DT == kInt4) {
-      uint32_t ev4[4], od4[4];
+    for (int ks = 0; ks < G_::KSTEPS; ++ks)
+      qb[ks] = __builtin_bit_cast(
+          half8_t, *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + k_channel<DT, D>(ks, g, 0)));
+    return a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
+  }
+  if constexpr (G_::IQK) {
+    // The row as a fixed-point integer vector in NSL int8 slices (see
+    // q_slices): 15 bits of the row's largest element, 23 with a
+    // per-channel K scale folded in.
+    constexpr int NSL = kQSlices<DT, MODE>;
+    float qv[G_::ISTEPS][16];
+    float amax = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t x = vw[e][w] ^ 0x88888888u;
-        ev4[e] = (x << 4) & 0xF0F0F0F0u;
-        od4[e] = x & 0xF0F0F0F0u;
+    for (int st = 0; st < G_::ISTEPS; ++st) {
+      const int base = k_channel_i8<DT, D>(st, g, 0);
+      const u32x4_t r0 = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base);
+      const u32x4_t r1 = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base + 8);
+      float x16[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x16[2 * i] = __uint_as_float(r0[i] << 16);
+        x16[2 * i + 1] = __uint_as_float(r0[i] & 0xFFFF0000u);
+        x16[8 + 2 * i] = __uint_as_float(r1[i] << 16);
+        x16[8 + 2 * i + 1] = __uint_as_float(r1[i] & 0xFFFF0000u);
       }
-      v_transpose4<0>(ev4[0], ev4[1], ev4[2], ev4[3], vb);
-      v_transpose4<0>(od4[0], od4[1], od4[2], od4[3], vb + 4);
-      constexpr int nb = G_::VLB >= 4 ? 4 : G_::VLB;
 #pragma unroll
-      for (int k = 0; k < nb; ++k)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          W.acc[rb][2 * nb * w + k] = mfma16(pa[rb], vb[k], W.acc[rb][2 * nb * w + k]);
-          W.acc[rb][2 * nb * w + nb + k] = mfma16(pa[rb], vb[4 + k], W.acc[rb][2 * nb * w + nb + k]);
-        }
-    } else if constexpr (DT == kBf16) {
-      // dword w of the lane's span holds channel columns 2w (low half) and 2w+1
-      const u32x2_t b0 = {perm(vw[1][w], vw[0][w], 0x05040100u), perm(vw[3][w], vw[2][w], 0x05040100u)};
-      const u32x2_t b1 = {perm(vw[1][w], vw[0][w], 0x07060302u), perm(vw[3][w], vw[2][w], 0x07060302u)};
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        W.acc[rb][2 * w] = mfma16_bf16(phi[rb], b0, W.acc[rb][2 * w]);
-        W.acc[rb][2 * w] = mfma16_bf16(plo[rb], b0, W.acc[rb][2 * w]);
-        W.acc[rb][2 * w + 1] = mfma16_bf16(phi[rb], b1, W.acc[rb][2 * w + 1]);
-        W.acc[rb][2 * w + 1] = mfma16_bf16(plo[rb], b1, W.acc[rb][2 * w + 1]);
+      for (int p = 0; p < 16; ++p) {
+        const int off = k_offset_i8<DT>(p);  // 0..15
+        float x = x16[off];
+        if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
+        qv[st][p] = x;
+        amax = fmaxf(amax, fabsf(x));
       }
-    } else if constexpr (DT == kInt8) {
-      v_transpose4<0>(vw[0][w] ^ 0x80808080u, vw[1][w] ^ 0x80808080u, vw[2][w] ^ 0x80808080u,
-                      vw[3][w] ^ 0x80808080u, vb);
+    }
+    amax = group_max4(amax);
+    int ex = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+    for (int st = 0; st < G_::ISTEPS; ++st) {
+      u32x4_t w[NSL];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) W.acc[rb][4 * w + q] = mfma16(pa[rb], vb[q], W.acc[rb][4 * w + q]);
-    } else {
-      v_transpose4<1>(vw[0][w], vw[1][w], vw[2][w], vw[3][w], vb);
+      for (int k = 0; k < NSL; ++k) w[k] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int p = 0; p < 16; ++p) {
+        int sl[NSL];
+        q_slices<NSL>(qv[st][p], ex, sl);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) W.acc[rb][4 * w + q] = mfma16(pa[rb], vb[q], W.acc[rb][4 * w + q]);
+        for (int k = 0; k < NSL; ++k) w[k][p / 4] |= ((uint32_t)sl[k] & 0xFFu) << (8 * (p % 4));
+      }
+#pragma unroll
+      for (int k = 0; k < NSL; ++k) qb[NSL * st + k] = __builtin_bit_cast(half8_t, w[k]);
+    }
+    float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
+    if constexpr (MODE == kPerTensor) mul *= kst[0];
+    if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
+    return ldexpf(mul, ex - (8 * NSL - 2));
+  }
+  float qv[G_::KSTEPS][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < G_::KSTEPS; ++ks) {
+    // the 8 channels of a k-step are 8 consecutive channels (permuted for int4)
+    const int base = k_channel<DT, D>(ks, g, 0);
+    u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base);
+    float x8[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x8[2 * i] = __uint_as_float(raw[i] << 16);
+      x8[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int off = k_channel<DT, D>(ks, g, e) - base;  // 0..7
+      float x = x8[off];
+      if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
+      qv[ks][e] = x;
+      amax = fmaxf(amax, fabsf(x));
     }
   }
+  amax = group_max4(amax);
+  int ex = 0;
+  if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
+#pragma unroll
+  for (int ks = 0; ks < G_::KSTEPS; ++ks) {
+    half8_t h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (_Float16)ldexpf(qv[ks][e], -ex);
+    qb[ks] = h;
+  }
+  float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
+  if constexpr (MODE == kPerTensor) mul *= kst[0];
+  if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
+  return ldexpf(mul, ex);
 }
+
+// Tokens visible to query row `row` (of the sequence's R rows; `live` false
+// for padding rows, which see none): lo <= t < lim.
+__device__ __forceinline__ void row_window(const SplitArgs& a, int L, int row, bool live, int& lim, int& lo) {
+  lim = live ? (L - a.Tq + row / a.G + 1) : 0;
+  if (lim > L) lim = L;
+  lo = a.window > 0 ? lim - a.window : 0;
+  if (lim < lo) lim = lo;  // a query before the first token sees none
+}
+
+// This workgroup's chunk under the balanced schedule -- sequence b (length L)
+// and its tiles [tb, te) -- the same for every wavefront; false for an idle
+// slot.  load_q(b) issues the query loads as soon as the sequence is known
+// (one sequence: chunk = slot, and the loads go out before the length
+// arrives).  `record`: this wavefront also writes every sequence's chunk slots
+// for the combine.
+template <class LoadQ>
+__device__ __forceinline__ bool workgroup_chunk(const SplitArgs& a, int slot, bool record, int lane,
+                                                LoadQ&& load_q, int& b, int& L, int& tb, int& te) {
+  if (a.B == 1) {
+    b = 0;
+    load_q(0);
+    L = clamp_len(a.seq_lens[0], a.max_seq_len);
+    const Span sp = visible_tiles(L, a.Tq, a.window);
+    const int C = max((sp.end - sp.first + a.NW - 1) / a.NW, kMinTilesPerSplit);
+    tb = sp.first + slot * C;
+    te = min(tb + C, sp.end);
+    return tb < sp.end;
+  }
+  const Chunk ch = find_chunk(a.seq_lens, a.B, a.max_seq_len, a.NW, a.Tq, a.window, slot, -1, lane,
+                              record ? a.ws_chunks : nullptr);
+  if (ch.b < 0) return false;
+  b = ch.b;
+  L = ch.L;
+  tb = ch.first;
+  te = ch.end;
+  load_q(b);
+  return true;
+}
+
+// Fused append: the new K and V rows of the query tokens j with mine[j]
+// (position L - Tq + j), loaded from the bf16 inputs, then quantized and
+// stored into the cache with the same arithmetic as kvq_append.  store() waits
+// until the stores are acknowledged, so the wavefront's later loads of those
+// rows see them.
+template <int DT, int MODE, int D>
+struct NewRows {
+  using RG = RowGeo<DT, D>;
+  uint16_t rk[kMaxQTokens][RG::EPL], rv[kMaxQTokens][RG::EPL];
+  int rblk[kMaxQTokens];
+
+  __device__ __forceinline__ void load(const SplitArgs& a, const bool (&mine)[kMaxQTokens], int b, int hkv,
+                                       int L, int lane) {
+#pragma unroll
+    for (int j = 0; j < kMaxQTokens; ++j) {
+      if (!mine[j]) continue;
+      const int p = L - a.Tq + j;
+      const size_t xi = (((size_t)b * a.Tq + j) * a.c.Hkv + hkv) * D;
+      load_row<DT, D>(a.k_new + xi, lane, rk[j]);
+      load_row<DT, D>(a.v_new + xi, lane, rv[j]);
+      rblk[j] = a.c.block_table != nullptr
+                    ? a.c.block_table[(size_t)b * a.c.max_blocks + p / a.c.block_size]
+                    : b;
+    }
+  }
+
+  __device__ __forceinline__ void store(const SplitArgs& a, const bool (&mine)[kMaxQTokens], int hkv, int L,
+                                        int lane) {
+#pragma unroll
+    for (int j = 0; j < kMaxQTokens; ++j) {
+      if (!mine[j] || (unsigned)rblk[j] >= (unsigned)a.c.num_blocks) continue;
+      const int p = L - a.Tq + j;
+      const size_t ri =
+          ((size_t)rblk[j] * a.c.Hkv + hkv) * a.c.block_size + (size_t)(p % a.c.block_size);
+      quantize_store_row<DT, MODE, D>(rk[j], lane, a.c.k_codes + ri * RG::ROWB, a.c.k_scales + ri,
+                                      MODE == kPerChannel ? a.c.k_scales + (size_t)hkv * D : a.c.k_scales);
+      if constexpr (kVRow)  // V per row: known at compile time
+        quantize_store_row<DT, kPerRow, D>(rv[j], lane, a.c.v_codes + ri * RG::ROWB, a.c.v_scales + ri,
+                                           a.c.v_scales);
+      else
+        quantize_store_row_mode<DT, D>(a.vmode, rv[j], lane, a.c.v_codes + ri * RG::ROWB,
+                                       a.c.v_scales + ri,
+                                       a.vmode == kPerChannel ? a.c.v_scales + (size_t)hkv * D : a.c.v_scales);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before any load of those rows
+  }
+};
 
 // NB tiles of codes are held per wavefront: while one is processed, the loads
 // of the next NB-1 are in flight.
@@ -676,31 +939,12 @@ split_decode_kernel(SplitArgs a) {
 
   // ---- this workgroup's chunk under the balanced schedule (every wavefront
   // derives the same one; an idle slot leaves as a whole before any barrier).
-  // One sequence: chunk = slot, and the query loads go out before the length
-  // arrives.
+  // The first wavefront of slot 0, KV head 0, row block 0 also records every
+  // sequence's chunk slots for the combine.
   int b, L, tb, te;
-  if (a.B == 1) {
-    b = 0;
-    load_q(0);
-    L = clamp_len(a.seq_lens[0], a.max_seq_len);
-    const Span sp = visible_tiles(L, a.Tq, a.window);
-    const int C = max((sp.end - sp.first + a.NW - 1) / a.NW, kMinTilesPerSplit);
-    tb = sp.first + slot * C;
-    te = min(tb + C, sp.end);
-    if (tb >= sp.end) return;
-  } else {
-    // the first wavefront of slot 0, KV head 0, row block 0 also records every
-    // sequence's chunk slots for the combine
-    int32_t* table = (slot == 0 && hkv == 0 && rbi == 0 && wave == 0) ? a.ws_chunks : nullptr;
-    const Chunk ch = find_chunk(a.seq_lens, a.B, a.max_seq_len, a.NW, a.Tq, a.window, slot, -1, lane,
-                                table);
-    if (ch.b < 0) return;
-    b = ch.b;
-    L = ch.L;
-    tb = ch.first;
-    te = ch.end;
-    load_q(b);
-  }
+  if (!workgroup_chunk(a, slot, slot == 0 && hkv == 0 && rbi == 0 && wave == 0, lane, load_q, b, L, tb,
+                       te))
+    return;
 
   // ---- fused append: the wavefront that will read the tile holding a new
   // position quantizes and stores that row (the same arithmetic as
@@ -718,42 +962,9 @@ split_decode_kernel(SplitArgs a) {
     any_mine |= mine[j];
     early_hit |= mine[j] && t < t0 + NB * kWaves;  // among the first NB tiles
   }
-  using RG = RowGeo<DT, D>;
-  uint16_t rk[kMaxQTokens][RG::EPL], rv[kMaxQTokens][RG::EPL];
-  int rblk[kMaxQTokens];
-  if (any_mine) {
-    // the rows first, so their latency overlaps the tile loads
-#pragma unroll
-    for (int j = 0; j < kMaxQTokens; ++j) {
-      if (!mine[j]) continue;
-      const int p = L - a.Tq + j;
-      const size_t xi = (((size_t)b * a.Tq + j) * a.c.Hkv + hkv) * D;
-      load_row<DT, D>(a.k_new + xi, lane, rk[j]);
-      load_row<DT, D>(a.v_new + xi, lane, rv[j]);
-      rblk[j] = a.c.block_table != nullptr
-                    ? a.c.block_table[(size_t)b * a.c.max_blocks + p / a.c.block_size]
-                    : b;
-    }
-  }
-  auto append_rows = [&]() {
-#pragma unroll
-    for (int j = 0; j < kMaxQTokens; ++j) {
-      if (!mine[j] || (unsigned)rblk[j] >= (unsigned)a.c.num_blocks) continue;
-      const int p = L - a.Tq + j;
-      const size_t ri =
-          ((size_t)rblk[j] * a.c.Hkv + hkv) * a.c.block_size + (size_t)(p % a.c.block_size);
-      quantize_store_row<DT, MODE, D>(rk[j], lane, a.c.k_codes + ri * RG::ROWB, a.c.k_scales + ri,
-                                      MODE == kPerChannel ? a.c.k_scales + (size_t)hkv * D : a.c.k_scales);
-      if constexpr (kVRow)  // V per row: known at compile time
-        quantize_store_row<DT, kPerRow, D>(rv[j], lane, a.c.v_codes + ri * RG::ROWB, a.c.v_scales + ri,
-                                           a.c.v_scales);
-      else
-        quantize_store_row_mode<DT, D>(a.vmode, rv[j], lane, a.c.v_codes + ri * RG::ROWB,
-                                       a.c.v_scales + ri,
-                                       a.vmode == kPerChannel ? a.c.v_scales + (size_t)hkv * D : a.c.v_scales);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // stores acknowledged before any load of those rows
-  };
+  NewRows<DT, MODE, D> nr;
+  if (any_mine) nr.load(a, mine, b, hkv, L, lane);  // first, so their latency overlaps the tile loads
+  auto append_rows = [&]() { nr.store(a, mine, hkv, L, lane); };
 
   // ---- start the loads of the wavefront's first NB tiles now so their
   // latency overlaps the query prologue (and the append).  Every load is
@@ -790,114 +1001,11 @@ split_decode_kernel(SplitArgs a) {
   float rowmul[RB];  // logit (log2 units) = dot * rowmul * per-row K scale
   int lim[RB];       // tokens visible to this lane's row n: lo <= t < lim
   int lo[RB];
-  {
-    const float* kst = a.c.k_scales;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int r = rb * 16 + n;
-      lim[rb] = (r < Rw) ? (L - a.Tq + (row0 + r) / a.G + 1) : 0;
-      if (lim[rb] > L) lim[rb] = L;
-      lo[rb] = a.window > 0 ? lim[rb] - a.window : 0;
-      if (lim[rb] < lo[rb]) lim[rb] = lo[rb];  // a query before the first token sees none
-      if constexpr (DT == kBf16) {
-        // the q rows as they are: bf16 products are exact in the fp32 accumulation
-#pragma unroll
-        for (int ks = 0; ks < G_::KSTEPS; ++ks)
-          qb[rb][ks] = __builtin_bit_cast(
-              half8_t, *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + k_channel<DT, D>(ks, g, 0)));
-        rowmul[rb] = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
-        continue;
-      }
-      if constexpr (G_::IQK) {
-        // The row as a fixed-point integer vector in NSL int8 slices (see
-        // q_slices): 15 bits of the row's largest element, 23 with a
-        // per-channel K scale folded in.
-        constexpr int NSL = kQSlices<DT, MODE>;
-        float qv[G_::ISTEPS][16];
-        float amax = 0.0f;
-#pragma unroll
-        for (int st = 0; st < G_::ISTEPS; ++st) {
-          const int base = k_channel_i8<DT, D>(st, g, 0);
-          const u32x4_t r0 = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base);
-          const u32x4_t r1 = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base + 8);
-          float x16[16];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x16[2 * i] = __uint_as_float(r0[i] << 16);
-            x16[2 * i + 1] = __uint_as_float(r0[i] & 0xFFFF0000u);
-            x16[8 + 2 * i] = __uint_as_float(r1[i] << 16);
-            x16[8 + 2 * i + 1] = __uint_as_float(r1[i] & 0xFFFF0000u);
-          }
-#pragma unroll
-          for (int p = 0; p < 16; ++p) {
-            const int off = k_offset_i8<DT>(p);  // 0..15
-            float x = x16[off];
-            if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
-            qv[st][p] = x;
-            amax = fmaxf(amax, fabsf(x));
-          }
-        }
-        amax = group_max4(amax);
-        int ex = 0;
-        if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
-#pragma unroll
-        for (int st = 0; st < G_::ISTEPS; ++st) {
-          u32x4_t w[NSL];
-#pragma unroll
-          for (int k = 0; k < NSL; ++k) w[k] = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int p = 0; p < 16; ++p) {
-            int sl[NSL];
-            q_slices<NSL>(qv[st][p], ex, sl);
-#pragma unroll
-            for (int k = 0; k < NSL; ++k) w[k][p / 4] |= ((uint32_t)sl[k] & 0xFFu) << (8 * (p % 4));
-          }
-#pragma unroll
-          for (int k = 0; k < NSL; ++k) qb[rb][NSL * st + k] = __builtin_bit_cast(half8_t, w[k]);
-        }
-        float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
-        if constexpr (MODE == kPerTensor) mul *= kst[0];
-        if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
-        rowmul[rb] = ldexpf(mul, ex - (8 * NSL - 2));
-        continue;
-      }
-      float qv[G_::KSTEPS][8];
-      float amax = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < G_::KSTEPS; ++ks) {
-        // the 8 channels of a k-step are 8 consecutive channels (permuted for int4)
-        const int base = k_channel<DT, D>(ks, g, 0);
-        u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base);
-        float x8[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x8[2 * i] = __uint_as_float(raw[i] << 16);
-          x8[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int off = k_channel<DT, D>(ks, g, e) - base;  // 0..7
-          float x = x8[off];
-          if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
-          qv[ks][e] = x;
-          amax = fmaxf(amax, fabsf(x));
-        }
-      }
-      amax = group_max4(amax);
-      int ex = 0;
-      if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
-#pragma unroll
-      for (int ks = 0; ks < G_::KSTEPS; ++ks) {
-        half8_t h;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (_Float16)ldexpf(qv[ks][e], -ex);
-        qb[rb][ks] = h;
-      }
-      float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
-      if constexpr (MODE == kPerTensor) mul *= kst[0];
-      if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
-      rowmul[rb] = ldexpf(mul, ex);
-    }
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = rb * 16 + n;
+    row_window(a, L, row0 + r, r < Rw, lim[rb], lo[rb]);
+    rowmul[rb] = fold_q_row<DT, MODE, D>(a, qs, r, g, hkv, qb[rb]);
   }
   // With QLDS the operand goes to this wavefront's own LDS copy (lane-linear),
   // which only its own lanes read back: no barrier needed.
