@@ -326,6 +326,9 @@ def time_prefill(kvq, torch, ki, dtype: str, past: int, chunk: int, layers: int,
     lens = torch.from_numpy(w.lens).to(dev)
     msl = past + chunk
     out = torch.empty_like(q)
+    # the context-split workspace of kvq_prefill_attend_ws (0 bytes: unsplit)
+    need = kvq.prefill_workspace_bytes(caches[0], 1, w.Hq, chunk, msl)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     res = {}
@@ -333,7 +336,7 @@ def time_prefill(kvq, torch, ki, dtype: str, past: int, chunk: int, layers: int,
         for name, fused in (("step", True), ("attend", False)):
             def run(c):
                 kvq.prefill_attend(c, q, lens, msl, w.sm_scale, k_new=kn if fused else None,
-                                   v_new=vn if fused else None, out=out, stream=stream)
+                                   v_new=vn if fused else None, out=out, workspace=ws, stream=stream)
             for c in caches:
                 run(c)
             g = torch.cuda.CUDAGraph()
@@ -354,7 +357,8 @@ def time_prefill(kvq, torch, ki, dtype: str, past: int, chunk: int, layers: int,
     del caches
     torch.cuda.empty_cache()
     fl = prefill_flops(w)
-    return dict(dtype=dtype, past=past, chunk=chunk, step_ms=res["step"], attend_ms=res["attend"],
+    return dict(dtype=dtype, past=past, chunk=chunk, workspace_bytes=need,
+                step_ms=res["step"], attend_ms=res["attend"],
                 flops=fl, attend_TFLOPs=fl / (res["attend"] * 1e-3) / 1e12,
                 step_TFLOPs=fl / (res["step"] * 1e-3) / 1e12)
 
@@ -433,6 +437,9 @@ def main():
                     help="time the int8 step against the same step over an unquantized bf16 "
                          "cache (this library's kernel) and torch bf16 SDPA, over the context "
                          "sweep, and write JSON lines to this file")
+    ap.add_argument("--prefill-cases", default="",
+                    help="with --prefill: comma-separated dtype:past:chunk cases "
+                         "(default: int8/int4/fp8/bf16 x 0+2048, 16384+2048, 32768+1024, 4096+512)")
     ap.add_argument("--prefill", default="",
                     help="time chunked prefill (workload-3 geometry, int8 / int4 / bf16 "
                          "caches, several past lengths and chunk sizes) and write JSON lines to this "
@@ -484,16 +491,22 @@ def main():
         return
 
     if args.prefill:
+        cases = [(dt, past, chunk) for dt in ("int8", "int4", "fp8", "bf16")
+                 for past, chunk in ((0, 2048), (16384, 2048), (32768, 1024), (4096, 512))]
+        if args.prefill_cases:
+            cases = []
+            for item in args.prefill_cases.split(","):
+                dt, past, chunk = item.split(":")
+                cases.append((dt, int(past), int(chunk)))
         with open(args.prefill, "w") as f:
-            for dt in ("int8", "int4", "fp8", "bf16"):
-                for past, chunk in ((0, 2048), (16384, 2048), (32768, 1024), (4096, 512)):
-                    r = time_prefill(kvq, torch, ki, dt, past, chunk, 4, 8, dev)
-                    r["attend_frac_of_fp16_peak"] = r["attend_TFLOPs"] * 1e12 / PEAK_F16_FLOPS
-                    f.write(json.dumps(r) + "\n")
-                    f.flush()
-                    print(f"[prefill] {dt} past={past} chunk={chunk} step {r['step_ms']:.3f} ms "
-                          f"attend {r['attend_ms']:.3f} ms {r['attend_TFLOPs']:.0f} TFLOP/s",
-                          file=sys.stderr, flush=True)
+            for dt, past, chunk in cases:
+                r = time_prefill(kvq, torch, ki, dt, past, chunk, 4, 8, dev)
+                r["attend_frac_of_fp16_peak"] = r["attend_TFLOPs"] * 1e12 / PEAK_F16_FLOPS
+                f.write(json.dumps(r) + "\n")
+                f.flush()
+                print(f"[prefill] {dt} past={past} chunk={chunk} step {r['step_ms']:.3f} ms "
+                      f"attend {r['attend_ms']:.3f} ms {r['attend_TFLOPs']:.0f} TFLOP/s",
+                      file=sys.stderr, flush=True)
         return
 
     if args.copy_probe_mib:

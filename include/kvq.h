@@ -336,6 +336,38 @@ int kvq_prefill_attend(const kvq_cache* cache, const void* k_new, const void* v_
                        const kvq_attn_options* options, void* out, void* stream);
 
 /*
+ * kvq_prefill_workspace_bytes -- device workspace for kvq_prefill_attend_ws:
+ * when the prefill's workgroups (one per 64 or 128 query rows of a KV head)
+ * would leave part of the GPU idle in their last round, each one's cached
+ * tiles are cut into up to 8 consecutive parts of one workgroup each, whose
+ * partial outputs the workspace holds until a fixed-order merge ([K]
+ * "Method": the sequence is split across workgroups and the partials are
+ * merged in a fixed order).  A host-only, pure function of the shape
+ * (options: its sliding window, or NULL); 0 when no split pays, or for an
+ * invalid shape.  Holds batch * num_kv_heads * G * q_tokens * parts rows of
+ * head_dim + 2 floats.
+ */
+size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                                   int32_t q_tokens, int32_t max_seq_len,
+                                   const kvq_attn_options* options);
+
+/*
+ * kvq_prefill_attend_ws -- kvq_prefill_attend with that workspace: the same
+ * arguments and result (up to the rounding of the merge), with the split.
+ * workspace (device, 16-byte aligned) must hold kvq_prefill_workspace_bytes
+ * for the same shape and options (it may be NULL when that is 0), else
+ * KVQ_EINVAL before anything is enqueued; the caller owns it, and calls that
+ * overlap must not share it.  Up to three launches on `stream` (append,
+ * attention, merge); graph-capturable.
+ */
+int kvq_prefill_attend_ws(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                          int32_t batch, int32_t num_q_heads, int32_t q_tokens, const int32_t* seq_lens,
+                          int32_t max_seq_len, float softmax_scale, const float* head_sink,
+                          const int32_t* block_table, int32_t max_blocks,
+                          const kvq_attn_options* options, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * kvq_cache_bytes -- host-only footprint of one layer's cache: codes of K and
  * V plus, for KVQ_PER_ROW, one fp32 scale per row ([K] opening paragraphs
  * and "Cache footprint"; [F] "Motivation and Context": static per-channel

@@ -18,7 +18,7 @@ __all__ = [
     "INT8", "INT4", "FP8_E4M3FN", "BF16", "NO_SCALE", "PER_ROW", "PER_TENSOR", "PER_CHANNEL",
     "KVCache", "KvqError", "append", "num_splits", "workspace_bytes", "decode_attend",
     "paged_decode_attend", "append_decode_attend", "attend_ex", "attend_ex_noalloc", "prefill_attend",
-    "split_decode", "NOALLOC_SCRATCH_BYTES",
+    "split_decode", "NOALLOC_SCRATCH_BYTES", "prefill_workspace_bytes",
     "combine",
     "cache_bytes",
     "lib", "LIB_PATH",
@@ -33,7 +33,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 EXPORTS = (
     "kvq_append", "kvq_num_splits", "kvq_workspace_bytes", "kvq_decode_attend",
     "kvq_paged_decode_attend", "kvq_append_decode_attend", "kvq_attend_ex", "kvq_attend_ex_noalloc",
-    "kvq_prefill_attend",
+    "kvq_prefill_attend", "kvq_prefill_workspace_bytes", "kvq_prefill_attend_ws",
     "kvq_split_decode",
     "kvq_combine", "kvq_cache_bytes",
     "kvq_status_string",
@@ -94,6 +94,11 @@ def lib():
         L.kvq_prefill_attend.argtypes = [CP, P, P, P, I32, I32, I32, P, I32, F, P, P, I32,
                                          ctypes.POINTER(_Options), P, P]
         L.kvq_prefill_attend.restype = ctypes.c_int
+        L.kvq_prefill_workspace_bytes.argtypes = [CP, I32, I32, I32, I32, ctypes.POINTER(_Options)]
+        L.kvq_prefill_workspace_bytes.restype = SZ
+        L.kvq_prefill_attend_ws.argtypes = [CP, P, P, P, I32, I32, I32, P, I32, F, P, P, I32,
+                                            ctypes.POINTER(_Options), P, P, SZ, P]
+        L.kvq_prefill_attend_ws.restype = ctypes.c_int
         L.kvq_split_decode.argtypes = [CP, P, I32, I32, I32, P, I32, F, P, I32, P, SZ, P]
         L.kvq_split_decode.restype = ctypes.c_int
         L.kvq_combine.argtypes = [CP, I32, I32, I32, P, I32, P, P, P, SZ, P]
@@ -427,13 +432,25 @@ def attend_ex_noalloc(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, m
     return out
 
 
+def prefill_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, q_tokens: int,
+                            max_seq_len: int, window: int = 0) -> int:
+    """Workspace of the context-split prefill (0: this shape runs unsplit)."""
+    opts = _Options(0.0, int(window))
+    return lib().kvq_prefill_workspace_bytes(cache.struct, batch, num_q_heads, q_tokens, max_seq_len,
+                                             ctypes.byref(opts))
+
+
 def prefill_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                    softmax_scale: float, k_new: Optional[torch.Tensor] = None,
                    v_new: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
                    head_sink: Optional[torch.Tensor] = None, softcap: float = 0.0, window: int = 0,
-                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   split: bool = True, stream=None) -> torch.Tensor:
     """Chunked prefill: the Tq = q.shape[1] tokens of a chunk (k_new, v_new bf16
-    [B, Tq, Hkv, D], appended first unless None) attend causally to the cache."""
+    [B, Tq, Hkv, D], appended first unless None) attend causally to the cache.
+    With `split` (kvq_prefill_attend_ws) the workgroups' context may be cut into
+    parts merged through `workspace` (uint8, prefill_workspace_bytes; allocated
+    here when None and needed); without it, kvq_prefill_attend."""
     B, Tq, Hq = _query(cache, q)
     _common(cache, B, Tq, Hq, seq_lens, head_sink, k_new, v_new)
     mb = _table(block_table, B)
@@ -441,11 +458,27 @@ def prefill_attend(cache: KVCache, q: torch.Tensor, seq_lens: torch.Tensor, max_
     _on_gpu(cache, q=q, seq_lens=seq_lens, head_sink=head_sink, block_table=block_table,
             k_new=k_new, v_new=v_new, out=out)
     opts = _Options(float(softcap), int(window))
-    _check(lib().kvq_prefill_attend(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, Tq,
-                                    _ptr(seq_lens), max_seq_len, float(softmax_scale),
-                                    _ptr(head_sink), _ptr(block_table), mb, ctypes.byref(opts),
-                                    _ptr(out), _stream(stream)),
-           "kvq_prefill_attend")
+    if not split:
+        _check(lib().kvq_prefill_attend(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, Tq,
+                                        _ptr(seq_lens), max_seq_len, float(softmax_scale),
+                                        _ptr(head_sink), _ptr(block_table), mb, ctypes.byref(opts),
+                                        _ptr(out), _stream(stream)),
+               "kvq_prefill_attend")
+        return out
+    need = prefill_workspace_bytes(cache, B, Hq, Tq, max_seq_len, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _want(workspace, torch.uint8, "workspace")
+        if workspace.numel() < need:
+            raise KvqError(f"prefill workspace holds {workspace.numel()} bytes, needs {need}")
+        _on_gpu(cache, workspace=workspace)
+    _check(lib().kvq_prefill_attend_ws(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, Tq,
+                                       _ptr(seq_lens), max_seq_len, float(softmax_scale),
+                                       _ptr(head_sink), _ptr(block_table), mb, ctypes.byref(opts),
+                                       _ptr(out), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)),
+           "kvq_prefill_attend_ws")
     return out
 
 

@@ -1,5 +1,6 @@
 // kvq_combine.hip -- fixed-order merge of the split partials, static V scale,
-// head sink, bf16 output.
+// head sink, bf16 output: the decode's chunks and a split prefill's context
+// parts.
 //
 // Kernel page "kv-quant-attn", "Method": the sequence is split across
 // workgroups and the partials are merged in a fixed order, so repeated decodes
@@ -163,6 +164,65 @@ hipError_t launch_mode(int D, const CombineArgs& a, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+
+// Merge of a split prefill's KS context parts, one thread per (sequence, KV
+// head, query row, 4 channels): with part p holding (m_p in log2 units, l_p,
+// o_p normalized), M = max_p m_p, w_p = l_p 2^(m_p - M), L = sum_p w_p and
+// o = sum_p w_p o_p / L in part order; then the head sink and the static V
+// scale as in the decode combine, bf16 out.
+template <int MODE, int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillCombineArgs a) {
+  constexpr int Q = D / 4;  // channel quads per row
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)a.R * Q) return;
+  const int r = (int)(i / Q), d = 4 * (int)(i % Q);
+  const int head = blockIdx.y;  // b * Hkv + hkv
+  const int b = head / a.Hkv, hkv = head % a.Hkv;
+  const size_t row = (size_t)head * a.R + r;
+  const float* ml = a.ws_ml + row * a.KS * 2;
+  float M = -INFINITY;
+  for (int p = 0; p < a.KS; ++p) M = fmaxf(M, ml[2 * p]);
+  float Lsum = 0.0f;
+  float4_t o = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < a.KS; ++p) {
+    const float l = ml[2 * p + 1];
+    const float w = (M == -INFINITY || l == 0.0f) ? 0.0f : l * exp2f(ml[2 * p] - M);
+    Lsum += w;
+    o += w * *reinterpret_cast<const float4_t*>(a.ws_o + (row * a.KS + p) * D + d);
+  }
+  float f = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+  const int jq = r / a.G, gh = r % a.G;
+  const int h = hkv * a.G + gh;
+  if (a.sink != nullptr && Lsum > 0.0f) {
+    const float lse = 0.6931471805599453f * (M + log2f(Lsum));
+    f *= 1.0f / (1.0f + expf(a.sink[h] - lse));
+  }
+  uint16_t ob[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float x = o[e] * f;
+    if constexpr (MODE == kPerTensor) x *= a.v_static[0];
+    if constexpr (MODE == kPerChannel) x *= a.v_static[(size_t)hkv * D + d + e];
+    ob[e] = f32_to_bf16(x);
+  }
+  u32x2_t packed = {(uint32_t)ob[0] | ((uint32_t)ob[1] << 16), (uint32_t)ob[2] | ((uint32_t)ob[3] << 16)};
+  *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.Tq + jq) * a.Hq + h) * D + d) = packed;
+}
+
+template <int MODE>
+hipError_t launch_prefill_mode(int D, const PrefillCombineArgs& a, int B, hipStream_t st) {
+  if (a.KS < 2 || a.R < 1) return hipErrorInvalidValue;
+  const long n = (long)a.R * (D / 4);
+  dim3 grid((unsigned)((n + 255) / 256), (unsigned)(B * a.Hkv), 1);
+  switch (D) {
+    case 64: hipLaunchKernelGGL((prefill_combine_kernel<MODE, 64>), grid, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((prefill_combine_kernel<MODE, 128>), grid, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((prefill_combine_kernel<MODE, 256>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(int mode, int D, const CombineArgs& a, int B, hipStream_t st) {
@@ -172,6 +232,16 @@ hipError_t launch_combine(int mode, int D, const CombineArgs& a, int B, hipStrea
     case kPerRow: return launch_mode<kPerRow>(D, a, grid, st);
     case kPerTensor: return launch_mode<kPerTensor>(D, a, grid, st);
     case kPerChannel: return launch_mode<kPerChannel>(D, a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prefill_combine(int mode, int D, const PrefillCombineArgs& a, int B, hipStream_t st) {
+  switch (mode) {
+    case kNoScale:  // unquantized cache: nothing to apply
+    case kPerRow: return launch_prefill_mode<kPerRow>(D, a, B, st);
+    case kPerTensor: return launch_prefill_mode<kPerTensor>(D, a, B, st);
+    case kPerChannel: return launch_prefill_mode<kPerChannel>(D, a, B, st);
     default: return hipErrorInvalidValue;
   }
 }

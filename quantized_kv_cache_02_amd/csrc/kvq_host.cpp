@@ -205,6 +205,75 @@ hipError_t dispatch_split(int dt, int md, bool vrow, int D, int RB, const kvq::S
   return hipErrorInvalidValue;
 }
 
+// Chunked prefill: workgroup size W and context split KS.  A workgroup owns
+// 16 * W query rows (32 * W below D = 256) of one KV head and walks the
+// 64-token tiles they see; workgroups run one per CU.  An 8-wavefront
+// workgroup (D = 256 only) gets through 128 rows in 1 / 0.8 of the time a
+// 4-wavefront one takes for 64 (measured on MI355X at 32K + 1K tokens: 1.66x
+// the row rate for int4, 1.63x for bf16).  When the workgroups do not fill
+// whole rounds of 256 CUs (384 for 2K query tokens at 24 / 4 heads: a second
+// round half empty), the tiles of each are cut into KS parts, one workgroup
+// each, and a combine merges the parts.  Cost model per (W, KS): rounds of
+// one workgroup per CU times (tiles per part + 4 tiles of per-workgroup
+// overhead), times 0.8 for W = 4; KS only where the workspace is given, each
+// part keeping at least 8 tiles; a larger KS must beat a smaller one by 3 %
+// per step.  A pure function of the shape, so workspaces sized once stay
+// valid.
+struct PrefillPlan {
+  int W, KS;
+};
+
+PrefillPlan prefill_plan(const kvq_cache* c, int32_t batch, int G, int32_t tq, int32_t max_seq_len,
+                         int32_t window, bool split) {
+  const int D = c->head_dim;
+  const int64_t R = (int64_t)G * tq;
+  int64_t tiles = ((int64_t)max_seq_len + 63) / 64;  // a workgroup sees at most these
+  PrefillPlan best{4, 1};
+  double best_cost = 0.0;
+  bool first = true;
+  for (int W : {4, 8}) {
+    if (W == 8 && D != 256) continue;
+    const int64_t rows = 16 * (D >= 256 ? 1 : 2) * W;
+    int64_t t = tiles;
+    if (window > 0) t = std::min<int64_t>(t, ((int64_t)window + rows / G + 63) / 64 + 1);
+    for (int ks = 1; ks <= (split ? kvq::kPrefillMaxParts : 1); ++ks) {
+      if (ks > 1 && t < (int64_t)ks * 8) break;
+      const int64_t items = (R + rows - 1) / rows * c->num_kv_heads * batch * ks;
+      const int64_t rounds = (items + kvq::kNumCUs - 1) / kvq::kNumCUs;
+      double cost = (double)rounds * ((double)t / ks + 4.0) * (W == 4 ? 0.8 : 1.0);
+      cost *= 1.0 + 0.03 * (ks - 1);
+      if (first || cost < best_cost) {
+        best = PrefillPlan{W, ks};
+        best_cost = cost;
+        first = false;
+      }
+    }
+  }
+  return best;
+}
+
+size_t prefill_workspace_size(const kvq_cache* c, int32_t batch, int32_t R, int KS) {
+  if (KS <= 1) return 0;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)batch * c->num_kv_heads * R * KS;
+  return up(rows * c->head_dim * 4) + up(rows * 2 * 4);
+}
+
+// Shape checks shared by the prefill entry points.
+int prefill_check(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int32_t q_tokens,
+                  int32_t max_seq_len, int* G) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (batch < 1 || num_q_heads < 1 || q_tokens < 1 || max_seq_len < 1) return KVQ_EINVAL;
+  if (num_q_heads % cache->num_kv_heads != 0) return KVQ_EINVAL;
+  *G = num_q_heads / cache->num_kv_heads;
+  if (*G > kMaxGroup) return KVQ_EUNSUPPORTED;
+  if (batch > 65535 || cache->num_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+  if ((int64_t)*G * q_tokens > INT32_MAX / 2) return KVQ_EUNSUPPORTED;
+  return KVQ_OK;
+}
+
+
 hipError_t dispatch_prefill(int dt, int md, bool vrow, int D, const kvq::PrefillArgs& a, int B,
                             hipStream_t st) {
 #define KVQ_CASE(DT, MD)                                                                        \
@@ -223,6 +292,98 @@ hipError_t dispatch_prefill(int dt, int md, bool vrow, int D, const kvq::Prefill
 #undef KVQ_CASE
   if (dt == KVQ_BF16 && md == KVQ_NO_SCALE && !vrow) return kvq::launch_prefill_4_0_0(D, a, B, st);
   return hipErrorInvalidValue;
+}
+
+int prefill_impl(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                 int32_t batch, int32_t num_q_heads, int32_t q_tokens, const int32_t* seq_lens,
+                 int32_t max_seq_len, float softmax_scale, const float* head_sink,
+                 const int32_t* block_table, int32_t max_blocks, const kvq_attn_options* options,
+                 void* out, void* workspace, size_t workspace_bytes, bool split, void* stream) {
+  int G = 0;
+  int st = prefill_check(cache, batch, num_q_heads, q_tokens, max_seq_len, &G);
+  if (st != KVQ_OK) return st;
+  st = check_layout(cache, batch, max_seq_len, block_table, max_blocks);
+  if (st != KVQ_OK) return st;
+  if (q == nullptr || seq_lens == nullptr || out == nullptr || !aligned16(q) || !aligned16(out))
+    return KVQ_EINVAL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return KVQ_EINVAL;
+  if (k_new != nullptr && (!aligned16(k_new) || !aligned16(v_new))) return KVQ_EINVAL;
+  if (options != nullptr) {
+    const float cap = options->softcap;
+    if (!(cap >= 0.0f) || cap > 3.0e38f || options->window < 0) return KVQ_EINVAL;
+  }
+  const int32_t window = options ? options->window : 0;
+  const PrefillPlan plan = prefill_plan(cache, batch, G, q_tokens, max_seq_len, window, split);
+  const size_t need = prefill_workspace_size(cache, batch, G * q_tokens, plan.KS);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return KVQ_EINVAL;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (k_new != nullptr) {
+    // the chunk's rows first, at positions seq_lens[b] - q_tokens + j
+    kvq::AppendArgs ap;
+    ap.c = cache_args(cache, block_table, max_blocks);
+    ap.k = static_cast<const uint16_t*>(k_new);
+    ap.v = static_cast<const uint16_t*>(v_new);
+    ap.positions = nullptr;
+    ap.seq_lens = seq_lens;
+    ap.max_len = max_seq_len;
+    ap.B = batch;
+    ap.Tn = q_tokens;
+    const int64_t capacity =
+        block_table == nullptr ? cache->block_size : (int64_t)max_blocks * cache->block_size;
+    if (capacity > INT32_MAX) return KVQ_EUNSUPPORTED;
+    ap.capacity = (int32_t)capacity;
+    ap.kmode = cache->scale_mode;
+    ap.vmode = v_mode_of(cache);
+    hipError_t e = kvq::launch_append(cache->dtype, ap.kmode, ap.vmode, cache->head_dim, ap, hs);
+    if (e != hipSuccess) return KVQ_EHIP;
+  }
+  kvq::PrefillArgs a;
+  a.c = cache_args(cache, block_table, max_blocks);
+  a.q = static_cast<const uint16_t*>(q);
+  a.seq_lens = seq_lens;
+  a.Hq = num_q_heads;
+  a.Tq = q_tokens;
+  a.G = G;
+  a.R = G * q_tokens;
+  a.max_seq_len = max_seq_len;
+  a.sm_scale = softmax_scale;
+  a.vmode = v_mode_of(cache);
+  a.softcap = options ? options->softcap : 0.0f;
+  a.window = window;
+  a.v_static = (a.vmode == KVQ_PER_TENSOR || a.vmode == KVQ_PER_CHANNEL) ? cache->v_scales : nullptr;
+  a.sink = head_sink;
+  a.out = static_cast<uint16_t*>(out);
+  a.W = plan.W;
+  a.KS = plan.KS;
+  a.ws_o = nullptr;
+  a.ws_ml = nullptr;
+  if (plan.KS > 1) {
+    const size_t rows = (size_t)batch * cache->num_kv_heads * a.R * plan.KS;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       ((rows * cache->head_dim * 4 + 255) & ~(size_t)255));
+  }
+  hipError_t e = dispatch_prefill(cache->dtype, cache->scale_mode, a.vmode == KVQ_PER_ROW,
+                                  cache->head_dim, a, batch, hs);
+  if (e != hipSuccess) return KVQ_EHIP;
+  if (plan.KS > 1) {
+    kvq::PrefillCombineArgs cb;
+    cb.ws_o = a.ws_o;
+    cb.ws_ml = a.ws_ml;
+    cb.v_static = a.v_static;
+    cb.sink = head_sink;
+    cb.out = a.out;
+    cb.Hkv = cache->num_kv_heads;
+    cb.Hq = num_q_heads;
+    cb.Tq = q_tokens;
+    cb.G = G;
+    cb.R = a.R;
+    cb.KS = plan.KS;
+    e = kvq::launch_prefill_combine(a.vmode, cache->head_dim, cb, batch, hs);
+    if (e != hipSuccess) return KVQ_EHIP;
+  }
+  return KVQ_OK;
 }
 
 int split_impl(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, int32_t tq,
@@ -491,64 +652,29 @@ int kvq_prefill_attend(const kvq_cache* cache, const void* k_new, const void* v_
                        int32_t max_seq_len, float softmax_scale, const float* head_sink,
                        const int32_t* block_table, int32_t max_blocks,
                        const kvq_attn_options* options, void* out, void* stream) {
-  int st = check_cache(cache);
-  if (st != KVQ_OK) return st;
-  if (batch < 1 || num_q_heads < 1 || q_tokens < 1 || max_seq_len < 1) return KVQ_EINVAL;
-  if (num_q_heads % cache->num_kv_heads != 0) return KVQ_EINVAL;
-  const int G = num_q_heads / cache->num_kv_heads;
-  if (G > kMaxGroup) return KVQ_EUNSUPPORTED;
-  if (batch > 65535 || cache->num_kv_heads > 65535) return KVQ_EUNSUPPORTED;
-  if ((int64_t)G * q_tokens > INT32_MAX / 2) return KVQ_EUNSUPPORTED;
-  st = check_layout(cache, batch, max_seq_len, block_table, max_blocks);
-  if (st != KVQ_OK) return st;
-  if (q == nullptr || seq_lens == nullptr || out == nullptr || !aligned16(q) || !aligned16(out))
-    return KVQ_EINVAL;
-  if ((k_new == nullptr) != (v_new == nullptr)) return KVQ_EINVAL;
-  if (k_new != nullptr && (!aligned16(k_new) || !aligned16(v_new))) return KVQ_EINVAL;
-  if (options != nullptr) {
-    const float cap = options->softcap;
-    if (!(cap >= 0.0f) || cap > 3.0e38f || options->window < 0) return KVQ_EINVAL;
-  }
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (k_new != nullptr) {
-    // the chunk's rows first, at positions seq_lens[b] - q_tokens + j
-    kvq::AppendArgs ap;
-    ap.c = cache_args(cache, block_table, max_blocks);
-    ap.k = static_cast<const uint16_t*>(k_new);
-    ap.v = static_cast<const uint16_t*>(v_new);
-    ap.positions = nullptr;
-    ap.seq_lens = seq_lens;
-    ap.max_len = max_seq_len;
-    ap.B = batch;
-    ap.Tn = q_tokens;
-    const int64_t capacity =
-        block_table == nullptr ? cache->block_size : (int64_t)max_blocks * cache->block_size;
-    if (capacity > INT32_MAX) return KVQ_EUNSUPPORTED;
-    ap.capacity = (int32_t)capacity;
-    ap.kmode = cache->scale_mode;
-    ap.vmode = v_mode_of(cache);
-    hipError_t e = kvq::launch_append(cache->dtype, ap.kmode, ap.vmode, cache->head_dim, ap, hs);
-    if (e != hipSuccess) return KVQ_EHIP;
-  }
-  kvq::PrefillArgs a;
-  a.c = cache_args(cache, block_table, max_blocks);
-  a.q = static_cast<const uint16_t*>(q);
-  a.seq_lens = seq_lens;
-  a.Hq = num_q_heads;
-  a.Tq = q_tokens;
-  a.G = G;
-  a.R = G * q_tokens;
-  a.max_seq_len = max_seq_len;
-  a.sm_scale = softmax_scale;
-  a.vmode = v_mode_of(cache);
-  a.softcap = options ? options->softcap : 0.0f;
-  a.window = options ? options->window : 0;
-  a.v_static = (a.vmode == KVQ_PER_TENSOR || a.vmode == KVQ_PER_CHANNEL) ? cache->v_scales : nullptr;
-  a.sink = head_sink;
-  a.out = static_cast<uint16_t*>(out);
-  hipError_t e = dispatch_prefill(cache->dtype, cache->scale_mode, a.vmode == KVQ_PER_ROW,
-                                  cache->head_dim, a, batch, hs);
-  return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+  return prefill_impl(cache, k_new, v_new, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len,
+                      softmax_scale, head_sink, block_table, max_blocks, options, out, nullptr, 0, false,
+                      stream);
+}
+
+size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                                   int32_t q_tokens, int32_t max_seq_len, const kvq_attn_options* options) {
+  int G = 0;
+  if (prefill_check(cache, batch, num_q_heads, q_tokens, max_seq_len, &G) != KVQ_OK) return 0;
+  const int32_t window = options ? options->window : 0;
+  const PrefillPlan plan = prefill_plan(cache, batch, G, q_tokens, max_seq_len, window, true);
+  return prefill_workspace_size(cache, batch, G * q_tokens, plan.KS);
+}
+
+int kvq_prefill_attend_ws(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                          int32_t batch, int32_t num_q_heads, int32_t q_tokens, const int32_t* seq_lens,
+                          int32_t max_seq_len, float softmax_scale, const float* head_sink,
+                          const int32_t* block_table, int32_t max_blocks,
+                          const kvq_attn_options* options, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return prefill_impl(cache, k_new, v_new, q, batch, num_q_heads, q_tokens, seq_lens, max_seq_len,
+                      softmax_scale, head_sink, block_table, max_blocks, options, out, workspace,
+                      workspace_bytes, true, stream);
 }
 
 size_t kvq_cache_bytes(int32_t dtype, int32_t scale_mode, int32_t num_kv_heads, int32_t head_dim,

@@ -28,6 +28,8 @@ constexpr int kMaxTilesPerSplit = kWaves * 64 * kTableRegs;
 constexpr int kMaxQTokens = 8;
 // Smallest chunk of the balanced split schedule, in tiles.
 constexpr int kMinTilesPerSplit = 8;
+// Most context parts a prefill workgroup's tiles are cut into.
+constexpr int kPrefillMaxParts = 8;
 
 // Decode-kernel register budget: two wavefronts per SIMD (<= 256 registers
 // per lane).  The kernel is built for row-block counts RB (16 query rows each)
@@ -121,6 +123,23 @@ struct PrefillArgs {
   const float* v_static;  // per-tensor [1] / per-channel [Hkv, D] / nullptr
   const float* sink;      // [Hq] or nullptr
   uint16_t* out;          // bf16 [B, Tq, Hq, D]
+  int32_t W;              // wavefronts per workgroup (4, or 8 at D = 256)
+  // Context split: each workgroup's visible tiles are cut into KS parts, one
+  // workgroup each; with KS > 1 the parts write their normalized partial
+  // outputs and (m, l) to the workspace and a combine merges them.
+  int32_t KS;
+  float* ws_o;   // [B, Hkv, R, KS, D]
+  float* ws_ml;  // [B, Hkv, R, KS, 2]: max logit (log2 units), normalizer
+};
+
+// The merge of a split prefill's parts (kvq_combine.hip).
+struct PrefillCombineArgs {
+  const float* ws_o;
+  const float* ws_ml;
+  const float* v_static;  // per-tensor [1] / per-channel [Hkv, D] / nullptr (per-row)
+  const float* sink;      // [Hq] or nullptr
+  uint16_t* out;          // bf16 [B, Tq, Hq, D]
+  int32_t Hkv, Hq, Tq, G, R, KS;
 };
 
 hipError_t launch_append(int dtype, int kmode, int vmode, int D, const AppendArgs& a,
@@ -128,6 +147,7 @@ hipError_t launch_append(int dtype, int kmode, int vmode, int D, const AppendArg
 hipError_t launch_split(int dtype, int mode, int D, int RB, const SplitArgs& a, int B,
                         hipStream_t st);
 hipError_t launch_combine(int mode, int D, const CombineArgs& a, int B, hipStream_t st);
+hipError_t launch_prefill_combine(int mode, int D, const PrefillCombineArgs& a, int B, hipStream_t st);
 
 // translation units of the split kernel per (dtype, K scale mode, V scale per
 // row or static): launch_split_<dtype>_<K mode>_<V per row>

@@ -21,8 +21,9 @@
 // one is used (one barrier per tile), and every wavefront runs
 //   S^T = K . Q^T   v_mfma_f32_16x16x32_f16 (A: K rows from LDS, B: its q rows),
 //   online softmax over the tile's 64 tokens per row,
-//   O  += P . V     v_mfma_f32_16x16x16_f16 (A: the weights where S^T left
-//                   them, B: 4 tokens of one channel read from the transposed V).
+//   O  += P . V     v_mfma_f32_16x16x32_f16 over two 16-token sub-tiles (A: the
+//                   weights where S^T left them, B: the same 8 tokens of one
+//                   channel read from the transposed V).
 // Scales enter as in the decode kernel: a per-row K scale multiplies the
 // logit, a per-row V scale the weight (over a power-of-two reference),
 // per-channel K is folded into q, static V scales are applied at the output.
@@ -295,7 +296,8 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
   const int lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
   const int hkv = blockIdx.y, b = blockIdx.z;
-  const int rbase = blockIdx.x * kRows;        // first row of the workgroup
+  const int part = blockIdx.x % a.KS;          // context part (KS > 1: split launch)
+  const int rbase = blockIdx.x / a.KS * kRows;  // first row of the workgroup
   const int rwave = rbase + 16 * RBW * wave;   // first row of this wavefront
   const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
   const int pos0 = L - a.Tq;                   // position of query token 0
@@ -439,13 +441,20 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
   // tiles any row of the workgroup can see
   const int rlast = min(rbase + kRows, a.R) - 1;
   const int pos_hi = min(pos0 + rlast / a.G, L - 1);
-  const int kt_end = pos_hi >= 0 ? pos_hi / kPT + 1 : 0;
+  int kt_end = pos_hi >= 0 ? pos_hi / kPT + 1 : 0;
   int kt_begin = 0;
   if (a.window > 0) {
     const int first = pos0 + rbase / a.G - a.window + 1;
     kt_begin = first > 0 ? first / kPT : 0;
   }
   if (kt_begin > kt_end) kt_begin = kt_end;
+  if (a.KS > 1) {
+    // this workgroup's part: consecutive tiles, as even as whole tiles allow
+    const int nt = kt_end - kt_begin;
+    const int C = (nt + a.KS - 1) / a.KS;
+    kt_begin = min(kt_begin + part * C, kt_end);
+    kt_end = min(kt_begin + C, kt_end);
+  }
 
   const float cap2 = CAP ? a.softcap * 1.4426950408889634f : 0.0f;
   const float icap2 = CAP ? 2.0f / a.softcap : 0.0f;
@@ -653,64 +662,78 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
       }
     }
 
-    // ---- O += P . V per sub-tile
+    // ---- O += P . V, two sub-tiles (32 tokens) per 16x16x32 MFMA: lane group
+    // g's A operand holds tokens 16s + 4g + 0..3 then 16s + 16 + 4g + 0..3 of its
+    // row, and the B operand the same tokens of its channel (two 8-byte reads
+    // of the transposed V)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      half4_t ph[RBW];
-      u32x2_t phi[RBW], plo[RBW];
+    for (int sp = 0; sp < 2; ++sp) {
+      half8_t ph[RBW];
+      half8_t phi[RBW], plo[RBW];
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) {
         const float msafe = m[rb] == -INFINITY ? 0.0f : m[rb];
-        float pf[4];
+        float pf[8];
         float psum = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(z[rb][s][e] - msafe);
-          psum += p;
-          if constexpr (kVRow)
-            pf[e] = p * vsn[s][e];
-          else
-            pf[e] = p;
-        }
-        l[rb] += psum;
-        if constexpr (DT == kBf16) {
-          uint16_t hh[4], ll[4];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
+            const int s = 2 * sp + h;
+            const float p = __builtin_amdgcn_exp2f(z[rb][s][e] - msafe);
+            psum += p;
+            if constexpr (kVRow)
+              pf[4 * h + e] = p * vsn[s][e];
+            else
+              pf[4 * h + e] = p;
+          }
+        l[rb] += psum;
+        if constexpr (DT == kBf16) {
+          uint16_t hh[8], ll[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
             hh[e] = f32_to_bf16(pf[e]);
             ll[e] = f32_to_bf16(pf[e] - bf16_to_f32(hh[e]));
           }
-          phi[rb] = u32x2_t{hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16)};
-          plo[rb] = u32x2_t{ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16)};
+          u32x4_t wh, wl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            wh[i] = hh[2 * i] | ((uint32_t)hh[2 * i + 1] << 16);
+            wl[i] = ll[2 * i] | ((uint32_t)ll[2 * i + 1] << 16);
+          }
+          phi[rb] = __builtin_bit_cast(half8_t, wh);
+          plo[rb] = __builtin_bit_cast(half8_t, wl);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ph[rb][e] = (_Float16)pf[e];
+          for (int e = 0; e < 8; ++e) ph[rb][e] = (_Float16)pf[e];
         }
       }
-      // the sub-tile's V operands in groups read ahead of their MFMAs, so their
+      // the pair's V operands in groups read ahead of their MFMAs, so their
       // LDS latencies overlap (all at once with 4 wavefronts; two halves with
       // 8, whose registers are shared by two wavefronts per SIMD)
-      const uint16_t* vcol = vt_lds + 16 * s + 4 * g;
+      const uint16_t* vcol = vt_lds + 32 * sp + 4 * g;
       constexpr int VG = W > 4 ? NCOL / 2 : NCOL;
 #pragma unroll
       for (int c0 = 0; c0 < NCOL; c0 += VG) {
-        u32x2_t vop[VG];
-#pragma unroll
-        for (int c = 0; c < VG; ++c)
-          vop[c] = *reinterpret_cast<const u32x2_t*>(vcol + (16 * (c0 + c) + n) * P::VST);
+        u32x4_t vop[VG];
 #pragma unroll
         for (int c = 0; c < VG; ++c) {
-          if constexpr (DT == kBf16) {
-            const u32x2_t vb = vop[c];
+          const uint16_t* src = vcol + (16 * (c0 + c) + n) * P::VST;
+          const u32x2_t a0 = *reinterpret_cast<const u32x2_t*>(src);
+          const u32x2_t a1 = *reinterpret_cast<const u32x2_t*>(src + 16);
+          vop[c] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+        }
 #pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) {
-              acc[rb][c0 + c] = mfma16_bf16(phi[rb], vb, acc[rb][c0 + c]);
-              acc[rb][c0 + c] = mfma16_bf16(plo[rb], vb, acc[rb][c0 + c]);
+        for (int c = 0; c < VG; ++c) {
+          const half8_t vb = __builtin_bit_cast(half8_t, vop[c]);
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+            if constexpr (DT == kBf16) {
+              acc[rb][c0 + c] = mfma32_bf16(phi[rb], vb, acc[rb][c0 + c]);
+              acc[rb][c0 + c] = mfma32_bf16(plo[rb], vb, acc[rb][c0 + c]);
+            } else {
+              acc[rb][c0 + c] = mfma32(ph[rb], vb, acc[rb][c0 + c]);
             }
-          } else {
-            const half4_t vb = __builtin_bit_cast(half4_t, vop[c]);
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) acc[rb][c0 + c] = mfma16(ph[rb], vb, acc[rb][c0 + c]);
           }
         }
       }
@@ -725,18 +748,26 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
   }
 
   // ---- epilogue: per row 1 / l (with the V reference and the int4 factor),
-  // the head sink, then the static V scale per channel, bf16 out
+  // the head sink, then the static V scale per channel, bf16 out; a split
+  // launch's part writes its normalized rows and (m, l) for the combine
+  // instead, which applies the sink and the static V scale
+  const bool split = a.KS > 1;
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     const float lt = group_sum4(l[rb]);
     if (g == 0) {
       const int r = rwave + 16 * rb + n;
       float f = 0.0f, sk = 1.0f;
+      if (split && r < a.R) {
+        float* ml = a.ws_ml + (((size_t)b * a.c.Hkv + hkv) * a.R + r) * a.KS * 2 + 2 * part;
+        ml[0] = lt > 0.0f ? m[rb] : -INFINITY;
+        ml[1] = lt;
+      }
       if (lt > 0.0f) {
         f = 1.0f / lt;
         if constexpr (kVRow) f *= vref;           // weights carried v_scale / vref
         if constexpr (DT == kInt4) f *= 0.0625f;  // V tile holds 16 * code
-        if (a.sink != nullptr && r < a.R) {
+        if (!split && a.sink != nullptr && r < a.R) {
           const int h = hkv * a.G + r % a.G;
           const float lse = 0.6931471805599453f * (m[rb] + log2f(lt));
           sk = 1.0f / (1.0f + expf(a.sink[h] - lse));
@@ -763,6 +794,11 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
     if (row >= a.R) continue;
     const float f = rowf[wave][rr] * rowsink[wave][rr];
     const float4_t v = *reinterpret_cast<const float4_t*>(ob + rr * (D + 4) + d);
+    if (split) {
+      *reinterpret_cast<float4_t*>(a.ws_o + ((((size_t)b * a.c.Hkv + hkv) * a.R + row) * a.KS + part) * D +
+                                   d) = v * f;
+      continue;
+    }
     uint16_t o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -779,8 +815,8 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 
 template <int DT, int MODE, int D, int W>
 hipError_t launch_w(const PrefillArgs& a, int B, hipStream_t st) {
-  const long nx = ((long)a.R + kPRows<D, W> - 1) / kPRows<D, W>;
-  if (nx > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  const long nx = ((long)a.R + kPRows<D, W> - 1) / kPRows<D, W> * a.KS;
+  if (nx > 0x7FFFFFFFL || a.KS < 1) return hipErrorInvalidValue;
   dim3 grid((unsigned)nx, a.c.Hkv, B);
   if (a.softcap > 0.0f)
     hipLaunchKernelGGL((prefill_kernel<DT, MODE, D, W, true>), grid, dim3(64 * W), 0, st, a);
@@ -789,21 +825,14 @@ hipError_t launch_w(const PrefillArgs& a, int B, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The host picks the workgroup size (prefill_plan in kvq_host.cpp): 8
+// wavefronts only at D = 256.
 template <int DT, int MODE, int D>
 hipError_t launch_d(const PrefillArgs& a, int B, hipStream_t st) {
   if constexpr (D == 256) {
-    // An 8-wavefront workgroup (128 rows) gets through its rows S times faster
-    // than a 4-wavefront one (measured on MI355X at 32K + 1K tokens: S = 1.66
-    // int4, 1.63 bf16; taken as 1.6 for every cache: with the 84-half V stride
-    // it put fp8 at 16K + 2K on 8 wavefronts, 282 -> 360 TFLOP/s).  Rows per
-    // CU in rounds of one workgroup per CU: 8 wavefronts when 2 r8 / S < r4.
-    const long nx8 = ((long)a.R + kPRows<D, 8> - 1) / kPRows<D, 8>;
-    const long nx4 = ((long)a.R + kPRows<D, 4> - 1) / kPRows<D, 4>;
-    const long r8 = (nx8 * a.c.Hkv * B + kNumCUs - 1) / kNumCUs;
-    const long r4 = (nx4 * a.c.Hkv * B + kNumCUs - 1) / kNumCUs;
-    constexpr long S100 = 160;
-    if (2 * r8 * 100 < r4 * S100) return launch_w<DT, MODE, D, 8>(a, B, st);
+    if (a.W == 8) return launch_w<DT, MODE, D, 8>(a, B, st);
   }
+  if (a.W != 4) return hipErrorInvalidValue;
   return launch_w<DT, MODE, D, 4>(a, B, st);
 }
 

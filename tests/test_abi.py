@@ -169,6 +169,56 @@ def test_invalid_prefill_rejected():
     assert call(opts=(0.0, -3)) == -1
 
 
+def _prefill_ws(c, batch=1, hq=24, tq=2048, msl=18432, window=0):
+    o = ctypes.byref(kvq._Options(0.0, window))
+    return kvq.lib().kvq_prefill_workspace_bytes(ctypes.byref(c), batch, hq, tq, msl, o)
+
+
+def _prefill_rows_bytes(rows, D):
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    return up(rows * D * 4) + up(rows * 8)
+
+
+def test_prefill_workspace_follows_the_round_model():
+    """The context split of kvq_prefill_attend_ws on the host: 24 / 4 heads at
+    D 256 and a 2,048-token chunk after 16,384 cached tokens make 384 workgroups
+    of 128 rows (one round of 256 CUs and a half-empty second); two parts each
+    fill exactly three rounds.  1,024 tokens after 32,768: 192 workgroups, four
+    parts (768, three full rounds).  A context of 8 tiles does not split (no
+    part would keep 8); an invalid shape reports 0."""
+    c = _cache(block_size=65536)
+    R = 6 * 2048
+    assert _prefill_ws(c) == _prefill_rows_bytes(4 * R * 2, 256)
+    assert _prefill_ws(c, tq=1024, msl=33792) == _prefill_rows_bytes(4 * 6 * 1024 * 4, 256)
+    # a one-token chunk: 4 workgroups, each split into the 8 parts allowed
+    assert _prefill_ws(c, tq=1, msl=4096) == _prefill_rows_bytes(4 * 6 * 8, 256)
+    assert _prefill_ws(c, tq=64, msl=512) == 0         # 8 tiles: no part would keep 8
+    assert _prefill_ws(c, hq=25) == 0                  # invalid shape
+    # a sliding window bounds the tiles a workgroup sees: 500 tokens -> no split
+    assert _prefill_ws(c, window=500) == 0
+    # every size is whole parts of the rows' (D + 2) floats
+    for tq, msl in ((512, 4096), (100, 3000), (2048, 18432), (7, 65536)):
+        n = _prefill_ws(c, tq=tq, msl=msl)
+        if n:
+            rows = 4 * 6 * tq
+            assert any(n == _prefill_rows_bytes(rows * ks, 256) for ks in range(2, 9)), (tq, msl, n)
+
+
+def test_prefill_ws_needs_its_workspace():
+    L = kvq.lib()
+    c = _cache(block_size=65536)
+    need = _prefill_ws(c)
+    assert need > 0
+
+    def call(ws, nbytes):
+        return L.kvq_prefill_attend_ws(ctypes.byref(c), FAKE, FAKE, FAKE, 1, 24, 2048, FAKE, 18432, 0.1,
+                                       None, None, 0, None, FAKE, ws, nbytes, None)
+
+    assert call(None, 0) == -1
+    assert call(FAKE, need - 1) == -1
+    assert call(ctypes.c_void_p(0x50008), need) == -1  # misaligned
+
+
 def test_invalid_stream_read_rejected():
     L = kprobe.lib()
     buf = ctypes.c_void_p(0x1000)  # never dereferenced: every call below is rejected first

@@ -36,9 +36,10 @@ def _gpu():
     kvq.lib()
 
 
-def _run_prefill(w: ki.Workload, dev="cuda"):
+def _run_prefill(w: ki.Workload, dev="cuda", split=True):
     """Append each sequence's rows before the chunk with kvq_append, then the
-    chunk (the last Tq rows) through kvq_prefill_attend.  Returns (out, cache)."""
+    chunk (the last Tq rows) through kvq_prefill_attend_ws (with `split`, the
+    default) or kvq_prefill_attend.  Returns (out, cache)."""
     cache = gu.gpu_cache(w)
     table = None if w.block_table is None else torch.from_numpy(w.block_table).to(dev)
     kn = torch.zeros(w.B, w.Tq, w.Hkv, w.D, dtype=torch.bfloat16)
@@ -62,7 +63,8 @@ def _run_prefill(w: ki.Workload, dev="cuda"):
     sink = None if w.sink is None else torch.from_numpy(w.sink).to(dev)
     msl = max(int(w.lens.max()), 1)
     out = kvq.prefill_attend(cache, q, lens, msl, w.sm_scale, k_new=kn.to(dev), v_new=vn.to(dev),
-                             block_table=table, head_sink=sink, softcap=w.softcap, window=w.window)
+                             block_table=table, head_sink=sink, softcap=w.softcap, window=w.window,
+                             split=split)
     torch.cuda.synchronize()
     return out, cache
 
@@ -294,3 +296,80 @@ def test_prefill_per_channel_k_table_spanning_2_pow_10(dtype):
     z = float(torch.sqrt((qs * qs).sum())) * w.sm_scale
     w.q = (w.q.float() * (2.0 / z)).to(torch.bfloat16)
     _check(w, f"prefill, K table over 2^-5..2^5, dt={dtype}")
+
+
+# ------------------------------------------------- context split
+# kvq_prefill_attend_ws: when the workgroups leave part of the GPU idle in
+# their last round, each one's tiles are cut into parts whose partial outputs a
+# fixed-order merge combines.  Both paths against the oracle on shapes the host
+# does split (ragged lengths, paged, sink, window, soft cap, every dtype).
+
+SPLIT_CASES = [
+    # seed, dtype, mode, vmode, D, Hkv, G, Tq, lens, paged, sink, cap, window
+    (8900, INT8, PER_ROW, None, 128, 2, 4, 32, [1500], False, False, 0.0, 0),
+    (8901, INT4, PER_ROW, None, 256, 2, 6, 30, [2100, 900], True, True, 0.0, 0),
+    (8902, INT4, PER_CHANNEL, PER_CHANNEL, 256, 4, 6, 64, [3000], True, True, 0.0, 1500),
+    (8903, FP8, PER_TENSOR, PER_TENSOR, 256, 2, 3, 40, [2500, 1700], True, False, 30.0, 0),
+    (8904, INT8, PER_CHANNEL, PER_ROW, 64, 1, 8, 16, [1300], False, True, 0.0, 0),
+    (8905, INT8, PER_ROW, None, 256, 4, 6, 1, [4000], False, False, 0.0, 0),
+]
+
+
+def _split_workload(case):
+    seed, dtype, mode, vmode, D, Hkv, G, Tq, lens, paged, sink, cap, window = case
+    return ki.random_workload(seed, B=len(lens), Hkv=Hkv, G=G, D=D, Tq=Tq, lens=lens, dtype=dtype,
+                              mode=mode, block_size=16 if paged else None, sink=sink, softcap=cap,
+                              window=window, v_mode=vmode)
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[str(c[0]) for c in SPLIT_CASES])
+def test_prefill_context_split(case):
+    w = _split_workload(case)
+    cache0 = gu.gpu_cache(w)
+    need = kvq.prefill_workspace_bytes(cache0, w.B, w.Hq, w.Tq, int(w.lens.max()), w.window)
+    del cache0
+    assert need > 0, "the shape should split"
+    ref, tol, ocache = gu.reference(w)
+    out_split, cache = _run_prefill(w, split=True)
+    gu.compare_codes(w, cache, ocache)
+    gu.check_output(out_split, ref, f"prefill split {case[0]}", tol)
+    out_plain, _ = _run_prefill(w, split=False)
+    gu.check_output(out_plain, ref, f"prefill unsplit {case[0]}", tol)
+
+
+def test_prefill_split_graph_replays_and_repeats():
+    """The split prefill with a caller workspace, captured in a HIP graph:
+    repeated eager calls and every replay write the same bits."""
+    w = _split_workload(SPLIT_CASES[1])
+    eager, cache = _run_prefill(w)
+    dev = "cuda"
+    table = torch.from_numpy(w.block_table).to(dev)
+    q = w.q.to(dev)
+    lens = torch.from_numpy(w.lens).to(dev)
+    sink = torch.from_numpy(w.sink).to(dev)
+    msl = int(w.lens.max())
+    need = kvq.prefill_workspace_bytes(cache, w.B, w.Hq, w.Tq, msl)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        # the chunk is in the cache already: attention (and merge) only
+        kvq.prefill_attend(cache, q, lens, msl, w.sm_scale, block_table=table, head_sink=sink,
+                           out=out, workspace=ws, stream=s)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), "repeat"
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            kvq.prefill_attend(cache, q, lens, msl, w.sm_scale, block_table=table, head_sink=sink,
+                               out=out, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+
