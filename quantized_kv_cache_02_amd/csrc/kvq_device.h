@@ -160,6 +160,14 @@ __device__ __forceinline__ void q_slices(float x, int ex, int (&sl)[NSL]) {
   sl[NSL - 1] = qi;
 }
 
+// The softmax weights of a row are exp2(z - m) for a reference m that moves
+// only when a logit exceeds it by more than this (log2 units): the weights stay
+// below 2^8 -- exact in the fp16 (and bf16 hi + lo) P operand up to its usual
+// rounding, far from fp16's 65504 -- and the accumulators are rescaled a few
+// times per wavefront instead of on a large share of tiles.  Every merge
+// weighs a partial by its own reference.
+constexpr float kLazyHeadroom = 8.0f;
+
 // The dot product of the folded query with the codes from the per-slice int32
 // dot products (dots[k] for slice k): exact integers, one rounding to fp32 at
 // the end (two slices: the sum is below 2^30 and exact in int32).

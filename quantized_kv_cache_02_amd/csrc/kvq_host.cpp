@@ -270,6 +270,9 @@ int prefill_check(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, in
   if (*G > kMaxGroup) return KVQ_EUNSUPPORTED;
   if (batch > 65535 || cache->num_kv_heads > 65535) return KVQ_EUNSUPPORTED;
   if ((int64_t)*G * q_tokens > INT32_MAX / 2) return KVQ_EUNSUPPORTED;
+  // the prefill kernel addresses a 16-row group by its first pool row over 16 in an int
+  if ((int64_t)cache->num_blocks * cache->num_kv_heads * cache->block_size / 16 > INT32_MAX)
+    return KVQ_EUNSUPPORTED;
   return KVQ_OK;
 }
 

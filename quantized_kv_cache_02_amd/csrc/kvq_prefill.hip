@@ -122,11 +122,12 @@ struct PTile {
 };
 
 // Cache rows of one 64-token tile: block sizes are multiples of 16, so each
-// aligned group of 16 tokens lies in one block; base[sg] is the cache row of
-// token 16 * sg of the tile (-1: past the length or outside the pool).
-// Computed once per tile from uniform values (no per-token division).
+// aligned group of 16 tokens lies in one block; r16[sg] is the cache row of
+// token 16 * sg of the tile over 16 (-1: past the length or outside the pool;
+// the host bounds the pool so that it fits an int).  Computed once per tile
+// from uniform values.
 struct TileRows {
-  long base[4];
+  int r16[4];
 };
 
 __device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int b, int hkv, int kt, int L) {
@@ -134,7 +135,7 @@ __device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int b, int h
 #pragma unroll
   for (int sg = 0; sg < 4; ++sg) {
     const int p = kt * kPT + 16 * sg;
-    long r = -1;
+    long r = -16;
     if (p < L) {
       if (a.c.block_table == nullptr) {
         r = ((long)b * a.c.Hkv + hkv) * a.c.block_size + p;  // contiguous: p < L <= block_size
@@ -144,42 +145,56 @@ __device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int b, int h
           r = ((long)blk * a.c.Hkv + hkv) * a.c.block_size + p % a.c.block_size;
       }
     }
-    tr.base[sg] = r;
+    tr.r16[sg] = __builtin_amdgcn_readfirstlane((int)(r / 16));  // uniform: scalar registers
   }
   return tr;
 }
 
-// Row of tile token tk (0..63), or -1.
-__device__ __forceinline__ long tile_row(const TileRows& tr, int kt, int tk, int L) {
-  const int sg = tk >> 4;
-  const long base = sg == 0 ? tr.base[0] : sg == 1 ? tr.base[1] : sg == 2 ? tr.base[2] : tr.base[3];
-  return (base < 0 || kt * kPT + tk >= L) ? -1 : base + (tk & 15);
+// r16 of group sg (0..3) by masked xors on its two bits (a select chain here
+// is turned into a table in scratch memory)
+__device__ __forceinline__ int group_r16(const TileRows& tr, int sg) {
+  const int m1 = -(sg & 1), m2 = -((sg >> 1) & 1);
+  const int lo = tr.r16[0] ^ ((tr.r16[0] ^ tr.r16[1]) & m1);
+  const int hi = tr.r16[2] ^ ((tr.r16[2] ^ tr.r16[3]) & m1);
+  return lo ^ ((lo ^ hi) & m2);
 }
 
+// Loads read row 0 (always present) in place of a row they may not read; the
+// flags say which rows are real, and the unpack zeroes the others.  Rows past
+// the length inside a present group are read and flagged the same way.
 template <int DT, int MODE, int D, int W>
 __device__ __forceinline__ void load_ptile(const PrefillArgs& a, int b, int hkv, int kt, int L, int tid,
                                            PTile<DT, D, W>& T) {
   using P = PGeo<DT, D, W>;
   const TileRows tr = tile_rows(a, b, hkv, kt, L);
-  // K: one row quarter per thread
+  const int lrem = L - kt * kPT;  // tokens of the tile before the length
+  // K: one row part per thread; a wavefront's tokens share one group
   {
-    const long ri = tile_row(tr, kt, tid / P::KP, L);
-    T.kok = ri >= 0;
-    gload<P::KQB>(a.c.k_codes + (ri < 0 ? 0 : ri) * P::ROWB + P::KQB * (tid % P::KP), T.k);
+    const int tk = tid / P::KP;
+    const int r16 = group_r16(tr, __builtin_amdgcn_readfirstlane(tk) >> 4);
+    T.kok = r16 >= 0 && tk < lrem;
+    const size_t row = T.kok ? (size_t)(uint32_t)r16 * 16 + (tk & 15) : 0;
+    gload<P::KQB>(a.c.k_codes + row * P::ROWB + P::KQB * (tid % P::KP), T.k);
   }
-  // V: 4 tokens of one channel chunk
+  // V: 4 consecutive tokens (one group) of one channel chunk
+  {
+    const int tv = 4 * (tid % 16);
+    const int r16 = group_r16(tr, tv >> 4);
+    const size_t row = r16 >= 0 ? (size_t)(uint32_t)r16 * 16 + (tv & 15) : 0;
+    const uint8_t* src = a.c.v_codes + row * P::ROWB + P::VCB * (tid / 16);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const long ri = tile_row(tr, kt, 4 * (tid % 16) + e, L);
-    T.vok[e] = ri >= 0;
-    if constexpr (P::VCB < 4) T.v[e][0] = 0u;  // the load fills the low bytes only
-    gload<P::VCB>(a.c.v_codes + (ri < 0 ? 0 : ri) * P::ROWB + P::VCB * (tid / 16), T.v[e]);
+    for (int e = 0; e < 4; ++e) {
+      T.vok[e] = r16 >= 0 && tv + e < lrem;
+      if constexpr (P::VCB < 4) T.v[e][0] = 0u;  // the load fills the low bytes only
+      gload<P::VCB>(src + e * P::ROWB, T.v[e]);
+    }
   }
   // per-row scales of token tid % 64 (every thread loads; threads 0..63 store)
   {
-    const long ri = tile_row(tr, kt, tid % kPT, L);
-    T.sok = ri >= 0;
-    const long rs = ri < 0 ? 0 : ri;
+    const int ts = tid % kPT;
+    const int r16 = group_r16(tr, ts >> 4);
+    T.sok = r16 >= 0 && ts < lrem;
+    const size_t rs = T.sok ? (size_t)(uint32_t)r16 * 16 + (ts & 15) : 0;
     T.ks = 0.0f;
     T.vs = 0.0f;
     if constexpr (MODE == kPerRow) T.ks = __builtin_nontemporal_load(a.c.k_scales + rs);
@@ -198,24 +213,27 @@ __device__ __forceinline__ void stage_ptile(const PTile<DT, D, W>& T, int tid, u
     // this thread's part of its row: channels (D / KP) * (tid % KP) .. + D / KP
     uint16_t* dst = ks_lds + (tid / P::KP) * P::KST + (P::IQK ? (D / P::KP) / 2 : (D / P::KP)) * (tid % P::KP);
     constexpr int NW = P::KQB / 4;  // dwords loaded
+    // the thread's part of the row as dwords, then 16-byte LDS writes
+    constexpr int OW = (DT == kInt4 || DT == kFp8) ? 2 * NW : NW;
+    static_assert(OW % 4 == 0, "whole 16-byte writes");
+    uint32_t ow[OW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const uint32_t kw = T.kok ? T.k[i] : 0u;
-      if constexpr (DT == kInt8) {
-        reinterpret_cast<uint32_t*>(dst)[i] = kw;  // the codes as they are
+      if constexpr (DT == kInt8 || DT == kBf16) {
+        ow[i] = kw;  // the codes (bf16 values) as they are
       } else if constexpr (P::IQK) {
         // 8 nibbles -> the bytes 16 n in channel order
         const uint32_t ev = (kw << 4) & 0xF0F0F0F0u, od = kw & 0xF0F0F0F0u;
-        *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint32_t*>(dst) + 2 * i) =
-            u32x2_t{perm(od, ev, 0x05010400u), perm(od, ev, 0x07030602u)};
-      } else if constexpr (DT == kBf16) {
-        reinterpret_cast<uint32_t*>(dst)[i] = kw;
+        ow[2 * i] = perm(od, ev, 0x05010400u);
+        ow[2 * i + 1] = perm(od, ev, 0x07030602u);
       } else {  // fp8 -> fp16
-        uint32_t lo, hi;
-        fp8x4_to_h(kw, lo, hi);
-        *reinterpret_cast<u32x2_t*>(dst + 4 * i) = u32x2_t{lo, hi};
+        fp8x4_to_h(kw, ow[2 * i], ow[2 * i + 1]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < OW / 4; ++j)
+      reinterpret_cast<u32x4_t*>(dst)[j] = u32x4_t{ow[4 * j], ow[4 * j + 1], ow[4 * j + 2], ow[4 * j + 3]};
   }
   {
     // channels [cb0, cb0 + D / 16) of tokens t0 .. t0 + 3
@@ -591,9 +609,11 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) up |= z[rb][s][e] > m[rb];
+        for (int e = 0; e < 4; ++e) up |= z[rb][s][e] > m[rb] + kLazyHeadroom;
 
-    // ---- online softmax over the tile's 64 tokens (row n: lanes n, n+16, n+32, n+48)
+    // ---- online softmax over the tile's 64 tokens (row n: lanes n, n+16, n+32,
+    // n+48), with the lazily moved reference of the decode kernel: m moves only
+    // when a logit exceeds it by more than kLazyHeadroom
     float alpha[RBW];
     float vfac = 1.0f;
     bool rescale = false;
@@ -607,11 +627,10 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
         for (int s = 0; s < 4; ++s)
           tmax = fmaxf(tmax, fmaxf(fmaxf(z[rb][s][0], z[rb][s][1]), fmaxf(z[rb][s][2], z[rb][s][3])));
         tmax = group_max4(tmax);
-        const float mnew = fmaxf(m[rb], tmax);
-        if (mnew > m[rb]) {
-          alpha[rb] = __builtin_amdgcn_exp2f(m[rb] - mnew);
+        if (tmax > m[rb] + kLazyHeadroom) {
+          alpha[rb] = __builtin_amdgcn_exp2f(m[rb] - tmax);
           l[rb] *= alpha[rb];
-          m[rb] = mnew;
+          m[rb] = tmax;
           rescale = true;
         }
       }

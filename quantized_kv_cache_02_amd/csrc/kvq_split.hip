@@ -350,13 +350,6 @@ __device__ __forceinline__ void load_tile(const SplitArgs& a, int t, bool live, 
 template <int D>
 constexpr int kQStride = D + 8;
 
-// The softmax weights of a row are exp2(z - m) for a reference m that moves
-// only when a logit exceeds it by more than this (log2 units): the weights stay
-// below 2^8 -- exact in the fp16 (and bf16 hi + lo) P operand up to its usual
-// rounding, far from fp16's 65504 -- and the accumulators are rescaled a few
-// times per wavefront instead of on a large share of tiles.  The merge and the
-// combine weigh each partial by its own reference, as before.
-constexpr float kLazyHeadroom = 8.0f;
 
 // Per-wavefront online-softmax state over its tiles.
 template <int DT, int D, int RB>

@@ -167,6 +167,10 @@ def test_invalid_prefill_rejected():
     assert call(v_new=None) == -1     # one of the new-row tensors only
     assert call(opts=(-1.0, 0)) == -1
     assert call(opts=(0.0, -3)) == -1
+    # a pool of 2^31 or more 16-row groups is beyond the prefill's row indices
+    big = _cache(block_size=16, num_blocks=1 << 30)
+    assert L.kvq_prefill_attend(ctypes.byref(big), FAKE, FAKE, FAKE, 1, 24, 100, FAKE, 4096, 0.1,
+                                None, FAKE, 256, None, FAKE, None) == -2
 
 
 def _prefill_ws(c, batch=1, hq=24, tq=2048, msl=18432, window=0):
