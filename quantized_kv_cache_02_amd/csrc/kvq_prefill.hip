@@ -284,10 +284,9 @@ __device__ __forceinline__ void stage_ptile(const PTile<DT, D, W>& T, int tid, u
       }
     }
   }
-  if (tid < kPT) {
-    ksc[tid] = T.sok ? T.ks : 0.0f;
-    vsc[tid] = T.sok ? T.vs : 0.0f;
-  }
+  // (every thread writes the scales of token tid % 64: the same values)
+  ksc[tid % kPT] = T.sok ? T.ks : 0.0f;
+  vsc[tid % kPT] = T.sok ? T.vs : 0.0f;
 }
 
 template <int DT, int MODE, int D, int W, bool CAP>
@@ -495,8 +494,9 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
   __syncthreads();
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int cur = (kt - kt_begin) & 1;
-    const bool more = kt + 1 < kt_end;
-    if (more) load_ptile<DT, MODE, D, W>(a, b, hkv, kt + 1, L, tid, T);
+    // the next tile's loads (past the last tile they read rows that exist and
+    // are never used)
+    load_ptile<DT, MODE, D, W>(a, b, hkv, kt + 1, L, tid, T);
     const uint16_t* ks_lds = lds + cur * BUF_ELEMS;
     const uint16_t* vt_lds = ks_lds + KTILE_ELEMS;
 
@@ -681,6 +681,12 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
       }
     }
 
+    // ---- unpack the next tile into the other buffer (nobody reads it during
+    // this tile; past the last tile it writes what nobody reads), ahead of the
+    // P . V MFMAs so that its VALU work and LDS writes interleave with them
+    stage_ptile<DT, MODE, D, W>(T, tid, lds + (cur ^ 1) * BUF_ELEMS, lds + (cur ^ 1) * BUF_ELEMS + KTILE_ELEMS,
+                                ksc[cur ^ 1], vsc[cur ^ 1]);
+
     // ---- O += P . V, two sub-tiles (32 tokens) per 16x16x32 MFMA: lane group
     // g's A operand holds tokens 16s + 4g + 0..3 then 16s + 16 + 4g + 0..3 of its
     // row, and the B operand the same tokens of its channel (two 8-byte reads
@@ -758,11 +764,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
       }
     }
 
-    // unpack the next tile into the other buffer (nobody reads it during this
-    // tile), then one barrier: it is complete, and this tile's buffer is free
-    if (more)
-      stage_ptile<DT, MODE, D, W>(T, tid, lds + (cur ^ 1) * BUF_ELEMS, lds + (cur ^ 1) * BUF_ELEMS + KTILE_ELEMS,
-                               ksc[cur ^ 1], vsc[cur ^ 1]);
+    // one barrier: the next tile is unpacked, and this tile's buffer is free
     __syncthreads();
   }
 
