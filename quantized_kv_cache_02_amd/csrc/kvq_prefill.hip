@@ -503,6 +503,12 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
     // ---- S^T for the 4 sub-tiles of 16 tokens: lane (n, g) gets tokens 4g + e
     // of its rows.  The K operands of sub-tile s + 1 are read from LDS before
     // sub-tile s's MFMAs in source order (the compiler schedules them).
+    // z: logits in log2 units relative to the row's reference, z - msafe
+    // (msafe = m, or 0 before the first visible token), folded into one fma
+    // (with a soft cap the capped logit comes first, then the subtraction)
+    float msafe[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) msafe[rb] = m[rb] == -INFINITY ? 0.0f : m[rb];
     float z[RBW][4][4];
     bool up = false;
     // (one sub-tile's K operands at a time at D = 256: two in flight cost 32
@@ -582,13 +588,16 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
       for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float zz = (s0[rb][e] + s1[rb][e]) * rowmul[rb];
-          if constexpr (MODE == kPerRow) zz *= ks4[e];
+          float d = s0[rb][e] + s1[rb][e];
+          if constexpr (MODE == kPerRow) d *= ks4[e];
           if constexpr (CAP) {
+            float zz = d * rowmul[rb];
             const float ex = __builtin_amdgcn_exp2f(zz * icap2);
             zz = cap2 - 2.0f * cap2 * __builtin_amdgcn_rcpf(ex + 1.0f);
+            z[rb][s][e] = zz - msafe[rb];
+          } else {
+            z[rb][s][e] = __builtin_fmaf(d, rowmul[rb], -msafe[rb]);
           }
-          z[rb][s][e] = zz;
         }
     }
     // causal / window / length mask, skipped on tiles every row of the
@@ -609,7 +618,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) up |= z[rb][s][e] > m[rb] + kLazyHeadroom;
+        for (int e = 0; e < 4; ++e) up |= z[rb][s][e] > kLazyHeadroom || m[rb] == -INFINITY;
 
     // ---- online softmax over the tile's 64 tokens (row n: lanes n, n+16, n+32,
     // n+48), with the lazily moved reference of the decode kernel: m moves only
@@ -626,11 +635,16 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           tmax = fmaxf(tmax, fmaxf(fmaxf(z[rb][s][0], z[rb][s][1]), fmaxf(z[rb][s][2], z[rb][s][3])));
-        tmax = group_max4(tmax);
-        if (tmax > m[rb] + kLazyHeadroom) {
-          alpha[rb] = __builtin_amdgcn_exp2f(m[rb] - tmax);
+        tmax = group_max4(tmax);  // relative to msafe
+        if (tmax > kLazyHeadroom || (m[rb] == -INFINITY && tmax > -INFINITY)) {
+          // hardware exp2; 0 when there was no reference yet
+          alpha[rb] = m[rb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(-tmax);
           l[rb] *= alpha[rb];
-          m[rb] = tmax;
+          m[rb] = msafe[rb] + tmax;
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[rb][s][e] -= tmax;
           rescale = true;
         }
       }
@@ -697,7 +711,6 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
       half8_t phi[RBW], plo[RBW];
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) {
-        const float msafe = m[rb] == -INFINITY ? 0.0f : m[rb];
         float pf[8];
         float psum = 0.0f;
 #pragma unroll
@@ -705,7 +718,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int s = 2 * sp + h;
-            const float p = __builtin_amdgcn_exp2f(z[rb][s][e] - msafe);
+            const float p = __builtin_amdgcn_exp2f(z[rb][s][e]);
             psum += p;
             if constexpr (kVRow)
               pf[4 * h + e] = p * vsn[s][e];
