@@ -646,112 +646,162 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L,
   accumulate_pv<DT, D, RB>(T.vw, pa, phi, plo, W.acc);
 }
 
-// B operand of S^T for query row r of the staged rows qs (bf16, kQStride
-// apart): the row in this lane's channel order, normalized by a power of two
-// so every element lies in (-1, 1) (integer caches: the row as a fixed-point
-// integer vector in int8 slices); returns the row multiplier that restores it
-// (logit in log2 units = dot * multiplier * per-row K scale).
-template <int DT, int MODE, int D>
-__device__ __forceinline__ float fold_q_row(const SplitArgs& a, const uint16_t* qs, int r, int g, int hkv,
-                                            half8_t (&qb)[kQOps<DT, MODE, D>]) {
+// B operands of S^T for the workgroup's RB row blocks, computed once per
+// workgroup (every wavefront needs the same ones) into the lane-linear LDS
+// array qop: operand k of row block rb for lane l at qop[(rb * QO + k) * 64 + l].
+// Each row is taken in this lane's channel order from the staged rows qs (bf16,
+// kQStride apart), times a per-channel K scale, and normalized by a power of
+// two: the integer caches get a fixed-point integer vector in NSL int8 slices
+// (see q_slices: 15 bits of the row's largest element, 23 with a per-channel
+// K scale folded in), fp8 an fp16 vector with every element in (-1, 1), bf16
+// the row as it is (bf16 products are exact in the fp32 accumulation).
+// Wavefront w folds the k-steps st = w, w + 4, ...: their row maxima meet in
+// s_pmax ([kWaves][16 RB]) across a barrier, the operands in qop across a
+// second one.  rowmul[rb] restores the power of two (logit in log2 units =
+// dot * rowmul * per-row K scale).  Every wavefront must call it.
+template <int DT, int MODE, int D, int RB>
+__device__ __forceinline__ void fold_q_shared(const SplitArgs& a, const uint16_t* qs, int hkv, int wave,
+                                              int n, int g, int lane, half8_t* qop, float* s_pmax,
+                                              float (&rowmul)[RB]) {
   using G_ = Geo<DT, D>;
+  constexpr int QO = kQOps<DT, MODE, D>;
+  constexpr int RP = 16 * RB;
   const float* kst = a.c.k_scales;
-  if constexpr (DT == kBf16) {
-    // the q rows as they are: bf16 products are exact in the fp32 accumulation
-#pragma unroll
-    for (int ks = 0; ks < G_::KSTEPS; ++ks)
-      qb[ks] = __builtin_bit_cast(
-          half8_t, *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + k_channel<DT, D>(ks, g, 0)));
-    return a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
-  }
-  if constexpr (G_::IQK) {
-    // The row as a fixed-point integer vector in NSL int8 slices (see
-    // q_slices): 15 bits of the row's largest element, 23 with a
-    // per-channel K scale folded in.
-    constexpr int NSL = kQSlices<DT, MODE>;
-    float qv[G_::ISTEPS][16];
-    float amax = 0.0f;
-#pragma unroll
-    for (int st = 0; st < G_::ISTEPS; ++st) {
-      const int base = k_channel_i8<DT, D>(st, g, 0);
-      const u32x4_t r0 = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base);
-      const u32x4_t r1 = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base + 8);
-      float x16[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x16[2 * i] = __uint_as_float(r0[i] << 16);
-        x16[2 * i + 1] = __uint_as_float(r0[i] & 0xFFFF0000u);
-        x16[8 + 2 * i] = __uint_as_float(r1[i] << 16);
-        x16[8 + 2 * i + 1] = __uint_as_float(r1[i] & 0xFFFF0000u);
-      }
-#pragma unroll
-      for (int p = 0; p < 16; ++p) {
-        const int off = k_offset_i8<DT>(p);  // 0..15
-        float x = x16[off];
-        if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
-        qv[st][p] = x;
-        amax = fmaxf(amax, fabsf(x));
-      }
-    }
-    amax = group_max4(amax);
-    int ex = 0;
-    if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
-#pragma unroll
-    for (int st = 0; st < G_::ISTEPS; ++st) {
-      u32x4_t w[NSL];
-#pragma unroll
-      for (int k = 0; k < NSL; ++k) w[k] = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int p = 0; p < 16; ++p) {
-        int sl[NSL];
-        q_slices<NSL>(qv[st][p], ex, sl);
-#pragma unroll
-        for (int k = 0; k < NSL; ++k) w[k][p / 4] |= ((uint32_t)sl[k] & 0xFFu) << (8 * (p % 4));
-      }
-#pragma unroll
-      for (int k = 0; k < NSL; ++k) qb[NSL * st + k] = __builtin_bit_cast(half8_t, w[k]);
-    }
-    float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
-    if constexpr (MODE == kPerTensor) mul *= kst[0];
-    if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
-    return ldexpf(mul, ex - (8 * NSL - 2));
-  }
-  float qv[G_::KSTEPS][8];
-  float amax = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < G_::KSTEPS; ++ks) {
-    // the 8 channels of a k-step are 8 consecutive channels (permuted for int4)
-    const int base = k_channel<DT, D>(ks, g, 0);
-    u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base);
-    float x8[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x8[2 * i] = __uint_as_float(raw[i] << 16);
-      x8[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int off = k_channel<DT, D>(ks, g, e) - base;  // 0..7
-      float x = x8[off];
-      if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
-      qv[ks][e] = x;
-      amax = fmaxf(amax, fabsf(x));
-    }
-  }
-  amax = group_max4(amax);
-  int ex = 0;
-  if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
-#pragma unroll
-  for (int ks = 0; ks < G_::KSTEPS; ++ks) {
-    half8_t h;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (_Float16)ldexpf(qv[ks][e], -ex);
-    qb[ks] = h;
-  }
   float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
   if constexpr (MODE == kPerTensor) mul *= kst[0];
   if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
-  return ldexpf(mul, ex);
+  if constexpr (G_::IQK) {
+    constexpr int NSL = kQSlices<DT, MODE>;
+    constexpr int NS = G_::ISTEPS;
+    constexpr int MY = (NS + kWaves - 1) / kWaves;  // steps per wavefront
+    float qv[RB][MY][16];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = rb * 16 + n;
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < MY; ++j) {
+        const int st = wave + kWaves * j;
+        if (st >= NS) continue;
+        const int base = k_channel_i8<DT, D>(st, g, 0);
+        const u32x4_t r0 = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base);
+        const u32x4_t r1 = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base + 8);
+        float x16[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x16[2 * i] = __uint_as_float(r0[i] << 16);
+          x16[2 * i + 1] = __uint_as_float(r0[i] & 0xFFFF0000u);
+          x16[8 + 2 * i] = __uint_as_float(r1[i] << 16);
+          x16[8 + 2 * i + 1] = __uint_as_float(r1[i] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+          const int off = k_offset_i8<DT>(p);  // 0..15
+          float x = x16[off];
+          if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
+          qv[rb][j][p] = x;
+          amax = fmaxf(amax, fabsf(x));
+        }
+      }
+      amax = group_max4(amax);
+      if (g == 0) s_pmax[wave * RP + r] = amax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = rb * 16 + n;
+      float amax = s_pmax[r];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, s_pmax[w * RP + r]);
+      int ex = 0;
+      if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
+      rowmul[rb] = ldexpf(mul, ex - (8 * NSL - 2));
+#pragma unroll
+      for (int j = 0; j < MY; ++j) {
+        const int st = wave + kWaves * j;
+        if (st >= NS) continue;
+        u32x4_t w4[NSL];
+#pragma unroll
+        for (int k = 0; k < NSL; ++k) w4[k] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+          int sl[NSL];
+          q_slices<NSL>(qv[rb][j][p], ex, sl);
+#pragma unroll
+          for (int k = 0; k < NSL; ++k) w4[k][p / 4] |= ((uint32_t)sl[k] & 0xFFu) << (8 * (p % 4));
+        }
+#pragma unroll
+        for (int k = 0; k < NSL; ++k)
+          qop[(rb * QO + NSL * st + k) * 64 + lane] = __builtin_bit_cast(half8_t, w4[k]);
+      }
+    }
+    __syncthreads();
+  } else {
+    constexpr int NS = G_::KSTEPS;
+    constexpr int MY = (NS + kWaves - 1) / kWaves;
+    float qv[RB][MY][8];
+    u32x4_t raw[RB][MY];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = rb * 16 + n;
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < MY; ++j) {
+        const int ks = wave + kWaves * j;
+        if (ks >= NS) continue;
+        // the 8 channels of a k-step are 8 consecutive channels
+        const int base = k_channel<DT, D>(ks, g, 0);
+        raw[rb][j] = *reinterpret_cast<const u32x4_t*>(qs + r * kQStride<D> + base);
+        if constexpr (DT != kBf16) {
+          float x8[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x8[2 * i] = __uint_as_float(raw[rb][j][i] << 16);
+            x8[2 * i + 1] = __uint_as_float(raw[rb][j][i] & 0xFFFF0000u);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int off = k_channel<DT, D>(ks, g, e) - base;  // 0..7
+            float x = x8[off];
+            if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
+            qv[rb][j][e] = x;
+            amax = fmaxf(amax, fabsf(x));
+          }
+        }
+      }
+      if constexpr (DT != kBf16) {
+        amax = group_max4(amax);
+        if (g == 0) s_pmax[wave * RP + r] = amax;
+      }
+    }
+    if constexpr (DT != kBf16) __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = rb * 16 + n;
+      int ex = 0;
+      if constexpr (DT != kBf16) {
+        float amax = s_pmax[r];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, s_pmax[w * RP + r]);
+        if (amax > 0.0f) (void)frexpf(amax, &ex);  // amax < 2^ex
+      }
+      rowmul[rb] = DT == kBf16 ? mul : ldexpf(mul, ex);
+#pragma unroll
+      for (int j = 0; j < MY; ++j) {
+        const int ks = wave + kWaves * j;
+        if (ks >= NS) continue;
+        half8_t h;
+        if constexpr (DT == kBf16) {
+          h = __builtin_bit_cast(half8_t, raw[rb][j]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = (_Float16)ldexpf(qv[rb][j][e], -ex);
+        }
+        qop[(rb * QO + ks) * 64 + lane] = h;
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // Tokens visible to query row `row` (of the sequence's R rows; `live` false
@@ -882,9 +932,9 @@ split_decode_kernel(SplitArgs a) {
   // operand after them), then the merge buffers
   __shared__ __attribute__((aligned(16))) float smem[K_::MERGE_BUFS * RP * D];
   constexpr int kQStageBytes = (RP * kQStride<D> * 2 + 255) / 256 * 256;
-  constexpr int kQOpBytes = RB * kQOps<DT, MODE, D> * 64 * 16;  // one wavefront's operand
-  static_assert(!K_::QLDS || kQStageBytes + kWaves * kQOpBytes <= (int)sizeof(smem),
-                "q operand copies do not fit the merge buffers");
+  constexpr int kQOpBytes = RB * kQOps<DT, MODE, D> * 64 * 16;  // the workgroup's q operand
+  static_assert(kQStageBytes + kQOpBytes <= (int)sizeof(smem), "the q operand does not fit the merge buffers");
+  __shared__ float s_pmax[kWaves * RP];  // row maxima of each wavefront's k-steps
   __shared__ float s_m[kWaves][RP];
   __shared__ float s_l[kWaves][RP];
   __shared__ float s_f[kWaves][RP];  // merge weight of each wavefront's rows
@@ -987,29 +1037,27 @@ split_decode_kernel(SplitArgs a) {
   }
   __syncthreads();
 
-  // ---- B operands of S^T: q rows in this lane's channel order, normalized by a
-  // power of two so every element lies in (-1, 1) (integer caches: the int8
-  // halves of the row scaled to 15 bits); the row multiplier restores it.
-  half8_t qb[RB][kQOps<DT, MODE, D>];
+  // ---- B operands of S^T, folded once for the workgroup into LDS (lane-
+  // linear, after the staged rows); the QLDS variants read them from there in
+  // the tile loop, the others copy them into registers
+  constexpr int QO = kQOps<DT, MODE, D>;
+  half8_t* qop = reinterpret_cast<half8_t*>(reinterpret_cast<char*>(smem) + kQStageBytes);
   float rowmul[RB];  // logit (log2 units) = dot * rowmul * per-row K scale
-  int lim[RB];       // tokens visible to this lane's row n: lo <= t < lim
+  fold_q_shared<DT, MODE, D, RB>(a, qs, hkv, wave, n, g, lane, qop, s_pmax, rowmul);
+  const half8_t* qlds = qop + lane;
+  half8_t qb[RB][QO];
+  if constexpr (!K_::QLDS) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int k = 0; k < QO; ++k) qb[rb][k] = qlds[(rb * QO + k) * 64];
+  }
+  int lim[RB];  // tokens visible to this lane's row n: lo <= t < lim
   int lo[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = rb * 16 + n;
     row_window(a, L, row0 + r, r < Rw, lim[rb], lo[rb]);
-    rowmul[rb] = fold_q_row<DT, MODE, D>(a, qs, r, g, hkv, qb[rb]);
-  }
-  // With QLDS the operand goes to this wavefront's own LDS copy (lane-linear),
-  // which only its own lanes read back: no barrier needed.
-  half8_t* qlds = reinterpret_cast<half8_t*>(reinterpret_cast<char*>(smem) + kQStageBytes +
-                                             wave * kQOpBytes) + lane;
-  if constexpr (K_::QLDS) {
-    constexpr int QO = kQOps<DT, MODE, D>;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int ks = 0; ks < QO; ++ks) qlds[(rb * QO + ks) * 64] = qb[rb][ks];
   }
 
   // soft cap in log2 units (the CAP variant is launched when softcap > 0)
