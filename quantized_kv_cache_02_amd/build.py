@@ -54,6 +54,13 @@ def _units():
     # the unquantized bf16 cache: no scales
     units.append(("kvq_split_4_0_0.o", os.path.join(CSRC, "kvq_split.hip"),
                   ["-DKVQ_DTYPE=4", "-DKVQ_MODE=0", "-DKVQ_VROW=0", *vf]))
+    # the wide-row-set variants (one wavefront per SIMD), in units of their own
+    # built in the default MFMA form: their accumulators (up to 192 registers)
+    # live in the accumulation registers, which the MFMAs read and write
+    # directly, and everything else in the ordinary ones
+    for dt, md, vr in [(d, m, v) for d in (1, 2, 3) for m in (1, 2, 3) for v in (0, 1)] + [(4, 0, 0)]:
+        units.append((f"kvq_split_wide_{dt}_{md}_{vr}.o", os.path.join(CSRC, "kvq_split.hip"),
+                      [f"-DKVQ_DTYPE={dt}", f"-DKVQ_MODE={md}", f"-DKVQ_VROW={vr}", "-DKVQ_WIDE=1"]))
     # the chunked-prefill kernel, split the same way.  Its accumulators stay in
     # ordinary vector registers: left to itself the backend parks them in the
     # accumulation registers and copies all of them in and out on every tile

@@ -108,12 +108,16 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   // wavefront, beat 512, 28.1 vs 29.4 us), with at least kMinTilesPerSplit
   // tiles per chunk for a full-length sequence, and few enough tiles per chunk
   // for the block-table registers.
-  // More than 256 accumulator columns per lane (row blocks x head_dim) do not
-  // fit a wavefront's registers with the q operand and the tiles in flight:
-  // then every 16-row block gets its own workgroup and the chunk's workgroups
-  // share its bytes through L2.
+  // More than 256 accumulator columns (row blocks x head_dim) do not fit the
+  // registers of two wavefronts per SIMD with the q operand and the tiles in
+  // flight.  Up to kSplitMaxWideColumns the chunk keeps one workgroup, built
+  // for one wavefront per SIMD with the accumulators in the accumulation
+  // registers, so every tile is unpacked once for all its rows; beyond that
+  // every 16-row block gets its own workgroup and the chunk's workgroups share
+  // its bytes through L2.
   const int RB = (G * tq + 15) / 16;
-  const int RBN = (RB > 1 && RB * c->head_dim > kvq::kSplitMaxAccColumns) ? RB : 1;
+  const int RBN = (RB > 1 && RB * c->head_dim > kvq::kSplitMaxWideColumns) ? RB : 1;
+  const bool wide = RBN == 1 && RB * c->head_dim > kvq::kSplitMaxAccColumns;
   // Compute-bound variants (rows of at most 128 bytes, whose tiles carry less
   // data per instruction: packed int4 at D 256, the 8-bit caches at D 128 and
   // below; and row-split launches) run two workgroups per CU -- two
@@ -125,7 +129,8 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   const int64_t all_tiles = (int64_t)batch * ntiles;
   int64_t NW = per_head - (batch - 1);
   bool doubled = false;
-  if ((RBN > 1 || row_bytes(c) <= 128) && 2 * per_head - (batch - 1) <= all_tiles / (2 * kvq::kMinTilesPerSplit)) {
+  if (!wide && (RBN > 1 || row_bytes(c) <= 128) &&
+      2 * per_head - (batch - 1) <= all_tiles / (2 * kvq::kMinTilesPerSplit)) {
     NW = 2 * per_head - (batch - 1);
     doubled = true;
   }

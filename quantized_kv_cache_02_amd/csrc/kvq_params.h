@@ -34,11 +34,17 @@ constexpr int kPrefillMaxParts = 8;
 // Decode-kernel register budget: two wavefronts per SIMD (<= 256 registers
 // per lane).  The kernel is built for row-block counts RB (16 query rows each)
 // with RB * D <= 256, whose accumulators fit that budget beside the q operand
-// and the tiles in flight; wider row sets get one workgroup per row block.
+// and the tiles in flight.  Wider row sets up to kSplitMaxWideColumns run as
+// one workgroup per chunk with one wavefront per SIMD, the accumulators in the
+// accumulation registers (the "wide" units); wider ones still get one
+// workgroup per row block.
 constexpr int kSplitWavesPerSimd = 2;
-constexpr int kSplitMaxAccColumns = 256;  // RB * D
+constexpr int kSplitMaxAccColumns = 256;   // RB * D
+constexpr int kSplitMaxWideColumns = 768;  // RB * D
 // Tiles of codes held in registers per wavefront (one in use, one loading).
 constexpr int kSplitTilesInFlight = 2;
+// ... and for the wide-row-set variants (one wavefront per SIMD)
+constexpr int kSplitWideTilesInFlight = 3;
 
 struct CacheArgs {
   uint8_t* k_codes;
@@ -165,6 +171,22 @@ KVQ_DECLARE_SPLIT(3, 2)
 KVQ_DECLARE_SPLIT(3, 3)
 #undef KVQ_DECLARE_SPLIT
 hipError_t launch_split_4_0_0(int D, int RB, const SplitArgs& a, int B, hipStream_t st);
+// their wide-row-set variants (kSplitMaxAccColumns < RB * D <= kSplitMaxWideColumns),
+// built in units of their own; called by the units above
+#define KVQ_DECLARE_WIDE(DT, MD)                                                                 \
+  hipError_t launch_split_wide_##DT##_##MD##_0(int D, int RB, const SplitArgs& a, hipStream_t st); \
+  hipError_t launch_split_wide_##DT##_##MD##_1(int D, int RB, const SplitArgs& a, hipStream_t st);
+KVQ_DECLARE_WIDE(1, 1)
+KVQ_DECLARE_WIDE(1, 2)
+KVQ_DECLARE_WIDE(1, 3)
+KVQ_DECLARE_WIDE(2, 1)
+KVQ_DECLARE_WIDE(2, 2)
+KVQ_DECLARE_WIDE(2, 3)
+KVQ_DECLARE_WIDE(3, 1)
+KVQ_DECLARE_WIDE(3, 2)
+KVQ_DECLARE_WIDE(3, 3)
+#undef KVQ_DECLARE_WIDE
+hipError_t launch_split_wide_4_0_0(int D, int RB, const SplitArgs& a, hipStream_t st);
 
 // prefill translation units, the same split by (dtype, K mode, V per row)
 #define KVQ_DECLARE_PREFILL(DT, MD)                                                             \

@@ -48,6 +48,9 @@
 #ifndef KVQ_MODE
 #error "KVQ_MODE must be defined"
 #endif
+#ifndef KVQ_WIDE
+#define KVQ_WIDE 0  // 1: the unit holds the wide-row-set variants only
+#endif
 
 namespace kvq {
 namespace {
@@ -460,14 +463,12 @@ __device__ __forceinline__ void tile_logits(const float (&dot)[4], const float4_
 // logits, the lazily moved reference m, the running sum l and the P operand
 // (bf16 cache: its hi and lo parts).  alpha is the factor the row's
 // accumulators take when m moved (1 otherwise), and `rescale` is set then.
-template <int DT, int MODE, int D, bool CAP, class QOp>
-__device__ __forceinline__ void row_block_weights(const uint32_t* kw, const float4_t& ks4, bool ok,
-                                                  int tbase, QOp qop, float rowmul, int lim, int lo,
-                                                  float cap2, float icap2, const float (&vsn)[4],
-                                                  float& m, float& l, float& alpha, bool& rescale,
-                                                  half4_t& pa, u32x2_t& phi, u32x2_t& plo) {
-  float dot[4];
-  tile_dots<DT, MODE, D>(kw, qop, dot);
+template <int DT, int MODE, bool CAP>
+__device__ __forceinline__ void row_block_softmax(const float (&dot)[4], const float4_t& ks4, bool ok,
+                                                  int tbase, float rowmul, int lim, int lo, float cap2,
+                                                  float icap2, const float (&vsn)[4], float& m, float& l,
+                                                  float& alpha, bool& rescale, half4_t& pa, u32x2_t& phi,
+                                                  u32x2_t& plo) {
   float z[4];
   tile_logits<MODE, CAP>(dot, ks4, ok, tbase, rowmul, lim, lo, cap2, icap2, z);
   bool up = false;
@@ -516,8 +517,6 @@ __device__ __forceinline__ void row_block_weights(const uint32_t* kw, const floa
   }
 }
 
-// O += P . V for one tile: unpack the lane's V column blocks (VD channels) and
-// accumulate every row block's weights into them.
 // The B operands of the P . V MFMA from dword w of the lane's V codes (tokens
 // 4g..4g+3 of the tile): vb[k] feeds accumulator column v_column(w, k), for k
 // < 8 (int4: both nibbles of the bytes of the dword, nb of them valid) or
@@ -558,6 +557,120 @@ __device__ __forceinline__ constexpr int v_column(int w, int k) {
   }
 }
 
+template <int DT, int MODE, int D, bool CAP, class QOp>
+__device__ __forceinline__ void row_block_weights(const uint32_t* kw, const float4_t& ks4, bool ok,
+                                                  int tbase, QOp qop, float rowmul, int lim, int lo,
+                                                  float cap2, float icap2, const float (&vsn)[4],
+                                                  float& m, float& l, float& alpha, bool& rescale,
+                                                  half4_t& pa, u32x2_t& phi, u32x2_t& plo) {
+  float dot[4];
+  tile_dots<DT, MODE, D>(kw, qop, dot);
+  row_block_softmax<DT, MODE, CAP>(dot, ks4, ok, tbase, rowmul, lim, lo, cap2, icap2, vsn, m, l, alpha,
+                                   rescale, pa, phi, plo);
+}
+
+// S^T of one tile for all RB row blocks at once, their q operands read from
+// the lane-linear LDS copy (operand k of row block rb at qlds[(rb * QO + k) *
+// 64]).  The reads of every block's operands of k-step st + 1 are interleaved
+// with the MFMAs of step st (scheduling group barriers), so the LDS latency
+// hides under the MFMAs instead of stalling one wavefront per SIMD before
+// each of them.
+template <int DT, int MODE, int D, int RB>
+__device__ __forceinline__ void tile_dots_lds(const uint32_t* kw, const half8_t* qlds, float (&dot)[RB][4]) {
+  using G_ = Geo<DT, D>;
+  constexpr int QO = kQOps<DT, MODE, D>;
+  // opaque base: keeps the reads inside the tile loop (in registers the
+  // operands of every block would not fit)
+  int qb = 0;
+  asm volatile("" : "+v"(qb));
+  const half8_t* q = qlds + qb;
+  if constexpr (G_::IQK) {
+    constexpr int NSL = kQSlices<DT, MODE>;
+    i32x4_t acc[RB][NSL];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int k = 0; k < NSL; ++k) acc[rb][k] = i32x4_t{0, 0, 0, 0};
+    half8_t qv[2][RB][NSL];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int k = 0; k < NSL; ++k) qv[0][rb][k] = q[(rb * QO + k) * 64];
+#pragma unroll
+    for (int st = 0; st < G_::ISTEPS; ++st) {
+      const i32x4_t ka = k_operand_i8<DT, D>(kw, st);
+      if (st + 1 < G_::ISTEPS) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int k = 0; k < NSL; ++k) qv[(st + 1) & 1][rb][k] = q[(rb * QO + NSL * (st + 1) + k) * 64];
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int k = 0; k < NSL; ++k)
+          acc[rb][k] = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qv[st & 1][rb][k]), acc[rb][k]);
+    }
+    // schedule: step 0's reads, then each MFMA of step st after one read of
+    // step st + 1, so a step's reads complete under the previous step's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, RB * NSL, 0);
+#pragma unroll
+    for (int st = 0; st < G_::ISTEPS; ++st)
+#pragma unroll
+      for (int j = 0; j < RB * NSL; ++j) {
+        if (st + 1 < G_::ISTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (NSL == 3) {
+          const int dd[3] = {acc[rb][0][e], acc[rb][1][e], acc[rb][2][e]};
+          dot[rb][e] = q_dot<3>(dd);
+        } else {
+          const int dd[2] = {acc[rb][0][e], acc[rb][1][e]};
+          dot[rb][e] = q_dot<2>(dd);
+        }
+      }
+  } else {
+    float4_t s[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    half8_t qv[2][RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) qv[0][rb] = q[(rb * QO) * 64];
+#pragma unroll
+    for (int ks = 0; ks < G_::KSTEPS; ++ks) {
+      const half8_t ka = k_operand<DT, D>(kw, ks);
+      if (ks + 1 < G_::KSTEPS) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) qv[(ks + 1) & 1][rb] = q[(rb * QO + ks + 1) * 64];
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if constexpr (DT == kBf16)
+          s[rb] = mfma32_bf16(ka, qv[ks & 1][rb], s[rb]);
+        else
+          s[rb] = mfma32(ka, qv[ks & 1][rb], s[rb]);
+      }
+    }
+    // the same schedule as the integer path
+    __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);
+#pragma unroll
+    for (int ks = 0; ks < G_::KSTEPS; ++ks)
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        if (ks + 1 < G_::KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot[rb][e] = s[rb][e];
+  }
+}
+
 // O += P . V for one tile: unpack the lane's V column blocks (VD channels) and
 // accumulate every row block's weights into them.
 template <int DT, int VD, int RB>
@@ -595,54 +708,219 @@ __device__ __forceinline__ void accumulate_pv(const uint32_t (&vw)[4][Geo<DT, VD
   }
 }
 
+// The same P . V in two parts for the quantized caches: the whole tile's V
+// operands unpacked first (so the unpack can run beside the tile's S^T
+// MFMAs), then the MFMAs.
+template <int DT, int VD>
+struct VTile {
+  half4_t vb[Geo<DT, VD>::VDW][8];
+};
+
+template <int DT, int VD>
+__device__ __forceinline__ void unpack_v(const uint32_t (&vw)[4][Geo<DT, VD>::VDW], VTile<DT, VD>& V) {
+  static_assert(DT != kBf16, "unpack_v: quantized caches");
+#pragma unroll
+  for (int w = 0; w < Geo<DT, VD>::VDW; ++w) v_block<DT, VD>(vw, w, V.vb[w]);
+}
+
+template <int DT, int VD, int RB>
+__device__ __forceinline__ void pv_unpacked(const VTile<DT, VD>& V, const half4_t (&pa)[RB],
+                                            float4_t (&acc)[RB][Geo<DT, VD>::NCOL]) {
+  constexpr int NO = v_block_ops<DT, VD>();
+#pragma unroll
+  for (int w = 0; w < Geo<DT, VD>::VDW; ++w)
+#pragma unroll
+    for (int k0 = 0; k0 < NO; ++k0) {
+      const int k = DT == kInt4 ? (k0 % 2 == 0 ? k0 / 2 : 4 + k0 / 2) : k0;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[rb][v_column<DT, VD>(w, k)] = mfma16(pa[rb], V.vb[w][k], acc[rb][v_column<DT, VD>(w, k)]);
+    }
+}
+
+// One tile's softmax weights for every row block (pa, or phi + plo for the
+// bf16 cache), with the factors alpha (per row) and vfac (V reference) that
+// the accumulators take before its P . V.  Returns whether they must be
+// applied (wave-uniform): some row's reference or the V reference moved.  For
+// wide row sets it is also false while no weight of the wavefront has been
+// nonzero yet (l = 0 everywhere), as the accumulators are then still zero.
 template <int DT, int MODE, int D, int RB, bool CAP, bool QLDS>
-__device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int L, int n, int g,
+__device__ __forceinline__ bool tile_weights(const Tile<DT, D>& T, int t, int n, int g,
                                              const half8_t (&qb)[RB][kQOps<DT, MODE, D>],
-                                             const half8_t* qlds,
-                                             const float (&rowmul)[RB], const int (&lim)[RB],
-                                             const int (&lo)[RB], float cap2, float icap2,
-                                             WaveState<DT, D, RB>& W) {
-  using G_ = Geo<DT, D>;
+                                             const half8_t* qlds, const float (&rowmul)[RB],
+                                             const int (&lim)[RB], const int (&lo)[RB], float cap2,
+                                             float icap2, WaveState<DT, D, RB>& W, half4_t (&pa)[RB],
+                                             u32x2_t (&phi)[RB], u32x2_t (&plo)[RB], float (&alpha)[RB],
+                                             float& vfac) {
   const int tok0 = t * kTile;
   const int tbase = tok0 + 4 * g;
   const bool ok = T.ok != 0;
-  (void)L;
+  (void)n;
 
-  float vfac = 1.0f;
+  vfac = 1.0f;
   bool rescale = false;
   float vsn[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (kVRow) v_reference(T.vs4, W.vref, W.ivref, vfac, rescale, vsn);
 
-  half4_t pa[RB];
-  u32x2_t phi[RB], plo[RB];  // bf16 cache: p = hi + lo, each a bf16 A operand
-  float alpha[RB];
+  bool live = false;
+  if constexpr (RB * D > kSplitMaxAccColumns) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    // the q operand of k-step k: registers, or this wavefront's LDS copy (lane-
-    // linear, so conflict-free).  The LDS offset is made opaque so the compiler
-    // cannot hoist those reads out of the tile loop back into registers.
-    int qo = rb * kQOps<DT, MODE, D> * 64;
-    if constexpr (QLDS) asm volatile("" : "+v"(qo));
-    auto qop = [&](int k) { return QLDS ? qlds[qo + 64 * k] : qb[rb][k]; };
-    row_block_weights<DT, MODE, D, CAP>(T.kw, T.ks4, ok, tbase, qop, rowmul[rb], lim[rb], lo[rb],
-                                        cap2, icap2, vsn, W.m[rb], W.l[rb], alpha[rb], rescale,
-                                        pa[rb], phi[rb], plo[rb]);
+    for (int rb = 0; rb < RB; ++rb) live |= W.l[rb] != 0.0f;
   }
-  // Rescale the accumulators when some row's max grew or the V reference moved
-  // (rare after the first tiles).  Accumulator rows 4g+e belong to the P rows
-  // held by lanes 4g+e.
-  if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+  if constexpr (RB * D > kSplitMaxAccColumns) {
+    float dot[RB][4];
+    tile_dots_lds<DT, MODE, D, RB>(T.kw, qlds, dot);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      row_block_softmax<DT, MODE, CAP>(dot[rb], T.ks4, ok, tbase, rowmul[rb], lim[rb], lo[rb], cap2, icap2,
+                                       vsn, W.m[rb], W.l[rb], alpha[rb], rescale, pa[rb], phi[rb], plo[rb]);
+  } else {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float f[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] = __shfl(alpha[rb], 4 * g + e) * vfac;
-#pragma unroll
-      for (int c = 0; c < G_::NCOL; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) W.acc[rb][c][e] *= f[e];
+      // the q operand of k-step k: registers, or this wavefront's LDS copy
+      // (lane-linear, so conflict-free).  The LDS offset is made opaque so the
+      // compiler cannot hoist those reads out of the tile loop back into
+      // registers.
+      int qo = rb * kQOps<DT, MODE, D> * 64;
+      if constexpr (QLDS) asm volatile("" : "+v"(qo));
+      auto qop = [&](int k) { return QLDS ? qlds[qo + 64 * k] : qb[rb][k]; };
+      row_block_weights<DT, MODE, D, CAP>(T.kw, T.ks4, ok, tbase, qop, rowmul[rb], lim[rb], lo[rb],
+                                          cap2, icap2, vsn, W.m[rb], W.l[rb], alpha[rb], rescale,
+                                          pa[rb], phi[rb], plo[rb]);
     }
   }
+  if constexpr (RB * D > kSplitMaxAccColumns)
+    return __builtin_amdgcn_ballot_w64(rescale) != 0 && __builtin_amdgcn_ballot_w64(live) != 0;
+  else
+    return __builtin_amdgcn_ballot_w64(rescale) != 0;
+}
+
+// The tile loop's common case for wide row sets, free of branches so the
+// scheduler can interleave its vector work with the MFMAs: S^T of every row
+// block, the logits, and -- when no logit exceeds its row's reference by more
+// than kLazyHeadroom and (per-row V) no V scale exceeds the V reference -- the
+// weights and running sums.  Otherwise it returns true and changes nothing;
+// the caller then runs the tile through tile_weights, which moves the
+// references (so a wavefront's first tile, against m = -inf, always goes
+// there).
+template <int DT, int MODE, int D, int RB, bool CAP, class VT>
+__device__ __forceinline__ bool tile_fast(const Tile<DT, D>& T, int t, int g, const half8_t* qlds,
+                                          const float (&rowmul)[RB], const int (&lim)[RB], const int (&lo)[RB],
+                                          float cap2, float icap2, WaveState<DT, D, RB>& W, half4_t (&pa)[RB],
+                                          u32x2_t (&phi)[RB], u32x2_t (&plo)[RB], const VT* V) {
+  const int tbase = t * kTile + 4 * g;
+  const bool ok = T.ok != 0;
+  bool slow = false;
+  float vsn[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (kVRow) {
+    slow = fmaxf(fmaxf(T.vs4[0], T.vs4[1]), fmaxf(T.vs4[2], T.vs4[3])) > W.vref;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vsn[e] = T.vs4[e] * W.ivref;  // exact: ivref is a power of two
+  }
+  float dot[RB][4];
+  tile_dots_lds<DT, MODE, D, RB>(T.kw, qlds, dot);
+  (void)V;
+  float z[RB][4];
+  // largest logit over reference (m = -inf: +inf for a finite logit; NaN
+  // for -inf - -inf, which fmaxf drops)
+  float over = -INFINITY;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    tile_logits<MODE, CAP>(dot[rb], T.ks4, ok, tbase, rowmul[rb], lim[rb], lo[rb], cap2, icap2, z[rb]);
+    over = fmaxf(over, fmaxf(fmaxf(z[rb][0], z[rb][1]), fmaxf(z[rb][2], z[rb][3])) - W.m[rb]);
+  }
+  slow |= over > kLazyHeadroom;
+  if (__builtin_amdgcn_ballot_w64(slow) != 0) return true;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    // m is finite here unless every logit so far, these included, was -inf
+    const float msafe = (W.m[rb] == -INFINITY) ? 0.0f : W.m[rb];
+    float psum = 0.0f;
+    float pf[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = __builtin_amdgcn_exp2f(z[rb][e] - msafe);
+      psum += p;
+      pf[e] = kVRow ? p * vsn[e] : p;
+      pa[rb][e] = (_Float16)pf[e];
+    }
+    W.l[rb] += psum;
+    if constexpr (DT == kBf16) {
+      uint16_t h[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = f32_to_bf16(pf[e]);
+        lw[e] = f32_to_bf16(pf[e] - bf16_to_f32(h[e]));  // exact difference
+      }
+      phi[rb] = u32x2_t{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+      plo[rb] = u32x2_t{lw[0] | ((uint32_t)lw[1] << 16), lw[2] | ((uint32_t)lw[3] << 16)};
+    }
+  }
+  return false;
+}
+
+// The accumulators' rescale when the tile's reference moved: accumulator rows
+// 4g+e belong to the P rows held by lanes 4g+e.
+template <int DT, int D, int RB>
+__device__ __forceinline__ void rescale_acc(WaveState<DT, D, RB>& W, const float (&alpha)[RB], float vfac,
+                                            int g) {
+  if constexpr (RB * D > kSplitMaxAccColumns) {
+    // Wide row sets: their accumulators sit in the accumulation registers,
+    // which vector ALU instructions cannot multiply (a multiply made the
+    // compiler copy all of them out and spill).  The rows are scaled on the
+    // fp32 MFMA instead, which writes the accumulation registers directly:
+    // register e of a 16 x 16 block is the B operand (k = lane group) of
+    // v_mfma_f32_16x16x4_f32, and A_e holds row i's factor at k = (i - e) / 4
+    // when i = e (mod 4), so the sum over e gives every element its factor
+    // times itself plus exact zeros -- one rounding, as the multiply.  A
+    // scheduling barrier after each block keeps its operand copies to 4
+    // registers at a time.
+    const int n = __lane_id() & 15;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float fi = alpha[rb] * vfac;  // row n's factor
+      float ae[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ae[e] = n == 4 * g + e ? fi : 0.0f;
+#pragma unroll
+      for (int c = 0; c < Geo<DT, D>::NCOL; ++c) {
+        __builtin_amdgcn_sched_barrier(0);
+        float4_t d = __builtin_amdgcn_mfma_f32_16x16x4f32(ae[0], W.acc[rb][c][0], float4_t{0.f, 0.f, 0.f, 0.f},
+                                                          0, 0, 0);
+#pragma unroll
+        for (int e = 1; e < 4; ++e) d = __builtin_amdgcn_mfma_f32_16x16x4f32(ae[e], W.acc[rb][c][e], d, 0, 0, 0);
+        W.acc[rb][c] = d;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    return;
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float f[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __shfl(alpha[rb], 4 * g + e) * vfac;
+#pragma unroll
+    for (int c = 0; c < Geo<DT, D>::NCOL; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) W.acc[rb][c][e] *= f[e];
+  }
+}
+
+// One tile: weights, the rescale when needed (rare after the first tiles),
+// then O += P . V.
+template <int DT, int MODE, int D, int RB, bool CAP, bool QLDS>
+__device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int n, int g,
+                                             const half8_t (&qb)[RB][kQOps<DT, MODE, D>],
+                                             const half8_t* qlds, const float (&rowmul)[RB],
+                                             const int (&lim)[RB], const int (&lo)[RB], float cap2,
+                                             float icap2, WaveState<DT, D, RB>& W) {
+  half4_t pa[RB];
+  u32x2_t phi[RB], plo[RB];  // bf16 cache: p = hi + lo, each a bf16 A operand
+  float alpha[RB], vfac;
+  if (tile_weights<DT, MODE, D, RB, CAP, QLDS>(T, t, n, g, qb, qlds, rowmul, lim, lo, cap2, icap2, W, pa,
+                                               phi, plo, alpha, vfac))
+    rescale_acc<DT, D, RB>(W, alpha, vfac, g);
   accumulate_pv<DT, D, RB>(T.vw, pa, phi, plo, W.acc);
 }
 
@@ -901,13 +1179,18 @@ struct Knobs {
   // in registers they spilled 13-45 of them to scratch).  (For the 8-bit
   // caches with two slices this measured slower on MI355X: 64K int8
   // 28.9 -> 30.5 us, and 3 tiles in flight with it 33.6 us, with spills.)
+  // Wide row sets (RB * D above kSplitMaxAccColumns) always read it from LDS.
+  static constexpr bool WIDE = RB * D > kSplitMaxAccColumns;
   static constexpr bool QLDS =
-      DT == kBf16 || (DT == kInt8 && MODE == kPerChannel && RB * D >= kSplitMaxAccColumns);
-  static constexpr int NB = kSplitTilesInFlight;
+      WIDE || DT == kBf16 || (DT == kInt8 && MODE == kPerChannel && RB * D >= kSplitMaxAccColumns);
+  static constexpr int NB = WIDE ? kSplitWideTilesInFlight : kSplitTilesInFlight;
   static constexpr int WAVES_PER_EU = WPE;
-  // merge buffers: one per wavefront (RB * D <= 256 keeps them within 64 KiB)
+  static_assert(!WIDE || WPE == 1, "wide row sets need one wavefront per SIMD");
+  // merge buffers: one per wavefront, MRB row blocks at a time (64 KiB)
   static constexpr int MERGE_BUFS = kWaves;
-  static_assert(MERGE_BUFS * 16 * RB * D * 4 <= 65536, "merge buffers exceed 64 KiB");
+  static constexpr int MRB = WIDE ? kSplitMaxAccColumns / D : RB;
+  static constexpr int MPASS = (RB + MRB - 1) / MRB;
+  static_assert(MERGE_BUFS * 16 * MRB * D * 4 <= 65536, "merge buffers exceed 64 KiB");
 };
 
 // Variants whose accumulators fill a wavefront and whose rows exceed 128 bytes
@@ -928,12 +1211,15 @@ split_decode_kernel(SplitArgs a) {
   constexpr int RP = 16 * RB;  // padded query rows
   constexpr int NB = K_::NB;
 
-  // q rows staged as bf16 (and, with QLDS, each wavefront's copy of its q
-  // operand after them), then the merge buffers
-  __shared__ __attribute__((aligned(16))) float smem[K_::MERGE_BUFS * RP * D];
+  // q rows staged as bf16 and the workgroup's q operand after them, then the
+  // merge buffers
   constexpr int kQStageBytes = (RP * kQStride<D> * 2 + 255) / 256 * 256;
   constexpr int kQOpBytes = RB * kQOps<DT, MODE, D> * 64 * 16;  // the workgroup's q operand
-  static_assert(kQStageBytes + kQOpBytes <= (int)sizeof(smem), "the q operand does not fit the merge buffers");
+  constexpr int kMergeFloats = K_::MERGE_BUFS * 16 * K_::MRB * D;
+  constexpr int kSmemFloats = kMergeFloats > (kQStageBytes + kQOpBytes) / 4 ? kMergeFloats
+                                                                            : (kQStageBytes + kQOpBytes) / 4;
+  __shared__ __attribute__((aligned(16))) float smem[kSmemFloats];
+  static_assert(kSmemFloats * 4 <= 65536, "the q operand does not fit 64 KiB");
   __shared__ float s_pmax[kWaves * RP];  // row maxima of each wavefront's k-steps
   __shared__ float s_m[kWaves][RP];
   __shared__ float s_l[kWaves][RP];
@@ -1074,16 +1360,95 @@ split_decode_kernel(SplitArgs a) {
   W.vref = 0x1p-126f;  // smallest normal: any nonzero scale above it raises the reference
   W.ivref = 0x1p126f;
 
-  for (int t = t0, k = 0; t < te;) {
+  if constexpr (!K_::WIDE) {
+    for (int t = t0, k = 0; t < te;) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (t < te)
-        process_tile<DT, MODE, D, RB, CAP, K_::QLDS>(buf[i], t, L, n, g, qb, qlds, rowmul, lim, lo,
-                                                     cap2, icap2, W);
-      load_tile<DT, MODE, D>(a, t + NB * kWaves, t + NB * kWaves < te, table_entry(tbl, k + NB), L, n,
-                             g, buf[i]);
-      t += kWaves;
-      ++k;
+      for (int i = 0; i < NB; ++i) {
+        if (t < te)
+          process_tile<DT, MODE, D, RB, CAP, K_::QLDS>(buf[i], t, n, g, qb, qlds, rowmul, lim, lo, cap2,
+                                                       icap2, W);
+        load_tile<DT, MODE, D>(a, t + NB * kWaves, t + NB * kWaves < te, table_entry(tbl, k + NB), L, n,
+                               g, buf[i]);
+        t += kWaves;
+        ++k;
+      }
+    }
+  } else {
+    // Wide row sets: the accumulators live in the accumulation registers,
+    // which vector ALU instructions cannot multiply, so the rare reference
+    // moves and rescales run outside the tile loop (inside it, the compiler
+    // copied every accumulator out and back on every tile).  The loop runs
+    // tile_fast and leaves at a tile that needs a move, before its P . V and
+    // its slot's next load; the tail below takes that tile and the rest of the
+    // ring through the general step, so the loop always resumes at the ring's
+    // first slot with the usual loads in flight.
+    static_assert(!K_::WIDE || K_::QLDS, "wide row sets read q from LDS");
+    // The references start at the first tile's row maxima (and, per-row V,
+    // its largest V scale), so that tile and the many like it stay in the
+    // loop; the accumulators are still zero, so nothing is rescaled.
+    if (t0 < te) {
+      float dot[RB][4];
+      tile_dots_lds<DT, MODE, D, RB>(buf[0].kw, qlds, dot);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float z[4];
+        tile_logits<MODE, CAP>(dot[rb], buf[0].ks4, buf[0].ok != 0, t0 * kTile + 4 * g, rowmul[rb], lim[rb],
+                               lo[rb], cap2, icap2, z);
+        W.m[rb] = group_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+      }
+      if constexpr (kVRow) {
+        float vfac, vsn[4];
+        bool moved = false;
+        v_reference(buf[0].vs4, W.vref, W.ivref, vfac, moved, vsn);
+      }
+    }
+    int t = t0, k = 0;
+    while (t < te) {
+      int hit = -1;
+      do {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          if (t >= te) break;
+          half4_t pa[RB];
+          u32x2_t phi[RB], plo[RB];
+          if constexpr (DT == kBf16) {
+            if (tile_fast<DT, MODE, D, RB, CAP>(buf[i], t, g, qlds, rowmul, lim, lo, cap2, icap2, W, pa, phi,
+                                                plo, (const VTile<kInt8, D>*)nullptr)) {
+              hit = i;
+              break;
+            }
+            accumulate_pv<DT, D, RB>(buf[i].vw, pa, phi, plo, W.acc);
+          } else {
+            VTile<DT, D> V;
+            unpack_v<DT, D>(buf[i].vw, V);
+            if (tile_fast<DT, MODE, D, RB, CAP>(buf[i], t, g, qlds, rowmul, lim, lo, cap2, icap2, W, pa, phi,
+                                                plo, &V)) {
+              hit = i;
+              break;
+            }
+            pv_unpacked<DT, D, RB>(V, pa, W.acc);
+          }
+          load_tile<DT, MODE, D>(a, t + NB * kWaves, t + NB * kWaves < te, table_entry(tbl, k + NB), L, n,
+                                 g, buf[i]);
+          t += kWaves;
+          ++k;
+        }
+      } while (hit < 0 && t < te);
+      if (hit < 0) break;
+      // the tile that left the loop and the rest of the ring through the
+      // general step (references moved, accumulators rescaled)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (i >= hit) {
+          if (t < te)
+            process_tile<DT, MODE, D, RB, CAP, true>(buf[i], t, n, g, qb, qlds, rowmul, lim, lo, cap2, icap2,
+                                                     W);
+          load_tile<DT, MODE, D>(a, t + NB * kWaves, t + NB * kWaves < te, table_entry(tbl, k + NB), L, n,
+                                 g, buf[i]);
+          t += kWaves;
+          ++k;
+        }
+      }
     }
   }
 
@@ -1141,49 +1506,66 @@ split_decode_kernel(SplitArgs a) {
   // hit distinct banks.
   constexpr int NCH = G_::NCOL / 4;                 // 16-byte chunks per lane and row
   constexpr int ROT = G_::NCOL >= 16 ? 4 : (G_::NCOL == 8 ? 8 : 16);
-  {
-    float* ob = smem + (size_t)wave * RP * D;
+  // Wide row sets merge MRB row blocks per pass (the buffers hold 64 KiB).
+  constexpr int MRB = K_::MRB;
+  constexpr int MR = 16 * MRB;  // rows per pass
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+  for (int p = 0; p < K_::MPASS; ++p) {
+    if (p > 0) __syncthreads();  // the previous pass's readback is done
+    float* ob = smem + (size_t)wave * MR * D;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rb * 16 + 4 * g + e;
-        if (r < Rw) {
+    for (int rr = 0; rr < MRB; ++rr) {
+      const int rb = p * MRB + rr;
+      if (rb < RB) {
 #pragma unroll
-          for (int k = 0; k < NCH; ++k) {
-            float4_t v;
+        for (int e = 0; e < 4; ++e) {
+          const int r = rb * 16 + 4 * g + e;
+          if (r < Rw) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = W.acc[rb][col_of<DT, D>(4 * k + i)][e];
-            const int slot = (k + n / ROT) % NCH;
-            *reinterpret_cast<float4_t*>(ob + r * D + G_::NCOL * n + 4 * slot) = v;
+            for (int k = 0; k < NCH; ++k) {
+              float4_t v;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = W.acc[rb][col_of<DT, D>(4 * k + i)][e];
+              const int slot = (k + n / ROT) % NCH;
+              *reinterpret_cast<float4_t*>(ob + (r - p * MR) * D + G_::NCOL * n + 4 * slot) = v;
+            }
           }
         }
       }
-  }
-  __syncthreads();
+    }
+    __syncthreads();
 
-  for (int idx = tid * 4; idx < Rw * D; idx += 256 * 4) {
-    const int r = idx / D, d = idx % D;
-    int jn, k;
-    group_owner<DT, D>(d, jn, k);
-    const int off = r * D + G_::NCOL * jn + 4 * ((k + jn / ROT) % NCH);
-    float4_t v = s_f[0][r] * *reinterpret_cast<const float4_t*>(smem + off);
+    const int rn = min(MR, Rw - p * MR);  // rows of this pass
+    for (int idx = tid * 4; idx < rn * D; idx += 256 * 4) {
+      const int lr = idx / D, d = idx % D, r = p * MR + lr;
+      int jn, k;
+      group_owner<DT, D>(d, jn, k);
+      const int off = lr * D + G_::NCOL * jn + 4 * ((k + jn / ROT) % NCH);
+      float4_t v = s_f[0][r] * *reinterpret_cast<const float4_t*>(smem + off);
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-      v += s_f[w][r] * *reinterpret_cast<const float4_t*>(smem + (size_t)w * RP * D + off);
-    *reinterpret_cast<float4_t*>(a.ws_o + (((size_t)hkv * a.R + row0 + r) * a.S + slot) * D + d) = v;
+      for (int w = 1; w < kWaves; ++w)
+        v += s_f[w][r] * *reinterpret_cast<const float4_t*>(smem + (size_t)w * MR * D + off);
+      *reinterpret_cast<float4_t*>(a.ws_o + (((size_t)hkv * a.R + row0 + r) * a.S + slot) * D + d) = v;
+    }
   }
 }
 
+#define KVQ_CAT2(a, b, c, d) a##b##_##c##_##d
+#define KVQ_CAT(a, b, c, d) KVQ_CAT2(a, b, c, d)
+
+#if !KVQ_WIDE
 template <int DT, int MODE, int D, int RB>
 hipError_t launch_one(const SplitArgs& a, int B, hipStream_t st) {
-  // Only variants whose accumulators fit a wavefront's registers are built: the
-  // host gives wider row sets one workgroup per 16-row block instead.
+  // Row sets whose accumulators exceed a two-wavefronts-per-SIMD budget run in
+  // the unit's wide variants; the host gives wider ones one workgroup per
+  // 16-row block instead.
   (void)B;
-  if constexpr (RB * D > kSplitMaxAccColumns) {
+  if constexpr (RB * D > kSplitMaxWideColumns) {
     (void)a;
     (void)st;
     return hipErrorInvalidValue;
+  } else if constexpr (RB * D > kSplitMaxAccColumns) {
+    return KVQ_CAT(launch_split_wide_, KVQ_DTYPE, KVQ_MODE, KVQ_VROW)(D, RB, a, st);
   } else {
     const int gx = a.RBN > 1 ? (a.S + 7) / 8 * 8 * a.RBN : a.S;
     dim3 grid(gx, a.c.Hkv, 1);
@@ -1215,12 +1597,24 @@ hipError_t launch_d(int RB, const SplitArgs& a, int B, hipStream_t st) {
     default: return hipErrorInvalidValue;
   }
 }
+#else
+// A wide row set: one workgroup per chunk slot, one wavefront per SIMD.
+template <int DT, int MODE, int D, int RB>
+hipError_t launch_wide(const SplitArgs& a, hipStream_t st) {
+  static_assert(RB * D > kSplitMaxAccColumns && RB * D <= kSplitMaxWideColumns, "not a wide row set");
+  if (a.RBN != 1) return hipErrorInvalidValue;
+  dim3 grid(a.S, a.c.Hkv, 1);
+  if (a.softcap > 0.0f)
+    hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, true, 1>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, false, 1>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+#endif
 
 }  // namespace
 
-#define KVQ_CAT2(a, b, c, d) a##b##_##c##_##d
-#define KVQ_CAT(a, b, c, d) KVQ_CAT2(a, b, c, d)
-
+#if !KVQ_WIDE
 hipError_t KVQ_CAT(launch_split_, KVQ_DTYPE, KVQ_MODE, KVQ_VROW)(int D, int RB, const SplitArgs& a,
                                                                   int B, hipStream_t st) {
   switch (D) {
@@ -1230,5 +1624,15 @@ hipError_t KVQ_CAT(launch_split_, KVQ_DTYPE, KVQ_MODE, KVQ_VROW)(int D, int RB, 
     default: return hipErrorInvalidValue;
   }
 }
+#else
+hipError_t KVQ_CAT(launch_split_wide_, KVQ_DTYPE, KVQ_MODE, KVQ_VROW)(int D, int RB, const SplitArgs& a,
+                                                                       hipStream_t st) {
+  if (D == 128 && RB == 3) return launch_wide<KVQ_DTYPE, KVQ_MODE, 128, 3>(a, st);
+  if (D == 128 && RB == 4) return launch_wide<KVQ_DTYPE, KVQ_MODE, 128, 4>(a, st);
+  if (D == 256 && RB == 2) return launch_wide<KVQ_DTYPE, KVQ_MODE, 256, 2>(a, st);
+  if (D == 256 && RB == 3) return launch_wide<KVQ_DTYPE, KVQ_MODE, 256, 3>(a, st);
+  return hipErrorInvalidValue;
+}
+#endif
 
 }  // namespace kvq

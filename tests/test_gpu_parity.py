@@ -229,6 +229,81 @@ def test_gqa_and_query_tokens(G, Tq):
     gu.run_and_check(w, f"G={G} Tq={Tq}")
 
 
+# Wide row sets: 17-48 query rows per KV head at D 256 and 33-64 at D 128
+# (row blocks x head_dim of 512 or 768 accumulator columns) run as one
+# workgroup per chunk with one wavefront per SIMD, which unpacks every tile
+# once for all rows and rescales its accumulators outside the tile loop.
+WIDE_CASES = [
+    # dtype, mode, D, G, Tq, paged, lens, softcap, window
+    (INT8, PER_ROW, 256, 6, 8, True, [8, 700, 3000], 0.0, 0),      # 48 rows
+    (INT8, PER_CHANNEL, 256, 4, 5, False, [2100, 40], 0.0, 0),     # 20 rows
+    (INT4, PER_ROW, 256, 6, 8, False, [1900, 9], 0.0, 0),
+    (INT4, PER_TENSOR, 256, 5, 8, True, [77, 2600], 0.0, 0),       # 40 rows
+    (FP8, PER_TENSOR, 256, 6, 8, True, [1500, 3100], 0.0, 0),
+    (FP8, PER_ROW, 256, 8, 3, False, [5000], 0.0, 0),               # 24 rows
+    (INT8, PER_TENSOR, 128, 8, 5, True, [33, 4000], 0.0, 0),       # 40 rows
+    (INT4, PER_CHANNEL, 128, 8, 8, False, [2000, 500], 0.0, 0),    # 64 rows
+    (FP8, PER_CHANNEL, 128, 7, 5, True, [900, 1], 0.0, 0),         # 35 rows
+    (ki.BF16, 0, 256, 6, 8, True, [1200, 2500], 0.0, 0),
+    (ki.BF16, 0, 128, 8, 6, False, [3000], 0.0, 0),                # 48 rows
+    (INT8, PER_ROW, 256, 6, 8, True, [2000, 4100], 30.0, 0),       # soft cap variant
+    (INT4, PER_CHANNEL, 256, 6, 8, True, [3000, 700], 2.0, 500),
+    (FP8, PER_ROW, 128, 6, 8, False, [2500], 0.0, 1000),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[f"case{i}" for i in range(len(WIDE_CASES))])
+def test_wide_row_sets(case):
+    dt, md, D, G, Tq, paged, lens, cap, win = case
+    w = ki.random_workload(3500 + sum(lens) + 7 * G + Tq + D, B=len(lens), Hkv=2, G=G, D=D, Tq=Tq,
+                           lens=lens, dtype=dt, mode=md, block_size=16 if paged else None,
+                           sink=(G + Tq) % 2 == 0, softcap=cap, window=win)
+    if cap or win:
+        _attend_ex_and_check(w, f"wide {case}")
+    else:
+        gu.run_and_check(w, f"wide {case}")
+
+
+def _ramp_workload(seed, dt, md, D, G, Tq, lens, per_tile):
+    """Every query head of a KV head looks along one direction u (plus noise) and
+    key t is (per_tile / 16) * t * u / |u| (plus noise): logits climb by about
+    per_tile (natural units) every 16 tokens.  A wavefront reads every fourth
+    tile, so with per_tile = 2 its logits climb by about 11.5 in log2 units from
+    one of its tiles to the next, past the reference's headroom of 8: the
+    reference of every row moves on every tile the wavefront reads."""
+    w = ki.random_workload(seed, B=len(lens), Hkv=2, G=G, D=D, Tq=Tq, lens=lens, dtype=dt, mode=md,
+                           block_size=16)
+    g = torch.Generator().manual_seed(seed + 99)
+    q = w.q.float()
+    k = w.k.float()
+    L = k.shape[1]
+    for h in range(w.Hkv):
+        u = torch.randn(D, generator=g)
+        u = u / u.norm()
+        for j in range(G):
+            q[:, :, h * G + j] = 0.2 * q[:, :, h * G + j] + u * D ** 0.5
+        ramp = (per_tile / 16.0) * torch.arange(L, dtype=torch.float32)
+        k[:, :, h] = 0.2 * k[:, :, h] + ramp.view(1, L, 1) * u.view(1, 1, D)
+    w.q = q.to(torch.bfloat16)
+    w.k = k.to(torch.bfloat16)
+    return w
+
+
+@pytest.mark.parametrize("dt,md,D,G,Tq", [(INT8, PER_ROW, 256, 6, 8), (INT4, PER_ROW, 256, 4, 5),
+                                          (FP8, PER_ROW, 128, 8, 5), (ki.BF16, 0, 256, 6, 8)])
+def test_wide_row_sets_rescale_every_tile(dt, md, D, G, Tq):
+    w = _ramp_workload(3900 + 10 * dt + D, dt, md, D, G, Tq, [1100, 2900], per_tile=2.0)
+    gu.run_and_check(w, f"wide rescale ramp dt={dt} D={D} G={G} Tq={Tq}")
+
+
+def test_rescale_every_tile_narrow_row_sets():
+    """The same climbing logits through the two-wavefronts-per-SIMD variants."""
+    w = _ramp_workload(3950, INT8, PER_ROW, 256, 6, 1, [1100, 2900], per_tile=2.0)
+    gu.run_and_check(w, "rescale ramp, 6 rows")
+    w = _ramp_workload(3951, INT4, PER_ROW, 128, 8, 2, [3000], per_tile=2.0)
+    gu.run_and_check(w, "rescale ramp, 16 rows")
+
+
 @pytest.mark.parametrize("lens", [[1], [15], [16], [17], [0, 5], [2, 1000], [4095, 4096, 4097]])
 def test_ragged_lengths(lens):
     w = ki.random_workload(4000 + sum(lens), B=len(lens), Hkv=2, G=4, D=128, Tq=1, lens=lens,
