@@ -36,6 +36,8 @@
 //   into two bf16 terms hi + lo (hi = bf16(p), lo = bf16(p - hi), together
 //   within 2^-17 of p) and both go through v_mfma_f32_16x16x16_bf16.
 
+#include <utility>
+
 #include "kvq_quant.h"
 #include "kvq_sched.h"
 
@@ -59,6 +61,16 @@ namespace {
 // static V scale (per tensor or per channel) is applied by the combine.  The
 // template MODE is the K side's scale mode.
 constexpr bool kVRow = KVQ_VROW != 0;
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <int DT, int D>
 struct Geo {
@@ -569,14 +581,24 @@ __device__ __forceinline__ void row_block_weights(const uint32_t* kw, const floa
                                    rescale, pa, phi, plo);
 }
 
+// S^T accumulators of one tile for all RB row blocks: exact int32 per query
+// slice for the integer caches, fp32 otherwise.
+template <int DT, int MODE, int D, int RB>
+struct QKAcc {
+  static constexpr bool IQK = Geo<DT, D>::IQK;
+  static constexpr int NSL = IQK ? kQSlices<DT, MODE> : 1;
+  i32x4_t ia[RB][IQK ? NSL : 1];
+  float4_t fa[RB];
+};
+
 // S^T of one tile for all RB row blocks at once, their q operands read from
 // the lane-linear LDS copy (operand k of row block rb at qlds[(rb * QO + k) *
 // 64]).  The reads of every block's operands of k-step st + 1 are interleaved
 // with the MFMAs of step st (scheduling group barriers), so the LDS latency
 // hides under the MFMAs instead of stalling one wavefront per SIMD before
-// each of them.
+// each of them.  Only issues the MFMAs: qk_dots reads the results.
 template <int DT, int MODE, int D, int RB>
-__device__ __forceinline__ void tile_dots_lds(const uint32_t* kw, const half8_t* qlds, float (&dot)[RB][4]) {
+__device__ __forceinline__ void qk_issue(const uint32_t* kw, const half8_t* qlds, QKAcc<DT, MODE, D, RB>& A) {
   using G_ = Geo<DT, D>;
   constexpr int QO = kQOps<DT, MODE, D>;
   // opaque base: keeps the reads inside the tile loop (in registers the
@@ -586,11 +608,10 @@ __device__ __forceinline__ void tile_dots_lds(const uint32_t* kw, const half8_t*
   const half8_t* q = qlds + qb;
   if constexpr (G_::IQK) {
     constexpr int NSL = kQSlices<DT, MODE>;
-    i32x4_t acc[RB][NSL];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int k = 0; k < NSL; ++k) acc[rb][k] = i32x4_t{0, 0, 0, 0};
+      for (int k = 0; k < NSL; ++k) A.ia[rb][k] = i32x4_t{0, 0, 0, 0};
     half8_t qv[2][RB][NSL];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -609,7 +630,7 @@ __device__ __forceinline__ void tile_dots_lds(const uint32_t* kw, const half8_t*
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int k = 0; k < NSL; ++k)
-          acc[rb][k] = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qv[st & 1][rb][k]), acc[rb][k]);
+          A.ia[rb][k] = mfma64_i8(ka, __builtin_bit_cast(i32x4_t, qv[st & 1][rb][k]), A.ia[rb][k]);
     }
     // schedule: step 0's reads, then each MFMA of step st after one read of
     // step st + 1, so a step's reads complete under the previous step's MFMAs
@@ -621,22 +642,9 @@ __device__ __forceinline__ void tile_dots_lds(const uint32_t* kw, const half8_t*
         if (st + 1 < G_::ISTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (NSL == 3) {
-          const int dd[3] = {acc[rb][0][e], acc[rb][1][e], acc[rb][2][e]};
-          dot[rb][e] = q_dot<3>(dd);
-        } else {
-          const int dd[2] = {acc[rb][0][e], acc[rb][1][e]};
-          dot[rb][e] = q_dot<2>(dd);
-        }
-      }
   } else {
-    float4_t s[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) s[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) A.fa[rb] = float4_t{0.f, 0.f, 0.f, 0.f};
     half8_t qv[2][RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) qv[0][rb] = q[(rb * QO) * 64];
@@ -650,9 +658,9 @@ __device__ __forceinline__ void tile_dots_lds(const uint32_t* kw, const half8_t*
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if constexpr (DT == kBf16)
-          s[rb] = mfma32_bf16(ka, qv[ks & 1][rb], s[rb]);
+          A.fa[rb] = mfma32_bf16(ka, qv[ks & 1][rb], A.fa[rb]);
         else
-          s[rb] = mfma32(ka, qv[ks & 1][rb], s[rb]);
+          A.fa[rb] = mfma32(ka, qv[ks & 1][rb], A.fa[rb]);
       }
     }
     // the same schedule as the integer path
@@ -664,11 +672,39 @@ __device__ __forceinline__ void tile_dots_lds(const uint32_t* kw, const half8_t*
         if (ks + 1 < G_::KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
+  }
+}
+
+// The dot products of qk_issue's accumulators (in the q operand's units).
+template <int DT, int MODE, int D, int RB>
+__device__ __forceinline__ void qk_dots(const QKAcc<DT, MODE, D, RB>& A, float (&dot)[RB][4]) {
+  if constexpr (Geo<DT, D>::IQK) {
+    constexpr int NSL = kQSlices<DT, MODE>;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dot[rb][e] = s[rb][e];
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (NSL == 3) {
+          const int dd[3] = {A.ia[rb][0][e], A.ia[rb][1][e], A.ia[rb][2][e]};
+          dot[rb][e] = q_dot<3>(dd);
+        } else {
+          const int dd[2] = {A.ia[rb][0][e], A.ia[rb][1][e]};
+          dot[rb][e] = q_dot<2>(dd);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot[rb][e] = A.fa[rb][e];
   }
+}
+
+template <int DT, int MODE, int D, int RB>
+__device__ __forceinline__ void tile_dots_lds(const uint32_t* kw, const half8_t* qlds, float (&dot)[RB][4]) {
+  QKAcc<DT, MODE, D, RB> A;
+  qk_issue<DT, MODE, D, RB>(kw, qlds, A);
+  qk_dots<DT, MODE, D, RB>(A, dot);
 }
 
 // O += P . V for one tile: unpack the lane's V column blocks (VD channels) and
@@ -796,37 +832,32 @@ __device__ __forceinline__ bool tile_weights(const Tile<DT, D>& T, int t, int n,
 }
 
 // The tile loop's common case for wide row sets, free of branches so the
-// scheduler can interleave its vector work with the MFMAs: S^T of every row
-// block, the logits, and -- when no logit exceeds its row's reference by more
-// than kLazyHeadroom and (per-row V) no V scale exceeds the V reference -- the
-// weights and running sums.  Otherwise it returns true and changes nothing;
-// the caller then runs the tile through tile_weights, which moves the
-// references (so a wavefront's first tile, against m = -inf, always goes
-// there).
-template <int DT, int MODE, int D, int RB, bool CAP, class VT>
-__device__ __forceinline__ bool tile_fast(const Tile<DT, D>& T, int t, int g, const half8_t* qlds,
-                                          const float (&rowmul)[RB], const int (&lim)[RB], const int (&lo)[RB],
-                                          float cap2, float icap2, WaveState<DT, D, RB>& W, half4_t (&pa)[RB],
-                                          u32x2_t (&phi)[RB], u32x2_t (&plo)[RB], const VT* V) {
+// scheduler can interleave its vector work with the MFMAs: from the tile's
+// S^T dot products, the logits, and -- when no logit exceeds its row's
+// reference by more than kLazyHeadroom and (per-row V) no V scale exceeds the
+// V reference -- the weights and running sums.  Otherwise it returns true and
+// changes nothing; the caller then takes the tile through weights_general,
+// which moves the references.
+template <int DT, int MODE, int RB, bool CAP, class WS>
+__device__ __forceinline__ bool weights_fast(const float (&dot)[RB][4], const float4_t& ks4, const float4_t& vs4,
+                                             bool ok, int t, int g, const float (&rowmul)[RB],
+                                             const int (&lim)[RB], const int (&lo)[RB], float cap2, float icap2,
+                                             WS& W, half4_t (&pa)[RB], u32x2_t (&phi)[RB], u32x2_t (&plo)[RB]) {
   const int tbase = t * kTile + 4 * g;
-  const bool ok = T.ok != 0;
   bool slow = false;
   float vsn[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (kVRow) {
-    slow = fmaxf(fmaxf(T.vs4[0], T.vs4[1]), fmaxf(T.vs4[2], T.vs4[3])) > W.vref;
+    slow = fmaxf(fmaxf(vs4[0], vs4[1]), fmaxf(vs4[2], vs4[3])) > W.vref;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vsn[e] = T.vs4[e] * W.ivref;  // exact: ivref is a power of two
+    for (int e = 0; e < 4; ++e) vsn[e] = vs4[e] * W.ivref;  // exact: ivref is a power of two
   }
-  float dot[RB][4];
-  tile_dots_lds<DT, MODE, D, RB>(T.kw, qlds, dot);
-  (void)V;
   float z[RB][4];
   // largest logit over reference (m = -inf: +inf for a finite logit; NaN
   // for -inf - -inf, which fmaxf drops)
   float over = -INFINITY;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    tile_logits<MODE, CAP>(dot[rb], T.ks4, ok, tbase, rowmul[rb], lim[rb], lo[rb], cap2, icap2, z[rb]);
+    tile_logits<MODE, CAP>(dot[rb], ks4, ok, tbase, rowmul[rb], lim[rb], lo[rb], cap2, icap2, z[rb]);
     over = fmaxf(over, fmaxf(fmaxf(z[rb][0], z[rb][1]), fmaxf(z[rb][2], z[rb][3])) - W.m[rb]);
   }
   slow |= over > kLazyHeadroom;
@@ -857,6 +888,17 @@ __device__ __forceinline__ bool tile_fast(const Tile<DT, D>& T, int t, int g, co
     }
   }
   return false;
+}
+
+template <int DT, int MODE, int D, int RB, bool CAP>
+__device__ __forceinline__ bool tile_fast(const Tile<DT, D>& T, int t, int g, const half8_t* qlds,
+                                          const float (&rowmul)[RB], const int (&lim)[RB], const int (&lo)[RB],
+                                          float cap2, float icap2, WaveState<DT, D, RB>& W, half4_t (&pa)[RB],
+                                          u32x2_t (&phi)[RB], u32x2_t (&plo)[RB]) {
+  float dot[RB][4];
+  tile_dots_lds<DT, MODE, D, RB>(T.kw, qlds, dot);
+  return weights_fast<DT, MODE, RB, CAP>(dot, T.ks4, T.vs4, T.ok != 0, t, g, rowmul, lim, lo, cap2, icap2, W, pa,
+                                         phi, plo);
 }
 
 // The accumulators' rescale when the tile's reference moved: accumulator rows
@@ -905,6 +947,34 @@ __device__ __forceinline__ void rescale_acc(WaveState<DT, D, RB>& W, const float
 #pragma unroll
       for (int e = 0; e < 4; ++e) W.acc[rb][c][e] *= f[e];
   }
+}
+
+// The general step of a wide row set's tile from its S^T dot products: moves
+// the references (row maxima, V reference) as tile_weights does and rescales
+// the accumulators when it moved one and some weight of the wavefront has
+// been nonzero.
+template <int DT, int MODE, int D, int RB, bool CAP>
+__device__ __forceinline__ void weights_general(const float (&dot)[RB][4], const float4_t& ks4,
+                                                const float4_t& vs4, bool ok, int t, int g,
+                                                const float (&rowmul)[RB], const int (&lim)[RB],
+                                                const int (&lo)[RB], float cap2, float icap2,
+                                                WaveState<DT, D, RB>& W, half4_t (&pa)[RB],
+                                                u32x2_t (&phi)[RB], u32x2_t (&plo)[RB]) {
+  const int tbase = t * kTile + 4 * g;
+  float vfac = 1.0f;
+  bool rescale = false;
+  float vsn[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (kVRow) v_reference(vs4, W.vref, W.ivref, vfac, rescale, vsn);
+  bool live = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) live |= W.l[rb] != 0.0f;
+  float alpha[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    row_block_softmax<DT, MODE, CAP>(dot[rb], ks4, ok, tbase, rowmul[rb], lim[rb], lo[rb], cap2, icap2, vsn,
+                                     W.m[rb], W.l[rb], alpha[rb], rescale, pa[rb], phi[rb], plo[rb]);
+  if (__builtin_amdgcn_ballot_w64(rescale) != 0 && __builtin_amdgcn_ballot_w64(live) != 0)
+    rescale_acc<DT, D, RB>(W, alpha, vfac, g);
 }
 
 // One tile: weights, the rescale when needed (rare after the first tiles),
@@ -1183,7 +1253,12 @@ struct Knobs {
   static constexpr bool WIDE = RB * D > kSplitMaxAccColumns;
   static constexpr bool QLDS =
       WIDE || DT == kBf16 || (DT == kInt8 && MODE == kPerChannel && RB * D >= kSplitMaxAccColumns);
-  static constexpr int NB = WIDE ? kSplitWideTilesInFlight : kSplitTilesInFlight;
+  // Wide row sets of the quantized caches pipeline the tile loop by one tile
+  // -- except where the accumulators fill the accumulation registers (RB * D
+  // = 768), whose pipelined loop spilled.  The pipelined loop keeps two tiles
+  // in flight (a third spilled in some variants), the other wide loops three.
+  static constexpr bool PIPE = WIDE && DT != kBf16 && RB * D < kSplitMaxWideColumns;
+  static constexpr int NB = !WIDE || PIPE ? kSplitTilesInFlight : kSplitWideTilesInFlight;
   static constexpr int WAVES_PER_EU = WPE;
   static_assert(!WIDE || WPE == 1, "wide row sets need one wavefront per SIMD");
   // merge buffers: one per wavefront, MRB row blocks at a time (64 KiB)
@@ -1373,6 +1448,106 @@ split_decode_kernel(SplitArgs a) {
         ++k;
       }
     }
+  } else if constexpr (K_::PIPE) {
+    // Wide row sets of the quantized caches: the accumulators live in the
+    // accumulation registers, which vector ALU instructions cannot multiply,
+    // so the rare reference moves and their rescales run outside the tile
+    // loop, and the loop is pipelined by one tile so that one wavefront per
+    // SIMD keeps both units busy: while tile t's logits and weights are
+    // computed, tile t + 1's S^T MFMAs run; while tile t's P . V MFMAs run,
+    // tile t + 1's V is unpacked.  A tile's slot is free once its S^T and V
+    // unpack are done, so its next load is issued at the start of the tile's
+    // step.  A tile whose references must move leaves the ring: it and the
+    // rest of the ring take the general weights, and the ring restarts at its
+    // first slot.
+    QKAcc<DT, MODE, D, RB> qa;  // S^T of the next tile
+    VTile<DT, D> vc;            // V operands of the current tile
+    float4_t nks, nvs;          // scales and pool flag of the next tile
+    int nok;
+    float cdot[RB][4];          // the current tile's
+    float4_t cks, cvs;
+    int cok;
+    half4_t pa[RB];
+    u32x2_t phi[RB], plo[RB];
+    int t = t0, k = 0;
+    if (t0 < te) {
+      qk_issue<DT, MODE, D, RB>(buf[0].kw, qlds, qa);
+      nks = buf[0].ks4;
+      nvs = buf[0].vs4;
+      nok = buf[0].ok;
+      unpack_v<DT, D>(buf[0].vw, vc);
+      // the references start at the first tile's row maxima (and, per-row
+      // V, its largest V scale); the accumulators are still zero
+      float dot[RB][4];
+      qk_dots<DT, MODE, D, RB>(qa, dot);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float z[4];
+        tile_logits<MODE, CAP>(dot[rb], nks, nok != 0, t0 * kTile + 4 * g, rowmul[rb], lim[rb], lo[rb], cap2,
+                               icap2, z);
+        W.m[rb] = group_max4(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+      }
+      if constexpr (kVRow) {
+        float vfac, vsn[4];
+        bool moved = false;
+        v_reference(nvs, W.vref, W.ivref, vfac, moved, vsn);
+      }
+    }
+    // the first half of tile t's step in slot S: the slot's next load, the
+    // tile's dot products, the next tile's S^T
+    auto front = [&](auto S) {
+      constexpr int sl = decltype(S)::value, s1 = (sl + 1) % NB;
+      load_tile<DT, MODE, D>(a, t + NB * kWaves, t + NB * kWaves < te, table_entry(tbl, k + NB), L, n, g,
+                             buf[sl]);
+      qk_dots<DT, MODE, D, RB>(qa, cdot);
+      cks = nks;
+      cvs = nvs;
+      cok = nok;
+      qk_issue<DT, MODE, D, RB>(buf[s1].kw, qlds, qa);
+      nks = buf[s1].ks4;
+      nvs = buf[s1].vs4;
+      nok = buf[s1].ok;
+    };
+    // the second half: P . V, the next tile's V operands
+    auto back = [&](auto S) {
+      constexpr int s1 = (decltype(S)::value + 1) % NB;
+      pv_unpacked<DT, D, RB>(vc, pa, W.acc);
+      unpack_v<DT, D>(buf[s1].vw, vc);
+      t += kWaves;
+      ++k;
+    };
+    while (t < te) {
+      int hit = -1;
+      bool stop = false;
+      do {
+        static_for<NB>([&](auto S) {
+          if (stop) return;
+          if (t >= te) {
+            stop = true;
+            return;
+          }
+          front(S);
+          if (weights_fast<DT, MODE, RB, CAP>(cdot, cks, cvs, cok != 0, t, g, rowmul, lim, lo, cap2, icap2, W,
+                                              pa, phi, plo)) {
+            hit = decltype(S)::value;
+            stop = true;
+            return;
+          }
+          back(S);
+        });
+      } while (!stop);
+      if (hit < 0) break;
+      // the tile that left the ring (its front half done) and the rest of
+      // the ring through the general weights
+      static_for<NB>([&](auto S) {
+        constexpr int sl = decltype(S)::value;
+        if (sl < hit || t >= te) return;
+        if (sl > hit) front(S);
+        weights_general<DT, MODE, D, RB, CAP>(cdot, cks, cvs, cok != 0, t, g, rowmul, lim, lo, cap2, icap2, W, pa,
+                                              phi, plo);
+        back(S);
+      });
+    }
   } else {
     // Wide row sets: the accumulators live in the accumulation registers,
     // which vector ALU instructions cannot multiply, so the rare reference
@@ -1413,7 +1588,7 @@ split_decode_kernel(SplitArgs a) {
           u32x2_t phi[RB], plo[RB];
           if constexpr (DT == kBf16) {
             if (tile_fast<DT, MODE, D, RB, CAP>(buf[i], t, g, qlds, rowmul, lim, lo, cap2, icap2, W, pa, phi,
-                                                plo, (const VTile<kInt8, D>*)nullptr)) {
+                                                plo)) {
               hit = i;
               break;
             }
@@ -1422,7 +1597,7 @@ split_decode_kernel(SplitArgs a) {
             VTile<DT, D> V;
             unpack_v<DT, D>(buf[i].vw, V);
             if (tile_fast<DT, MODE, D, RB, CAP>(buf[i], t, g, qlds, rowmul, lim, lo, cap2, icap2, W, pa, phi,
-                                                plo, &V)) {
+                                                plo)) {
               hit = i;
               break;
             }
