@@ -405,6 +405,46 @@ def cpu_baseline(ki, w, seconds: float, seconds_1t: float):
     return n, sec, threads, n1, sec1
 
 
+# Wide query-row sets (G query heads x Tq draft tokens per KV head, more than
+# 16 rows per 16-row block budget): dtype, K scale mode, D, B, Hkv, G, Tq,
+# context per sequence, paged.
+WIDE_ROW_SHAPES = [
+    ("int8", "per-row", 256, 1, 4, 4, 8, 65536, False),
+    ("int8", "per-row", 256, 1, 4, 6, 8, 65536, False),
+    ("int8", "per-row", 128, 4, 8, 8, 8, 16384, True),
+    ("int4", "per-row", 128, 4, 8, 6, 8, 16384, True),
+    ("fp8", "per-tensor", 256, 2, 4, 6, 4, 32768, True),
+]
+
+
+def time_wide_rows(kvq, torch, ki, args, dev, fused):
+    """Split-kernel and step times of the wide row sets above and of workload 5."""
+    dts = {"int8": ki.INT8, "int4": ki.INT4, "fp8": ki.FP8}
+    mds = {"per-row": ki.PER_ROW, "per-tensor": ki.PER_TENSOR}
+    with open(args.wide_rows, "w") as f:
+        shapes = [("workload5", None)] + [(sh, None) for sh in WIDE_ROW_SHAPES]
+        for sh, _ in shapes:
+            if sh == "workload5":
+                w = ki.make_workload(5)
+                desc = "workload 5: paged int4 per-channel, B4 Hq24 Hkv4 D256, 32,768 + 8 tokens"
+            else:
+                dt, md, D, B, Hkv, G, Tq, ctx, paged = sh
+                w = ki.random_workload(4400 + D + G * Tq, B=B, Hkv=Hkv, G=G, D=D, Tq=Tq, lens=[ctx] * B,
+                                       dtype=dts[dt], mode=mds[md], block_size=16 if paged else None)
+                desc = (f"{dt} {md}, B{B} Hq{G * Hkv} Hkv{Hkv} D{D}, {ctx} tokens, Tq {Tq} "
+                        f"({G * Tq} rows per KV head){', paged' if paged else ''}")
+            s = time_workload(kvq, torch, w, 4, max(64, args.steps // 4), args.warmup, dev, fused)
+            s["what"] = desc
+            s["rows_per_kv_head"] = (w.Hq // w.Hkv) * w.Tq
+            s["split_GBps"] = s["bytes"] / (s["split_ms"] * 1e-3) / 1e9
+            f.write(json.dumps(s) + "\n")
+            f.flush()
+            print(f"[wide] {desc}: split {s['split_ms'] * 1e3:.2f} us, step {s['step_ms'] * 1e3:.2f} us",
+                  file=sys.stderr, flush=True)
+            del w
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -444,6 +484,10 @@ def main():
                     help="time chunked prefill (workload-3 geometry, int8 / int4 / bf16 "
                          "caches, several past lengths and chunk sizes) and write JSON lines to this "
                          "file")
+    ap.add_argument("--wide-rows", default="",
+                    help="time the split kernel on wide query-row sets (17-64 rows per KV head: "
+                         "speculative drafts over grouped heads, several dtypes and head dims) and "
+                         "write JSON lines to this file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 20 times "
                          "(reference dispatch for HBM byte counters)")
@@ -520,6 +564,9 @@ def main():
         return
 
     fused = not args.separate_append
+    if args.wide_rows:
+        time_wide_rows(kvq, torch, ki, args, dev, fused)
+        return
     if args.workload != 3:
         w = ki.make_workload(args.workload)
         r = time_workload(kvq, torch, w, args.layers, args.steps, args.warmup, dev, fused,
