@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -45,11 +46,19 @@ KERNEL_SOURCES = ["quantized_kv_cache_02_amd/csrc/kvq_split.hip",
                   "quantized_kv_cache_02_amd/csrc/kvq_sched.h"]
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and blank space, so that a comment edit
+    does not invalidate a counter summary taken on the same code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_digest() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

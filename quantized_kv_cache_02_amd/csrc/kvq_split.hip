@@ -21,15 +21,19 @@
 //     (V) of their token.
 //
 // gfx950 mapping:
-//   S^T = K . Q^T  on v_mfma_f32_16x16x32_f16: A = 16 tokens x 32 channels of
-//                 K codes unpacked to fp16 (integers are exact in fp16), B = q
-//                 rows in fp16 after a power-of-two row normalization.
+//   S^T = K . Q^T  int8 / int4 caches: on v_mfma_i32_16x16x64_i8 with the K
+//                 codes as loaded (int4: each nibble moved to a byte's high
+//                 half) and the query as a fixed-point vector in 2 or 3 int8
+//                 slices (exact int32 dot products); fp8: on
+//                 v_mfma_f32_16x16x32_f16, A = 16 tokens x 32 channels of K
+//                 codes unpacked to fp16, B = q rows in fp16 after a
+//                 power-of-two row normalization.
 //   O  += P . V    on v_mfma_f32_16x16x16_f16: A = the softmax weights, which
 //                 sit in exactly the lanes the S^T result left them in; B = V
 //                 codes, transposed token-major -> channel-major in registers
 //                 with byte permutes and unpacked to fp16.
-//   The softmax weights are fp16 in [0, 1] (relative rounding 2^-11); the
-//   accumulators are fp32.
+//   The softmax weights are fp16 in [0, 2^8] (a lazily moved reference,
+//   relative rounding 2^-11); the accumulators are fp32.
 //   An unquantized bf16 cache (the baseline the kernel page compares against,
 //   "Performance") takes the same path with the bf16 MFMAs: K rows and q rows
 //   enter v_mfma_f32_16x16x32_bf16 as they are; for P . V each weight is split
@@ -377,7 +381,7 @@ struct WaveState {
 };
 
 // Per-row V scales: keep vref a power of two >= every scale seen, so the
-// weights p * s / vref stay in [0, 1].  The reduction runs only on the rare
+// weights p * s / vref stay at most p.  The reduction runs only on the rare
 // tiles where some scale exceeds the current reference; then vfac = old vref /
 // new vref (exact) multiplies the accumulators.
 __device__ __forceinline__ void v_reference(const float4_t& vs4, float& vref, float& ivref, float& vfac,
