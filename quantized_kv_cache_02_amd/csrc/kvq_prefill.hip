@@ -130,22 +130,30 @@ struct TileRows {
   int r16[4];
 };
 
+// In units of 16 rows throughout (block sizes are multiples of 16, and the host
+// bounds the pool to 2^31 such groups), so every step is 32-bit and wave-uniform.
 __device__ __forceinline__ TileRows tile_rows(const PrefillArgs& a, int b, int hkv, int kt, int L) {
   TileRows tr;
+  const int bs16 = a.c.block_size >> 4;
 #pragma unroll
   for (int sg = 0; sg < 4; ++sg) {
     const int p = kt * kPT + 16 * sg;
-    long r = -16;
+    int r16 = -1;
     if (p < L) {
       if (a.c.block_table == nullptr) {
-        r = ((long)b * a.c.Hkv + hkv) * a.c.block_size + p;  // contiguous: p < L <= block_size
+        r16 = (b * a.c.Hkv + hkv) * bs16 + (p >> 4);  // contiguous: p < L <= block_size
       } else {
-        const int blk = a.c.block_table[(size_t)b * a.c.max_blocks + p / a.c.block_size];
+        // a wave-uniform index, so the entry comes through a scalar load: a
+        // vector load here would make its wait wait for the tile loads in
+        // flight before it
+        const unsigned q = (unsigned)p / (unsigned)a.c.block_size;
+        const int col = __builtin_amdgcn_readfirstlane((int)q);
+        const int blk = a.c.block_table[(size_t)__builtin_amdgcn_readfirstlane(b) * a.c.max_blocks + col];
         if ((unsigned)blk < (unsigned)a.c.num_blocks)
-          r = ((long)blk * a.c.Hkv + hkv) * a.c.block_size + p % a.c.block_size;
+          r16 = (blk * a.c.Hkv + hkv) * bs16 + ((p - col * a.c.block_size) >> 4);
       }
     }
-    tr.r16[sg] = __builtin_amdgcn_readfirstlane((int)(r / 16));  // uniform: scalar registers
+    tr.r16[sg] = __builtin_amdgcn_readfirstlane(r16);  // uniform: scalar registers
   }
   return tr;
 }
@@ -613,12 +621,19 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
             if (!(t < lim[rb] && t >= lo[rb])) z[rb][s][e] = -INFINITY;
           }
     }
+    // one comparison of the largest relative logit instead of one per logit
+    {
+      float zmax = -INFINITY;
+      bool noref = false;
 #pragma unroll
-    for (int rb = 0; rb < RBW; ++rb)
+      for (int rb = 0; rb < RBW; ++rb) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) up |= z[rb][s][e] > kLazyHeadroom || m[rb] == -INFINITY;
+        for (int s = 0; s < 4; ++s)
+          zmax = fmaxf(zmax, fmaxf(fmaxf(z[rb][s][0], z[rb][s][1]), fmaxf(z[rb][s][2], z[rb][s][3])));
+        noref |= m[rb] == -INFINITY;
+      }
+      up = zmax > kLazyHeadroom || noref;
+    }
 
     // ---- online softmax over the tile's 64 tokens (row n: lanes n, n+16, n+32,
     // n+48), with the lazily moved reference of the decode kernel: m moves only
