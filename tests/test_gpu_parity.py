@@ -249,6 +249,9 @@ WIDE_CASES = [
     (INT8, PER_ROW, 256, 6, 8, True, [2000, 4100], 30.0, 0),       # soft cap variant
     (INT4, PER_CHANNEL, 256, 6, 8, True, [3000, 700], 2.0, 500),
     (FP8, PER_ROW, 128, 6, 8, False, [2500], 0.0, 1000),
+    # beyond 768 columns (49-64 rows at D 256): one workgroup per 16-row block
+    (INT8, PER_ROW, 256, 7, 7, True, [1800, 300], 0.0, 0),           # 49 rows
+    (INT4, PER_CHANNEL, 256, 8, 8, False, [2200], 0.0, 0),           # 64 rows
 ]
 
 
