@@ -420,9 +420,11 @@ def cpu_baseline(ki, w, seconds: float, seconds_1t: float):
 WIDE_ROW_SHAPES = [
     ("int8", "per-row", 256, 1, 4, 4, 8, 65536, False),
     ("int8", "per-row", 256, 1, 4, 6, 8, 65536, False),
+    ("int8", "per-row", 256, 1, 4, 8, 8, 65536, False),
     ("int8", "per-row", 128, 4, 8, 8, 8, 16384, True),
     ("int4", "per-row", 128, 4, 8, 6, 8, 16384, True),
     ("fp8", "per-tensor", 256, 2, 4, 6, 4, 32768, True),
+    ("fp8", "per-tensor", 256, 2, 4, 8, 8, 32768, True),
 ]
 
 

@@ -113,23 +113,34 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   // flight.  Up to kSplitMaxWideColumns the chunk keeps one workgroup, built
   // for one wavefront per SIMD with the accumulators in the accumulation
   // registers, so every tile is unpacked once for all its rows; beyond that
-  // every 16-row block gets its own workgroup and the chunk's workgroups share
-  // its bytes through L2.
+  // the row blocks are shared out evenly over RBN such workgroups per chunk
+  // (49-64 rows at D 256: two of 2 blocks), which read the chunk's bytes
+  // through L2.
+  // At exactly kSplitMaxWideColumns (33-48 rows at D 256) the one-workgroup
+  // loop is not pipelined, and with per-row V scales (multiplied into the
+  // weights: more live registers) it measured slower on MI355X than two
+  // pipelined workgroups of 2 row blocks (64K int8 per-row, 48 rows:
+  // 56.5 -> 45.7 us; fp8 K per-channel + V per-row 57.6 -> 48.9 us); with
+  // static V scales one workgroup stays (int4 per-channel 68.3 vs 81.4 us).
   const int RB = (G * tq + 15) / 16;
-  const int RBN = (RB > 1 && RB * c->head_dim > kvq::kSplitMaxWideColumns) ? RB : 1;
-  const bool wide = RBN == 1 && RB * c->head_dim > kvq::kSplitMaxAccColumns;
-  // Compute-bound variants (rows of at most 128 bytes, whose tiles carry less
-  // data per instruction: packed int4 at D 256, the 8-bit caches at D 128 and
-  // below; and row-split launches) run two workgroups per CU -- two
-  // wavefronts per SIMD hide each other's dependency stalls (measured on
-  // MI355X: int4 at 256K tokens 78.1 -> 68.6 us, workload 5 173.6 -> 90.7 us,
-  // paged fp8 at D 128 28.9 -> 27.9 us per step) -- as long as a chunk keeps
-  // at least 2 * kMinTilesPerSplit tiles.
+  const int rb_max = std::max(kvq::kSplitMaxWideColumns / c->head_dim, 1);
+  const bool vrow_768 = RB * c->head_dim == kvq::kSplitMaxWideColumns && RB > 2 &&
+                        c->dtype != KVQ_BF16 && v_mode_of(c) == KVQ_PER_ROW;
+  const int RBN = vrow_768 ? 2 : (RB + rb_max - 1) / rb_max;
+  const int RBK = (RB + RBN - 1) / RBN;  // row blocks per workgroup
+  const bool wide = RBK * c->head_dim > kvq::kSplitMaxAccColumns;
+  // Compute-bound variants of at most 256 accumulator columns (rows of at
+  // most 128 bytes, whose tiles carry less data per instruction: packed int4
+  // at D 256, the 8-bit caches at D 128 and below) run two workgroups per
+  // CU -- two wavefronts per SIMD hide each other's dependency stalls
+  // (measured on MI355X: int4 at 256K tokens 78.1 -> 68.6 us, paged fp8 at
+  // D 128 28.9 -> 27.9 us per step) -- as long as a chunk keeps at least
+  // 2 * kMinTilesPerSplit tiles.  (Every row-split launch is wide.)
   const int64_t per_head = std::max<int64_t>(kvq::kNumCUs / (Hkv * RBN), 1);
   const int64_t all_tiles = (int64_t)batch * ntiles;
   int64_t NW = per_head - (batch - 1);
   bool doubled = false;
-  if (!wide && (RBN > 1 || row_bytes(c) <= 128) &&
+  if (!wide && row_bytes(c) <= 128 &&
       2 * per_head - (batch - 1) <= all_tiles / (2 * kvq::kMinTilesPerSplit)) {
     NW = 2 * per_head - (batch - 1);
     doubled = true;
@@ -150,7 +161,7 @@ int decode_shape(const kvq_cache* c, int32_t batch, int32_t hq, int32_t tq, int3
   sh->NW = (int)NW;
   sh->RBN = RBN;
   sh->SMAX = (int)std::min<int64_t>(most, NW + batch - 1);
-  sh->RBK = RBN > 1 ? 1 : RB;
+  sh->RBK = RBK;
   sh->NSLOT = (int)(NW + batch - 1);
   // (the need-based minimum below can exceed the CU count for very long
   // batches; then the grid holds more than one workgroup per CU)

@@ -80,8 +80,8 @@ struct SplitArgs {
   int32_t B;   // sequences
   int32_t NW;  // nominal workgroups per KV head (the schedule's divisor)
   int32_t S;   // chunk slots per KV head: NW + B - 1
-  int32_t RBN; // workgroups per chunk, one per 16-row block of query rows (1: one
-               // workgroup serves every row)
+  int32_t RBN; // workgroups per chunk, each serving the kernel's RB 16-row blocks
+               // of query rows (1: one workgroup serves every row)
   int32_t one_per_cu;  // the grid holds at most one workgroup per CU, so a variant
                        // may use one wavefront per SIMD's register budget
   float sm_scale;

@@ -1275,8 +1275,7 @@ struct Knobs {
 // Variants whose accumulators fill a wavefront and whose rows exceed 128 bytes
 // sit at the 256-register budget of two wavefronts per SIMD (a spill there is a
 // scratch reload in the tile loop, which waits for every tile load before it).
-// Launches that place one workgroup per CU -- all of these but the row-split
-// ones -- run them with WPE = 1 instead: up to 512 registers, the MFMA
+// Launches that place one workgroup per CU run them with WPE = 1 instead: up to 512 registers, the MFMA
 // accumulators in ordinary VGPRs (the units build with -amdgpu-mfma-vgpr-form)
 // and any excess held in the accumulation registers, not in memory.
 template <int DT, int D, int RB>
@@ -1306,11 +1305,13 @@ split_decode_kernel(SplitArgs a) {
   __shared__ float s_vref[kWaves];
 
   const int hkv = blockIdx.y;
-  // Row-split launches (RBN > 1) give each of a chunk's RBN row blocks its own
-  // workgroup.  The x index packs (chunk slot, row block) so that the RBN
-  // workgroups of one chunk are 8 dispatch positions apart: the dispatcher
-  // deals workgroups to the 8 XCDs in turn, so they share one L2 and read the
-  // chunk's bytes from HBM once.
+  // Row-split launches (RBN > 1) share a chunk's query rows out over RBN
+  // workgroups of RB 16-row blocks each.  The x index packs (chunk slot, row
+  // set) so that the RBN workgroups of one chunk are 8 dispatch positions
+  // apart: the dispatcher deals workgroups to the 8 XCDs in turn, so they
+  // share one L2 and read the chunk's bytes from HBM once.  (With a fused
+  // append, each of them quantizes and stores the same new rows before it
+  // reads them: identical bytes, so no workgroup waits for another.)
   int slot = blockIdx.x, rbi = 0;
   if (a.RBN > 1) {
     const int grp = slot / (8 * a.RBN), rem = slot % (8 * a.RBN);
@@ -1357,7 +1358,7 @@ split_decode_kernel(SplitArgs a) {
   // ---- fused append: the wavefront that will read the tile holding a new
   // position quantizes and stores that row (the same arithmetic as
   // kvq_append) and waits for its stores before it issues the load of that
-  // tile.  No other wavefront reads those rows in this launch.  Position
+  // tile.  No other wavefront of the workgroup reads those rows.  Position
   // L - Tq + j holds query token j's row.
   const int t0 = tb + wave;  // the wavefront's tiles are t0, t0 + 4, ...
   bool mine[kMaxQTokens];    // wave-uniform
@@ -1777,12 +1778,13 @@ hipError_t launch_d(int RB, const SplitArgs& a, int B, hipStream_t st) {
   }
 }
 #else
-// A wide row set: one workgroup per chunk slot, one wavefront per SIMD.
+// A wide row set: one workgroup per chunk slot (RBN of them when the row
+// blocks are shared out), one wavefront per SIMD.
 template <int DT, int MODE, int D, int RB>
 hipError_t launch_wide(const SplitArgs& a, hipStream_t st) {
   static_assert(RB * D > kSplitMaxAccColumns && RB * D <= kSplitMaxWideColumns, "not a wide row set");
-  if (a.RBN != 1) return hipErrorInvalidValue;
-  dim3 grid(a.S, a.c.Hkv, 1);
+  const int gx = a.RBN > 1 ? (a.S + 7) / 8 * 8 * a.RBN : a.S;
+  dim3 grid(gx, a.c.Hkv, 1);
   if (a.softcap > 0.0f)
     hipLaunchKernelGGL((split_decode_kernel<DT, MODE, D, RB, true, 1>), grid, dim3(256), 0, st, a);
   else

@@ -234,7 +234,8 @@ def test_gqa_and_query_tokens(G, Tq):
 # workgroup per chunk with one wavefront per SIMD, which unpacks every tile
 # once for all rows and rescales its accumulators outside the tile loop.
 WIDE_CASES = [
-    # dtype, mode, D, G, Tq, paged, lens, softcap, window
+    # dtype, mode, D, G, Tq, paged, lens, softcap, window.  (33-48 rows at D 256
+    # with per-row V scales run as two workgroups of 2 row blocks, as beyond 48.)
     (INT8, PER_ROW, 256, 6, 8, True, [8, 700, 3000], 0.0, 0),      # 48 rows
     (INT8, PER_CHANNEL, 256, 4, 5, False, [2100, 40], 0.0, 0),     # 20 rows
     (INT4, PER_ROW, 256, 6, 8, False, [1900, 9], 0.0, 0),
@@ -249,9 +250,12 @@ WIDE_CASES = [
     (INT8, PER_ROW, 256, 6, 8, True, [2000, 4100], 30.0, 0),       # soft cap variant
     (INT4, PER_CHANNEL, 256, 6, 8, True, [3000, 700], 2.0, 500),
     (FP8, PER_ROW, 128, 6, 8, False, [2500], 0.0, 1000),
-    # beyond 768 columns (49-64 rows at D 256): one workgroup per 16-row block
+    # beyond 768 columns (49-64 rows at D 256): two workgroups of 2 row blocks
     (INT8, PER_ROW, 256, 7, 7, True, [1800, 300], 0.0, 0),           # 49 rows
     (INT4, PER_CHANNEL, 256, 8, 8, False, [2200], 0.0, 0),           # 64 rows
+    (FP8, PER_ROW, 256, 8, 8, True, [3000, 45], 0.0, 0),             # 64 rows
+    (ki.BF16, 0, 256, 8, 7, True, [2500], 0.0, 0),                   # 56 rows
+    (INT8, PER_CHANNEL, 256, 8, 8, True, [2100, 900], 20.0, 300),    # 64 rows, cap, window
 ]
 
 
@@ -293,7 +297,8 @@ def _ramp_workload(seed, dt, md, D, G, Tq, lens, per_tile):
 
 
 @pytest.mark.parametrize("dt,md,D,G,Tq", [(INT8, PER_ROW, 256, 6, 8), (INT4, PER_ROW, 256, 4, 5),
-                                          (FP8, PER_ROW, 128, 8, 5), (ki.BF16, 0, 256, 6, 8)])
+                                          (FP8, PER_ROW, 128, 8, 5), (ki.BF16, 0, 256, 6, 8),
+                                          (INT8, PER_ROW, 256, 8, 8), (FP8, PER_TENSOR, 256, 6, 8)])
 def test_wide_row_sets_rescale_every_tile(dt, md, D, G, Tq):
     w = _ramp_workload(3900 + 10 * dt + D, dt, md, D, G, Tq, [1100, 2900], per_tile=2.0)
     gu.run_and_check(w, f"wide rescale ramp dt={dt} D={D} G={G} Tq={Tq}")
@@ -523,6 +528,19 @@ def test_fused_append_decode_drafts_across_tiles(lens):
         w = ki.random_workload(5000 + sum(lens) + dt, B=len(lens), Hkv=2, G=3, D=128, Tq=8,
                                lens=lens, dtype=dt, mode=md, block_size=16 if paged else None)
         _fused_vs_separate(w, f"fused dt={dt} lens={lens}")
+
+
+@pytest.mark.parametrize("dt,md,D,G,paged", [(INT8, PER_ROW, 256, 6, True),    # 48 rows, one workgroup
+                                             (INT4, PER_ROW, 128, 8, False),   # 64 rows, one workgroup
+                                             (INT8, PER_ROW, 256, 7, False),   # 56 rows, two workgroups
+                                             (FP8, PER_TENSOR, 256, 8, True),  # 64 rows, two workgroups
+                                             (ki.BF16, 0, 256, 8, True)])
+def test_fused_append_decode_wide_row_sets(dt, md, D, G, paged):
+    """Wide row sets append the new rows too; where a chunk's rows are shared out
+    over two workgroups, both store the same bytes before they read them."""
+    w = ki.random_workload(6100 + 10 * dt + G + D, B=3, Hkv=2, G=G, D=D, Tq=8, lens=[5, 1700, 2903],
+                           dtype=dt, mode=md, block_size=16 if paged else None)
+    _fused_vs_separate(w, f"fused wide dt={dt} D={D} G={G}")
 
 
 # ------------------------------------------- soft cap and sliding window
