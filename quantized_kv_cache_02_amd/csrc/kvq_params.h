@@ -36,8 +36,8 @@ constexpr int kPrefillMaxParts = 8;
 // with RB * D <= 256, whose accumulators fit that budget beside the q operand
 // and the tiles in flight.  Wider row sets up to kSplitMaxWideColumns run as
 // one workgroup per chunk with one wavefront per SIMD, the accumulators in the
-// accumulation registers (the "wide" units); wider ones still get one
-// workgroup per row block.
+// accumulation registers (the "wide" units); wider ones share their row blocks
+// out over several such workgroups per chunk.
 constexpr int kSplitWavesPerSimd = 2;
 constexpr int kSplitMaxAccColumns = 256;   // RB * D
 constexpr int kSplitMaxWideColumns = 768;  // RB * D

@@ -485,6 +485,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
   const float icap2 = CAP ? 2.0f / a.softcap : 0.0f;
   float m[RBW], l[RBW];
   float vref = 0x1p-126f;
+  float ivref = 0x1p126f;  // 1 / vref, exact (vref is a power of two)
   float4_t acc[RBW][NCOL];
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
@@ -686,12 +687,14 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
         (void)frexpf(vmax, &en);
         const float nref = ldexpf(1.0f, en);
         if (nref > vref) {
-          vfac = vref / nref;
+          // powers of two: both products are exact, no division per tile
+          ivref = ldexpf(1.0f, -en);
+          vfac = vref * ivref;
           vref = nref;
           rescale = true;
         }
       }
-      const float inv = 1.0f / vref;
+      const float inv = ivref;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll

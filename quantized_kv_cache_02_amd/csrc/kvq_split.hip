@@ -1301,7 +1301,6 @@ split_decode_kernel(SplitArgs a) {
   __shared__ float s_pmax[kWaves * RP];  // row maxima of each wavefront's k-steps
   __shared__ float s_m[kWaves][RP];
   __shared__ float s_l[kWaves][RP];
-  __shared__ float s_f[kWaves][RP];  // merge weight of each wavefront's rows
   __shared__ float s_vref[kWaves];
 
   const int hkv = blockIdx.y;
@@ -1417,6 +1416,9 @@ split_decode_kernel(SplitArgs a) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int k = 0; k < QO; ++k) qb[rb][k] = qlds[(rb * QO + k) * 64];
+    // every wavefront holds its copy before any overwrites the area (the
+    // merge writes its accumulators there as soon as its loop ends)
+    __syncthreads();
   }
   int lim[RB];  // tokens visible to this lane's row n: lo <= t < lim
   int lo[RB];
@@ -1633,12 +1635,12 @@ split_decode_kernel(SplitArgs a) {
   }
 
   // ---- merge the 4 wavefronts in fixed order, write the split partial.
-  // Each wavefront publishes its row statistics; after the barrier (every loop
-  // has ended, so the q staging area is free) it writes its raw accumulator
-  // rows to its own LDS buffer while one lane per row of the last wavefront
-  // turns the statistics into the four per-wavefront weights (first, so the
-  // chain overlaps the other wavefronts' writes); the readback then sums the
-  // weighted buffers in wave order.
+  // Each wavefront publishes its row statistics and its raw accumulator rows
+  // (to its own LDS buffer).  Where the loop read q from registers the LDS is
+  // free by then, so a wavefront writes them as soon as its own loop ends,
+  // while slower ones are still loading, and one barrier is left: the
+  // readback weighs each wavefront's rows by exp2(m_w - M) / L, each thread
+  // computing the weights of its own row, and sums the buffers in wave order.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float lsum = group_sum4(W.l[rb]);
@@ -1649,37 +1651,7 @@ split_decode_kernel(SplitArgs a) {
   }
   if constexpr (kVRow)
     if (lane == 0) s_vref[wave] = W.vref;
-  __syncthreads();
 
-  // the chunk's statistics of row r (log2 units) and the weight of each
-  // wavefront's rows: exp2(m_w - M) / L (times its V reference; 1/16 for int4,
-  // whose V operand holds 16 * code), computed before this wavefront's own
-  // accumulator writes so that the chain does not wait behind them
-  constexpr int kStatWave = kWaves - 1;
-  if (wave == kStatWave && lane < Rw) {
-    const int r = lane;
-    float M = s_m[0][r];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
-    float Lt = 0.0f;
-    float ew[kWaves];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      // the hardware exp2, as in the tile loop (results below 2^-126 flush to 0)
-      ew[w] = M != -INFINITY ? __builtin_amdgcn_exp2f(s_m[w][r] - M) : 0.0f;
-      Lt += s_l[w][r] * ew[w];
-    }
-    const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      float f = ew[w] * inv;
-      if constexpr (kVRow) f *= s_vref[w];
-      if constexpr (DT == kInt4) f *= 0.0625f;
-      s_f[w][r] = f;
-    }
-    a.ws_m[((size_t)hkv * a.R + row0 + r) * a.S + slot] = M;
-    a.ws_l[((size_t)hkv * a.R + row0 + r) * a.S + slot] = Lt;
-  }
   // Lane column n owns NCOL channels, NCOL / 4 groups of 4 consecutive ones
   // (see group_owner); they go to the lane's NCOL-float LDS slot as 16-byte
   // chunks whose order is rotated by n / (64 / NCOL) so the 16 lanes of a pass
@@ -1689,9 +1661,8 @@ split_decode_kernel(SplitArgs a) {
   // Wide row sets merge MRB row blocks per pass (the buffers hold 64 KiB).
   constexpr int MRB = K_::MRB;
   constexpr int MR = 16 * MRB;  // rows per pass
-#pragma unroll
-  for (int p = 0; p < K_::MPASS; ++p) {
-    if (p > 0) __syncthreads();  // the previous pass's readback is done
+  constexpr bool kEarly = !K_::QLDS && K_::MPASS == 1;
+  auto write_rows = [&](int p) {
     float* ob = smem + (size_t)wave * MR * D;
 #pragma unroll
     for (int rr = 0; rr < MRB; ++rr) {
@@ -1713,19 +1684,54 @@ split_decode_kernel(SplitArgs a) {
         }
       }
     }
-    __syncthreads();
+  };
+  if constexpr (kEarly) write_rows(0);
+  __syncthreads();
 
+#pragma unroll
+  for (int p = 0; p < K_::MPASS; ++p) {
+    if constexpr (!kEarly) {
+      if (p > 0) __syncthreads();  // the previous pass's readback is done
+      write_rows(p);
+      __syncthreads();
+    }
     const int rn = min(MR, Rw - p * MR);  // rows of this pass
     for (int idx = tid * 4; idx < rn * D; idx += 256 * 4) {
       const int lr = idx / D, d = idx % D, r = p * MR + lr;
+      // the chunk's statistics of row r (log2 units) and the weight of each
+      // wavefront's rows: exp2(m_w - M) / L, times its V reference (1/16
+      // more for int4, whose V operand holds 16 * code)
+      float M = s_m[0][r];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+      float Lt = 0.0f;
+      float f[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        // the hardware exp2, as in the tile loop (results below 2^-126 flush to 0)
+        f[w] = M != -INFINITY ? __builtin_amdgcn_exp2f(s_m[w][r] - M) : 0.0f;
+        Lt += s_l[w][r] * f[w];
+      }
+      const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        f[w] *= inv;
+        if constexpr (kVRow) f[w] *= s_vref[w];
+        if constexpr (DT == kInt4) f[w] *= 0.0625f;
+      }
       int jn, k;
       group_owner<DT, D>(d, jn, k);
       const int off = lr * D + G_::NCOL * jn + 4 * ((k + jn / ROT) % NCH);
-      float4_t v = s_f[0][r] * *reinterpret_cast<const float4_t*>(smem + off);
+      float4_t v = f[0] * *reinterpret_cast<const float4_t*>(smem + off);
 #pragma unroll
       for (int w = 1; w < kWaves; ++w)
-        v += s_f[w][r] * *reinterpret_cast<const float4_t*>(smem + (size_t)w * MR * D + off);
-      *reinterpret_cast<float4_t*>(a.ws_o + (((size_t)hkv * a.R + row0 + r) * a.S + slot) * D + d) = v;
+        v += f[w] * *reinterpret_cast<const float4_t*>(smem + (size_t)w * MR * D + off);
+      const size_t ri = ((size_t)hkv * a.R + row0 + r) * a.S + slot;
+      *reinterpret_cast<float4_t*>(a.ws_o + ri * D + d) = v;
+      if (d == 0) {
+        a.ws_m[ri] = M;
+        a.ws_l[ri] = Lt;
+      }
     }
   }
 }
