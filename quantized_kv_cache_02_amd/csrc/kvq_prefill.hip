@@ -320,9 +320,18 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 15, g = lane >> 4;
-  const int hkv = blockIdx.y, b = blockIdx.z;
-  const int part = blockIdx.x % a.KS;          // context part (KS > 1: split launch)
-  const int rbase = blockIdx.x / a.KS * kRows;  // first row of the workgroup
+  // The workgroups of sequence b (x: row group and context part, y: KV head)
+  // in dispatch order are taken as (row group, KV head, part) with the part
+  // fastest and the row groups in reverse: later rows see more of the causal
+  // context, so the longest workgroups start first and the shortest fill the
+  // last round; and the dispatcher, dealing workgroups to the 8 XCDs in turn,
+  // gives each XCD the same (KV head, part) again and again when KS * Hkv
+  // divides 8 (the tiles they share stay in that XCD's L2).
+  const int lin = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  const int b = blockIdx.z;
+  const int part = lin % a.KS;                 // context part (KS > 1: split launch)
+  const int hkv = lin / a.KS % (int)gridDim.y;
+  const int rbase = ((int)gridDim.x / a.KS - 1 - lin / (a.KS * (int)gridDim.y)) * kRows;  // first row
   const int rwave = rbase + 16 * RBW * wave;   // first row of this wavefront
   const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
   const int pos0 = L - a.Tq;                   // position of query token 0
@@ -480,6 +489,10 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
     kt_begin = min(kt_begin + part * C, kt_end);
     kt_end = min(kt_begin + C, kt_end);
   }
+  // uniform, in scalar registers (the divisions above run on the vector
+  // unit), so the tile index and each tile's row arithmetic stay scalar
+  kt_begin = __builtin_amdgcn_readfirstlane(kt_begin);
+  kt_end = __builtin_amdgcn_readfirstlane(kt_end);
 
   const float cap2 = CAP ? a.softcap * 1.4426950408889634f : 0.0f;
   const float icap2 = CAP ? 2.0f / a.softcap : 0.0f;
