@@ -147,17 +147,24 @@ __device__ __forceinline__ i32x4_t mfma64_i8(i32x4_t a, i32x4_t b, i32x4_t c) {
 // channels) and combine into one float per logit (q_dot).  Two slices keep 15
 // bits of the row's largest element, three 23: a channel 2^r below the largest
 // keeps 15 - r or 23 - r bits.
+//
+// q_slice_bytes returns the slices as bytes 0 .. NSL-1 of one word: with the
+// bias c = sum_{k < NSL-1} 128 * 256^k, u = qi + c has s_k + 128 as its byte k
+// below the top (plain base-256 digits) and s_{NSL-1} as the rest, so the
+// slice bytes are those of u with the bias bits flipped back.
 template <int NSL>
-__device__ __forceinline__ void q_slices(float x, int ex, int (&sl)[NSL]) {
+__device__ __forceinline__ uint32_t q_slice_bytes(float x, int ex) {
   static_assert(NSL == 2 || NSL == 3, "two or three slices");
-  int qi = (int)__builtin_rintf(ldexpf(x, 8 * NSL - 2 - ex));
-#pragma unroll
-  for (int k = 0; k < NSL - 1; ++k) {
-    const int d = ((qi + 128) & 255) - 128;
-    sl[k] = d;
-    qi = (qi - d) >> 8;  // exact: qi - d is a multiple of 256
-  }
-  sl[NSL - 1] = qi;
+  constexpr uint32_t c = NSL == 2 ? 0x80u : 0x8080u;
+  const int qi = (int)__builtin_rintf(ldexpf(x, 8 * NSL - 2 - ex));
+  return ((uint32_t)qi + c) ^ c;
+}
+
+// Slice k of four consecutive values (their q_slice_bytes words w0..w3) as one
+// B-operand dword: byte p is byte k of w_p.
+__device__ __forceinline__ uint32_t slice_dword(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, int k) {
+  const uint32_t sel = (uint32_t)k | ((uint32_t)(4 + k) << 8);
+  return perm(perm(w3, w2, sel), perm(w1, w0, sel), 0x05040100u);
 }
 
 // The softmax weights of a row are exp2(z - m) for a reference m that moves

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 
   // q operand: row r, channels 32 ks + 8 g + 0..7 (zero rows past R).
   // Integer caches: channels 64 st + 16 g + 0..15 of the row as a fixed-point
-  // integer vector in NSL int8 slices (q_slices: 15 bits of the row's largest
+  // integer vector in NSL int8 slices (q_slice_bytes: 15 bits of the row's largest
   // element, 23 with a per-channel K scale folded in); qb[rb][NSL st + k]
   // holds slice k.
   constexpr int NSL = MODE == kPerChannel ? 3 : 2;
@@ -408,16 +408,15 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
       if (amax > 0.0f) (void)frexpf(amax, &ex);
 #pragma unroll
       for (int st = 0; st < P::ISTEPS; ++st) {
+        uint32_t wb[16];
+#pragma unroll
+        for (int p = 0; p < 16; ++p) wb[p] = q_slice_bytes<NSL>(qv[st][p], ex);
         u32x4_t wq[NSL];
 #pragma unroll
-        for (int k = 0; k < NSL; ++k) wq[k] = u32x4_t{0u, 0u, 0u, 0u};
+        for (int k = 0; k < NSL; ++k)
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-          int sl[NSL];
-          q_slices<NSL>(qv[st][p], ex, sl);
-#pragma unroll
-          for (int k = 0; k < NSL; ++k) wq[k][p / 4] |= ((uint32_t)sl[k] & 0xFFu) << (8 * (p % 4));
-        }
+          for (int i = 0; i < 4; ++i)
+            wq[k][i] = slice_dword(wb[4 * i], wb[4 * i + 1], wb[4 * i + 2], wb[4 * i + 3], k);
 #pragma unroll
         for (int k = 0; k < NSL; ++k) qb[rb][NSL * st + k] = __builtin_bit_cast(half8_t, wq[k]);
       }

@@ -103,7 +103,7 @@ struct Geo {
   static constexpr int NCOL = D / 16;      // 16x16x16 MFMAs per row block
 };
 
-// Query slices of the integer S^T (see q_slices): three for a per-channel K
+// Query slices of the integer S^T (see q_slice_bytes): three for a per-channel K
 // scale, whose folded query spans the table's range, two otherwise.  The q
 // operand array holds NSL slices per integer k-step (integer caches) or one
 // fp16 / bf16 operand per k-step.
@@ -1004,23 +1004,25 @@ __device__ __forceinline__ void process_tile(const Tile<DT, D>& T, int t, int n,
 // Each row is taken in this lane's channel order from the staged rows qs (bf16,
 // kQStride apart), times a per-channel K scale, and normalized by a power of
 // two: the integer caches get a fixed-point integer vector in NSL int8 slices
-// (see q_slices: 15 bits of the row's largest element, 23 with a per-channel
+// (see q_slice_bytes: 15 bits of the row's largest element, 23 with a per-channel
 // K scale folded in), fp8 an fp16 vector with every element in (-1, 1), bf16
 // the row as it is (bf16 products are exact in the fp32 accumulation).
 // Wavefront w folds the k-steps st = w, w + 4, ...: their row maxima meet in
 // s_pmax ([kWaves][16 RB]) across a barrier, the operands in qop across a
 // second one.  rowmul[rb] restores the power of two (logit in log2 units =
 // dot * rowmul * per-row K scale).  Every wavefront must call it.
+// The static K scales come in kst_lds, staged in LDS by the caller: the KV
+// head's D per-channel scales, or the per-tensor one.
 template <int DT, int MODE, int D, int RB>
 __device__ __forceinline__ void fold_q_shared(const SplitArgs& a, const uint16_t* qs, int hkv, int wave,
                                               int n, int g, int lane, half8_t* qop, float* s_pmax,
-                                              float (&rowmul)[RB]) {
+                                              const float* kst_lds, float (&rowmul)[RB]) {
   using G_ = Geo<DT, D>;
   constexpr int QO = kQOps<DT, MODE, D>;
   constexpr int RP = 16 * RB;
-  const float* kst = a.c.k_scales;
+  (void)hkv;
   float mul = a.sm_scale * 1.4426950408889634f;  // natural -> log2 units
-  if constexpr (MODE == kPerTensor) mul *= kst[0];
+  if constexpr (MODE == kPerTensor) mul *= kst_lds[0];
   if constexpr (DT == kInt4) mul *= 0.0625f;  // K operand holds 16 * code
   if constexpr (G_::IQK) {
     constexpr int NSL = kQSlices<DT, MODE>;
@@ -1050,7 +1052,7 @@ __device__ __forceinline__ void fold_q_shared(const SplitArgs& a, const uint16_t
         for (int p = 0; p < 16; ++p) {
           const int off = k_offset_i8<DT>(p);  // 0..15
           float x = x16[off];
-          if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
+          if constexpr (MODE == kPerChannel) x *= kst_lds[base + off];
           qv[rb][j][p] = x;
           amax = fmaxf(amax, fabsf(x));
         }
@@ -1072,16 +1074,15 @@ __device__ __forceinline__ void fold_q_shared(const SplitArgs& a, const uint16_t
       for (int j = 0; j < MY; ++j) {
         const int st = wave + kWaves * j;
         if (st >= NS) continue;
+        uint32_t wb[16];
+#pragma unroll
+        for (int p = 0; p < 16; ++p) wb[p] = q_slice_bytes<NSL>(qv[rb][j][p], ex);
         u32x4_t w4[NSL];
 #pragma unroll
-        for (int k = 0; k < NSL; ++k) w4[k] = u32x4_t{0u, 0u, 0u, 0u};
+        for (int k = 0; k < NSL; ++k)
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-          int sl[NSL];
-          q_slices<NSL>(qv[rb][j][p], ex, sl);
-#pragma unroll
-          for (int k = 0; k < NSL; ++k) w4[k][p / 4] |= ((uint32_t)sl[k] & 0xFFu) << (8 * (p % 4));
-        }
+          for (int i = 0; i < 4; ++i)
+            w4[k][i] = slice_dword(wb[4 * i], wb[4 * i + 1], wb[4 * i + 2], wb[4 * i + 3], k);
 #pragma unroll
         for (int k = 0; k < NSL; ++k)
           qop[(rb * QO + NSL * st + k) * 64 + lane] = __builtin_bit_cast(half8_t, w4[k]);
@@ -1115,7 +1116,7 @@ __device__ __forceinline__ void fold_q_shared(const SplitArgs& a, const uint16_t
           for (int e = 0; e < 8; ++e) {
             const int off = k_channel<DT, D>(ks, g, e) - base;  // 0..7
             float x = x8[off];
-            if constexpr (MODE == kPerChannel) x *= kst[(size_t)hkv * D + base + off];
+            if constexpr (MODE == kPerChannel) x *= kst_lds[base + off];
             qv[rb][j][e] = x;
             amax = fmaxf(amax, fabsf(x));
           }
@@ -1302,6 +1303,8 @@ split_decode_kernel(SplitArgs a) {
   __shared__ float s_m[kWaves][RP];
   __shared__ float s_l[kWaves][RP];
   __shared__ float s_vref[kWaves];
+  __shared__ float s_f[K_::MPASS > 1 ? kWaves : 1][RP];  // merge weights (several passes)
+  __shared__ float s_kst[MODE == kPerChannel ? D : 1];  // static K scales (per channel / tensor)
 
   const int hkv = blockIdx.y;
   // Row-split launches (RBN > 1) share a chunk's query rows out over RBN
@@ -1370,6 +1373,17 @@ split_decode_kernel(SplitArgs a) {
     any_mine |= mine[j];
     early_hit |= mine[j] && t < t0 + NB * kWaves;  // among the first NB tiles
   }
+  // The static K scales of this head (per channel: one per thread), loaded
+  // before the tile loads: loads return in order, so the query fold would
+  // otherwise wait for the first tiles (measured on MI355X, workload 5: the
+  // fold ended 8.2 us after the workgroup started).
+  float kst_v = 0.0f;
+  if constexpr (MODE == kPerChannel) {
+    static_assert(D <= 256, "one scale per thread");
+    kst_v = tid < D ? a.c.k_scales[(size_t)hkv * D + tid] : 0.0f;
+  } else if constexpr (MODE == kPerTensor) {
+    kst_v = a.c.k_scales[0];
+  }
   NewRows<DT, MODE, D> nr;
   if (any_mine) nr.load(a, mine, b, hkv, L, lane);  // first, so their latency overlaps the tile loads
   auto append_rows = [&]() { nr.store(a, mine, hkv, L, lane); };
@@ -1400,6 +1414,11 @@ split_decode_kernel(SplitArgs a) {
       *reinterpret_cast<u32x4_t*>(qs + (u / QU) * kQStride<D> + (u % QU) * 8) = v;
     }
   }
+  if constexpr (MODE == kPerChannel) {
+    if (tid < D) s_kst[tid] = kst_v;
+  } else if constexpr (MODE == kPerTensor) {
+    if (tid == 0) s_kst[0] = kst_v;
+  }
   __syncthreads();
 
   // ---- B operands of S^T, folded once for the workgroup into LDS (lane-
@@ -1408,7 +1427,7 @@ split_decode_kernel(SplitArgs a) {
   constexpr int QO = kQOps<DT, MODE, D>;
   half8_t* qop = reinterpret_cast<half8_t*>(reinterpret_cast<char*>(smem) + kQStageBytes);
   float rowmul[RB];  // logit (log2 units) = dot * rowmul * per-row K scale
-  fold_q_shared<DT, MODE, D, RB>(a, qs, hkv, wave, n, g, lane, qop, s_pmax, rowmul);
+  fold_q_shared<DT, MODE, D, RB>(a, qs, hkv, wave, n, g, lane, qop, s_pmax, s_kst, rowmul);
   const half8_t* qlds = qop + lane;
   half8_t qb[RB][QO];
   if constexpr (!K_::QLDS) {
@@ -1638,9 +1657,9 @@ split_decode_kernel(SplitArgs a) {
   // Each wavefront publishes its row statistics and its raw accumulator rows
   // (to its own LDS buffer).  Where the loop read q from registers the LDS is
   // free by then, so a wavefront writes them as soon as its own loop ends,
-  // while slower ones are still loading, and one barrier is left: the
-  // readback weighs each wavefront's rows by exp2(m_w - M) / L, each thread
-  // computing the weights of its own row, and sums the buffers in wave order.
+  // while slower ones are still loading, and one barrier is left.  The
+  // readback weighs each wavefront's rows by exp2(m_w - M) / L and sums the
+  // buffers in wave order.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float lsum = group_sum4(W.l[rb]);
@@ -1688,6 +1707,44 @@ split_decode_kernel(SplitArgs a) {
   if constexpr (kEarly) write_rows(0);
   __syncthreads();
 
+  // the chunk's statistics of row r (log2 units) and the weight of each
+  // wavefront's rows: exp2(m_w - M) / L, times its V reference (1/16 more for
+  // int4, whose V operand holds 16 * code); the partial's m and l stored
+  auto row_weights = [&](int r, float (&f)[kWaves]) {
+    float M = s_m[0][r];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+    float Lt = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      // the hardware exp2, as in the tile loop (results below 2^-126 flush to 0)
+      f[w] = M != -INFINITY ? __builtin_amdgcn_exp2f(s_m[w][r] - M) : 0.0f;
+      Lt += s_l[w][r] * f[w];
+    }
+    const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      f[w] *= inv;
+      if constexpr (kVRow) f[w] *= s_vref[w];
+      if constexpr (DT == kInt4) f[w] *= 0.0625f;
+    }
+    return std::pair<float, float>(M, Lt);
+  };
+  // Several passes (wide row sets): one thread per row turns the statistics
+  // into weights once, for every pass (its barriers publish them); one pass:
+  // each thread takes its own row's.
+  constexpr bool kRowTable = K_::MPASS > 1;
+  if constexpr (kRowTable) {
+    if (tid < Rw) {
+      float f[kWaves];
+      const auto ml = row_weights(tid, f);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) s_f[w][tid] = f[w];
+      const size_t ri = ((size_t)hkv * a.R + row0 + tid) * a.S + slot;
+      a.ws_m[ri] = ml.first;
+      a.ws_l[ri] = ml.second;
+    }
+  }
 #pragma unroll
   for (int p = 0; p < K_::MPASS; ++p) {
     if constexpr (!kEarly) {
@@ -1698,26 +1755,17 @@ split_decode_kernel(SplitArgs a) {
     const int rn = min(MR, Rw - p * MR);  // rows of this pass
     for (int idx = tid * 4; idx < rn * D; idx += 256 * 4) {
       const int lr = idx / D, d = idx % D, r = p * MR + lr;
-      // the chunk's statistics of row r (log2 units) and the weight of each
-      // wavefront's rows: exp2(m_w - M) / L, times its V reference (1/16
-      // more for int4, whose V operand holds 16 * code)
-      float M = s_m[0][r];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
-      float Lt = 0.0f;
+      const size_t ri = ((size_t)hkv * a.R + row0 + r) * a.S + slot;
       float f[kWaves];
+      if constexpr (kRowTable) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        // the hardware exp2, as in the tile loop (results below 2^-126 flush to 0)
-        f[w] = M != -INFINITY ? __builtin_amdgcn_exp2f(s_m[w][r] - M) : 0.0f;
-        Lt += s_l[w][r] * f[w];
-      }
-      const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        f[w] *= inv;
-        if constexpr (kVRow) f[w] *= s_vref[w];
-        if constexpr (DT == kInt4) f[w] *= 0.0625f;
+        for (int w = 0; w < kWaves; ++w) f[w] = s_f[w][r];
+      } else {
+        const auto ml = row_weights(r, f);
+        if (d == 0) {
+          a.ws_m[ri] = ml.first;
+          a.ws_l[ri] = ml.second;
+        }
       }
       int jn, k;
       group_owner<DT, D>(d, jn, k);
@@ -1726,12 +1774,7 @@ split_decode_kernel(SplitArgs a) {
 #pragma unroll
       for (int w = 1; w < kWaves; ++w)
         v += f[w] * *reinterpret_cast<const float4_t*>(smem + (size_t)w * MR * D + off);
-      const size_t ri = ((size_t)hkv * a.R + row0 + r) * a.S + slot;
       *reinterpret_cast<float4_t*>(a.ws_o + ri * D + d) = v;
-      if (d == 0) {
-        a.ws_m[ri] = M;
-        a.ws_l[ri] = Lt;
-      }
     }
   }
 }
