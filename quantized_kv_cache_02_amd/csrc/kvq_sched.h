@@ -90,12 +90,11 @@ __device__ __forceinline__ int chunk_tiles(const int32_t* seq_lens, int B, int m
 __device__ __forceinline__ Chunk find_chunk(const int32_t* seq_lens, int B, int max_seq_len, int NW,
                                             int Tq, int window, int slot, int want_b, int lane,
                                             int32_t* table = nullptr) {
-  const int C = chunk_tiles(seq_lens, B, max_seq_len, NW, Tq, window, lane);
   Chunk ch{-1, 0, 0, 0, 0, 0};
   int P = 0;  // chunks of the sequences before this pass
-  for (int base = 0; base < B; base += 64) {
+  // one pass: lane l holds sequence base + l (length L); true once done
+  auto pass = [&](int base, int L, int C) {
     const int i = base + lane;
-    const int L = i < B ? clamp_len(seq_lens[i], max_seq_len) : 0;
     const Span sp = visible_tiles(L, Tq, window);
     const int n = sp.end - sp.first;
     const int Sb = (n + C - 1) / C;
@@ -107,6 +106,7 @@ __device__ __forceinline__ Chunk find_chunk(const int32_t* seq_lens, int B, int 
     }
     const bool hit = (i < B) && (slot >= 0 ? (Sb > 0 && Pb <= slot && slot < Pb + Sb) : i == want_b);
     const uint64_t m = __ballot(hit);
+    bool done = false;
     if (m != 0 && ch.b < 0) {
       const int l = __builtin_ctzll(m);
       ch.b = base + l;
@@ -118,9 +118,24 @@ __device__ __forceinline__ Chunk find_chunk(const int32_t* seq_lens, int B, int 
       const int nb = __shfl(sp.end, l);
       ch.first = f0 + c * C;
       ch.end = min(ch.first + C, nb);
-      if (table == nullptr) break;  // the table needs every pass
+      done = table == nullptr;  // the table needs every pass
     }
     P += __shfl(incl, 63);
+    return done;
+  };
+  if (B <= 64) {
+    // one read of the lengths serves both the tile count and the search
+    const int L = lane < B ? clamp_len(seq_lens[lane], max_seq_len) : 0;
+    const Span sp = visible_tiles(L, Tq, window);
+    const int T = wave_sum_i(sp.end - sp.first);
+    const int C = (T + NW - 1) / NW;
+    pass(0, L, C > kMinTilesPerSplit ? C : kMinTilesPerSplit);
+  } else {
+    const int C = chunk_tiles(seq_lens, B, max_seq_len, NW, Tq, window, lane);
+    for (int base = 0; base < B; base += 64) {
+      const int i = base + lane;
+      if (pass(base, i < B ? clamp_len(seq_lens[i], max_seq_len) : 0, C)) break;
+    }
   }
   ch.b = __builtin_amdgcn_readfirstlane(ch.b);
   ch.first = __builtin_amdgcn_readfirstlane(ch.first);

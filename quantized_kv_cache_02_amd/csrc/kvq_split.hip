@@ -295,26 +295,46 @@ struct TableRegs {
 };
 static_assert(kTableRegs == 4, "TableRegs holds four registers");
 
-__device__ __forceinline__ int tile_row16(const SplitArgs& a, int b, int hkv, int t0, int waves,
-                                          int j, int lane) {
-  const int64_t t = (int64_t)t0 + (int64_t)waves * (64 * j + lane);
-  const int64_t tok0 = t * kTile;
-  const int64_t bs = a.c.block_size;
-  int64_t blk = b, off = tok0 < bs ? tok0 : 0;  // (tiles past a contiguous sequence read nothing)
-  if (a.c.block_table != nullptr) {
-    int64_t idx = tok0 / bs;
-    idx = idx < a.c.max_blocks ? idx : a.c.max_blocks - 1;  // dead tiles stay in range
-    blk = a.c.block_table[(size_t)b * a.c.max_blocks + idx];
-    off = tok0 % bs;
+// The block-table reads of a wavefront's tiles are issued first (TableLoads:
+// the block of each tile and its 16-row group inside the block), the rows
+// computed once they land (finish), so that other loads can be issued in
+// between.  All in 32 bits: the host bounds the pool to 2^31 groups of 16
+// rows, and tile indices stay below 2^27.
+struct TableLoads {
+  int blk[kTableRegs];  // the tile's block (contiguous: the sequence's)
+  int in[kTableRegs];   // its 16-row group inside the block
+};
+
+__device__ __forceinline__ TableLoads table_issue(const SplitArgs& a, int b, int t0, int waves, int lane) {
+  TableLoads tl;
+  const uint32_t bs16 = (uint32_t)a.c.block_size >> 4;
+#pragma unroll
+  for (int j = 0; j < kTableRegs; ++j) {
+    const uint32_t t = (uint32_t)t0 + (uint32_t)(waves * (64 * j + lane));
+    if (a.c.block_table != nullptr) {
+      uint32_t idx = t / bs16;
+      tl.in[j] = (int)(t - idx * bs16);
+      idx = idx < (uint32_t)a.c.max_blocks ? idx : (uint32_t)a.c.max_blocks - 1;  // dead tiles stay in range
+      tl.blk[j] = a.c.block_table[(size_t)b * a.c.max_blocks + idx];
+    } else {
+      tl.blk[j] = b;
+      tl.in[j] = t < bs16 ? (int)t : 0;  // (tiles past a contiguous sequence read nothing)
+    }
   }
-  if ((uint64_t)blk >= (uint64_t)a.c.num_blocks) return -1;
-  return (int)(((blk * a.c.Hkv + hkv) * bs + off) / kTile);
+  return tl;
 }
 
-__device__ __forceinline__ TableRegs load_table(const SplitArgs& a, int b, int hkv, int t0, int waves,
-                                                int lane) {
-  return TableRegs{tile_row16(a, b, hkv, t0, waves, 0, lane), tile_row16(a, b, hkv, t0, waves, 1, lane),
-                   tile_row16(a, b, hkv, t0, waves, 2, lane), tile_row16(a, b, hkv, t0, waves, 3, lane)};
+__device__ __forceinline__ TableRegs table_finish(const SplitArgs& a, int hkv, const TableLoads& tl) {
+  const uint32_t bs16 = (uint32_t)a.c.block_size >> 4;
+  int e[kTableRegs];
+#pragma unroll
+  for (int j = 0; j < kTableRegs; ++j) {
+    const uint32_t blk = (uint32_t)tl.blk[j];
+    e[j] = blk >= (uint32_t)a.c.num_blocks
+               ? -1
+               : (int)((blk * (uint32_t)a.c.Hkv + (uint32_t)hkv) * bs16 + (uint32_t)tl.in[j]);
+  }
+  return TableRegs{e[0], e[1], e[2], e[3]};
 }
 
 // Value of the wavefront's k-th tile (k wave-uniform, k < kTableRegs * 64 for
@@ -1168,10 +1188,11 @@ __device__ __forceinline__ void row_window(const SplitArgs& a, int L, int row, b
 
 // This workgroup's chunk under the balanced schedule -- sequence b (length L)
 // and its tiles [tb, te) -- the same for every wavefront; false for an idle
-// slot.  load_q(b) issues the query loads as soon as the sequence is known
-// (one sequence: chunk = slot, and the loads go out before the length
-// arrives).  `record`: this wavefront also writes every sequence's chunk slots
-// for the combine.
+// slot.  With one sequence load_q(0) issues the query loads at once (chunk =
+// slot: they go out before the length arrives); with several the caller
+// issues them once the sequence is known, after the block-table reads.
+// `record`: this wavefront also writes every sequence's chunk slots for the
+// combine.
 template <class LoadQ>
 __device__ __forceinline__ bool workgroup_chunk(const SplitArgs& a, int slot, bool record, int lane,
                                                 LoadQ&& load_q, int& b, int& L, int& tb, int& te) {
@@ -1192,7 +1213,6 @@ __device__ __forceinline__ bool workgroup_chunk(const SplitArgs& a, int slot, bo
   L = ch.L;
   tb = ch.first;
   te = ch.end;
-  load_q(b);
   return true;
 }
 
@@ -1356,13 +1376,18 @@ split_decode_kernel(SplitArgs a) {
   if (!workgroup_chunk(a, slot, slot == 0 && hkv == 0 && rbi == 0 && wave == 0, lane, load_q, b, L, tb,
                        te))
     return;
+  const int t0 = tb + wave;  // the wavefront's tiles are t0, t0 + 4, ...
+  // The block-table reads of its tiles go out first: loads return in order,
+  // so the first tile loads, which need them, wait for nothing issued after
+  // them (a batch's query rows, the new rows, the scales).
+  const TableLoads tl = table_issue(a, b, t0, kWaves, lane);
+  if (a.B > 1) load_q(b);
 
   // ---- fused append: the wavefront that will read the tile holding a new
   // position quantizes and stores that row (the same arithmetic as
   // kvq_append) and waits for its stores before it issues the load of that
   // tile.  No other wavefront of the workgroup reads those rows.  Position
   // L - Tq + j holds query token j's row.
-  const int t0 = tb + wave;  // the wavefront's tiles are t0, t0 + 4, ...
   bool mine[kMaxQTokens];    // wave-uniform
   bool any_mine = false, early_hit = false;
 #pragma unroll
@@ -1393,7 +1418,7 @@ split_decode_kernel(SplitArgs a) {
   // issued unconditionally (tiles past the split read nothing).  A wavefront
   // whose first tiles hold a new row appends first; any other appends after
   // issuing them, so the stores overlap the loads.
-  const TableRegs tbl = load_table(a, b, hkv, t0, kWaves, lane);
+  const TableRegs tbl = table_finish(a, hkv, tl);
   Tile<DT, D> buf[NB];
   // (the loads stay at one program point, so the compiler's waits for them
   // remain exact on the path every wavefront but one takes)

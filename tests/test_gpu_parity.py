@@ -329,6 +329,17 @@ def test_balanced_schedule_ragged(lens):
     gu.run_and_check(w, f"balanced lens={lens}")
 
 
+@pytest.mark.parametrize("B,Tq", [(64, 1), (65, 2), (130, 1)])
+def test_balanced_schedule_around_64_sequences(B, Tq):
+    """Up to 64 sequences one read of the lengths serves the chunk size and the
+    search; past 64 they are taken in passes of 64 (one per lane).  Paged."""
+    lens = [int(x) for x in np.random.default_rng(B + Tq).integers(0, 400, B)]
+    lens[B // 2] = 3000  # one long sequence: several chunks
+    w = ki.random_workload(4600 + B + Tq, B=B, Hkv=2, G=2, D=64, Tq=Tq, lens=lens, dtype=INT8,
+                           mode=PER_ROW, block_size=16, sink=B % 2 == 0)
+    gu.run_and_check(w, f"{B} sequences, Tq {Tq}")
+
+
 def test_balanced_schedule_many_sequences():
     """More sequences than lanes: the schedule's sums run over several passes."""
     rng = np.random.default_rng(4600)
