@@ -12,15 +12,19 @@
 //   M = max_s m_s,  w_s = l_s 2^(m_s - M),  L = sum_s w_s,  o = sum_s w_s o_s / L,
 //   lse = ln 2 (M + log2 L).
 //
-// One workgroup per (sequence, KV head, query row, 64 channels).  It first
-// locates the sequence's chunk slots (recorded by the decode kernel), then
-// its 256 threads -- 16 channel quads x 16 split groups -- issue the loads of
-// their splits' m and l and of the first batch of partial outputs before using
-// any (one round trip to the cache hierarchy: a second one, for l after the
-// maximum, cost 0.7 us of a 4.6 us combine at 64 splits), and the 16 groups
-// are summed in group order through LDS.  Every sum runs in the same order on
-// every call.  The batch loads stay unconditional (clamped to slot 0): guarding
-// them with the split count made the combine 1 us slower.
+// One workgroup per (sequence, KV head, query row, 64 channels) of W = 1 or 4
+// wavefronts: 16 channel quads x 4 W split groups.  It first locates the
+// sequence's chunk slots (recorded by the decode kernel); then every thread
+// issues the loads of its splits' m and l and of the first batch of partial
+// outputs before using any (one round trip to the cache hierarchy), the
+// weights follow, and the split groups are summed in group order -- across
+// lanes, and with 4 wavefronts through LDS.  Every sum runs in the same order
+// on every call.  The batch loads stay unconditional (clamped to slot 0).
+// One wavefront has no barrier but covers 64 splits per round trip, 4 cover
+// 128: the host takes one where the grid alone fills the CUs and a row has at
+// most 64 partials (measured on MI355X: workload 5 step 76.3 -> 74.2 us; the
+// int8 64K step, 96 workgroups, 0.1 us slower with one; int4 64K, 128
+// partials, 1.8 us slower).
 
 #include "kvq_device.h"
 #include "kvq_sched.h"  // clamp_len
@@ -29,15 +33,15 @@ namespace kvq {
 namespace {
 
 constexpr int kMaxSplits = 4096;
-constexpr int kGroups = 16;   // split groups per workgroup
-constexpr int kQuads = 16;    // 4-channel columns per workgroup (64 channels)
-constexpr int kBatch = 8;     // loads issued back to back per thread
+constexpr int kQuads = 16;  // 4-channel columns per workgroup (64 channels)
 
-template <int MODE, int D>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  extern __shared__ float w_s[];  // [SMAX] chunk weights
-  __shared__ float red[4];
-  __shared__ float4_t part[kGroups][kQuads];
+template <int MODE, int D, int W>
+__global__ __launch_bounds__(64 * W) void combine_kernel(CombineArgs a) {
+  constexpr int kGroups = 4 * W;           // split groups
+  constexpr int kBatch = W == 1 ? 16 : 8;  // loads issued back to back per thread
+  extern __shared__ float w_s[];           // [SMAX] chunk weights
+  __shared__ float red[W];
+  __shared__ float4_t part[W > 1 ? kGroups : 1][kQuads];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int quad = tid % kQuads, grp = tid / kQuads;
@@ -67,6 +71,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
   // Split tid's m and l, then the first batch of partial outputs (which does
   // not depend on the split maxima): all in one round trip.
+  constexpr int NT = 64 * W;
   const int sm = tid < Sld ? tid : 0;
   const float m0 = ms[sm], l0 = ls[sm];
   const float* os = a.ws_o + rowbase * D + d;
@@ -84,16 +89,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     S = min((nt + C - 1) / C, Sld);
   }
 
-  // M: per-thread max over s = tid, tid+256, ..., then waves, then in wave order
+  // M: per-thread max over s = tid, tid + NT, ..., then waves, then in wave order
   float M = tid < S ? m0 : -INFINITY;
-  for (int s = tid + 256; s < S; s += 256) M = fmaxf(M, ms[s]);
+  for (int s = tid + NT; s < S; s += NT) M = fmaxf(M, ms[s]);
   M = wave_max(M);
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
+  if constexpr (W > 1) {
+    if (lane == 0) red[wave] = M;
+    __syncthreads();
+    M = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) M = fmaxf(M, red[w]);
+    __syncthreads();
+  }
   float part_l = 0.0f;
-  for (int s = tid; s < S; s += 256) {
+  for (int s = tid; s < S; s += NT) {
     const float m = s == tid ? m0 : ms[s], l = s == tid ? l0 : ls[s];
     const float w = (M == -INFINITY || l == 0.0f) ? 0.0f : l * exp2f(m - M);
     w_s[s] = w;
@@ -101,11 +110,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) part_l += __shfl_xor(part_l, o);
-  if (lane == 0) red[wave] = part_l;
-  __syncthreads();
-  const float Lsum = ((red[0] + red[1]) + red[2]) + red[3];
+  float Lsum = part_l;
+  if constexpr (W > 1) {
+    if (lane == 0) red[wave] = part_l;
+    __syncthreads();  // (also publishes w_s to the other wavefronts)
+    Lsum = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) Lsum += red[w];
+  }
 
-  // weighted sum of this thread's splits s = grp, grp + 16, ... in order
+  // weighted sum of this thread's splits s = grp, grp + kGroups, ... in order
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < kBatch; ++i) {
@@ -125,13 +139,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       if (s < S) acc += w_s[s] * v[i];
     }
   }
-  part[grp][quad] = acc;
-  __syncthreads();
-  if (grp != 0) return;
-
-  float4_t o = part[0][quad];
+  float4_t o;
+  if constexpr (W == 1) {
 #pragma unroll
-  for (int g2 = 1; g2 < kGroups; ++g2) o += part[g2][quad];
+    for (int e = 0; e < 4; ++e) o[e] = group_sum4(acc[e]);  // the 4 groups, across lanes
+    if (grp != 0) return;
+  } else {
+    part[grp][quad] = acc;
+    __syncthreads();
+    if (grp != 0) return;
+    o = part[0][quad];
+#pragma unroll
+    for (int g2 = 1; g2 < kGroups; ++g2) o += part[g2][quad];
+  }
+
   float f = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
   const int jq = r / a.G, gh = r % a.G;
   const int h = hkv * a.G + gh;
@@ -151,17 +172,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.Tq + jq) * a.Hq + h) * D + d) = packed;
 }
 
+template <int MODE, int W>
+hipError_t launch_waves(int D, const CombineArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  switch (D) {
+    case 64: hipLaunchKernelGGL((combine_kernel<MODE, 64, W>), grid, dim3(64 * W), lds, st, a); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<MODE, 128, W>), grid, dim3(64 * W), lds, st, a); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<MODE, 256, W>), grid, dim3(64 * W), lds, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_mode(int D, const CombineArgs& a, dim3 grid, hipStream_t st) {
   if (a.SMAX < 1 || a.SMAX > kMaxSplits) return hipErrorInvalidValue;
   const size_t lds = (size_t)a.SMAX * sizeof(float);
-  switch (D) {
-    case 64: hipLaunchKernelGGL((combine_kernel<MODE, 64>), grid, dim3(256), lds, st, a); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<MODE, 128>), grid, dim3(256), lds, st, a); break;
-    case 256: hipLaunchKernelGGL((combine_kernel<MODE, 256>), grid, dim3(256), lds, st, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  // one wavefront per workgroup where the grid alone fills the CUs and every
+  // row has at most 64 partials (one round trip for one wavefront)
+  const bool one = (int64_t)grid.x * grid.y * grid.z >= kNumCUs && a.SMAX <= 64;
+  return one ? launch_waves<MODE, 1>(D, a, grid, lds, st) : launch_waves<MODE, 4>(D, a, grid, lds, st);
 }
 
 
