@@ -21,10 +21,8 @@
 // lanes, and with 4 wavefronts through LDS.  Every sum runs in the same order
 // on every call.  The batch loads stay unconditional (clamped to slot 0).
 // One wavefront has no barrier but covers 64 splits per round trip, 4 cover
-// 128: the host takes one where the grid alone fills the CUs and a row has at
-// most 64 partials (measured on MI355X: workload 5 step 76.3 -> 74.2 us; the
-// int8 64K step, 96 workgroups, 0.1 us slower with one; int4 64K, 128
-// partials, 1.8 us slower).
+// 128.  A third form (combine16_kernel) gives one wavefront 16 channels, for
+// grids too small to fill the CUs; launch_mode picks among them.
 
 #include "kvq_device.h"
 #include "kvq_sched.h"  // clamp_len
@@ -172,6 +170,102 @@ __global__ __launch_bounds__(64 * W) void combine_kernel(CombineArgs a) {
   *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.Tq + jq) * a.Hq + h) * D + d) = packed;
 }
 
+// One wavefront per (sequence, KV head, query row, 16 channels): its lanes are
+// 4 channel quads x 16 split groups.  Every lane loads the m, l and partial
+// output of its splits s = group + 16 i (all of them in one round trip for up
+// to 128 partials), and the split groups are summed across lanes in a fixed
+// order: no LDS and no barrier.
+template <int MODE, int D>
+__global__ __launch_bounds__(64) void combine16_kernel(CombineArgs a) {
+  constexpr int kG = 16;  // split groups
+  constexpr int kB = 8;   // partials per lane in the first round trip
+  const int lane = threadIdx.x;
+  const int quad = lane & 3, grp = lane >> 2;
+  const int d = blockIdx.x * 16 + quad * 4;
+  const int r = blockIdx.y;
+  const int head = blockIdx.z;  // b * Hkv + hkv
+  const int b = head / a.Hkv, hkv = head % a.Hkv;
+  const int L0 = a.seq_lens[0];
+  int P, Sld;
+  if (a.B == 1) {
+    P = 0;
+    Sld = min(a.S, a.SMAX);
+  } else {
+    const int Sb = a.chunks[2 * b + 1];
+    Sld = min(Sb, a.SMAX);  // the host bounds every S_b by SMAX
+    P = Sld > 0 ? a.chunks[2 * b] : 0;
+  }
+  const size_t rowbase = ((size_t)hkv * a.R + r) * a.S + P;
+  const float* ms = a.ws_m + rowbase;
+  const float* ls = a.ws_l + rowbase;
+  const float* os = a.ws_o + rowbase * D + d;
+  float mv[kB], lv[kB];
+  float4_t v0[kB];
+#pragma unroll
+  for (int i = 0; i < kB; ++i) {
+    const int s = grp + kG * i;
+    const int sc = s < Sld ? s : 0;
+    mv[i] = ms[sc];
+    lv[i] = ls[sc];
+    v0[i] = *reinterpret_cast<const float4_t*>(os + (size_t)sc * D);
+  }
+  int S = Sld;
+  if (a.B == 1) {
+    const Span sp = visible_tiles(clamp_len(L0, a.max_seq_len), a.Tq, a.window);
+    const int nt = sp.end - sp.first;
+    const int C = max((nt + a.NW - 1) / a.NW, kMinTilesPerSplit);
+    S = min((nt + C - 1) / C, Sld);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kB; ++i)
+    if (grp + kG * i < S) M = fmaxf(M, mv[i]);
+  for (int s = grp + kG * kB; s < S; s += kG) M = fmaxf(M, ms[s]);
+  M = wave_max(M);
+  float lsum = 0.0f;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kB; ++i) {
+    if (grp + kG * i < S) {
+      const float w = (M == -INFINITY || lv[i] == 0.0f) ? 0.0f : lv[i] * exp2f(mv[i] - M);
+      lsum += w;
+      acc += w * v0[i];
+    }
+  }
+  for (int s = grp + kG * kB; s < S; s += kG) {
+    const float l = ls[s];
+    const float w = (M == -INFINITY || l == 0.0f) ? 0.0f : l * exp2f(ms[s] - M);
+    lsum += w;
+    acc += w * *reinterpret_cast<const float4_t*>(os + (size_t)s * D);
+  }
+  // the 16 split groups (lane bits 2..5); the 4 quads hold the same weights
+#pragma unroll
+  for (int o = 4; o < 64; o <<= 1) {
+    lsum += __shfl_xor(lsum, o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], o);
+  }
+  if (grp != 0) return;
+  const float Lsum = lsum;
+  float f = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+  const int jq = r / a.G, gh = r % a.G;
+  const int h = hkv * a.G + gh;
+  if (a.sink != nullptr && Lsum > 0.0f) {
+    const float lse = 0.6931471805599453f * (M + log2f(Lsum));
+    f *= 1.0f / (1.0f + expf(a.sink[h] - lse));
+  }
+  uint16_t ob[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float x = acc[e] * f;
+    if constexpr (MODE == kPerTensor) x *= a.v_static[0];
+    if constexpr (MODE == kPerChannel) x *= a.v_static[(size_t)hkv * D + d + e];
+    ob[e] = f32_to_bf16(x);
+  }
+  u32x2_t packed = {(uint32_t)ob[0] | ((uint32_t)ob[1] << 16), (uint32_t)ob[2] | ((uint32_t)ob[3] << 16)};
+  *reinterpret_cast<u32x2_t*>(a.out + (((size_t)b * a.Tq + jq) * a.Hq + h) * D + d) = packed;
+}
+
 template <int MODE, int W>
 hipError_t launch_waves(int D, const CombineArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   switch (D) {
@@ -184,13 +278,32 @@ hipError_t launch_waves(int D, const CombineArgs& a, dim3 grid, size_t lds, hipS
 }
 
 template <int MODE>
+hipError_t launch_16(int D, const CombineArgs& a, dim3 grid, hipStream_t st) {
+  const dim3 g16(D / 16, grid.y, grid.z);
+  switch (D) {
+    case 64: hipLaunchKernelGGL((combine16_kernel<MODE, 64>), g16, dim3(64), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((combine16_kernel<MODE, 128>), g16, dim3(64), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((combine16_kernel<MODE, 256>), g16, dim3(64), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int MODE>
 hipError_t launch_mode(int D, const CombineArgs& a, dim3 grid, hipStream_t st) {
   if (a.SMAX < 1 || a.SMAX > kMaxSplits) return hipErrorInvalidValue;
   const size_t lds = (size_t)a.SMAX * sizeof(float);
-  // one wavefront per workgroup where the grid alone fills the CUs and every
-  // row has at most 64 partials (one round trip for one wavefront)
-  const bool one = (int64_t)grid.x * grid.y * grid.z >= kNumCUs && a.SMAX <= 64;
-  return one ? launch_waves<MODE, 1>(D, a, grid, lds, st) : launch_waves<MODE, 4>(D, a, grid, lds, st);
+  // Rows with at most 64 partials: one wavefront per 16 channels where the
+  // 64-channel grid leaves CUs idle, one per 64 where it fills them; more
+  // partials: four wavefronts per 64 channels.  Measured on MI355X, step us:
+  // int8 at 64K (96 workgroups of 64 channels) 29.34 with four wavefronts,
+  // 29.10 with one per 16 channels; workload 5 (3,072) 73.8 with one per 64,
+  // 76.7 with one per 16; int4 at 64K (128 partials) 22.16 with four, 22.45
+  // with one per 16, 24.4 with one per 64.
+  const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+  if (a.SMAX <= 64 && wgs < kNumCUs) return launch_16<MODE>(D, a, grid, st);
+  if (a.SMAX <= 64) return launch_waves<MODE, 1>(D, a, grid, lds, st);
+  return launch_waves<MODE, 4>(D, a, grid, lds, st);
 }
 
 
