@@ -4,7 +4,10 @@
 // into a HIP graph.
 
 #include <algorithm>
+#include <functional>
 #include <mutex>
+#include <queue>
+#include <vector>
 
 #include "kvq.h"
 
@@ -229,12 +232,17 @@ hipError_t dispatch_split(int dt, int md, bool vrow, int D, int RB, const kvq::S
 // the row rate for int4, 1.63x for bf16).  When the workgroups do not fill
 // whole rounds of 256 CUs (384 for 2K query tokens at 24 / 4 heads: a second
 // round half empty), the tiles of each are cut into KS parts, one workgroup
-// each, and a combine merges the parts.  Cost model per (W, KS): rounds of
-// one workgroup per CU times (tiles per part + 4 tiles of per-workgroup
-// overhead), times 0.8 for W = 4; KS only where the workspace is given, each
-// part keeping at least 8 tiles; a larger KS must beat a smaller one by 3 %
-// per step.  A pure function of the shape, so workspaces sized once stay
-// valid.
+// each, and a combine merges the parts.  Cost model per (W, KS): a
+// workgroup costs its part's tiles + 4 tiles of per-workgroup overhead, times
+// 0.8 for W = 4, and the kernel the makespan of the workgroups dealt longest
+// first to the least loaded of 256 CUs, as the kernel orders them (causal
+// rows see different tile counts: with no cached context a 2,048-token chunk
+// ran 330 TFLOP/s in two parts and 417 in one, which a model of whole rounds
+// of the longest workgroup had ranked the other way); past 16 rounds, rounds
+// of the longest workgroup.  KS only where the workspace is given, each part
+// keeping at least 8 tiles; a larger KS must beat a smaller one by 3 % per
+// step, and one that breaks the kernel's XCD grouping (below) by 10 %.  A
+// pure function of the shape, so workspaces sized once stay valid.
 struct PrefillPlan {
   int W, KS;
 };
@@ -243,21 +251,60 @@ PrefillPlan prefill_plan(const kvq_cache* c, int32_t batch, int G, int32_t tq, i
                          int32_t window, bool split) {
   const int D = c->head_dim;
   const int64_t R = (int64_t)G * tq;
-  int64_t tiles = ((int64_t)max_seq_len + 63) / 64;  // a workgroup sees at most these
+  const int64_t L = max_seq_len, pos0 = L - tq;  // position of the chunk's first token
+  int64_t tiles = (L + 63) / 64;  // a workgroup sees at most these
   PrefillPlan best{4, 1};
   double best_cost = 0.0;
   bool first = true;
+  std::vector<double> work;
   for (int W : {4, 8}) {
     if (W == 8 && D != 256) continue;
     const int64_t rows = 16 * (D >= 256 ? 1 : 2) * W;
+    const int64_t nrg = (R + rows - 1) / rows;
+    const double wgf = W == 4 ? 0.8 : 1.0;
     int64_t t = tiles;
     if (window > 0) t = std::min<int64_t>(t, ((int64_t)window + rows / G + 63) / 64 + 1);
     for (int ks = 1; ks <= (split ? kvq::kPrefillMaxParts : 1); ++ks) {
       if (ks > 1 && t < (int64_t)ks * 8) break;
-      const int64_t items = (R + rows - 1) / rows * c->num_kv_heads * batch * ks;
-      const int64_t rounds = (items + kvq::kNumCUs - 1) / kvq::kNumCUs;
-      double cost = (double)rounds * ((double)t / ks + 4.0) * (W == 4 ? 0.8 : 1.0);
+      const int64_t copies = (int64_t)c->num_kv_heads * batch;
+      const int64_t items = nrg * copies * ks;
+      double cost;
+      if (items > 16 * (int64_t)kvq::kNumCUs) {
+        const int64_t rounds = (items + kvq::kNumCUs - 1) / kvq::kNumCUs;
+        cost = (double)rounds * ((double)t / ks + 4.0) * wgf;
+      } else {
+        // the tiles each row group's rows see (as the kernel bounds them)
+        work.clear();
+        for (int64_t g = 0; g < nrg; ++g) {
+          const int64_t rlast = std::min((g + 1) * rows, R) - 1;
+          const int64_t hi = std::min(pos0 + rlast / G, L - 1);
+          const int64_t end = hi >= 0 ? hi / 64 + 1 : 0;
+          int64_t begin = 0;
+          if (window > 0) begin = std::max<int64_t>(pos0 + g * rows / G - window + 1, 0) / 64;
+          const int64_t tg = std::max<int64_t>(end - begin, 0);
+          const int64_t C = (tg + ks - 1) / ks;
+          for (int p = 0; p < ks; ++p) {
+            const int64_t tp = std::min(std::max<int64_t>(tg - p * C, 0), C);
+            for (int64_t k = 0; k < copies; ++k) work.push_back(((double)tp + 4.0) * wgf);
+          }
+        }
+        std::sort(work.begin(), work.end(), std::greater<double>());
+        std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+        for (int i = 0; i < kvq::kNumCUs; ++i) cu.push(0.0);
+        double span = 0.0;
+        for (double w : work) {
+          const double e = cu.top() + w;
+          cu.pop();
+          cu.push(e);
+          span = std::max(span, e);
+        }
+        cost = span;
+      }
       cost *= 1.0 + 0.03 * (ks - 1);
+      // the kernel keeps each XCD on the same (KV head, part) pairs only when
+      // KS * Hkv divides 8 or 8 divides it; other splits lose that L2 reuse
+      const int64_t hp = (int64_t)ks * c->num_kv_heads;
+      if (ks > 1 && 8 % hp != 0 && hp % 8 != 0) cost *= 1.1;
       if (first || cost < best_cost) {
         best = PrefillPlan{W, ks};
         best_cost = cost;
