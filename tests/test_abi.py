@@ -188,11 +188,15 @@ def test_prefill_workspace_follows_the_round_model():
     D 256 and a 2,048-token chunk after 16,384 cached tokens make 384 workgroups
     of 128 rows (one round of 256 CUs and a half-empty second); two parts each
     fill exactly three rounds.  1,024 tokens after 32,768: 192 workgroups, four
-    parts (768, three full rounds).  A context of 8 tiles does not split (no
-    part would keep 8); an invalid shape reports 0."""
+    parts (768, three full rounds).  A first 2,048-token chunk (no cached
+    context) does not split: its causal rows see 1 to 32 tiles, and the 384
+    whole workgroups dealt longest first end sooner than 768 halves.  A context
+    of 8 tiles does not split (no part would keep 8); an invalid shape reports
+    0."""
     c = _cache(block_size=65536)
     R = 6 * 2048
     assert _prefill_ws(c) == _prefill_rows_bytes(4 * R * 2, 256)
+    assert _prefill_ws(c, tq=2048, msl=2048) == 0
     assert _prefill_ws(c, tq=1024, msl=33792) == _prefill_rows_bytes(4 * 6 * 1024 * 4, 256)
     # a one-token chunk: 4 workgroups, each split into the 8 parts allowed
     assert _prefill_ws(c, tq=1, msl=4096) == _prefill_rows_bytes(4 * 6 * 8, 256)
