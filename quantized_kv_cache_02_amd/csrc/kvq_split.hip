@@ -8,7 +8,9 @@
 // with on-the-fly dequantization):
 //   * one workgroup owns (sequence b, KV head, split s) and serves every query
 //     row of that KV head -- the G grouped query heads times the Tq query
-//     tokens -- from a single pass over the split's cached rows;
+//     tokens -- from a single pass over the split's cached rows (past 768
+//     accumulator columns, two workgroups share the rows, reading the split
+//     through one L2);
 //   * its 4 wavefronts take interleaved 16-token tiles and keep private
 //     online-softmax state (max, sum, accumulator) with no barrier or atomic in
 //     the loop; the wavefronts merge once at the end in a fixed order and the
